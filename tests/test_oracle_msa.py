@@ -1,0 +1,225 @@
+"""Pins of the oracle's layer step against things other than itself:
+brute-force loops and subset enumeration on tiny inputs, torch's CPU fp64
+scaled_dot_product_attention (dense causal attention, and masked attention
+built from a selection), closed forms (q = 0, L = 1), page-order invariance,
+and the invariants the source pages state (own block kept, <= 16 blocks,
+<= 2,048 keys)."""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa as M
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
+SCALE = 1.0 / np.sqrt(128.0)
+
+
+def test_page_constants():
+    assert M.BLOCK == GOLD["block_tokens"]["value"]
+    assert M.TOPK == GOLD["selected_blocks"]["value"]
+    assert M.MAX_KEYS == GOLD["max_keys_per_query"]["value"]
+
+
+def test_indexer_scores_and_pool_brute_force():
+    rng = np.random.default_rng(3)
+    for L, T in [(1, 1), (130, 1), (300, 3), (257, 2), (128, 1), (129, 4)]:
+        G, D = 4, 8
+        q = rng.normal(size=(T, G, D))
+        k = rng.normal(size=(L, D))
+        s = M.indexer_token_scores(q, k, L, T)
+        S = M.block_max_pool(s, L)
+        nb = (L + 127) // 128
+        assert S.shape == (T, G, nb)
+        for t in range(T):
+            p = L - T + t
+            for g in range(G):
+                for j in range(L):
+                    want = sum(q[t, g, d] * k[j, d] for d in range(D)) if j <= p else -np.inf
+                    assert s[t, g, j] == pytest.approx(want, abs=1e-12) or (want == -np.inf and s[t, g, j] == -np.inf)
+                for i in range(nb):
+                    vals = [s[t, g, j] for j in range(i * 128, min((i + 1) * 128, L)) if j <= p]
+                    want = max(vals) if vals else -np.inf
+                    assert S[t, g, i] == want
+
+
+def brute_select(S, own, k=16):
+    """Enumerate every candidate subset; keep the one with the largest score
+    sum, then the smallest index sum (ties go to lower block ids)."""
+    if own + 1 <= k:
+        return list(range(own + 1))
+    best = None
+    for sub in itertools.combinations(range(own), k - 1):
+        key = (sum(S[i] for i in sub), -sum(sub))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return sorted(list(best[1]) + [own])
+
+
+@pytest.mark.parametrize("nb", [1, 5, 16, 17, 18, 19, 20])
+def test_selection_matches_subset_enumeration(nb):
+    rng = np.random.default_rng(nb)
+    for trial in range(3):
+        S = np.round(rng.normal(size=nb), 1 if trial == 2 else 6)      # trial 2: many exact ties
+        for own in sorted({nb - 1, max(0, nb - 3)}):
+            sel = M.select_blocks(S, own)
+            got = [int(i) for i in sel if i >= 0]
+            assert got == brute_select(S, own)
+            assert list(sel[len(got):]) == [-1] * (16 - len(got))
+
+
+def test_selection_invariants_random_rows():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        nb = int(rng.integers(1, 400))
+        own = int(rng.integers(0, nb))
+        S = rng.normal(size=nb)
+        S[own + 1:] = -np.inf
+        sel = M.select_blocks(S, own)
+        got = [int(i) for i in sel if i >= 0]
+        assert own in got                                      # most recent block kept
+        assert len(got) == min(16, own + 1)                    # <= 16 blocks
+        assert got == sorted(got) and len(set(got)) == len(got)
+        p = own * 128 + int(rng.integers(0, 128))
+        assert len(M.attended_keys(sel, p)) <= GOLD["max_keys_per_query"]["value"]
+        # every unselected older block scores no higher than every selected one
+        others = [i for i in range(own) if i not in got]
+        chosen = [i for i in got if i != own]
+        if others and chosen:
+            assert max(S[others]) <= min(S[chosen])
+
+
+def test_near_tie_flag():
+    S = np.arange(40, dtype=float)[::-1].copy()       # strictly decreasing
+    assert not M.near_tie(S, 39)
+    S[14] = S[15] * (1 + 5e-6)                          # ranks 16/17 overall
+    assert M.near_tie(S, 39)
+    assert not M.near_tie(S, 10)                        # <= 16 visible blocks
+
+
+def sdpa_masked(q, K, V, mask):
+    """torch fp64 SDPA with GQA expanded; mask [T, L] True = attend."""
+    T, H, D = q.shape
+    G = K.shape[0]
+    Kx = torch.tensor(K).repeat_interleave(H // G, dim=0)          # [H, L, D]
+    Vx = torch.tensor(V).repeat_interleave(H // G, dim=0)
+    qq = torch.tensor(q).permute(1, 0, 2)                           # [H, T, D]
+    m = torch.tensor(mask)[None].expand(H, -1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qq, Kx, Vx, attn_mask=m, scale=SCALE)
+    logits = (qq @ Kx.transpose(-1, -2)) * SCALE
+    lse = torch.logsumexp(logits.masked_fill(~m, -float("inf")), dim=-1)
+    return o.permute(1, 0, 2).numpy(), lse.T.numpy()
+
+
+@pytest.mark.parametrize("L,T", [(1, 1), (77, 1), (128, 1), (1000, 1), (2048, 1), (2048, 4), (1500, 7)])
+def test_short_context_equals_dense_causal_attention(L, T):
+    rng = np.random.default_rng(L + T)
+    G, H, D = 4, 64, 128
+    idx_q = rng.normal(size=(T, G, D))
+    idx_k = rng.normal(size=(L, D))
+    q = rng.normal(size=(T, H, D))
+    K = rng.normal(size=(G, L, D))
+    V = rng.normal(size=(G, L, D))
+    r = M.layer_step(idx_q, idx_k, q, K, V, L, T, SCALE)
+    pos = np.arange(L - T, L)
+    mask = np.arange(L)[None, :] <= pos[:, None]
+    o, lse = sdpa_masked(q, K, V, mask)
+    assert np.abs(r["out"] - o).max() < 1e-12
+    assert np.abs(r["lse"] - lse).max() < 1e-12
+
+
+def test_sparse_attention_equals_masked_sdpa_from_selection():
+    rng = np.random.default_rng(11)
+    G, H, D, L, T = 4, 64, 128, 128 * 40 + 55, 3
+    idx_q = rng.normal(size=(T, G, D))
+    idx_k = rng.normal(size=(L, D))
+    q = rng.normal(size=(T, H, D))
+    K = rng.normal(size=(G, L, D))
+    V = rng.normal(size=(G, L, D))
+    r = M.layer_step(idx_q, idx_k, q, K, V, L, T, SCALE)
+    for g in range(G):
+        mask = np.zeros((T, L), dtype=bool)
+        for t in range(T):
+            p = L - T + t
+            for i in r["sel"][t, g]:
+                if i >= 0:
+                    mask[t, i * 128:(i + 1) * 128] = True
+            mask[t, p + 1:] = False
+        o, lse = sdpa_masked(q[:, g * 16:(g + 1) * 16], K[g:g + 1], V[g:g + 1], mask)
+        assert np.abs(r["out"][:, g * 16:(g + 1) * 16] - o).max() < 1e-12
+        assert np.abs(r["lse"][:, g * 16:(g + 1) * 16] - lse).max() < 1e-12
+        assert mask.sum(axis=1).max() <= 2048
+
+
+def test_closed_forms_zero_query_and_single_key():
+    rng = np.random.default_rng(12)
+    G, H, D, L, T = 4, 64, 128, 128 * 20 + 3, 1
+    idx_q = rng.normal(size=(T, G, D))
+    idx_k = rng.normal(size=(L, D))
+    K = rng.normal(size=(G, L, D))
+    V = rng.normal(size=(G, L, D))
+    r = M.layer_step(idx_q, idx_k, np.zeros((T, H, D)), K, V, L, T, SCALE)
+    for g in range(G):
+        keys = M.attended_keys(r["sel"][0, g], L - 1)
+        assert np.abs(r["out"][0, g * 16] - V[g, keys].mean(axis=0)).max() < 1e-12
+        assert r["lse"][0, g * 16] == pytest.approx(np.log(len(keys)), abs=1e-12)
+    r1 = M.layer_step(idx_q, idx_k[:1], rng.normal(size=(1, H, D)), K[:, :1], V[:, :1], 1, 1, SCALE)
+    for h in range(H):
+        assert np.array_equal(r1["out"][0, h], V[h // 16, 0])
+
+
+def test_paged_batch_is_invariant_to_page_order_and_matches_layer_step():
+    rng = np.random.default_rng(13)
+    G, H, D = 4, 64, 128
+    lens = [128 * 21 + 9, 128 * 5, 700]
+    T = 2
+    nbs = [(L + 127) // 128 for L in lens]
+    P = sum(nbs)
+    maxb = max(nbs)
+    pools = {w: rng.normal(size=(P, h, 128, D)).astype(np.float32) for w, h in [("i", 1), ("k", 4), ("v", 4)]}
+    idx_q = rng.normal(size=(3, T, G, D)).astype(np.float32)
+    q = rng.normal(size=(3, T, H, D)).astype(np.float32)
+    results = []
+    for order in [np.arange(P), rng.permutation(P)]:
+        table = np.full((3, maxb), -1, np.int32)
+        off = 0
+        for b, n in enumerate(nbs):
+            table[b, :n] = order[off:off + n]
+            off += n
+        inv = np.argsort(order)                     # logical slot -> which original page
+        caches = {w: {"dtype": "f32", "data": pools[w][inv], "tensor_scale": 1.0} for w in pools}
+        results.append(M.batch_layer(idx_q, q, caches["i"], caches["k"], caches["v"], np.array(lens),
+                                     table, T, SCALE))
+    for key in ["block_scores", "sel", "out", "lse"]:
+        a, b = results
+        assert np.array_equal(np.nan_to_num(a[key[:]], nan=7.0), np.nan_to_num(b[key], nan=7.0)), key
+    # and each sequence equals the unpaged layer step
+    off = 0
+    for b, L in enumerate(lens):
+        n = nbs[b]
+        ik = pools["i"][off:off + n, 0].reshape(-1, D)[:L]
+        K = pools["k"][off:off + n].transpose(1, 0, 2, 3).reshape(4, -1, D)[:, :L]
+        V = pools["v"][off:off + n].transpose(1, 0, 2, 3).reshape(4, -1, D)[:, :L]
+        ref = M.layer_step(idx_q[b], ik, q[b], K, V, L, T, SCALE)
+        assert np.array_equal(results[0]["sel"][b], ref["sel"])
+        assert np.abs(results[0]["out"][b] - ref["out"]).max() < 1e-12
+        bs = results[0]["block_scores"][b]
+        assert np.array_equal(bs[:, :, :n], ref["block_scores"])
+        assert np.all(bs[:, :, n:] == -np.inf)
+        off += n
+
+
+def test_selection_boundary_tie_goes_to_lower_block():
+    # 19 older blocks: 14 clear winners, four blocks tied for the last slot,
+    # one loser; the lowest-numbered tied block must win the slot
+    own = 19
+    tied = [3, 7, 11, 16]
+    S = np.full(20, 0.1)
+    winners = [i for i in range(own) if i not in tied][:14]
+    S[winners] = np.linspace(9.0, 2.0, 14)
+    S[tied] = 0.5
+    sel = [int(i) for i in M.select_blocks(S, own) if i >= 0]
+    assert sel == brute_select(S, own) == sorted(winners + [3, own])

@@ -1,0 +1,65 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case swaps one oracle function for a plausibly wrong variant and checks
+that the pin meant to guard it fails."""
+import numpy as np
+import pytest
+
+import oracle.msa as M
+import oracle.formats as F
+from tests import test_oracle_msa as TM
+from tests import test_oracle_formats as TF
+
+
+def _select_ties_to_higher_index(S, own, k=16):
+    S = np.asarray(S, float)
+    if own + 1 <= k:
+        return np.array(list(range(own + 1)) + [-1] * (k - own - 1), np.int32)
+    cand = np.arange(own)
+    order = np.lexsort((-cand, -S[:own]))
+    ch = sorted([int(i) for i in cand[order[: k - 1]]] + [own])
+    return np.array(ch + [-1] * (k - len(ch)), np.int32)
+
+
+def _select_without_forcing_own(S, own, k=16):
+    S = np.asarray(S, float)
+    cand = np.arange(own + 1)
+    order = np.lexsort((cand, -S[:own + 1]))
+    ch = sorted(int(i) for i in cand[order[:k]])
+    return np.array(ch + [-1] * (k - len(ch)), np.int32)
+
+
+def _attended_keys_ignoring_causality(sel_row, p):
+    return np.concatenate([np.arange(i * 128, i * 128 + 128) for i in sel_row if i >= 0]).astype(np.int64)
+
+
+def _e4m3_ties_away(x):
+    x = np.asarray(x, float)
+    pos = F._E4M3_POS
+    a = np.abs(x)
+    idx = np.array([int(np.argmin(np.abs(pos - v) - 1e-300 * np.arange(len(pos)))) for v in np.minimum(a, 448.0)])
+    return (idx | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _sparse_attention_wrong_gqa(q, K, V, sel, L, T, scale):
+    # heads assigned round-robin instead of contiguously
+    q = np.asarray(q, float)
+    qq = q.reshape(q.shape[0], 16, 4, q.shape[2]).transpose(0, 2, 1, 3).reshape(q.shape)
+    return _orig_attention(qq, K, V, sel, L, T, scale)
+
+
+_orig_attention = M.sparse_attention
+
+
+@pytest.mark.parametrize("target,mutant,pin", [
+    (M, ("select_blocks", _select_ties_to_higher_index), TM.test_selection_boundary_tie_goes_to_lower_block),
+    (M, ("select_blocks", _select_without_forcing_own), TM.test_selection_invariants_random_rows),
+    (M, ("attended_keys", _attended_keys_ignoring_causality), lambda: TM.test_short_context_equals_dense_causal_attention(2048, 4)),
+    (M, ("sparse_attention", _sparse_attention_wrong_gqa), TM.test_sparse_attention_equals_masked_sdpa_from_selection),
+    (F, ("e4m3_encode", _e4m3_ties_away), TF.test_e4m3_encode_matches_torch_rne_in_range),
+])
+def test_planted_mistake_is_caught(monkeypatch, target, mutant, pin):
+    name, fn = mutant
+    monkeypatch.setattr(target, name, fn)
+    with pytest.raises(AssertionError):
+        pin()

@@ -1,0 +1,38 @@
+"""Pins of the bytes model against the numbers the source pages print
+(tests/golden/page_facts.json)."""
+import json
+import os
+
+import pytest
+
+from oracle import traffic as TR
+
+GOLD = {k: v["value"] for k, v in json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json"))).items()
+        if isinstance(v, dict)}
+
+
+def test_per_token_bytes_fp8():
+    assert TR.index_key_bytes_per_token("fp8") == GOLD["index_key_bytes_fp8"]
+    assert TR.kv_bytes_per_token("fp8", GOLD["kv_heads"]) == GOLD["kv_bytes_fp8"]
+    assert TR.index_key_bytes_per_token("fp8") / TR.kv_bytes_per_token("fp8") == GOLD["index_to_kv_fraction"]
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "nvfp4", "f32"])
+def test_long_context_traffic_tends_to_an_eighth(dtype):
+    # closed form: 1/8 + 2048 / L for L >= 2048, for every storage format
+    for L in [4096, 32768, 131072, 1 << 20]:
+        assert TR.sparse_to_dense_ratio(L, dtype) == pytest.approx(0.125 + 2048 / L, rel=1e-12)
+    assert TR.sparse_to_dense_ratio(1 << 30, dtype) == pytest.approx(GOLD["long_context_traffic"], abs=1e-5)
+    assert TR.sparse_to_dense_ratio(4096, "f32") == pytest.approx(0.625)
+
+
+def test_nvfp4_is_four_and_a_half_bits():
+    ratio = TR.kv_bytes_per_token("nvfp4") / TR.kv_bytes_per_token("fp8")
+    assert ratio == GOLD["model_bytes_nvfp4"] / GOLD["model_bytes_fp8"]
+    assert 1 - ratio == GOLD["nvfp4_saving"]
+    assert TR.ROW_BYTES["nvfp4"] * 8 / 128 == 4.5
+
+
+def test_dense_is_never_cheaper_past_2048():
+    for L in [2049, 5000, 10 ** 6]:
+        assert TR.sparse_decode_bytes(L, "fp8") < TR.dense_decode_bytes(L, "fp8") * (0.125 + 2048 / L + 1e-12)
