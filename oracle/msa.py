@@ -76,7 +76,8 @@ def indexer_token_scores(idx_q, idx_k, L, T):
     idx_q = np.asarray(idx_q, dtype=np.float64)
     idx_k = np.asarray(idx_k, dtype=np.float64)
     assert idx_k.shape[0] == L
-    s = np.einsum("tgd,jd->tgj", idx_q, idx_k)
+    T_, G, D = idx_q.shape
+    s = (idx_q.reshape(T_ * G, D) @ idx_k.T).reshape(T_, G, L)        # library matmul, fp64
     p = positions(L, T)
     visible = np.arange(L)[None, :] <= p[:, None]                      # [T, L]
     return np.where(visible[:, None, :], s, -np.inf)
@@ -89,6 +90,22 @@ def block_max_pool(token_scores, L):
     padded = np.full((T, G, nb * BLOCK), -np.inf)
     padded[:, :, :L] = token_scores
     return padded.reshape(T, G, nb, BLOCK).max(axis=-1)
+
+
+def pooled_scores(idx_q, idx_k, L, T, chunk=128):
+    """Steps 2-3 for all T query tokens, scored ``chunk`` tokens at a time so
+    that a long prefill never holds every per-key score at once.  Token t of
+    the whole sequence keeps its position L - T + t."""
+    out = np.empty((T, idx_q.shape[1], num_blocks(L)))
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        # tokens t0..t1-1 are the last (t1 - t0) tokens of a sequence cut at L - T + t1
+        Lc = L - T + t1
+        s = indexer_token_scores(idx_q[t0:t1], idx_k[:Lc], Lc, t1 - t0)
+        S = block_max_pool(s, Lc)
+        out[t0:t1] = -np.inf
+        out[t0:t1, :, :S.shape[-1]] = S
+    return out
 
 
 # ---------------------------------------------------------------- step 4
@@ -267,8 +284,7 @@ def batch_layer(idx_q, q, idx_cache, k_cache, v_cache, seq_lens, block_table, T,
         L = int(seq_lens[b])
         iq = decode_query(idx_q[b], idx_q_dtype, idx_q_scale)
         ik = sequence_view(idx_cache, block_table[b], L, mode)[0]
-        s = indexer_token_scores(iq, ik, L, T)
-        S = block_max_pool(s, L)
+        S = pooled_scores(iq, ik, L, T)
         nb = S.shape[-1]
         bs[b, :, :, :] = -np.inf
         bs[b, :, :, :nb] = S

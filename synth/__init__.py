@@ -31,6 +31,7 @@ queries are z + m_g with m_g shared by all tokens and qhat = m_g / |m_g|).
 from dataclasses import dataclass, field
 import math
 
+import numpy as np
 import torch
 
 BLOCK = 128
@@ -62,7 +63,8 @@ class Workload:
     prefill_planting: bool = False
 
     def tensor_scale(self):
-        return NVFP4_BOUND / 448.0 if self.kv_dtype == "nvfp4" else 1.0
+        """Per-tensor scale of the caches, as the fp32 value the library uses."""
+        return float(np.float32(NVFP4_BOUND / 448.0)) if self.kv_dtype == "nvfp4" else 1.0
 
 
 WORKLOADS = {

@@ -223,3 +223,16 @@ def test_selection_boundary_tie_goes_to_lower_block():
     S[tied] = 0.5
     sel = [int(i) for i in M.select_blocks(S, own) if i >= 0]
     assert sel == brute_select(S, own) == sorted(winners + [3, own])
+
+
+def test_chunked_pooling_equals_unchunked():
+    rng = np.random.default_rng(21)
+    L, T = 128 * 9 + 17, 300
+    q = rng.normal(size=(T, 4, 16))
+    k = rng.normal(size=(L, 16))
+    full = M.block_max_pool(M.indexer_token_scores(q, k, L, T), L)
+    for chunk in (1, 7, 128, 1000):
+        got = M.pooled_scores(q, k, L, T, chunk=chunk)
+        assert np.array_equal(np.isneginf(got), np.isneginf(full))
+        fin = np.isfinite(full)
+        assert np.abs(got[fin] - full[fin]).max() < 1e-12
