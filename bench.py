@@ -1,0 +1,273 @@
+"""Benchmark of the MSA decode layer step on one MI355X.
+
+One step = msa_indexer_scores -> msa_block_topk -> msa_sparse_attn_decode
+for the whole batch (one MSA layer).  Inputs are seeded synthetic data drawn
+and packed on the GPU before the timed region (resident in HBM).
+
+    python bench.py [--steps K] [--warmup W] [--workload c3_128k]
+                    [--dequant exact|fp8] [--no-cpu-baseline]
+
+Prints one JSON line.  ``value`` is layer-steps/s; ``roofline`` describes the
+dominant kernel (the index-key scan) from HIP events recorded around each of
+its launches on the stream it runs on; ``cpu_baseline`` is the CPU fp64
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA decode layer-steps/s at 128K ctx NVFP4; achieved HBM TB/s as % of peak"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3_128k")
+    ap.add_argument("--dequant", default="exact", choices=["exact", "fp8"])
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+class Workload:
+    """A decode workload drawn and packed on the GPU."""
+
+    def __init__(self, name, seed, keep_sequences=()):
+        import torch
+        import synth
+        import block_sparse_attention_indexer_amd as M
+        self.M = M
+        w = synth.WORKLOADS[name]
+        self.w = w
+        self.lay = lay = synth.make_layout(w, seed)
+        dev = "cuda"
+        idx_q, q, qhat = synth.queries(w, seed, device=dev)
+        hot = synth.hot_blocks(w, lay, seed)
+        S = w.tensor_scale()
+        self.S = S
+        P = lay.num_pages
+        self.seq = lay.seq_lens.to(dev)
+        self.table = lay.block_table.to(dev)
+        # pages of the sequences the CPU leg will use: their fp32 sources are kept on the host
+        keep_pages = {}
+        for b in keep_sequences:
+            nb = (int(lay.seq_lens[b]) + 127) // 128
+            keep_pages[b] = lay.block_table[b, :nb].long()
+        self.kept = {b: {} for b in keep_sequences}
+        self.caches = {}
+        chunk = 2048
+        for name_ in ("idx_k", "k", "v"):
+            heads = 1 if name_ == "idx_k" else 4
+            if w.kv_dtype == "nvfp4":
+                data = torch.empty((P, heads, 128, 64), dtype=torch.uint8, device=dev)
+                sc = torch.empty((P, heads, 128, 8), dtype=torch.uint8, device=dev)
+            elif w.kv_dtype == "fp8":
+                data = torch.empty((P, heads, 128, 128), dtype=torch.uint8, device=dev)
+                sc = None
+            else:
+                data = torch.empty((P, heads, 128, 128), dtype=torch.float32, device=dev)
+                sc = None
+            keep_host = {b: torch.empty((len(pg), heads, 128, 128)) for b, pg in keep_pages.items()}
+            for first in range(0, P, chunk):
+                n = min(chunk, P - first)
+                x = synth.cache_pages(w, lay, seed, name_, first, n, qhat, hot, device=dev)
+                if w.kv_dtype == "nvfp4":
+                    M.msa_pack_nvfp4(x, S, data[first:first + n], sc[first:first + n])
+                elif w.kv_dtype == "fp8":
+                    M.msa_pack_fp8(x, S, data[first:first + n])
+                else:
+                    data[first:first + n].copy_(x)
+                for b, pg in keep_pages.items():
+                    m = (pg >= first) & (pg < first + n)
+                    if m.any():
+                        keep_host[b][m] = x[(pg[m] - first).to(dev)].cpu()
+                del x
+            for b in keep_pages:
+                self.kept[b][name_] = keep_host[b].numpy()
+            self.caches[name_] = (data, sc, M.cache(w.kv_dtype, data, sc, S if w.kv_dtype != "f32" else 1.0, heads))
+        if w.q_dtype == "fp8":
+            self.idx_q = torch.empty(idx_q.shape, dtype=torch.uint8, device=dev)
+            self.q = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+            M.msa_pack_fp8(idx_q, 1.0, self.idx_q)
+            M.msa_pack_fp8(q, 1.0, self.q)
+        else:
+            self.idx_q, self.q = idx_q, q
+        self.idx_q32 = {b: idx_q[b].cpu().numpy() for b in keep_sequences}
+        self.q32 = {b: q[b].cpu().numpy() for b in keep_sequences}
+        B, T, maxb = w.B, w.T, lay.max_blocks
+        self.prob = M.problem(self.seq, self.table, T)
+        self.bs = torch.empty((B, T, 4, maxb), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, T, 4, 16), dtype=torch.int32, device=dev)
+        self.out = torch.empty((B, T, 64, 128), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, dequant, ev=None):
+        M, w = self.M, self.w
+        stream = None
+        if ev is not None:
+            ev[0].record()
+        M.msa_indexer_scores(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], dequant, self.bs,
+                             None, stream=stream)
+        if ev is not None:
+            ev[1].record()
+        M.msa_block_topk(self.prob, self.bs, self.sel, stream=stream)
+        if ev is not None:
+            ev[2].record()
+        fn = M.msa_sparse_attn_decode if w.T <= 8 else M.msa_sparse_attn_prefill
+        fn(self.prob, self.q, w.q_dtype, 1.0, self.caches["k"][2], self.caches["v"][2], dequant, self.sel,
+           1.0 / math.sqrt(128.0), self.out, None, stream=stream)
+        if ev is not None:
+            ev[3].record()
+
+
+def algorithmic_bytes(wl, sel_host):
+    """Bytes the method must move per layer step (oracle.traffic's model)."""
+    from oracle import traffic as TR
+    w, lay = wl.w, wl.lay
+    lens = [int(x) for x in lay.seq_lens]
+    maxb = lay.max_blocks
+    idx = TR.indexer_bytes(lens, w.T, w.kv_dtype, w.q_dtype, 4, maxb)
+    topk = TR.topk_bytes(w.B, w.T, 4, maxb)
+    # distinct (sequence, group, block) rows read, each key once per KV head
+    keys = 0
+    for b in range(w.B):
+        L = lens[b]
+        for g in range(4):
+            blocks = set(int(i) for i in sel_host[b, :, g].reshape(-1) if i >= 0)
+            for i in blocks:
+                keys += min(128, L - 128 * i)
+    attn = TR.attention_bytes(keys, w.kv_dtype, w.q_dtype, w.B, w.T, 64)
+    return idx, topk, attn
+
+
+def cpu_baseline(wl, dequant, sample):
+    """The oracle on `sample` sequences of the same workload, packed by the
+    oracle itself from the fp32 sources; timed from decode to attention."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import formats as OF
+    from oracle import msa as OM
+    w, lay = wl.w, wl.lay
+    mode = "exact" if dequant == "exact" else "fp8"
+    total = 0.0
+    with threadpool_limits(1):
+        for b, src in wl.kept.items():
+            L = int(lay.seq_lens[b])
+            nb = (L + 127) // 128
+            caches = {}
+            for n, x in src.items():
+                if w.kv_dtype == "nvfp4":
+                    c, s = OF.nvfp4_quantize(x, wl.S)
+                    caches[n] = {"dtype": "nvfp4", "data": c, "scales": s, "tensor_scale": wl.S}
+                elif w.kv_dtype == "fp8":
+                    caches[n] = {"dtype": "fp8", "data": OF.fp8_quantize(x, wl.S), "tensor_scale": wl.S}
+                else:
+                    caches[n] = {"dtype": "f32", "data": x, "tensor_scale": 1.0}
+            qd = w.q_dtype
+            idx_q = OF.fp8_quantize(wl.idx_q32[b], 1.0)[None] if qd == "fp8" else wl.idx_q32[b][None]
+            q = OF.fp8_quantize(wl.q32[b], 1.0)[None] if qd == "fp8" else wl.q32[b][None]
+            table = np.arange(nb, dtype=np.int32)[None]
+            t0 = time.perf_counter()
+            OM.batch_layer(idx_q, q, caches["idx_k"], caches["k"], caches["v"], np.array([L]), table, w.T,
+                           1.0 / math.sqrt(128.0), mode=mode, idx_q_dtype=qd, q_dtype=qd)
+            total += time.perf_counter() - t0
+    per_seq = total / max(1, len(wl.kept))
+    return {"value": 1.0 / (per_seq * w.B), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(wl.kept)} of {w.B} sequences of {w.name} (full layer step each: dequant, "
+                      f"score, pool, select, attend); rate scaled to the {w.B}-sequence step; "
+                      f"{total:.1f} s of CPU time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    torch.cuda.set_device(0)
+    sample = [] if args.no_cpu_baseline else list(range(0, 64, 64 // max(1, args.cpu_sample)))[: args.cpu_sample]
+    wl = Workload(args.workload, args.seed, keep_sequences=sample)
+    w = wl.w
+    print(f"[bench] workload {w.name} ready: B={w.B} T={w.T} pages={wl.lay.num_pages}", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        bbuf = torch.empty_like(a)
+        for _ in range(3):
+            bbuf.copy_(a)
+        torch.cuda.synchronize()
+        del a, bbuf
+
+    for _ in range(args.warmup):
+        wl.step(args.dequant)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        wl.step(args.dequant, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    k_idx = [evs[k][0].elapsed_time(evs[k][1]) for k in range(K)]
+    k_topk = [evs[k][1].elapsed_time(evs[k][2]) for k in range(K)]
+    k_attn = [evs[k][2].elapsed_time(evs[k][3]) for k in range(K)]
+
+    sel = wl.sel.cpu().numpy()
+    b_idx, b_topk, b_attn = algorithmic_bytes(wl, sel)
+    total_bytes = b_idx + b_topk + b_attn
+    idx_ms = float(np.mean(k_idx))
+    achieved_idx = b_idx / (idx_ms * 1e-3) / 1e9
+    step_tbps = total_bytes / (ms_step * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: decode, batch {w.B}, context {w.lens} tokens, NVFP4 K/V and index "
+                               f"keys, FP8 queries, shuffled 128-token pages",
+                   "batch": w.B, "query_tokens": w.T, "context": w.lens, "kv_storage": w.kv_dtype,
+                   "q_storage": w.q_dtype, "dequant": args.dequant, "compute": "f16 MFMA, fp32 accumulate"},
+        "hbm_TBps_step": round(step_tbps, 3),
+        "pct_of_peak_hbm_step": round(100 * step_tbps * 1e3 / HBM_PEAK_GBPS, 1),
+        "bytes_per_step": {"indexer": b_idx, "topk": b_topk, "attention": b_attn},
+        "kernel_ms": {"indexer": round(idx_ms, 5), "topk": round(float(np.mean(k_topk)), 5),
+                      "attention": round(float(np.mean(k_attn)), 5)},
+        "roofline": {"bound": "hbm", "kernel": "indexer_mfma_kernel (index-key scan + block max-pool)",
+                     "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved_idx / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    if sample:
+        out["cpu_baseline"] = cpu_baseline(wl, args.dequant, sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

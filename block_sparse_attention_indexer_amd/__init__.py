@@ -1,0 +1,183 @@
+"""Python binding of libmsa, the MI355X (gfx950) MSA hot path.
+
+Argument marshalling only: every step runs in the HIP kernels of libmsa.so
+(see include/msa.h for the contract of each call).  torch supplies device
+memory and the current stream; nothing here computes on the CPU, and if the
+library is missing every call raises instead of falling back.
+
+The functions keep the C names: msa_indexer_scores, msa_block_topk,
+msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_pack_fp8,
+msa_unpack_fp8, msa_pack_nvfp4, msa_unpack_nvfp4, msa_workspace_size.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
+MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
+MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
+MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN = 0, 1, 2
+
+EXPORTED = ("msa_indexer_scores", "msa_block_topk", "msa_sparse_attn_decode",
+            "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
+            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
+
+DTYPES = {"f32": MSA_F32, "fp8": MSA_FP8_E4M3, "nvfp4": MSA_NVFP4}
+DEQUANT = {"exact": MSA_DQ_EXACT, "fp8": MSA_DQ_FP8}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status, call):
+        self.status = status
+        super().__init__(f"{call}: {_lib().msa_status_string(status).decode()} (status {status})")
+
+
+class msa_cache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_float), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
+
+
+class msa_problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("tokens", ctypes.c_int32), ("groups", ctypes.c_int32),
+                ("heads_per_group", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("max_blocks", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                               "python -m block_sparse_attention_indexer_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        P = ctypes.POINTER
+        sig = {
+            "msa_indexer_scores": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp, vp],
+            "msa_block_topk": [P(msa_problem), vp, vp, vp],
+            "msa_sparse_attn_decode": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
+                                       ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
+            "msa_sparse_attn_prefill": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
+                                        ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
+            "msa_workspace_size": [P(msa_problem), ctypes.c_int],
+            "msa_pack_fp8": [vp, i64, f32, vp, vp],
+            "msa_unpack_fp8": [vp, i64, f32, vp, vp],
+            "msa_pack_nvfp4": [vp, i64, i32, f32, vp, vp, vp],
+            "msa_unpack_nvfp4": [vp, vp, i64, i32, f32, ctypes.c_int, vp, vp],
+            "msa_status_string": [ctypes.c_int],
+            "msa_abi_version": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.msa_workspace_size.restype = sz
+        lib.msa_status_string.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmsa must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status, call):
+    if status != MSA_OK:
+        raise MsaError(status, call)
+
+
+def problem(seq_lens, block_table, tokens):
+    """msa_problem for device int32 seq_lens [B] and block_table [B, max_blocks]."""
+    p = msa_problem(batch=int(seq_lens.shape[0]), tokens=int(tokens), groups=4, heads_per_group=16,
+                    head_dim=128, block_size=128, topk=16, seq_lens=_ptr(seq_lens),
+                    block_table=_ptr(block_table), max_blocks=int(block_table.shape[1]))
+    p._keep = (seq_lens, block_table)
+    return p
+
+
+def cache(dtype, data, scales=None, tensor_scale=1.0, heads=1):
+    """msa_cache over a device page pool (data: floats, FP8 bytes or NVFP4 codes)."""
+    per_page = heads * 128 * (128 * 4 if dtype == "f32" else 128 if dtype == "fp8" else 64)
+    nbytes = data.numel() * data.element_size()
+    c = msa_cache(dtype=DTYPES[dtype], data=_ptr(data), scales=_ptr(scales),
+                  tensor_scale=float(tensor_scale), heads=int(heads), head_dim=128,
+                  num_pages=int(nbytes // per_page))
+    c._keep = (data, scales)
+    return c
+
+
+def msa_indexer_scores(prob, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores,
+                       token_scores=None, stream=None):
+    _check(_lib().msa_indexer_scores(ctypes.byref(prob), _ptr(idx_q), DTYPES[q_dtype], float(q_scale),
+                                     ctypes.byref(idx_k), DEQUANT[dequant], _ptr(block_scores),
+                                     _ptr(token_scores), _stream(stream)), "msa_indexer_scores")
+
+
+def msa_block_topk(prob, block_scores, sel, stream=None):
+    _check(_lib().msa_block_topk(ctypes.byref(prob), _ptr(block_scores), _ptr(sel), _stream(stream)),
+           "msa_block_topk")
+
+
+def _attn(name, prob, q, q_dtype, q_scale, k, v, dequant, sel, softmax_scale, out, lse=None,
+          workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fn = getattr(_lib(), name)
+    _check(fn(ctypes.byref(prob), _ptr(q), DTYPES[q_dtype], float(q_scale), ctypes.byref(k),
+              ctypes.byref(v), DEQUANT[dequant], _ptr(sel), float(softmax_scale), _ptr(out),
+              _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)), name)
+
+
+def msa_sparse_attn_decode(*args, **kw):
+    _attn("msa_sparse_attn_decode", *args, **kw)
+
+
+def msa_sparse_attn_prefill(*args, **kw):
+    _attn("msa_sparse_attn_prefill", *args, **kw)
+
+
+def msa_workspace_size(prob, which):
+    return int(_lib().msa_workspace_size(ctypes.byref(prob), int(which)))
+
+
+def msa_pack_fp8(x, scale, out, stream=None):
+    _check(_lib().msa_pack_fp8(_ptr(x), x.numel(), float(scale), _ptr(out), _stream(stream)), "msa_pack_fp8")
+
+
+def msa_unpack_fp8(x, scale, out, stream=None):
+    _check(_lib().msa_unpack_fp8(_ptr(x), x.numel(), float(scale), _ptr(out), _stream(stream)), "msa_unpack_fp8")
+
+
+def msa_pack_nvfp4(x, tensor_scale, codes, scales, stream=None):
+    row_len = int(x.shape[-1])
+    rows = x.numel() // row_len
+    _check(_lib().msa_pack_nvfp4(_ptr(x), rows, row_len, float(tensor_scale), _ptr(codes), _ptr(scales),
+                                 _stream(stream)), "msa_pack_nvfp4")
+
+
+def msa_unpack_nvfp4(codes, scales, row_len, tensor_scale, dequant, out, stream=None):
+    rows = out.numel() // row_len
+    _check(_lib().msa_unpack_nvfp4(_ptr(codes), _ptr(scales), rows, int(row_len), float(tensor_scale),
+                                   DEQUANT[dequant], _ptr(out), _stream(stream)), "msa_unpack_nvfp4")
+
+
+def abi_version():
+    return int(_lib().msa_abi_version())

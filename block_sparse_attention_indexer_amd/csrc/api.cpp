@@ -1,0 +1,186 @@
+// The C ABI of libmsa (declared in include/msa.h): host-side argument
+// validation, then one or more kernel launches on the caller's stream.
+// Validation makes no HIP call, so a rejected call has no side effect.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/msa.h"
+#include "launch.hpp"
+
+namespace {
+
+using msa::CacheArgs;
+using msa::ProblemArgs;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+msa_status check_problem(const msa_problem* p) {
+  if (p == nullptr) return MSA_ERR_INVALID_ARG;
+  if (p->groups != 4 || p->heads_per_group != 16 || p->head_dim != 128 || p->block_size != 128 ||
+      p->topk != 16)
+    return MSA_ERR_UNSUPPORTED;
+  if (p->batch < 1 || p->tokens < 1 || p->max_blocks < 1) return MSA_ERR_INVALID_ARG;
+  if (p->batch > 65535 || p->max_blocks > 8192 || p->tokens > 262144) return MSA_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->tokens * 4 > 0x7FFFFFFF) return MSA_ERR_UNSUPPORTED;
+  if (p->seq_lens == nullptr || p->block_table == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(p->seq_lens, 4) || !aligned(p->block_table, 4)) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+msa_status check_cache(const msa_cache* c, int heads) {
+  if (c == nullptr || c->data == nullptr) return MSA_ERR_INVALID_ARG;
+  if (c->dtype != MSA_F32 && c->dtype != MSA_FP8_E4M3 && c->dtype != MSA_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (c->head_dim != 128) return MSA_ERR_UNSUPPORTED;
+  if (c->heads != heads) return MSA_ERR_INVALID_ARG;
+  if (c->num_pages < 1 || c->num_pages > 0x7FFFFFFF) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(c->tensor_scale)) return MSA_ERR_INVALID_ARG;
+  if (!aligned(c->data, 16)) return MSA_ERR_INVALID_ARG;
+  if (c->dtype == MSA_NVFP4 && (c->scales == nullptr || !aligned(c->scales, 8))) return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+// Allowed pairs: F32 query with F32 cache; FP8 query with FP8 or NVFP4 cache.
+msa_status check_pair(msa_dtype q_dtype, msa_dtype c_dtype) {
+  if (q_dtype == MSA_F32 && c_dtype == MSA_F32) return MSA_OK;
+  if (q_dtype == MSA_FP8_E4M3 && (c_dtype == MSA_FP8_E4M3 || c_dtype == MSA_NVFP4)) return MSA_OK;
+  return MSA_ERR_UNSUPPORTED;
+}
+
+CacheArgs to_args(const msa_cache* c) {
+  return CacheArgs{static_cast<const uint8_t*>(c->data), c->scales, c->num_pages, c->tensor_scale,
+                   (int)c->dtype};
+}
+ProblemArgs to_args(const msa_problem* p) {
+  return ProblemArgs{p->batch, p->tokens, p->max_blocks, p->seq_lens, p->block_table};
+}
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+msa_status attention(const msa_problem* prob, const void* q, msa_dtype q_dtype, float q_scale,
+                     const msa_cache* k, const msa_cache* v, msa_dequant dequant,
+                     const int32_t* sel, float softmax_scale, float* out, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream, int max_t) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (prob->tokens > max_t) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_cache(k, 4)) != MSA_OK) return st;
+  if ((st = check_cache(v, 4)) != MSA_OK) return st;
+  if (k->dtype != v->dtype) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_pair(q_dtype, k->dtype)) != MSA_OK) return st;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (q == nullptr || sel == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(sel, 4) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return MSA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale) || !good_scale(softmax_scale)) return MSA_ERR_INVALID_ARG;
+  if (msa_workspace_size(prob, MSA_CALL_ATTN) > workspace_bytes) return MSA_ERR_WORKSPACE;
+  (void)workspace;
+  return hip_status(msa::launch_attention(to_args(prob), q, (int)q_dtype, q_scale, to_args(k),
+                                          to_args(v), dequant == MSA_DQ_FP8, sel, softmax_scale,
+                                          out, lse, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_indexer_scores(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
+                              float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                              float* block_scores, float* token_scores, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
+  if ((st = check_pair(q_dtype, idx_k->dtype)) != MSA_OK) return st;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (idx_q == nullptr || block_scores == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(idx_q, 16) || !aligned(block_scores, 4) || (token_scores && !aligned(token_scores, 4)))
+    return MSA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale)) return MSA_ERR_INVALID_ARG;
+  return hip_status(msa::launch_indexer(to_args(prob), idx_q, (int)q_dtype, q_scale,
+                                        to_args(idx_k), dequant == MSA_DQ_FP8, block_scores,
+                                        token_scores, stream));
+}
+
+msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, int32_t* sel,
+                          hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (block_scores == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(block_scores, 4) || !aligned(sel, 4)) return MSA_ERR_INVALID_ARG;
+  return hip_status(msa::launch_topk(to_args(prob), block_scores, sel, stream));
+}
+
+msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, msa_dtype q_dtype,
+                                  float q_scale, const msa_cache* k, const msa_cache* v,
+                                  msa_dequant dequant, const int32_t* sel, float softmax_scale,
+                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  return attention(prob, q, q_dtype, q_scale, k, v, dequant, sel, softmax_scale, out, lse,
+                   workspace, workspace_bytes, stream, 8);
+}
+
+msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_dtype q_dtype,
+                                   float q_scale, const msa_cache* k, const msa_cache* v,
+                                   msa_dequant dequant, const int32_t* sel, float softmax_scale,
+                                   float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return attention(prob, q, q_dtype, q_scale, k, v, dequant, sel, softmax_scale, out, lse,
+                   workspace, workspace_bytes, stream, 262144);
+}
+
+size_t msa_workspace_size(const msa_problem* prob, msa_call which) {
+  (void)prob;
+  (void)which;
+  return 0;
+}
+
+msa_status msa_pack_fp8(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream) {
+  if (x == nullptr || out == nullptr || n < 0) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(scale) || !aligned(x, 4)) return MSA_ERR_INVALID_ARG;
+  if (n == 0) return MSA_OK;
+  return hip_status(msa::launch_pack_fp8(x, n, scale, out, stream));
+}
+
+msa_status msa_unpack_fp8(const uint8_t* x, int64_t n, float scale, float* out, hipStream_t stream) {
+  if (x == nullptr || out == nullptr || n < 0) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(scale) || !aligned(out, 4)) return MSA_ERR_INVALID_ARG;
+  if (n == 0) return MSA_OK;
+  return hip_status(msa::launch_unpack_fp8(x, n, scale, out, stream));
+}
+
+msa_status msa_pack_nvfp4(const float* x, int64_t rows, int32_t row_len, float tensor_scale,
+                          uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr || rows < 0 || row_len <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (row_len % 16 != 0 || !good_scale(tensor_scale)) return MSA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return MSA_ERR_INVALID_ARG;
+  if (rows == 0) return MSA_OK;
+  return hip_status(msa::launch_pack_nvfp4(x, rows * (row_len / 16), tensor_scale, codes, scales, stream));
+}
+
+msa_status msa_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                            int32_t row_len, float tensor_scale, msa_dequant dequant, float* out,
+                            hipStream_t stream) {
+  if (codes == nullptr || scales == nullptr || out == nullptr || rows < 0 || row_len <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (row_len % 16 != 0 || !good_scale(tensor_scale)) return MSA_ERR_INVALID_ARG;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (!aligned(codes, 8) || !aligned(out, 16)) return MSA_ERR_INVALID_ARG;
+  if (rows == 0) return MSA_OK;
+  return hip_status(msa::launch_unpack_nvfp4(codes, scales, rows * (row_len / 16), tensor_scale,
+                                             dequant == MSA_DQ_FP8, out, stream));
+}
+
+const char* msa_status_string(msa_status s) {
+  switch (s) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_INVALID_ARG: return "invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MSA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// Step 4 of MSA: exact attention over the selected blocks.
+//
+// Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
+// and its Figure 1 caption: attention runs exactly, but only over the top
+// blocks; every query head of a GQA group attends over its group's block
+// set, so a query reads full K/V for at most 2,048 keys.
+//
+// One workgroup per (sequence, query token, group) with 16 waves; wave w
+// takes the w-th selected block.  Per block (one KV head, 16 query heads):
+//   S^T = K Q^T on 16x16x32 f16 MFMAs (A = 16 keys x 32 dims of K, straight
+//         from the page: lane quarter Q loads dims [32Q, 32Q+32) of its key;
+//         B = Q^T, the 16 heads of the group, loaded once);
+//   softmax over the block's <= 128 keys in fp32 (exp2 domain);
+//   O^T += V^T P^T on 16x16x16 f16 MFMAs.  The lane layout of S^T is exactly
+//         the B operand P^T of the next product, so P never leaves registers;
+//         P is split into f16 hi + lo parts (two MFMAs) to keep ~2^-22
+//         relative precision.  V^T is staged per 16-key tile through a
+//         wave-private LDS slice (dequantised, transposed).
+// The 16 per-block partial states (max, sum, O) are merged in fixed order
+// (max, then a 4-level tree over LDS), so results are deterministic.
+// FP8 and NVFP4 values are exact in f16; the products are exact and the
+// accumulation is fp32.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace msa {
+
+constexpr int kAttnWaves = 16;
+constexpr int kVtDwords = kHeadDim * 8 + 64;   // 128 dims x 16 keys f16, padded per 16 dims
+
+__device__ __forceinline__ int vt_index(int d, int kp) {   // dword of (dim d, key pair kp)
+  return d * 8 + kp + ((d >> 4) << 3);
+}
+__device__ __forceinline__ h8 reorder_like_lut_a(h8 a) {
+  return h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]};
+}
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).
+template <int KT, bool FP8MODE>
+__global__ __launch_bounds__(1024) void attn_mfma_kernel(
+    const uint8_t* __restrict__ q, float c_log2, const uint8_t* __restrict__ kdata,
+    const uint8_t* __restrict__ kscales, int64_t kpages, const uint8_t* __restrict__ vdata,
+    const uint8_t* __restrict__ vscales, int64_t vpages, float v_scale,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ table, int max_blocks, int T, float* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ uint32_t lut[FP8MODE ? 512 : 2];
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kAttnWaves * kVtDwords];
+  __shared__ float m_sh[kAttnWaves][16], l_sh[kAttnWaves][16];
+  __shared__ int nan_sh;
+  if (threadIdx.x == 0) nan_sh = 0;
+  if (FP8MODE) build_fp8_lut(lut);
+  __syncthreads();
+
+  const int row = blockIdx.x;   // (b*T + t)*4 + g
+  const int g = row & 3;
+  const int bt = row >> 2;
+  const int t = bt % T, b = bt / T;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int Q = lane >> 4, j = lane & 15;
+  const int L = seq_lens[b];
+  const int p = L - T + t;
+  const float NEG_INF = -__builtin_inff();
+
+  // B operand of S^T = K Q^T: lane (Q, head j), k-chunk c = dims 32Q+8c..+7.
+  h8 Bq[4];
+  {
+    const uint4* src =
+        reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
+    const uint4 u0 = src[0], u1 = src[1];
+    const uint32_t wq[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
+      Bq[c] = (KT == 2 && FP8MODE) ? reorder_like_lut_a(a) : a;
+    }
+  }
+
+  float m = NEG_INF, l = 0.0f;
+  f4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int blk = sel[(size_t)row * kTopK + w];
+  int nkeys = 0;
+  int pg = -1;
+  if (blk >= 0) {
+    if (blk >= max_blocks) {
+      nan_sh = 1;
+    } else {
+      pg = table[(size_t)b * max_blocks + blk];
+      if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
+        nan_sh = 1;
+      } else {
+        nkeys = min(kBlock, p + 1 - blk * kBlock);
+      }
+    }
+  }
+  if (nkeys > 0) {
+    const size_t rowbase = ((size_t)pg * kGroups + g) * kBlock;   // (page, KV head g)
+    // ---------------- S^T = K Q^T, 8 tiles of 16 keys
+    float x[8][4];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      const size_t krow = rowbase + kt * 16 + j;
+      h8 Ak[4];
+      if (KT == 2) {
+        const uint4 cw = *reinterpret_cast<const uint4*>(kdata + krow * kNvfp4RowBytes + 16 * Q);
+        const uint32_t sw = *reinterpret_cast<const uint16_t*>(kscales + krow * kNvfp4ScaleBytes + 2 * Q);
+        const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
+        if (FP8MODE) {
+          const uint32_t s0 = sw & 0xFFu, s1 = (sw >> 8) & 0xFFu;
+          Ak[0] = fp4x8_lut_to_h8(wv[0], lut[2 * s0], lut[2 * s0 + 1]);
+          Ak[1] = fp4x8_lut_to_h8(wv[1], lut[2 * s0], lut[2 * s0 + 1]);
+          Ak[2] = fp4x8_lut_to_h8(wv[2], lut[2 * s1], lut[2 * s1 + 1]);
+          Ak[3] = fp4x8_lut_to_h8(wv[3], lut[2 * s1], lut[2 * s1 + 1]);
+        } else {
+          const h2 sc = fp8x2_to_h2<false>(sw);
+          const h8 s0 = h8{sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+          const h8 s1 = h8{sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+          Ak[0] = fp4x8_to_h8(wv[0]) * s0;
+          Ak[1] = fp4x8_to_h8(wv[1]) * s0;
+          Ak[2] = fp4x8_to_h8(wv[2]) * s1;
+          Ak[3] = fp4x8_to_h8(wv[3]) * s1;
+        }
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(kdata + krow * kHeadDim + 32 * Q);
+        const uint4 c0 = src[0], c1 = src[1];
+        Ak[0] = fp8x8_to_h8(c0.x, c0.y);
+        Ak[1] = fp8x8_to_h8(c0.z, c0.w);
+        Ak[2] = fp8x8_to_h8(c1.x, c1.y);
+        Ak[3] = fp8x8_to_h8(c1.z, c1.w);
+      }
+      f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
+      // lane (Q, head j) holds keys kt*16 + 4Q + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[kt][r] = (kt * 16 + 4 * Q + r < nkeys) ? acc[r] * c_log2 : NEG_INF;
+    }
+    // ---------------- softmax of this block (exp2 domain)
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kt][r]);
+    mx = max_over_quarters(mx);
+    float s = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[kt][r] = exp2f(x[kt][r] - mx);
+        s += x[kt][r];
+      }
+    m = mx;
+    l = sum_over_quarters(s);
+
+    // ---------------- O^T += V^T P^T, 8 tiles of 16 keys
+    uint32_t* vt = smem + w * kVtDwords;
+    const int kp = lane & 7;     // key pair within the tile (keys 2kp, 2kp+1)
+    const int dg = lane >> 3;    // 16-dim group
+#pragma unroll 1
+    for (int kt = 0; kt < 8; ++kt) {
+      // stage V^T for keys kt*16 .. kt*16+15
+      h8 v0[2], v1[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const size_t vrow = rowbase + kt * 16 + 2 * kp + u;
+        h8* dst = u == 0 ? v0 : v1;
+        if (KT == 2) {
+          const uint2 cw = *reinterpret_cast<const uint2*>(vdata + vrow * kNvfp4RowBytes + 8 * dg);
+          const uint32_t sb = vscales[vrow * kNvfp4ScaleBytes + dg];
+          if (FP8MODE) {
+            dst[0] = fp4x8_lut_to_h8(cw.x, lut[2 * sb], lut[2 * sb + 1]);
+            dst[1] = fp4x8_lut_to_h8(cw.y, lut[2 * sb], lut[2 * sb + 1]);
+          } else {
+            const _Float16 sh = e4m3_to_h(sb);
+            const h8 ss = h8{sh, sh, sh, sh, sh, sh, sh, sh};
+            dst[0] = fp4x8_to_h8(cw.x) * ss;
+            dst[1] = fp4x8_to_h8(cw.y) * ss;
+          }
+        } else {
+          const uint4 cw = *reinterpret_cast<const uint4*>(vdata + vrow * kHeadDim + 16 * dg);
+          dst[0] = fp8x8_to_h8(cw.x, cw.y);
+          dst[1] = fp8x8_to_h8(cw.z, cw.w);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 16 * dg + 8 * hh + ((KT == 2 && FP8MODE) ? lut_perm(e) : e);
+          vt[vt_index(d, kp)] = pack_h2(v0[hh][e], v1[hh][e]);
+        }
+      lds_wait();
+      // P^T operand: lane (Q, head j) holds keys 4Q..4Q+3 of this tile
+      h4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const _Float16 hv = (_Float16)x[kt][r];
+        phi[r] = hv;
+        plo[r] = (_Float16)(x[kt][r] - (float)hv);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = dt * 16 + j;   // A row = dim
+        const uint2 av = *reinterpret_cast<const uint2*>(vt + vt_index(d, 2 * Q));
+        const h4 a = __builtin_bit_cast(h4, av);
+        O[dt] = mfma_16x16x16(a, phi, O[dt]);
+        O[dt] = mfma_16x16x16(a, plo, O[dt]);
+      }
+      lds_wait();
+    }
+  }
+
+  // ---------------- merge the 16 block states in fixed order
+  if (Q == 0) {
+    m_sh[w][j] = m;
+    l_sh[w][j] = l;
+  }
+  __syncthreads();
+  float M = NEG_INF;
+#pragma unroll
+  for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, m_sh[ww][j]);
+  float Lt = 0.0f;
+#pragma unroll
+  for (int ww = 0; ww < kAttnWaves; ++ww) {
+    const float mw = m_sh[ww][j];
+    if (mw != NEG_INF) Lt += l_sh[ww][j] * exp2f(mw - M);
+  }
+  const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] *= f;
+  float* red = reinterpret_cast<float*>(smem);   // [8][16 heads][128 dims] fp32
+#pragma unroll 1
+  for (int sgap = kAttnWaves / 2; sgap >= 1; sgap >>= 1) {
+    __syncthreads();
+    if (w >= sgap && w < 2 * sgap) {
+      float* dst = red + ((size_t)(w - sgap) * 16 + j) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(dst + dt * 16 + 4 * Q) = O[dt];
+    }
+    __syncthreads();
+    if (w < sgap) {
+      const float* src = red + ((size_t)w * 16 + j) * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt] += *reinterpret_cast<const f4*>(src + dt * 16 + 4 * Q);
+    }
+  }
+  if (w == 0) {
+    const bool bad = nan_sh != 0;
+    const float inv = v_scale / Lt;
+    float* dst = out + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      f4 o = O[dt] * inv;
+      if (bad) o = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      *reinterpret_cast<f4*>(dst + dt * 16 + 4 * Q) = o;
+    }
+    if (lse != nullptr && Q == 0) {
+      const float v = (M + log2f(Lt)) * 0.69314718055994530942f;
+      lse[((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j] = bad ? __builtin_nanf("") : v;
+    }
+  }
+}
+
+// fp32 queries and caches: plain fp32 arithmetic on the vector ALUs.  One
+// workgroup per (sequence, token, group); thread (head h = tid/16, part =
+// tid%16) owns dims part*8 .. part*8+7 of head h's output.
+__global__ __launch_bounds__(256) void attn_f32_kernel(
+    const float* __restrict__ q, float c_nat, const float* __restrict__ kdata, int64_t kpages,
+    const float* __restrict__ vdata, int64_t vpages, float v_scale, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table, int max_blocks, int T,
+    float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float qs[16][kHeadDim];
+  __shared__ float logit[16][kBlock];
+  const int row = blockIdx.x;
+  const int g = row & 3, bt = row >> 2, t = bt % T, b = bt / T;
+  const int tid = threadIdx.x, h = tid >> 4, part = tid & 15;
+  const int L = seq_lens[b];
+  const int p = L - T + t;
+  const float NEG_INF = -__builtin_inff();
+  const float* qbase = q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup) * kHeadDim;
+  for (int e = tid; e < 16 * kHeadDim; e += 256) qs[e / kHeadDim][e % kHeadDim] = qbase[e];
+  float m = NEG_INF, lsum = 0.0f, o[8];
+  for (int d = 0; d < 8; ++d) o[d] = 0.0f;
+  bool bad = false;
+  for (int w = 0; w < kTopK; ++w) {
+    const int blk = sel[(size_t)row * kTopK + w];
+    if (blk < 0) continue;
+    if (blk >= max_blocks) { bad = true; continue; }
+    const int pg = table[(size_t)b * max_blocks + blk];
+    if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) { bad = true; continue; }
+    const int nkeys = min(kBlock, p + 1 - blk * kBlock);
+    if (nkeys <= 0) continue;
+    const size_t rowbase = ((size_t)pg * kGroups + g) * kBlock;
+    __syncthreads();
+    for (int kk = part; kk < kBlock; kk += 16) {
+      float v = NEG_INF;
+      if (kk < nkeys) {
+        const float* krow = kdata + (rowbase + kk) * kHeadDim;
+        float acc = 0.0f;
+        for (int d = 0; d < kHeadDim; ++d) acc = fmaf(qs[h][d], krow[d], acc);
+        v = acc * c_nat;
+      }
+      logit[h][kk] = v;
+    }
+    __syncthreads();
+    float bm = NEG_INF;
+    for (int kk = 0; kk < nkeys; ++kk) bm = fmaxf(bm, logit[h][kk]);
+    const float mn = fmaxf(m, bm);
+    const float corr = (m == NEG_INF) ? 0.0f : expf(m - mn);
+    lsum *= corr;
+    for (int d = 0; d < 8; ++d) o[d] *= corr;
+    for (int kk = 0; kk < nkeys; ++kk) {
+      const float pk = expf(logit[h][kk] - mn);
+      lsum += pk;
+      const float* vrow = vdata + (rowbase + kk) * kHeadDim + part * 8;
+      for (int d = 0; d < 8; ++d) o[d] = fmaf(pk, vrow[d], o[d]);
+    }
+    m = mn;
+  }
+  const int head = g * kHeadsPerGroup + h;
+  float* dst = out + (((size_t)b * T + t) * kHeads + head) * kHeadDim + part * 8;
+  for (int d = 0; d < 8; ++d) dst[d] = bad ? __builtin_nanf("") : o[d] * (v_scale / lsum);
+  if (lse != nullptr && part == 0)
+    lse[((size_t)b * T + t) * kHeads + head] = bad ? __builtin_nanf("") : m + logf(lsum);
+}
+
+hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, float q_scale,
+                            const CacheArgs& k, const CacheArgs& v, bool fp8mode,
+                            const int32_t* sel, float softmax_scale, float* out, float* lse,
+                            hipStream_t s) {
+  const unsigned rows = (unsigned)((int64_t)p.B * p.T * kGroups);
+  if (k.dtype == 0) {
+    const float c_nat = softmax_scale * q_scale * k.tensor_scale;
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(rows), dim3(256), 0, s, (const float*)q, c_nat,
+                       (const float*)k.data, k.num_pages, (const float*)v.data, v.num_pages,
+                       v.tensor_scale, sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse);
+    return hipGetLastError();
+  }
+  const float c_log2 = softmax_scale * q_scale * k.tensor_scale * 1.4426950408889634f;
+  const uint8_t* q8 = (const uint8_t*)q;
+#define MSA_ATTN_LAUNCH(KT, FM)                                                                 \
+  hipLaunchKernelGGL((attn_mfma_kernel<KT, FM>), dim3(rows), dim3(1024), 0, s, q8, c_log2, k.data, \
+                     k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale, sel,      \
+                     p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse)
+  if (k.dtype == 1) MSA_ATTN_LAUNCH(1, false);
+  else if (fp8mode) MSA_ATTN_LAUNCH(2, true);
+  else MSA_ATTN_LAUNCH(2, false);
+#undef MSA_ATTN_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace msa

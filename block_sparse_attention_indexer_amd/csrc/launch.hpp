@@ -1,0 +1,43 @@
+// Host-side launchers of the MSA kernels (internal to libmsa; the public
+// surface is include/msa.h).  Each returns hipGetLastError() after enqueueing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// Arguments common to the paged-cache kernels, already validated on the host.
+struct CacheArgs {
+  const uint8_t* data;     // F32 floats / FP8 bytes / NVFP4 codes
+  const uint8_t* scales;   // NVFP4 scale bytes or nullptr
+  int64_t num_pages;
+  float tensor_scale;
+  int dtype;               // 0 F32, 1 FP8, 2 NVFP4 (msa_dtype)
+};
+
+struct ProblemArgs {
+  int B, T, max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+};
+
+hipError_t launch_pack_fp8(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t s);
+hipError_t launch_unpack_fp8(const uint8_t* x, int64_t n, float scale, float* out, hipStream_t s);
+hipError_t launch_pack_nvfp4(const float* x, int64_t groups, float tensor_scale, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s);
+hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t groups,
+                               float tensor_scale, bool fp8mode, float* out, hipStream_t s);
+
+hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
+                          const CacheArgs& k, bool fp8mode, float* block_scores,
+                          float* token_scores, hipStream_t s);
+
+hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
+                       hipStream_t s);
+
+hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, float q_scale,
+                            const CacheArgs& k, const CacheArgs& v, bool fp8mode,
+                            const int32_t* sel, float softmax_scale, float* out, float* lse,
+                            hipStream_t s);
+
+}  // namespace msa

@@ -1,0 +1,189 @@
+/*
+ * msa.h -- C ABI of libmsa, the MI355X (gfx950) hot path of MiniMax Sparse
+ * Attention (MSA).
+ *
+ * The method (source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", English
+ * post, section "MSA primer" and its Figure 1 caption): the KV cache is cut
+ * into 128-token blocks; a lightweight indexer scores every key of the
+ * context with one index query per GQA group against one shared 128-dim
+ * index-key head; the scores are max-pooled into one score per block; exact
+ * attention then runs over the top 16 blocks only, the most recent block
+ * always kept, so a query attends at most 2,048 keys; every query head of a
+ * group uses its group's block set.  K/V and index keys are stored in FP8 or
+ * NVFP4 and the query is FP8 (sections "What is new in the MiniMax-M3.1
+ * architecture" and "NVIDIA Blackwell optimized MSA kernels").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Shapes are fixed by the model: groups G = 4 (= KV heads), 16 query
+ *    heads per group (64 query heads), head_dim 128, block 128 tokens,
+ *    top-k 16.  Other values return MSA_ERR_UNSUPPORTED.
+ *  - Sequence b has length L_b = seq_lens[b], counting its T new query
+ *    tokens; query token t sits at position p = L_b - T + t, sees keys 0..p,
+ *    and its own ("most recent") block is p / 128.
+ *  - A paged cache holds pages of 128 tokens.  Page `pg`, head `h`, token `r`
+ *    of a cache with `heads` heads is row ((pg*heads + h)*128 + r):
+ *       MSA_F32      : 128 floats per row
+ *       MSA_FP8_E4M3 : 128 bytes per row (OCP E4M3)
+ *       MSA_NVFP4    : 64 bytes of E2M1 codes per row in `data` (two per
+ *                      byte, even dim in the low nibble) and 8 E4M3 scale
+ *                      bytes per row in `scales` (one per 16 dims)
+ *    Logical block i of sequence b lives in page block_table[b*max_blocks+i].
+ *    The index-key cache has heads = 1; the K and V caches have heads = 4.
+ *  - Every decoded value is tensor_scale * element (NVFP4: tensor_scale *
+ *    e4m3(scale byte) * e2m1(code), or that product re-rounded to E4M3 under
+ *    MSA_DQ_FP8).
+ *  - Ownership: every array is caller-owned device memory (except where a
+ *    host pointer is stated).  The library allocates nothing on these
+ *    paths and keeps no state besides immutable code; calls are re-entrant.
+ *  - Asynchrony: every compute call enqueues its kernels on `stream` and
+ *    returns at once; outputs are valid once the stream reaches that point.
+ *  - Errors: argument errors that can be seen from the host (null pointers,
+ *    unsupported shapes or dtype pairs, non-positive scales, a workspace
+ *    that is too small) return their status before any HIP call and leave
+ *    the outputs untouched.  A failed launch returns MSA_ERR_HIP.  Device
+ *    arrays are not validated from the host: seq_lens must satisfy
+ *    T <= L_b <= max_blocks*128; a page id outside [0, num_pages) is never
+ *    dereferenced -- that block's scores and any attention output touching
+ *    it become NaN.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, non-positive scale   */
+  MSA_ERR_UNSUPPORTED = 2,   /* shape or dtype combination not implemented   */
+  MSA_ERR_WORKSPACE = 3,     /* workspace null or smaller than required      */
+  MSA_ERR_HIP = 4            /* a HIP launch or query failed                 */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_FP8_E4M3 = 1, MSA_NVFP4 = 2 } msa_dtype;
+
+/* How NVFP4 elements are decoded before a dot product (ignored for F32/FP8).
+ *  MSA_DQ_EXACT: e2m1 * e4m3 scale, exactly -- the reading under which
+ *    "the scores become exact" ("NVIDIA Rubin optimized MSA").
+ *  MSA_DQ_FP8:   that product re-rounded to E4M3 (nearest-even, saturating
+ *    at 448), as the Blackwell and CDNA4 kernels that feed an FP8 MMA do
+ *    ("NVIDIA Blackwell optimized MSA kernels", "NVFP4 MSA kernel"). */
+typedef enum { MSA_DQ_EXACT = 0, MSA_DQ_FP8 = 1 } msa_dequant;
+
+typedef struct {
+  msa_dtype dtype;
+  const void* data;          /* F32 floats, FP8 bytes, or NVFP4 codes        */
+  const uint8_t* scales;     /* NVFP4 only: 8 E4M3 bytes per row; else NULL  */
+  float tensor_scale;        /* > 0, finite                                  */
+  int32_t heads;             /* 1 for the index-key cache, 4 for K and V     */
+  int32_t head_dim;          /* 128                                          */
+  int64_t num_pages;         /* pages in the pool                            */
+} msa_cache;
+
+typedef struct {
+  int32_t batch;             /* B >= 1                                       */
+  int32_t tokens;            /* T >= 1 query tokens per sequence             */
+  int32_t groups;            /* 4                                            */
+  int32_t heads_per_group;   /* 16                                           */
+  int32_t head_dim;          /* 128                                          */
+  int32_t block_size;        /* 128                                          */
+  int32_t topk;              /* 16                                           */
+  const int32_t* seq_lens;   /* device [B]                                   */
+  const int32_t* block_table;/* device [B][max_blocks]                       */
+  int32_t max_blocks;        /* >= 1; <= 8192                                */
+} msa_problem;
+
+/* Steps 1+2: index scores max-pooled per block ("MSA primer": a lightweight
+ * indexer scores every key with one index query per GQA group against a
+ * single shared index-key head, then max-pools the scores per block).
+ *   idx_q        device [B][T][4][128]: F32 floats or FP8 bytes (q_dtype),
+ *                each decoded value times q_scale.
+ *   idx_k        the index-key cache (heads = 1): F32 with F32 queries;
+ *                FP8 or NVFP4 with FP8 queries.
+ *   block_scores device out [B][T][4][max_blocks] fp32:
+ *                max over block i's keys j <= p of (q . k); -inf for blocks
+ *                wholly after p and for i >= ceil(L_b/128).
+ *   token_scores device out, nullable, [B][T][4][max_blocks*128] fp32:
+ *                the per-key scores (-inf past p), for inspection only.
+ * Any T >= 1: T <= 8 runs the decode scan, larger T the prefill kernel. */
+msa_status msa_indexer_scores(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
+                              float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                              float* block_scores, float* token_scores, hipStream_t stream);
+
+/* Step 3: top-16 blocks per (sequence, token, group) ("MSA primer": the top
+ * 16 blocks, the most recent block always kept).  With own+1 <= 16 visible
+ * blocks all of them are selected; otherwise the own block plus the 15 best
+ * older blocks by (score descending, block index ascending).  NaN ranks
+ * below every number.
+ *   block_scores device [B][T][4][max_blocks] (as written above).
+ *   sel          device out [B][T][4][16] int32 logical block ids,
+ *                ascending, padded with -1. */
+msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, int32_t* sel,
+                          hipStream_t stream);
+
+/* Step 4: exact attention over the selected blocks ("MSA primer" and Figure
+ * 1: attention runs exactly, but only over the selected blocks; every query
+ * head of a group uses its group's selection).  Head h uses group h / 16.
+ *   q            device [B][T][64][128]: F32 floats or FP8 bytes, times q_scale.
+ *   k, v         caches with heads = 4 (F32 with F32 q; FP8 or NVFP4 with FP8 q).
+ *   sel          device [B][T][4][16] as written by msa_block_topk.
+ *   softmax_scale  logits are softmax_scale * (q . k) (1/sqrt(128) for MSA).
+ *   out          device out [B][T][64][128] fp32.
+ *   lse          device out, nullable, [B][T][64] fp32: natural-log
+ *                log-sum-exp of the scaled logits.
+ *   workspace    device scratch of at least msa_workspace_size(prob,
+ *                MSA_CALL_ATTN) bytes (may be NULL when that size is 0).
+ * msa_sparse_attn_decode requires T <= 8; msa_sparse_attn_prefill takes any
+ * T >= 1 (same results). */
+msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, msa_dtype q_dtype,
+                                  float q_scale, const msa_cache* k, const msa_cache* v,
+                                  msa_dequant dequant, const int32_t* sel, float softmax_scale,
+                                  float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_dtype q_dtype,
+                                   float q_scale, const msa_cache* k, const msa_cache* v,
+                                   msa_dequant dequant, const int32_t* sel, float softmax_scale,
+                                   float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+typedef enum { MSA_CALL_INDEXER = 0, MSA_CALL_TOPK = 1, MSA_CALL_ATTN = 2 } msa_call;
+
+/* Bytes of device workspace a call needs for this problem (0 = none).
+ * Reads only host-visible fields of prob. */
+size_t msa_workspace_size(const msa_problem* prob, msa_call which);
+
+/* Pack / unpack helpers (section "QKV GEMM + norm + RoPE + KV insert fusion":
+ * K, V and the index key are quantised to NVFP4 when inserted).
+ * FP8:   out[i] = E4M3_RNE_SAT(x[i] / scale), the division in fp32.
+ * NVFP4: rows of row_len (a multiple of 16) floats; per 16 elements
+ *        scale byte s = E4M3_RNE_SAT(amax / (6*tensor_scale)) and
+ *        code = E2M1_RNE(x / (e4m3(s)*tensor_scale)) clamped to +-6, every
+ *        step in fp32 in that order; s = 0 gives zero codes.  codes has
+ *        rows*row_len/2 bytes, scales rows*row_len/16 bytes.
+ * Unpack writes fp32: scale * value (NVFP4 value per `dequant`).
+ * Inputs must be finite. */
+msa_status msa_pack_fp8(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t stream);
+msa_status msa_unpack_fp8(const uint8_t* x, int64_t n, float scale, float* out, hipStream_t stream);
+msa_status msa_pack_nvfp4(const float* x, int64_t rows, int32_t row_len, float tensor_scale,
+                          uint8_t* codes, uint8_t* scales, hipStream_t stream);
+msa_status msa_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                            int32_t row_len, float tensor_scale, msa_dequant dequant, float* out,
+                            hipStream_t stream);
+
+/* Static string for a status code; never NULL. */
+const char* msa_status_string(msa_status s);
+/* MSA_ABI_VERSION of the built library. */
+int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

@@ -1,0 +1,119 @@
+"""The C-ABI library loads on a host without a GPU, exports every function
+include/msa.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_indexer_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:msa_status|size_t|const char\*|int)\s+(msa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        pytest.skip("libmsa.so not built")
+    return M._lib()
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_functions() == sorted(M.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.msa_abi_version() == 1
+    for s in range(5):
+        assert lib.msa_status_string(s)
+
+
+def _prob(**kw):
+    d = dict(batch=2, tokens=1, groups=4, heads_per_group=16, head_dim=128, block_size=128, topk=16,
+             seq_lens=64, block_table=128, max_blocks=8)
+    d.update(kw)
+    return M.msa_problem(**d)
+
+
+def _cache(**kw):
+    d = dict(dtype=M.MSA_NVFP4, data=256, scales=512, tensor_scale=0.5, heads=1, head_dim=128, num_pages=4)
+    d.update(kw)
+    return M.msa_cache(**d)
+
+
+def idx(lib, prob, cache, q=1024, qd=M.MSA_FP8_E4M3, qs=1.0, dq=M.MSA_DQ_EXACT, bs=2048):
+    return lib.msa_indexer_scores(ctypes.byref(prob) if prob is not None else None, q, qd, qs,
+                                  ctypes.byref(cache) if cache is not None else None, dq, bs, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(groups=8), M.MSA_ERR_UNSUPPORTED), (dict(head_dim=64), M.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=64), M.MSA_ERR_UNSUPPORTED), (dict(topk=8), M.MSA_ERR_UNSUPPORTED),
+    (dict(heads_per_group=8), M.MSA_ERR_UNSUPPORTED), (dict(batch=0), M.MSA_ERR_INVALID_ARG),
+    (dict(tokens=0), M.MSA_ERR_INVALID_ARG), (dict(max_blocks=0), M.MSA_ERR_INVALID_ARG),
+    (dict(max_blocks=9000), M.MSA_ERR_UNSUPPORTED), (dict(seq_lens=None), M.MSA_ERR_INVALID_ARG),
+    (dict(block_table=None), M.MSA_ERR_INVALID_ARG), (dict(seq_lens=66), M.MSA_ERR_INVALID_ARG),
+])
+def test_problem_validation(lib, kw, status):
+    assert idx(lib, _prob(**kw), _cache()) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(data=None), M.MSA_ERR_INVALID_ARG), (dict(scales=None), M.MSA_ERR_INVALID_ARG),
+    (dict(heads=4), M.MSA_ERR_INVALID_ARG), (dict(head_dim=64), M.MSA_ERR_UNSUPPORTED),
+    (dict(tensor_scale=0.0), M.MSA_ERR_INVALID_ARG), (dict(tensor_scale=-1.0), M.MSA_ERR_INVALID_ARG),
+    (dict(tensor_scale=math.inf), M.MSA_ERR_INVALID_ARG), (dict(num_pages=0), M.MSA_ERR_INVALID_ARG),
+    (dict(dtype=7), M.MSA_ERR_UNSUPPORTED), (dict(data=257), M.MSA_ERR_INVALID_ARG),
+])
+def test_cache_validation(lib, kw, status):
+    assert idx(lib, _prob(), _cache(**kw)) == status
+
+
+def test_dtype_pairs_and_scalars(lib):
+    assert idx(lib, None, _cache()) == M.MSA_ERR_INVALID_ARG
+    assert idx(lib, _prob(), None) == M.MSA_ERR_INVALID_ARG
+    assert idx(lib, _prob(), _cache(), qd=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED          # f32 q, nvfp4 keys
+    assert idx(lib, _prob(), _cache(dtype=M.MSA_F32), qd=M.MSA_FP8_E4M3) == M.MSA_ERR_UNSUPPORTED
+    assert idx(lib, _prob(), _cache(), qs=0.0) == M.MSA_ERR_INVALID_ARG
+    assert idx(lib, _prob(), _cache(), dq=5) == M.MSA_ERR_INVALID_ARG
+    assert idx(lib, _prob(), _cache(), q=None) == M.MSA_ERR_INVALID_ARG
+    assert idx(lib, _prob(), _cache(), bs=None) == M.MSA_ERR_INVALID_ARG
+
+
+def test_attention_and_topk_validation(lib):
+    p = _prob()
+    kc = _cache(heads=4)
+    args = lambda **o: dict(dict(q=1024, qd=M.MSA_FP8_E4M3, qs=1.0, k=kc, v=kc, dq=0, sel=4096, sm=0.088, out=8192), **o)
+
+    def call(fn, a, prob=p):
+        return fn(ctypes.byref(prob), a["q"], a["qd"], a["qs"], ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                  a["dq"], a["sel"], a["sm"], a["out"], None, None, 0, None)
+    assert call(lib.msa_sparse_attn_decode, args(sel=None)) == M.MSA_ERR_INVALID_ARG
+    assert call(lib.msa_sparse_attn_decode, args(out=None)) == M.MSA_ERR_INVALID_ARG
+    assert call(lib.msa_sparse_attn_decode, args(sm=0.0)) == M.MSA_ERR_INVALID_ARG
+    assert call(lib.msa_sparse_attn_decode, args(v=_cache(heads=4, dtype=M.MSA_FP8_E4M3))) == M.MSA_ERR_UNSUPPORTED
+    assert call(lib.msa_sparse_attn_decode, args(k=_cache(heads=1))) == M.MSA_ERR_INVALID_ARG
+    assert call(lib.msa_sparse_attn_decode, args(), prob=_prob(tokens=9)) == M.MSA_ERR_UNSUPPORTED
+    assert lib.msa_block_topk(ctypes.byref(p), None, 4096, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_block_topk(ctypes.byref(p), 4096, None, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_ATTN) == 0
+
+
+def test_pack_validation(lib):
+    assert lib.msa_pack_nvfp4(None, 1, 128, 1.0, 64, 64, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_pack_nvfp4(64, 1, 100, 1.0, 64, 64, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_pack_nvfp4(64, 1, 128, 0.0, 64, 64, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_pack_nvfp4(64, 0, 128, 1.0, 64, 64, None) == M.MSA_OK          # empty: no launch
+    assert lib.msa_unpack_nvfp4(64, 64, 1, 128, 1.0, 9, 64, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_pack_fp8(None, 4, 1.0, 64, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_pack_fp8(64, -1, 1.0, 64, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_pack_fp8(64, 0, 1.0, 64, None) == M.MSA_OK
+    assert lib.msa_unpack_fp8(64, 4, float("nan"), 64, None) == M.MSA_ERR_INVALID_ARG

@@ -1,0 +1,193 @@
+"""HIP path against the CPU fp64 oracle, through the C ABI.
+
+Bars: pack/unpack bit-exact; block scores within 1e-5 relative (1 + |s|);
+selected block ids bit-exact except rows the oracle flags as near-ties
+(16th/17th scores within 1e-5 relative), which must still be a valid top-16;
+attention within max-abs 2e-3 and mean-abs 2e-4 of the oracle run on the
+GPU's selection; LSE within 1e-4."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as OF
+from oracle import msa as OM
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import block_sparse_attention_indexer_amd as M
+    assert os.path.exists(M.LIB_PATH), "libmsa.so must be built before the GPU tests"
+    return M
+
+
+def _say(*a):
+    print("[gpu-test]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ pack / unpack
+
+def _edge_values(rng):
+    pos = OF.e4m3_value(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    return np.concatenate([rng.normal(0, 1, 60000), rng.normal(0, 100, 20000), mids, -mids, pos, -pos,
+                           [0.0, -0.0, 448.0, 460.0, 470.0, 1e5, -1e5, 2.0 ** -10, 3 * 2.0 ** -11]]).astype(np.float32)
+
+
+@pytest.mark.parametrize("scale", [1.0, float(np.float32(0.37)), float(np.float32(32.0 / 448.0))])
+def test_pack_fp8_bit_exact(M, scale):
+    x = _edge_values(np.random.default_rng(1))
+    x = x[: (len(x) // 4) * 4]
+    d = torch.from_numpy(x).cuda()
+    out = torch.empty(len(x), dtype=torch.uint8, device="cuda")
+    M.msa_pack_fp8(d, scale, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), OF.fp8_quantize(x, scale))
+
+
+@pytest.mark.parametrize("S", [float(np.float32(32.0 / 448.0)), 1.0, float(np.float32(0.0123)), 5.0])
+def test_pack_nvfp4_bit_exact(M, S):
+    rng = np.random.default_rng(2)
+    x = rng.normal(0, 1, (2048, 128)).astype(np.float32)
+    x[rng.random(x.shape) < 0.05] *= 4.0
+    x[5, 16:32] = 0.0                      # an all-zero group
+    x[6] = _edge_values(rng)[:128]
+    x[7, :16] = np.float32(1e-7)           # scale underflows to zero
+    d = torch.from_numpy(x).cuda()
+    codes = torch.empty((2048, 64), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((2048, 8), dtype=torch.uint8, device="cuda")
+    M.msa_pack_nvfp4(d, S, codes, sc)
+    torch.cuda.synchronize()
+    oc, os_ = OF.nvfp4_quantize(x, S)
+    assert np.array_equal(sc.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+@pytest.mark.parametrize("mode", ["exact", "fp8"])
+def test_unpack_nvfp4_every_scale_and_code(M, mode):
+    scales = np.array([s for s in range(256) if not (s & 0x80) and s != 0x7F], dtype=np.uint8)
+    codes16 = np.arange(16, dtype=np.uint8)
+    row = (codes16[0::2] | (codes16[1::2] << 4)).astype(np.uint8)       # 16 codes
+    codes = np.tile(row, (len(scales), 1))                               # [n, 8] -> 16 elements per row
+    sb = scales[:, None].copy()
+    for S in [1.0, float(np.float32(32.0 / 448.0))]:
+        out = torch.empty((len(scales), 16), dtype=torch.float32, device="cuda")
+        M.msa_unpack_nvfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(sb).cuda(), 16, S, mode, out)
+        torch.cuda.synchronize()
+        ref = OF.nvfp4_dequantize(codes, sb, S, OF.EXACT if mode == "exact" else OF.FP8_ROUNDED)
+        assert np.array_equal(out.cpu().numpy(), ref.astype(np.float32))
+
+
+def test_unpack_fp8_every_code(M):
+    b = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    for S in [1.0, float(np.float32(0.37))]:
+        out = torch.empty(len(b), dtype=torch.float32, device="cuda")
+        M.msa_unpack_fp8(torch.from_numpy(b).cuda(), S, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), OF.fp8_dequantize(b, S).astype(np.float32))
+
+
+# ------------------------------------------------------------------ small cases, full comparison
+
+SMALL = [("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"),
+         ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"), ("tiny_spec", "fp8"),
+         ("tiny_prefill", "exact"), ("tiny_prefill", "fp8")]
+
+
+@pytest.mark.parametrize("wname,mode", SMALL)
+def test_layer_parity_small(M, wname, mode):
+    _say("small case", wname, mode)
+    case = H.HostCase(wname).upload()
+    w, lay = case.w, case.lay
+    res = H.to_host(H.run_path(case, mode, token_scores=True))
+    seq_lens, table = lay.seq_lens.numpy(), lay.block_table.numpy()
+    ora = H.oracle_scores(case.caches, case.idx_q, seq_lens, table, w.T, mode, w.q_dtype)
+    H.compare_scores(res["block_scores"], ora["block_scores"])
+    # per-key scores
+    for b in range(w.B):
+        L = int(seq_lens[b])
+        iq = OM.decode_query(case.idx_q[b], w.q_dtype, 1.0)
+        ik = OM.sequence_view(case.caches["idx_k"], table[b], L, mode)[0]
+        s = OM.indexer_token_scores(iq, ik, L, w.T)
+        full = np.full((w.T, 4, lay.max_blocks * 128), -np.inf)
+        full[:, :, :L] = s
+        H.compare_scores(res["token_scores"][b], full)
+    nties = H.compare_selection(res["sel"], ora["sel"], ora["block_scores"], ora["near_tie"], seq_lens, w.T)
+    for b in range(w.B):
+        o, lse = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, res["sel"][b], mode, w.q_dtype, b)
+        H.compare_out(res["out"][b], o)
+        assert np.abs(res["lse"][b] - lse).max() <= 1e-4
+    _say(wname, mode, "ok; near-tie rows that differ:", nties)
+
+
+def test_deterministic_and_page_order_invariant(M):
+    case = H.HostCase("tiny_nvfp4").upload()
+    r1 = H.to_host(H.run_path(case, "exact"))
+    r2 = H.to_host(H.run_path(case, "exact"))
+    for k in ("block_scores", "sel", "out", "lse"):
+        assert np.array_equal(r1[k], r2[k]), k
+    # permute the physical pages and the table consistently
+    P = case.lay.num_pages
+    perm = np.random.default_rng(9).permutation(P)            # new page id of old page p: perm[p]
+    inv = np.argsort(perm)
+    for name, (data, scales, _) in list(case.d_caches.items()):
+        nd = data[torch.from_numpy(inv).cuda()].contiguous()
+        ns = scales[torch.from_numpy(inv).cuda()].contiguous() if scales is not None else None
+        heads = 1 if name == "idx_k" else 4
+        case.d_caches[name] = (nd, ns, M.cache("nvfp4", nd, ns, case.S, heads))
+    tab = case.lay.block_table.numpy()
+    new_tab = np.where(tab >= 0, perm[np.maximum(tab, 0)], -1).astype(np.int32)
+    case.d_table = torch.from_numpy(new_tab).cuda()
+    r3 = H.to_host(H.run_path(case, "exact"))
+    for k in ("block_scores", "sel", "out", "lse"):
+        assert np.array_equal(r1[k], r3[k]), k
+
+
+def test_out_of_range_page_gives_nan_not_a_fault(M):
+    case = H.HostCase("tiny_fp8").upload()
+    tab = case.lay.block_table.numpy().copy()
+    tab[0, 2] = case.lay.num_pages + 5            # never dereferenced by the kernels
+    case.d_table = torch.from_numpy(tab).cuda()
+    res = H.to_host(H.run_path(case, "exact", attention=False))
+    assert np.isnan(res["block_scores"][0, :, :, 2]).all()
+    assert not np.isnan(res["block_scores"][1]).any()
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+
+FULL = [("c2", [0, 17, 31]), ("c3", [0, 21, 63]), ("c3_128k", [5, 40]), ("c4", [3, 11]), ("c5", [1])]
+
+
+@pytest.mark.parametrize("wname,samples", FULL)
+def test_full_size_sampled(M, wname, samples):
+    _say("full-size case", wname, "samples", samples)
+    case = H.DeviceCase(wname)
+    w, lay = case.w, case.lay
+    res = H.to_host(H.run_path(case, "exact"))
+    T = w.T
+    for b in samples:
+        gsel = res["sel"][b]
+        # oracle scores over the whole sequence, K/V packed for the oracle's and GPU's blocks
+        inp = case.oracle_inputs(b, kv_blocks=None if w.kv_dtype == "f32" else [])
+        ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], T, "exact", w.q_dtype)
+        H.compare_scores(res["block_scores"][b:b + 1], ora["block_scores"])
+        H.compare_selection(gsel[None], ora["sel"], ora["block_scores"], ora["near_tie"], inp["seq_lens"], T)
+        blocks = np.union1d(gsel[gsel >= 0], ora["sel"][ora["sel"] >= 0])
+        inp = case.oracle_inputs(b, kv_blocks=blocks)
+        rows = range(T) if T <= 8 else np.random.default_rng(b).choice(T, 64, replace=False)
+        for t in rows:
+            qq = OM.decode_query(inp["q"][0, t:t + 1], w.q_dtype, 1.0)
+            L = int(inp["seq_lens"][0])
+            K = OM.sequence_view(inp["caches"]["k"], inp["kv_table"][0], L)
+            V = OM.sequence_view(inp["caches"]["v"], inp["kv_table"][0], L)
+            # a single query token at position L - T + t: view the sequence as ending there
+            Lt = L - T + t + 1
+            o, lse = OM.sparse_attention(qq, K[:, :Lt], V[:, :Lt], gsel[t:t + 1], Lt, 1, H.SOFTMAX_SCALE)
+            H.compare_out(res["out"][b, t], o[0])
+            assert np.abs(res["lse"][b, t] - lse[0]).max() <= 1e-4
+        _say(wname, "sample", b, "ok")
