@@ -6,18 +6,22 @@
 // set, so a query reads full K/V for at most 2,048 keys.
 //
 // One workgroup per (sequence, query token, group) with 16 waves; wave w
-// takes the w-th selected block.  Per block (one KV head, 16 query heads):
+// takes the w-th selected block.  All of a block's K loads and the first V
+// tiles are issued together right after the block-table lookup, so a wave
+// waits on memory about twice (K, then the rest of V) rather than once per
+// tile.  Per block (one KV head, 16 query heads):
 //   S^T = K Q^T on 16x16x32 f16 MFMAs (A = 16 keys x 32 dims of K, straight
 //         from the page: lane quarter Q loads dims [32Q, 32Q+32) of its key;
-//         B = Q^T, the 16 heads of the group, loaded once);
+//         B = Q^T, the 16 heads of the group);
 //   softmax over the block's <= 128 keys in fp32 (exp2 domain);
 //   O^T += V^T P^T on 16x16x16 f16 MFMAs.  The lane layout of S^T is exactly
 //         the B operand P^T of the next product, so P never leaves registers;
 //         P is split into f16 hi + lo parts (two MFMAs) to keep ~2^-22
 //         relative precision.  V^T is staged per 16-key tile through a
-//         wave-private LDS slice (dequantised, transposed).
-// The 16 per-block partial states (max, sum, O) are merged in fixed order
-// (max, then a 4-level tree over LDS), so results are deterministic.
+//         wave-private LDS slice (dequantised, transposed); keys past the
+//         query's position are staged as zeros.
+// The 16 per-block partial states (max, sum, O) are merged in one pass over
+// LDS, summed in wave order, so results are deterministic.
 // FP8 and NVFP4 values are exact in f16; the products are exact and the
 // accumulation is fp32.
 #include <math.h>
@@ -40,6 +44,120 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// One 16-key tile of K or V as loaded from a page, before decoding.
+//   K tile, lane (quarter Q, key j): dims [32Q, 32Q+32) of key j.
+//   V tile, lane (key pair kp, 16-dim group dg): dims [16dg, 16dg+16) of keys 2kp, 2kp+1.
+template <int KT> struct KRaw;
+template <> struct KRaw<1> { uint4 c0, c1; };
+template <> struct KRaw<2> { uint4 c; uint32_t s; };
+template <int KT> struct VRaw;
+template <> struct VRaw<1> { uint4 c[2]; };
+template <> struct VRaw<2> { uint2 c[2]; uint32_t s[2]; };
+
+template <int KT>
+__device__ __forceinline__ KRaw<KT> load_k_tile(const uint8_t* kdata, const uint8_t* kscales,
+                                                 size_t krow, int Q) {
+  KRaw<KT> r;
+  if constexpr (KT == 2) {
+    r.c = *reinterpret_cast<const uint4*>(kdata + krow * kNvfp4RowBytes + 16 * Q);
+    r.s = *reinterpret_cast<const uint16_t*>(kscales + krow * kNvfp4ScaleBytes + 2 * Q);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(kdata + krow * kHeadDim + 32 * Q);
+    r.c0 = src[0];
+    r.c1 = src[1];
+  }
+  return r;
+}
+
+template <int KT>
+__device__ __forceinline__ VRaw<KT> load_v_tile(const uint8_t* vdata, const uint8_t* vscales,
+                                                 size_t vrow0, int dg) {
+  VRaw<KT> r;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const size_t vrow = vrow0 + u;
+    if constexpr (KT == 2) {
+      r.c[u] = *reinterpret_cast<const uint2*>(vdata + vrow * kNvfp4RowBytes + 8 * dg);
+      r.s[u] = vscales[vrow * kNvfp4ScaleBytes + dg];
+    } else {
+      r.c[u] = *reinterpret_cast<const uint4*>(vdata + vrow * kHeadDim + 16 * dg);
+    }
+  }
+  return r;
+}
+
+// K tile -> the four 16x32 A fragments of S^T = K Q^T (k-chunk c = dims 32Q+8c .. +7).
+template <int KT, bool FP8MODE>
+__device__ __forceinline__ void decode_k_tile(const KRaw<KT>& r, const uint32_t* lut, h8 (&Ak)[4]) {
+  if constexpr (KT == 2) {
+    const uint32_t wv[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
+    if constexpr (FP8MODE) {
+      const uint32_t s0 = r.s & 0xFFu, s1 = (r.s >> 8) & 0xFFu;
+      Ak[0] = fp4x8_lut_to_h8(wv[0], lut[2 * s0], lut[2 * s0 + 1]);
+      Ak[1] = fp4x8_lut_to_h8(wv[1], lut[2 * s0], lut[2 * s0 + 1]);
+      Ak[2] = fp4x8_lut_to_h8(wv[2], lut[2 * s1], lut[2 * s1 + 1]);
+      Ak[3] = fp4x8_lut_to_h8(wv[3], lut[2 * s1], lut[2 * s1 + 1]);
+    } else {
+      const h2 sc = fp8x2_to_h2<false>(r.s);
+      const h8 s0 = h8{sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+      const h8 s1 = h8{sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+      Ak[0] = fp4x8_to_h8(wv[0]) * s0;
+      Ak[1] = fp4x8_to_h8(wv[1]) * s0;
+      Ak[2] = fp4x8_to_h8(wv[2]) * s1;
+      Ak[3] = fp4x8_to_h8(wv[3]) * s1;
+    }
+  } else {
+    Ak[0] = fp8x8_to_h8(r.c0.x, r.c0.y);
+    Ak[1] = fp8x8_to_h8(r.c0.z, r.c0.w);
+    Ak[2] = fp8x8_to_h8(r.c1.x, r.c1.y);
+    Ak[3] = fp8x8_to_h8(r.c1.z, r.c1.w);
+  }
+}
+
+// V tile -> this lane's 2 keys x 16 dims as f16, written transposed (V^T,
+// dim-major, key pairs packed in one dword) into the wave's LDS slice.
+// Keys at or past `valid` are written as zeros, so unwritten rows of a
+// partly filled page never reach the product (0 * NaN would).
+template <int KT, bool FP8MODE>
+__device__ __forceinline__ void stage_v_tile(const VRaw<KT>& r, const uint32_t* lut, uint32_t* vt,
+                                             int kp, int dg, bool keep0, bool keep1) {
+  h8 v0[2], v1[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    h8* dst = u == 0 ? v0 : v1;
+    if constexpr (KT == 2) {
+      const uint32_t sb = r.s[u];
+      if constexpr (FP8MODE) {
+        dst[0] = fp4x8_lut_to_h8(r.c[u].x, lut[2 * sb], lut[2 * sb + 1]);
+        dst[1] = fp4x8_lut_to_h8(r.c[u].y, lut[2 * sb], lut[2 * sb + 1]);
+      } else {
+        const _Float16 sh = e4m3_to_h(sb);
+        const h8 ss = h8{sh, sh, sh, sh, sh, sh, sh, sh};
+        dst[0] = fp4x8_to_h8(r.c[u].x) * ss;
+        dst[1] = fp4x8_to_h8(r.c[u].y) * ss;
+      }
+    } else {
+      dst[0] = fp8x8_to_h8(r.c[u].x, r.c[u].y);
+      dst[1] = fp8x8_to_h8(r.c[u].z, r.c[u].w);
+    }
+  }
+  const h8 zero = h8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const h8 a = keep0 ? v0[hh] : zero;
+    const h8 c = keep1 ? v1[hh] : zero;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 16 * dg + 8 * hh + ((KT == 2 && FP8MODE) ? lut_perm(e) : e);
+      vt[vt_index(d, kp)] = pack_h2(a[e], c[e]);
+    }
+  }
+}
+
+// V tiles in flight ahead of the one being multiplied.
+template <int KT> constexpr int kVAhead = KT == 2 ? 4 : 2;
+constexpr int kMergeStride = kHeadDim + 4;   // fp32 row of one head in the merge buffer (padded)
+
 // KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).
 template <int KT, bool FP8MODE>
 __global__ __launch_bounds__(1024) void attn_mfma_kernel(
@@ -50,12 +168,11 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
     const int32_t* __restrict__ table, int max_blocks, int T, float* __restrict__ out,
     float* __restrict__ lse) {
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
-  __shared__ __attribute__((aligned(16))) uint32_t smem[kAttnWaves * kVtDwords];
+  // V^T staging (16 x kVtDwords dwords), later reused as the merge buffer
+  // [16 waves][16 heads][kMergeStride] fp32.
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kAttnWaves * 16 * kMergeStride];
   __shared__ float m_sh[kAttnWaves][16], l_sh[kAttnWaves][16];
   __shared__ int nan_sh;
-  if (threadIdx.x == 0) nan_sh = 0;
-  if (FP8MODE) build_fp8_lut(lut);
-  __syncthreads();
 
   const int row = blockIdx.x;   // (b*T + t)*4 + g
   const int g = row & 3;
@@ -63,21 +180,32 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
   const int t = bt % T, b = bt / T;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int Q = lane >> 4, j = lane & 15;
-  const int L = seq_lens[b];
-  const int p = L - T + t;
   const float NEG_INF = -__builtin_inff();
 
-  // B operand of S^T = K Q^T: lane (Q, head j), k-chunk c = dims 32Q+8c..+7.
-  h8 Bq[4];
-  {
-    const uint4* src =
-        reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
-    const uint4 u0 = src[0], u1 = src[1];
-    const uint32_t wq[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
-      Bq[c] = (KT == 2 && FP8MODE) ? reorder_like_lut_a(a) : a;
+  // independent loads first: length, this wave's block, the query
+  const int L = seq_lens[b];
+  const int blk = sel[(size_t)row * kTopK + w];
+  const uint4* qsrc =
+      reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
+  const uint4 qu0 = qsrc[0], qu1 = qsrc[1];
+  if (threadIdx.x == 0) nan_sh = 0;
+  if (FP8MODE) build_fp8_lut(lut);
+  __syncthreads();
+
+  const int p = L - T + t;
+  int nkeys = 0;
+  size_t rowbase = 0;
+  if (blk >= 0) {
+    if (blk >= max_blocks) {
+      nan_sh = 1;
+    } else {
+      const int pg = table[(size_t)b * max_blocks + blk];
+      if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
+        nan_sh = 1;
+      } else {
+        nkeys = min(kBlock, p + 1 - blk * kBlock);
+        rowbase = ((size_t)pg * kGroups + g) * kBlock;   // (page, KV head g)
+      }
     }
   }
 
@@ -86,56 +214,36 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int blk = sel[(size_t)row * kTopK + w];
-  int nkeys = 0;
-  int pg = -1;
-  if (blk >= 0) {
-    if (blk >= max_blocks) {
-      nan_sh = 1;
-    } else {
-      pg = table[(size_t)b * max_blocks + blk];
-      if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
-        nan_sh = 1;
-      } else {
-        nkeys = min(kBlock, p + 1 - blk * kBlock);
+  if (nkeys > 0) {
+    const int kp = lane & 7;     // key pair within a V tile (keys 2kp, 2kp+1)
+    const int dg = lane >> 3;    // 16-dim group of a V tile
+    // Every K load and the first V tiles are issued before the first product.
+    // All 128 rows of the page are read (they exist even when the block is
+    // only partly visible), which keeps control flow uniform so that each
+    // wait covers exactly the tile it needs.
+    KRaw<KT> kraw[8];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) kraw[kt] = load_k_tile<KT>(kdata, kscales, rowbase + kt * 16 + j, Q);
+    VRaw<KT> vraw[8];
+#pragma unroll
+    for (int kt = 0; kt < kVAhead<KT>; ++kt)
+      vraw[kt] = load_v_tile<KT>(vdata, vscales, rowbase + kt * 16 + 2 * kp, dg);
+
+    h8 Bq[4];
+    {
+      const uint32_t wq[8] = {qu0.x, qu0.y, qu0.z, qu0.w, qu1.x, qu1.y, qu1.z, qu1.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
+        Bq[c] = (KT == 2 && FP8MODE) ? reorder_like_lut_a(a) : a;
       }
     }
-  }
-  if (nkeys > 0) {
-    const size_t rowbase = ((size_t)pg * kGroups + g) * kBlock;   // (page, KV head g)
     // ---------------- S^T = K Q^T, 8 tiles of 16 keys
     float x[8][4];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
-      const size_t krow = rowbase + kt * 16 + j;
       h8 Ak[4];
-      if (KT == 2) {
-        const uint4 cw = *reinterpret_cast<const uint4*>(kdata + krow * kNvfp4RowBytes + 16 * Q);
-        const uint32_t sw = *reinterpret_cast<const uint16_t*>(kscales + krow * kNvfp4ScaleBytes + 2 * Q);
-        const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
-        if (FP8MODE) {
-          const uint32_t s0 = sw & 0xFFu, s1 = (sw >> 8) & 0xFFu;
-          Ak[0] = fp4x8_lut_to_h8(wv[0], lut[2 * s0], lut[2 * s0 + 1]);
-          Ak[1] = fp4x8_lut_to_h8(wv[1], lut[2 * s0], lut[2 * s0 + 1]);
-          Ak[2] = fp4x8_lut_to_h8(wv[2], lut[2 * s1], lut[2 * s1 + 1]);
-          Ak[3] = fp4x8_lut_to_h8(wv[3], lut[2 * s1], lut[2 * s1 + 1]);
-        } else {
-          const h2 sc = fp8x2_to_h2<false>(sw);
-          const h8 s0 = h8{sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
-          const h8 s1 = h8{sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
-          Ak[0] = fp4x8_to_h8(wv[0]) * s0;
-          Ak[1] = fp4x8_to_h8(wv[1]) * s0;
-          Ak[2] = fp4x8_to_h8(wv[2]) * s1;
-          Ak[3] = fp4x8_to_h8(wv[3]) * s1;
-        }
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(kdata + krow * kHeadDim + 32 * Q);
-        const uint4 c0 = src[0], c1 = src[1];
-        Ak[0] = fp8x8_to_h8(c0.x, c0.y);
-        Ak[1] = fp8x8_to_h8(c0.z, c0.w);
-        Ak[2] = fp8x8_to_h8(c1.x, c1.y);
-        Ak[3] = fp8x8_to_h8(c1.z, c1.w);
-      }
+      decode_k_tile<KT, FP8MODE>(kraw[kt], lut, Ak);
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
@@ -163,41 +271,13 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
 
     // ---------------- O^T += V^T P^T, 8 tiles of 16 keys
     uint32_t* vt = smem + w * kVtDwords;
-    const int kp = lane & 7;     // key pair within the tile (keys 2kp, 2kp+1)
-    const int dg = lane >> 3;    // 16-dim group
-#pragma unroll 1
+#pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
-      // stage V^T for keys kt*16 .. kt*16+15
-      h8 v0[2], v1[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const size_t vrow = rowbase + kt * 16 + 2 * kp + u;
-        h8* dst = u == 0 ? v0 : v1;
-        if (KT == 2) {
-          const uint2 cw = *reinterpret_cast<const uint2*>(vdata + vrow * kNvfp4RowBytes + 8 * dg);
-          const uint32_t sb = vscales[vrow * kNvfp4ScaleBytes + dg];
-          if (FP8MODE) {
-            dst[0] = fp4x8_lut_to_h8(cw.x, lut[2 * sb], lut[2 * sb + 1]);
-            dst[1] = fp4x8_lut_to_h8(cw.y, lut[2 * sb], lut[2 * sb + 1]);
-          } else {
-            const _Float16 sh = e4m3_to_h(sb);
-            const h8 ss = h8{sh, sh, sh, sh, sh, sh, sh, sh};
-            dst[0] = fp4x8_to_h8(cw.x) * ss;
-            dst[1] = fp4x8_to_h8(cw.y) * ss;
-          }
-        } else {
-          const uint4 cw = *reinterpret_cast<const uint4*>(vdata + vrow * kHeadDim + 16 * dg);
-          dst[0] = fp8x8_to_h8(cw.x, cw.y);
-          dst[1] = fp8x8_to_h8(cw.z, cw.w);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 16 * dg + 8 * hh + ((KT == 2 && FP8MODE) ? lut_perm(e) : e);
-          vt[vt_index(d, kp)] = pack_h2(v0[hh][e], v1[hh][e]);
-        }
+      if (kt + kVAhead<KT> < 8)
+        vraw[kt + kVAhead<KT>] =
+            load_v_tile<KT>(vdata, vscales, rowbase + (kt + kVAhead<KT>) * 16 + 2 * kp, dg);
+      const int key0 = kt * 16 + 2 * kp;
+      stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt, kp, dg, key0 < nkeys, key0 + 1 < nkeys);
       lds_wait();
       // P^T operand: lane (Q, head j) holds keys 4Q..4Q+3 of this tile
       h4 phi, plo;
@@ -219,53 +299,51 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
     }
   }
 
-  // ---------------- merge the 16 block states in fixed order
+  // ---------------- merge the 16 block states in a fixed order
   if (Q == 0) {
     m_sh[w][j] = m;
     l_sh[w][j] = l;
   }
+  __syncthreads();   // also: every wave is done with its V^T slice
+  {
+    float M = NEG_INF;
+#pragma unroll
+    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, m_sh[ww][j]);
+    const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
+    float* red = reinterpret_cast<float*>(smem) + ((size_t)w * 16 + j) * kMergeStride;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(red + dt * 16 + 4 * Q) = O[dt] * f;
+  }
   __syncthreads();
-  float M = NEG_INF;
+  {
+    // thread -> head hh, dims 2*dl, 2*dl+1
+    const int hh = threadIdx.x >> 6, dl = threadIdx.x & 63;
+    float M = NEG_INF;
 #pragma unroll
-  for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, m_sh[ww][j]);
-  float Lt = 0.0f;
+    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, m_sh[ww][hh]);
+    float Lt = 0.0f;
 #pragma unroll
-  for (int ww = 0; ww < kAttnWaves; ++ww) {
-    const float mw = m_sh[ww][j];
-    if (mw != NEG_INF) Lt += l_sh[ww][j] * exp2f(mw - M);
-  }
-  const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] *= f;
-  float* red = reinterpret_cast<float*>(smem);   // [8][16 heads][128 dims] fp32
-#pragma unroll 1
-  for (int sgap = kAttnWaves / 2; sgap >= 1; sgap >>= 1) {
-    __syncthreads();
-    if (w >= sgap && w < 2 * sgap) {
-      float* dst = red + ((size_t)(w - sgap) * 16 + j) * kHeadDim;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(dst + dt * 16 + 4 * Q) = O[dt];
+    for (int ww = 0; ww < kAttnWaves; ++ww) {
+      const float mw = m_sh[ww][hh];
+      if (mw != NEG_INF) Lt += l_sh[ww][hh] * exp2f(mw - M);
     }
-    __syncthreads();
-    if (w < sgap) {
-      const float* src = red + ((size_t)w * 16 + j) * kHeadDim;
+    const float* red = reinterpret_cast<const float*>(smem) + (size_t)hh * kMergeStride + 2 * dl;
+    float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt] += *reinterpret_cast<const f4*>(src + dt * 16 + 4 * Q);
+    for (int ww = 0; ww < kAttnWaves; ++ww) {
+      const float2 v = *reinterpret_cast<const float2*>(red + (size_t)ww * 16 * kMergeStride);
+      acc.x += v.x;
+      acc.y += v.y;
     }
-  }
-  if (w == 0) {
     const bool bad = nan_sh != 0;
     const float inv = v_scale / Lt;
-    float* dst = out + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      f4 o = O[dt] * inv;
-      if (bad) o = f4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      *reinterpret_cast<f4*>(dst + dt * 16 + 4 * Q) = o;
-    }
-    if (lse != nullptr && Q == 0) {
+    float2 o = make_float2(acc.x * inv, acc.y * inv);
+    if (bad) o = make_float2(__builtin_nanf(""), __builtin_nanf(""));
+    const size_t orow = ((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + hh;
+    *reinterpret_cast<float2*>(out + orow * kHeadDim + 2 * dl) = o;
+    if (lse != nullptr && dl == 0) {
       const float v = (M + log2f(Lt)) * 0.69314718055994530942f;
-      lse[((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j] = bad ? __builtin_nanf("") : v;
+      lse[orow] = bad ? __builtin_nanf("") : v;
     }
   }
 }

@@ -184,6 +184,223 @@ __global__ __launch_bounds__(256) void indexer_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode and speculative decode (T <= 4): a streaming scan.
+//
+// Grid (page range, sequence); each of the 4 waves of a workgroup owns
+// kDecPagesPerWave consecutive logical blocks.  A wave reads its page ids
+// once (one lane per block), then walks its pages in units of TPU key tiles
+// (16 keys each).  With PIPE the next unit's loads are issued before the
+// current unit is contracted, so memory and math overlap inside the wave;
+// those loads are unconditional (past the last unit a wave re-reads its last
+// unit, which hits in cache) so that every wait covers exactly one unit.
+// The MFMA rows are 4 tokens x 4 groups.  sigma > 0 is applied to the pooled
+// maximum only: fl(sigma*x) is monotone in x, so this equals the maximum of
+// the scaled scores.
+#ifndef MSA_DEC_PAGES_PER_WAVE
+#define MSA_DEC_PAGES_PER_WAVE 8
+#endif
+#ifndef MSA_DEC_TPU
+#define MSA_DEC_TPU 4
+#endif
+#ifndef MSA_DEC_PIPE
+#define MSA_DEC_PIPE 1
+#endif
+constexpr int kDecWaves = 4;
+constexpr int kDecPagesPerWave = MSA_DEC_PAGES_PER_WAVE;
+
+template <int KT, int TPU> struct IdxUnit;
+template <int TPU> struct IdxUnit<2, TPU> { uint4 c[TPU]; uint32_t s[TPU]; };   // NVFP4 codes + 2 scale bytes
+template <int TPU> struct IdxUnit<1, TPU> { uint4 c[TPU][2]; };                 // FP8
+
+template <int KT, int TPU>
+__device__ __forceinline__ void load_idx_unit(IdxUnit<KT, TPU>& u, const uint8_t* __restrict__ kdata,
+                                              const uint8_t* __restrict__ kscales, size_t row0, int Q) {
+#pragma unroll
+  for (int kt = 0; kt < TPU; ++kt) {
+    const size_t row = row0 + kt * 16;
+    if constexpr (KT == 2) {
+      u.c[kt] = *reinterpret_cast<const uint4*>(kdata + row * kNvfp4RowBytes + 16 * Q);
+      u.s[kt] = *reinterpret_cast<const uint16_t*>(kscales + row * kNvfp4ScaleBytes + 2 * Q);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(kdata + row * kHeadDim + 32 * Q);
+      u.c[kt][0] = src[0];
+      u.c[kt][1] = src[1];
+    }
+  }
+}
+
+// One 16-key tile -> the four 32-dim B fragments (k-chunk c = dims 32Q+8c .. +7).
+template <int KT, bool FP8MODE, int TPU>
+__device__ __forceinline__ void decode_idx_tile(const IdxUnit<KT, TPU>& u, int kt, const uint32_t* lut,
+                                                h8 (&Bc)[4]) {
+  if constexpr (KT == 2) {
+    const uint32_t w[4] = {u.c[kt].x, u.c[kt].y, u.c[kt].z, u.c[kt].w};
+    if constexpr (FP8MODE) {
+      const uint32_t s0 = u.s[kt] & 0xFFu, s1 = (u.s[kt] >> 8) & 0xFFu;
+      const uint32_t l0 = lut[2 * s0], h0 = lut[2 * s0 + 1];
+      const uint32_t l1 = lut[2 * s1], h1 = lut[2 * s1 + 1];
+      Bc[0] = fp4x8_lut_to_h8(w[0], l0, h0);
+      Bc[1] = fp4x8_lut_to_h8(w[1], l0, h0);
+      Bc[2] = fp4x8_lut_to_h8(w[2], l1, h1);
+      Bc[3] = fp4x8_lut_to_h8(w[3], l1, h1);
+    } else {
+      const h2 sc = fp8x2_to_h2<false>(u.s[kt]);
+      const h8 s0 = h8{sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+      const h8 s1 = h8{sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+      Bc[0] = fp4x8_to_h8(w[0]) * s0;
+      Bc[1] = fp4x8_to_h8(w[1]) * s0;
+      Bc[2] = fp4x8_to_h8(w[2]) * s1;
+      Bc[3] = fp4x8_to_h8(w[3]) * s1;
+    }
+  } else {
+    Bc[0] = fp8x8_to_h8(u.c[kt][0].x, u.c[kt][0].y);
+    Bc[1] = fp8x8_to_h8(u.c[kt][0].z, u.c[kt][0].w);
+    Bc[2] = fp8x8_to_h8(u.c[kt][1].x, u.c[kt][1].y);
+    Bc[3] = fp8x8_to_h8(u.c[kt][1].z, u.c[kt][1].w);
+  }
+}
+
+// Contract one unit: per tile four 16x16x32 MFMAs and the masked running max.
+// Lane (Q, j) gets token Q, groups 0..3 of key `key0 + 16*kt` (key0 includes j).
+template <int KT, bool FP8MODE, bool TOKSC, int TPU>
+__device__ __forceinline__ void contract_idx_unit(const IdxUnit<KT, TPU>& u, const h8 (&A)[4],
+                                                  const uint32_t* lut, int key0, int p_tok, bool tok_ok,
+                                                  float sigma, float (&bmax)[4], float* tsc_row,
+                                                  size_t tsc_stride) {
+  const float NEG_INF = -__builtin_inff();
+#pragma unroll
+  for (int kt = 0; kt < TPU; ++kt) {
+    h8 Bc[4];
+    decode_idx_tile<KT, FP8MODE, TPU>(u, kt, lut, Bc);
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(A[c], Bc[c], acc);
+    const int key = key0 + 16 * kt;
+    const bool vis = tok_ok && key <= p_tok;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bmax[r] = fmaxf(bmax[r], vis ? acc[r] : NEG_INF);
+      if constexpr (TOKSC) {
+        if (tok_ok) tsc_row[r * tsc_stride + key] = vis ? acc[r] * sigma : NEG_INF;
+      }
+    }
+  }
+}
+
+template <int KT, bool FP8MODE, bool TOKSC, int TPU, bool PIPE>
+__global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
+    const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
+    const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
+    float* __restrict__ block_scores, float* __restrict__ token_scores) {
+  constexpr int UPP = 8 / TPU;             // units per page
+  static_assert(kDecPagesPerWave >= 1 && kDecPagesPerWave <= 64, "page ids are held one per lane");
+  __shared__ uint32_t lut[FP8MODE ? 512 : 2];
+  // pooled scores of each wave's blocks, [block][token*4 + group], written out at the end
+  __shared__ float pooled[kDecWaves][kDecPagesPerWave][16];
+  if (FP8MODE) {
+    build_fp8_lut(lut);
+    __syncthreads();
+  }
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Q = lane >> 4, j = lane & 15;
+  const float NEG_INF = -__builtin_inff();
+  const float QNAN = __builtin_nanf("");
+  const int L = seq_lens[b];
+  const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
+  const int w0 = (blockIdx.x * kDecWaves + wave) * kDecPagesPerWave;   // first block of this wave
+  if (w0 >= max_blocks) return;
+  const int wend = min(w0 + kDecPagesPerWave, max_blocks);
+  const int nreal = max(0, min(wend, nb) - w0);                        // blocks with keys
+
+  // page ids of this wave's blocks: lane i holds block w0 + i; bad ids read page 0
+  int pid = 0;
+  if (lane < nreal) pid = table[(size_t)b * max_blocks + w0 + lane];
+  const int pid_bad = (pid < 0 || (int64_t)pid >= num_pages) ? 1 : 0;
+  const int pid_safe = pid_bad ? 0 : pid;
+
+  // A operand: row j = token j/4, group j%4; k-chunk c = dims 32Q+8c .. +7
+  h8 A[4];
+  {
+    const int t = j >> 2, g = j & 3;
+    if (t < T) {
+      const uint4* src =
+          reinterpret_cast<const uint4*>(idx_q + (((size_t)b * T + t) * kGroups + g) * kHeadDim + 32 * Q);
+      const uint4 u0 = src[0], u1 = src[1];
+      const uint32_t wq[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
+        A[c] = (KT == 2 && FP8MODE) ? h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]} : a;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) A[c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  const bool tok_ok = Q < T;
+  const int p_tok = L - T + Q;
+  const size_t tstride = (size_t)max_blocks * kBlock;
+  float* tsc_row = TOKSC ? token_scores + (((size_t)b * T + (tok_ok ? Q : 0)) * kGroups) * tstride : nullptr;
+
+  // blocks of this wave past the sequence: -inf
+  if (TOKSC && tok_ok) {
+    for (int i = w0 + nreal; i < wend; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)i * kBlock + kk] = NEG_INF;
+  }
+  for (int e = lane; e < 16 * (wend - w0 - nreal); e += 64) {
+    const int n = wend - w0 - nreal;
+    const int rowi = e / n, i = w0 + nreal + e % n;
+    if ((rowi >> 2) < T) block_scores[(((size_t)b * T + (rowi >> 2)) * kGroups + (rowi & 3)) * max_blocks + i] = NEG_INF;
+  }
+
+  const int nunits = nreal * UPP;
+  float bmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+  IdxUnit<KT, TPU> buf0, buf1;
+  if (PIPE && nunits > 0)
+    load_idx_unit<KT, TPU>(buf0, kdata, kscales, (size_t)__builtin_amdgcn_readlane(pid_safe, 0) * kBlock + j, Q);
+  for (int uu = 0; uu < nunits; ++uu) {
+    const int blk = uu / UPP, part = uu % UPP;
+    if (PIPE) {
+      const int un = min(uu + 1, nunits - 1);
+      const size_t row_n = (size_t)__builtin_amdgcn_readlane(pid_safe, un / UPP) * kBlock + (un % UPP) * (16 * TPU) + j;
+      load_idx_unit<KT, TPU>(buf1, kdata, kscales, row_n, Q);
+    } else {
+      const size_t row0 = (size_t)__builtin_amdgcn_readlane(pid_safe, blk) * kBlock + part * (16 * TPU) + j;
+      load_idx_unit<KT, TPU>(buf0, kdata, kscales, row0, Q);
+    }
+    contract_idx_unit<KT, FP8MODE, TOKSC, TPU>(buf0, A, lut, (w0 + blk) * kBlock + part * (16 * TPU) + j,
+                                               p_tok, tok_ok, sigma, bmax, tsc_row, tstride);
+    if (PIPE) buf0 = buf1;
+    if (part == UPP - 1) {
+      const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = max16(bmax[r]);
+        if (j == 0) pooled[wave][blk][4 * Q + r] = bad ? QNAN : m * sigma;
+        bmax[r] = NEG_INF;
+      }
+      if (TOKSC && bad && tok_ok) {
+        const int i = w0 + blk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)i * kBlock + kk] = QNAN;
+      }
+    }
+  }
+  lds_wait();
+  // write the pooled scores: entry e -> row (token, group) e / nreal, block w0 + e % nreal
+  for (int e = lane; e < 16 * nreal; e += 64) {
+    const int rowi = e / nreal, i = e % nreal;
+    const int tt = rowi >> 2, g = rowi & 3;
+    if (tt < T) block_scores[(((size_t)b * T + tt) * kGroups + g) * max_blocks + w0 + i] = pooled[wave][i][rowi];
+  }
+}
+
 // fp32 index keys and queries: one workgroup per (block, sequence), one
 // thread per key, fp32 FMAs in dimension order.
 __global__ __launch_bounds__(128) void indexer_f32_kernel(
@@ -248,9 +465,21 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
                      k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, \
                      sigma, block_scores, token_scores)
   if (p.T <= 4) {
-    if (k.dtype == 1) MSA_IDX_LAUNCH(1, false, 1);
-    else if (fp8mode) MSA_IDX_LAUNCH(2, true, 1);
-    else MSA_IDX_LAUNCH(2, false, 1);
+    const unsigned per_wg = kDecWaves * kDecPagesPerWave;
+    const dim3 grid((unsigned)((p.max_blocks + per_wg - 1) / per_wg), (unsigned)p.B);
+#define MSA_DEC_LAUNCH(KT, FM, TS)                                                              \
+  hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2), MSA_DEC_PIPE != 0>), grid, dim3(kDecWaves * 64), 0, s, q8,  \
+                     k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, \
+                     sigma, block_scores, token_scores)
+    const bool ts = token_scores != nullptr;
+    if (k.dtype == 1) {
+      if (ts) MSA_DEC_LAUNCH(1, false, true); else MSA_DEC_LAUNCH(1, false, false);
+    } else if (fp8mode) {
+      if (ts) MSA_DEC_LAUNCH(2, true, true); else MSA_DEC_LAUNCH(2, true, false);
+    } else {
+      if (ts) MSA_DEC_LAUNCH(2, false, true); else MSA_DEC_LAUNCH(2, false, false);
+    }
+#undef MSA_DEC_LAUNCH
   } else {
     if (k.dtype == 1) MSA_IDX_LAUNCH(1, false, 2);
     else if (fp8mode) MSA_IDX_LAUNCH(2, true, 2);

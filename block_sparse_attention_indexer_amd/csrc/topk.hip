@@ -7,34 +7,31 @@
 // select them all.  Otherwise the own block is joined by the 15 best older
 // blocks under the strict order (score descending, block index ascending).
 //
-// One wavefront per row.  Each candidate is a 64-bit key (order-preserving
-// score bits, then the complement of the block index), so all keys are
-// distinct and the order above is plain integer order.  Fifteen rounds each
-// take the wave-wide maximum among keys below the previous round's winner --
-// no per-element state, the row is read from L1/L2.  The 16 winners are then
-// ranked with a 16-way compare and written ascending.
+// One workgroup of 256 threads per row.  Each older block becomes a 64-bit
+// key: order-preserving score bits above the complemented block index, so
+// the keys are distinct and the order above is plain integer order.  The row
+// is read once into registers; a most-significant-digit radix select over
+// 8-bit digits (LDS histogram, one wave finds the digit) narrows a key prefix
+// until exactly 15 keys lie at or above it -- usually after two or three
+// digits.  The 15 winners plus the own block are then ranked and written
+// ascending.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace msa {
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
-}
+constexpr int kTopkThreads = 256;
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ block_scores,
-                                                   int32_t* __restrict__ sel,
-                                                   const int32_t* __restrict__ seq_lens, int B,
-                                                   int T, int max_blocks) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t rows = (int64_t)B * T * kGroups;
-  if (row >= rows) return;
+template <int E>   // keys per thread: rows of up to 256*E older blocks
+__global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(
+    const float* __restrict__ block_scores, int32_t* __restrict__ sel,
+    const int32_t* __restrict__ seq_lens, int T, int max_blocks) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t pick_digit, pick_above, pick_count, n_won;
+  __shared__ int32_t won[kTopK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t row = blockIdx.x;
   const int b = (int)(row / ((int64_t)T * kGroups));
   const int t = (int)((row / kGroups) % T);
   const int L = seq_lens[b];
@@ -42,37 +39,90 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ blo
   own = max(0, min(own, max_blocks - 1));
   int32_t* out = sel + row * kTopK;
   if (own + 1 <= kTopK) {
-    if (lane < kTopK) out[lane] = lane <= own ? lane : -1;
+    if (tid < kTopK) out[tid] = tid <= own ? tid : -1;
     return;
   }
   const float* S = block_scores + row * max_blocks;
-  uint64_t prev = ~0ull;
-  int32_t mine = -1;
-  for (int r = 0; r < kTopK - 1; ++r) {
-    uint64_t best = 0;
-    for (int i = lane; i < own; i += 64) {
-      const uint64_t key = ((uint64_t)order_key(S[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-      if (key < prev && key > best) best = key;
-    }
-    best = wave_max_u64(best);
-    prev = best;
-    if (lane == r) mine = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-  }
-  if (lane == kTopK - 1) mine = own;
-  int rank = 0;
+  const int n = own;   // candidates: blocks 0 .. own-1
+
+  uint64_t key[E];
 #pragma unroll
-  for (int s = 0; s < kTopK; ++s) {
-    const int32_t other = __shfl(mine, s);
-    rank += (other < mine) ? 1 : 0;
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + e * kTopkThreads;
+    key[e] = i < n ? ((uint64_t)order_key(S[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
   }
-  if (lane < kTopK) out[rank] = mine;
+  // Index 0xFFFFFFFF is never a block, so a real key is never 0: 0 marks "no key".
+  uint64_t prefix = 0, mask = 0;
+  uint32_t need = kTopK - 1;
+  if (tid == 0) n_won = 0;
+#pragma unroll 1
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e] != 0ull && (key[e] & mask) == prefix)
+        atomicAdd(&hist[(uint32_t)(key[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 4l..4l+3; find digit d with above(d) < need <= above(d) + hist[d]
+      uint32_t h[4], s = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { h[u] = hist[4 * lane + u]; s += h[u]; }
+      // suffix sum over lanes above this one
+      uint32_t incl = s;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(incl, off);
+        if (lane + off < 64) incl += o;
+      }
+      uint32_t above = incl - s;          // keys in bins of higher lanes
+#pragma unroll
+      for (int u = 3; u >= 0; --u) {
+        if (above < need && need <= above + h[u]) {
+          pick_digit = 4 * lane + u;
+          pick_above = above;
+          pick_count = h[u];
+        }
+        above += h[u];
+      }
+    }
+    __syncthreads();
+    const uint32_t d = pick_digit, a = pick_above, c = pick_count;
+    prefix |= (uint64_t)d << shift;
+    mask |= 255ull << shift;
+    need -= a;
+    // pick_* is next written after two more barriers, so no barrier is needed here
+    if (c == need) break;
+  }
+  // exactly 15 keys satisfy (key & mask) >= prefix
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (key[e] != 0ull && (key[e] & mask) >= prefix) {
+      const uint32_t slot = atomicAdd(&n_won, 1u);
+      if (slot < (uint32_t)(kTopK - 1)) won[slot] = tid + e * kTopkThreads;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int32_t mine = lane < kTopK - 1 ? won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
+    int rank = 0;
+#pragma unroll
+    for (int s = 0; s < kTopK; ++s) rank += (__shfl(mine, s) < mine) ? 1 : 0;
+    if (lane < kTopK) out[rank] = mine;
+  }
 }
 
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.T * kGroups;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, block_scores,
-                     sel, p.seq_lens, p.B, p.T, p.max_blocks);
+  const dim3 grid((unsigned)rows), block(kTopkThreads);
+  if (p.max_blocks <= 8 * kTopkThreads)
+    hipLaunchKernelGGL(topk_radix_kernel<8>, grid, block, 0, s, block_scores, sel, p.seq_lens, p.T,
+                       p.max_blocks);
+  else
+    hipLaunchKernelGGL(topk_radix_kernel<32>, grid, block, 0, s, block_scores, sel, p.seq_lens,
+                       p.T, p.max_blocks);
   return hipGetLastError();
 }
 
