@@ -205,11 +205,13 @@ def main():
     print(f"[bench] workload {w.name} ready: B={w.B} T={w.T} pages={wl.lay.num_pages}", file=sys.stderr, flush=True)
 
     if args.calib_copy_mib:
+        # a plain elementwise copy kernel (reads and writes calib_copy_mib MiB each) whose
+        # FETCH_SIZE / WRITE_SIZE counter readings calibrate the counters of the kernels above
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
         bbuf = torch.empty_like(a)
         for _ in range(3):
-            bbuf.copy_(a)
+            torch.mul(a, 1.0, out=bbuf)
         torch.cuda.synchronize()
         del a, bbuf
 

@@ -401,6 +401,214 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-token decode (T = 1): a streaming scan on the 4x4x4 f16 MFMA.
+//
+// With one query token there are only 4 query rows (the groups), so a 16-row
+// MFMA tile would leave 12 rows empty.  The 4x4x4 form computes 16
+// independent 4x4 blocks: block b = lane/4; lane (b, i) supplies row i of A
+// (group i of the index query), lane (b, j) supplies column j of B (key
+// 4b+j), and lane (b, j) receives all 4 rows of its column.  So every lane
+// owns one key of a 64-key set and gets that key's 4 group scores.
+// NVFP4 keys are contracted one 16-dim scale group at a time (4 MFMAs on the
+// unscaled E2M1 values; products and sums exact), then each group's partial
+// dot is multiplied by its E4M3 scale in one fp32 FMA -- one FMA per 16
+// elements instead of a multiply per element.  FP8 keys chain all 32 MFMAs.
+// A lane reads its own key's row (4 x 16 B of NVFP4 codes + 8 B of scales,
+// or 8 x 16 B of FP8); the loads of a set together cover every cache line
+// of the set's 64 rows.
+template <int KT> struct KeySet;
+template <> struct KeySet<2> { uint4 c[4]; uint2 s; };   // NVFP4: 64 B codes + 8 scale bytes
+template <> struct KeySet<1> { uint4 c[8]; };            // FP8: 128 B
+
+template <int KT>
+__device__ __forceinline__ void load_key_set(KeySet<KT>& u, const uint8_t* __restrict__ kdata,
+                                             const uint8_t* __restrict__ kscales, size_t row) {
+  if constexpr (KT == 2) {
+    const uint4* src = reinterpret_cast<const uint4*>(kdata + row * kNvfp4RowBytes);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u.c[q] = src[q];
+    u.s = *reinterpret_cast<const uint2*>(kscales + row * kNvfp4ScaleBytes);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(kdata + row * kHeadDim);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u.c[q] = src[q];
+  }
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ h4 cat4(h2 a, h2 b) { return h4{a[0], a[1], b[0], b[1]}; }
+// E4M3 byte k (0..3, a constant after unrolling) of w, as float.
+__device__ __forceinline__ float e4m3_byte_to_f(uint32_t w, int k) {
+  switch (k) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8(w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8(w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  }
+}
+
+// The 4 group scores of this lane's key (before the tensor scales).
+// A[c] holds dims 4c .. 4c+3 of this lane's group (lane % 4).
+template <int KT>
+__device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const h4 (&A)[32]) {
+  f4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (KT == 2) {
+    // two scale groups at a time, their MFMA chains interleaved
+#pragma unroll
+    for (int s0 = 0; s0 < 8; s0 += 2) {
+      f4 part[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {               // dword 2s+h: dims 16s+8h .. +7, low nibble first
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int s = s0 + g;
+            const uint32_t w = dword_of(u.c[s >> 1], 2 * (s & 1) + h);
+            const h4 bv = e == 0 ? cat4(fp4x2_to_h2<0>(w), fp4x2_to_h2<1>(w)) : cat4(fp4x2_to_h2<2>(w), fp4x2_to_h2<3>(w));
+            part[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[4 * s + 2 * h + e], bv, part[g], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int s = s0 + g;
+        const float sc = e4m3_byte_to_f(s < 4 ? u.s.x : u.s.y, s & 3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] = fmaf(sc, part[g][i], tot[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {                // dword c = dims 4c .. 4c+3
+      const uint32_t w = dword_of(u.c[c >> 2], c & 3);
+      tot = __builtin_amdgcn_mfma_f32_4x4x4f16(A[c], cat4(fp8x2_to_h2<false>(w), fp8x2_to_h2<true>(w)), tot, 0, 0, 0);
+    }
+  }
+  return tot;
+}
+
+// Max over the 64 lanes of 4 values: 7 exchanges.  Lane l returns the
+// maximum of value g = 2*(l/32) + (l/16)%2.
+__device__ __forceinline__ float wave_max4(f4 v, int lane) {
+  const bool up = lane & 32;
+  float a = up ? v[2] : v[0], b = up ? v[3] : v[1];          // keep these two
+  const float sa = up ? v[0] : v[2], sb = up ? v[1] : v[3];  // partner keeps these
+  a = fmaxf(a, __shfl_xor(sa, 32));
+  b = fmaxf(b, __shfl_xor(sb, 32));
+  const bool up16 = lane & 16;
+  float m = up16 ? b : a;
+  m = fmaxf(m, __shfl_xor(up16 ? a : b, 16));
+  m = fmaxf(m, __shfl_xor(m, 8));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  return m;
+}
+
+#ifndef MSA_DEC1_PAGES_PER_WAVE
+#define MSA_DEC1_PAGES_PER_WAVE 8
+#endif
+constexpr int kDec1PagesPerWave = MSA_DEC1_PAGES_PER_WAVE;
+
+template <int KT, bool TOKSC>
+__global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
+    const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
+    const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ table, int max_blocks, float sigma, float* __restrict__ block_scores,
+    float* __restrict__ token_scores) {
+  static_assert(kDec1PagesPerWave >= 1 && kDec1PagesPerWave <= 64, "page ids are held one per lane");
+  __shared__ float pooled[kDecWaves][kDec1PagesPerWave][kGroups];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float NEG_INF = -__builtin_inff();
+  const float QNAN = __builtin_nanf("");
+  const int L = seq_lens[b];
+  const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
+  const int w0 = (blockIdx.x * kDecWaves + wave) * kDec1PagesPerWave;
+  if (w0 >= max_blocks) return;
+  const int wend = min(w0 + kDec1PagesPerWave, max_blocks);
+  const int nreal = max(0, min(wend, nb) - w0);
+
+  int pid = 0;
+  if (lane < nreal) pid = table[(size_t)b * max_blocks + w0 + lane];
+  const int pid_bad = (pid < 0 || (int64_t)pid >= num_pages) ? 1 : 0;
+  const int pid_safe = pid_bad ? 0 : pid;
+
+  // A operand: this lane's group g = lane % 4, all 128 dims as f16
+  h4 A[32];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(idx_q + ((size_t)b * kGroups + (lane & 3)) * kHeadDim);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = src[q];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) A[4 * q + k] = cat4(fp8x2_to_h2<false>(wv[k]), fp8x2_to_h2<true>(wv[k]));
+    }
+  }
+  const size_t tstride = (size_t)max_blocks * kBlock;
+  float* tsc = TOKSC ? token_scores + (size_t)b * kGroups * tstride : nullptr;
+
+  // blocks of this wave past the sequence: -inf
+  for (int e = lane; e < kGroups * (wend - w0 - nreal); e += 64) {
+    const int n = wend - w0 - nreal;
+    block_scores[((size_t)b * kGroups + e / n) * max_blocks + w0 + nreal + e % n] = NEG_INF;
+  }
+  if (TOKSC) {
+    for (int i = w0 + nreal; i < wend; ++i)
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g)
+        for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)i * kBlock + kk] = NEG_INF;
+  }
+
+  const int nsets = 2 * nreal;               // two 64-key sets per page
+  KeySet<KT> cur, nxt;
+  load_key_set<KT>(cur, kdata, kscales, (size_t)__builtin_amdgcn_readlane(pid_safe, 0) * kBlock + lane);
+  f4 bmax = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+  for (int u = 0; u < nsets; ++u) {
+    const int blk = u >> 1, half = u & 1;
+    {
+      const int un = min(u + 1, nsets - 1);
+      load_key_set<KT>(nxt, kdata, kscales,
+                       (size_t)__builtin_amdgcn_readlane(pid_safe, un >> 1) * kBlock + (un & 1) * 64 + lane);
+    }
+    f4 sc = score_key_set<KT>(cur, A);
+    const int key = (w0 + blk) * kBlock + half * 64 + lane;
+    if (w0 + blk == nb - 1) {                    // only the last block can hold keys past L - 1
+      if (key >= L) sc = f4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    }
+    bmax[0] = fmaxf(bmax[0], sc[0]);
+    bmax[1] = fmaxf(bmax[1], sc[1]);
+    bmax[2] = fmaxf(bmax[2], sc[2]);
+    bmax[3] = fmaxf(bmax[3], sc[3]);
+    if constexpr (TOKSC) {
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) tsc[g * tstride + key] = key < L ? sc[g] * sigma : NEG_INF;
+    }
+    cur = nxt;
+    if (half == 1) {
+      const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
+      const float m = wave_max4(bmax, lane);
+      if ((lane & 15) == 0) pooled[wave][blk][2 * (lane >> 5) + ((lane >> 4) & 1)] = bad ? QNAN : m * sigma;
+      if (TOKSC && bad) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+          for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)(w0 + blk) * kBlock + kk] = QNAN;
+      }
+      bmax = f4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    }
+  }
+  lds_wait();
+  for (int e = lane; e < kGroups * nreal; e += 64) {
+    const int g = e / nreal, i = e % nreal;
+    block_scores[((size_t)b * kGroups + g) * max_blocks + w0 + i] = pooled[wave][i][g];
+  }
+}
+
 // fp32 index keys and queries: one workgroup per (block, sequence), one
 // thread per key, fp32 FMAs in dimension order.
 __global__ __launch_bounds__(128) void indexer_f32_kernel(
@@ -464,7 +672,23 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
                      dim3(gx, p.B, (unsigned)((p.T + 4 * RT - 1) / (4 * RT))), dim3(256), 0, s, q8, \
                      k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, \
                      sigma, block_scores, token_scores)
-  if (p.T <= 4) {
+  if (p.T == 1 && !(k.dtype == 2 && fp8mode)) {
+    // one token: 4x4x4 MFMA scan (the FP8-rounded NVFP4 reading keeps the 16-row path,
+    // since its re-rounded values cannot take the scale after the dot)
+    const unsigned per_wg = kDecWaves * kDec1PagesPerWave;
+    const dim3 grid((unsigned)((p.max_blocks + per_wg - 1) / per_wg), (unsigned)p.B);
+    const bool ts = token_scores != nullptr;
+#define MSA_DEC1_LAUNCH(KT, TS)                                                                  \
+  hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS>), grid, dim3(kDecWaves * 64), 0, s, q8, k.data, \
+                     k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,        \
+                     block_scores, token_scores)
+    if (k.dtype == 1) {
+      if (ts) MSA_DEC1_LAUNCH(1, true); else MSA_DEC1_LAUNCH(1, false);
+    } else {
+      if (ts) MSA_DEC1_LAUNCH(2, true); else MSA_DEC1_LAUNCH(2, false);
+    }
+#undef MSA_DEC1_LAUNCH
+  } else if (p.T <= 4) {
     const unsigned per_wg = kDecWaves * kDecPagesPerWave;
     const dim3 grid((unsigned)((p.max_blocks + per_wg - 1) / per_wg), (unsigned)p.B);
 #define MSA_DEC_LAUNCH(KT, FM, TS)                                                              \

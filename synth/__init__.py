@@ -165,12 +165,12 @@ def cache_pages(w: Workload, lay: Layout, seed: int, which: str, first: int, cou
     """fp32 values of pages [first, first+count) of one cache.
 
     which: 'idx_k' (one head) or 'k' / 'v' (four heads).  Shape
-    [count, heads, 128, 128].  Pages are drawn in chunks of 64 with their own
+    [count, heads, 128, 128].  Pages are drawn in chunks of 1024 with their own
     sub-seed, so any page range can be regenerated on its own (on the same
     device type).  Index-key pages of hot blocks get the planted direction.
     """
     heads = 1 if which == "idx_k" else GROUPS
-    CH = 64
+    CH = 1024
     c0, c1 = first // CH, (first + count - 1) // CH
     parts = []
     for c in range(c0, c1 + 1):
