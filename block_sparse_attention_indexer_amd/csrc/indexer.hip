@@ -451,9 +451,9 @@ __device__ __forceinline__ float e4m3_byte_to_f(uint32_t w, int k) {
 }
 
 // The 4 group scores of this lane's key (before the tensor scales).
-// A[c] holds dims 4c .. 4c+3 of this lane's group (lane % 4).
-template <int KT>
-__device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const h4 (&A)[32]) {
+// A[c] gives dims 4c .. 4c+3 of this lane's group (lane % 4).
+template <int KT, typename ASrc>
+__device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const ASrc& A) {
   f4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (KT == 2) {
     // two scale groups at a time, their MFMA chains interleaved
@@ -490,6 +490,13 @@ __device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const h4 (&A)[3
   }
   return tot;
 }
+
+// The index-query operand of a lane: 32 x h4 in registers.  (Reading it from
+// an LDS copy per MFMA instead frees 64 VGPRs but measured slower.)
+struct AInRegs {
+  h4 v[32];
+  __device__ __forceinline__ h4 operator[](int c) const { return v[c]; }
+};
 
 // Max over the 64 lanes of 4 values: 7 exchanges.  Lane l returns the
 // maximum of value g = 2*(l/32) + (l/16)%2.
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
   const int pid_safe = pid_bad ? 0 : pid;
 
   // A operand: this lane's group g = lane % 4, all 128 dims as f16
-  h4 A[32];
+  AInRegs A;
   {
     const uint4* src = reinterpret_cast<const uint4*>(idx_q + ((size_t)b * kGroups + (lane & 3)) * kHeadDim);
 #pragma unroll
@@ -547,7 +554,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
       const uint4 v = src[q];
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) A[4 * q + k] = cat4(fp8x2_to_h2<false>(wv[k]), fp8x2_to_h2<true>(wv[k]));
+      for (int k = 0; k < 4; ++k) A.v[4 * q + k] = cat4(fp8x2_to_h2<false>(wv[k]), fp8x2_to_h2<true>(wv[k]));
     }
   }
   const size_t tstride = (size_t)max_blocks * kBlock;
