@@ -152,6 +152,37 @@ def algorithmic_bytes(wl, sel_host):
     return idx, topk, attn
 
 
+def indexer_kernel_name(w, dequant):
+    """The index-scan kernel libmsa launches for this workload (as rocprofv3 names it)."""
+    kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
+    if kt is None:
+        return "msa::indexer_f32_kernel"
+    fp8mode = kt == 2 and dequant == "fp8"
+    if w.T == 1 and not fp8mode:
+        return f"msa::indexer_decode1_kernel<{kt}, false>"
+    if w.T <= 4:
+        return f"msa::indexer_decode_kernel<{kt}, {str(fp8mode).lower()}, false>"
+    return f"msa::indexer_mfma_kernel<{kt}, {str(fp8mode).lower()}, 2>"
+
+
+def measured_traffic(workload, role):
+    """Calibrated HBM bytes per launch (read + write) of one step's kernel, from the
+    rocprofv3 counter summary under profiles/ -- None when there is none or when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    import profile_step
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("sources_sha256") != profile_step.sources_hash():
+        return None
+    for e in d["kernels"].values():
+        if e.get("role") == role and "fetch_bytes" in e and "write_bytes" in e:
+            return round(e["fetch_bytes"] + e["write_bytes"])
+    return None
+
+
 def cpu_baseline(wl, dequant, sample):
     """The oracle on `sample` sequences of the same workload, packed by the
     oracle itself from the fp32 sources; timed from decode to attention."""
@@ -261,9 +292,10 @@ def main():
         "bytes_per_step": {"indexer": b_idx, "topk": b_topk, "attention": b_attn},
         "kernel_ms": {"indexer": round(idx_ms, 5), "topk": round(float(np.mean(k_topk)), 5),
                       "attention": round(float(np.mean(k_attn)), 5)},
-        "roofline": {"bound": "hbm", "kernel": "indexer_mfma_kernel (index-key scan + block max-pool)",
+        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant) + " (index-key scan + block max-pool)",
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved_idx / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name, "indexer")},
         "cpu_baseline": None,
     }
     if sample:

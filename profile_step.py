@@ -1,0 +1,177 @@
+"""Collect the rocprofv3 figures that bench.py reports, for one workload.
+
+    python profile_step.py [--workload c3_128k] [--out gpurun_out/profile]
+
+Runs bench.py three times as a child process under rocprofv3 (this process
+never touches the GPU):
+
+  1. --kernel-trace --stats      bench.py --steps 10 --warmup 2 --no-cpu-baseline
+  2. --pmc FETCH_SIZE            bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib 512
+  3. --pmc WRITE_SIZE            (same)
+
+Counter readings are per dispatch, in KiB.  Each is scaled by what the same
+counter reads for the 512 MiB elementwise copy that bench.py launches with
+--calib-copy-mib (which reads and writes exactly 512 MiB), so the reported
+bytes are calibrated HBM bytes per launch.  Writes, into --out:
+
+  decode_step_<workload>.md          per-kernel launches and durations, calibrated HBM
+                          bytes per launch, the calibration factors and the
+                          commands that produced them;
+  decode_step_<workload>_traffic.json the same numbers for bench.py, with a hash of the
+                          kernel sources they were measured on.
+Raw rocprofv3 output is deleted once summarised.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import shutil
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc")
+CALIB_MIB = 512
+
+
+def sources_hash():
+    """sha256 over the library's kernel and host sources (sorted by name)."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def role_of(name):
+    """Which step of the layer a kernel belongs to."""
+    for key, role in (("indexer", "indexer"), ("topk", "topk"), ("attn", "attention")):
+        if key in name:
+            return role
+    return None
+
+
+def short(name):
+    """Kernel name without the argument list."""
+    n = name.replace("void ", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def run(cmd, log):
+    env = dict(os.environ, TMPDIR="/tmp")
+    print("[profile] " + " ".join(cmd), flush=True)
+    with open(log, "w") as fh:
+        r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=fh, stderr=subprocess.STDOUT, timeout=300)
+    print(f"[profile] exit {r.returncode}", flush=True)
+    return r.returncode
+
+
+def read_counters(d):
+    """{(kernel, counter): [values]} and {kernel: grid sizes} from counter_collection CSVs."""
+    vals, grids = {}, {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "")
+                if "msa::" not in name and "MulFunctor" not in name:
+                    continue
+                vals.setdefault((name, row["Counter_Name"]), []).append(
+                    (int(row.get("Grid_Size", 0) or 0), float(row["Counter_Value"])))
+    return vals
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="c3_128k")
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
+    args = ap.parse_args()
+    os.makedirs(args.out, exist_ok=True)
+    py = sys.executable
+    bench = os.path.join(ROOT, "bench.py")
+    w = args.workload
+    raw = os.path.join(args.out, "raw")
+    shutil.rmtree(raw, ignore_errors=True)
+
+    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(raw, "trace"), "-o", "run",
+                 "-f", "csv", "--", py, bench, "--workload", w, "--steps", "10", "--warmup", "2",
+                 "--no-cpu-baseline"]
+    pmc_bench = [py, bench, "--workload", w, "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+                 "--calib-copy-mib", str(CALIB_MIB)]
+    cmds = {"trace": trace_cmd}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds[c] = ["rocprofv3", "--pmc", c, "-d", os.path.join(raw, c), "-o", "run", "-f", "csv", "--"] + pmc_bench
+    for k, cmd in cmds.items():
+        if run(cmd, os.path.join(args.out, f"{w}_{k}.log")) != 0:
+            sys.exit(f"rocprofv3 pass {k} failed; see {args.out}/{w}_{k}.log")
+
+    # kernel trace statistics
+    stats = {}
+    for f in glob.glob(os.path.join(raw, "trace", "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if "msa::" in row["Name"]:
+                    stats[short(row["Name"])] = {"calls": int(row["Calls"]), "avg_us": float(row["AverageNs"]) / 1e3,
+                                                 "min_us": float(row["MinNs"]) / 1e3, "max_us": float(row["MaxNs"]) / 1e3}
+    # counters
+    kib = {}
+    calib = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        vals = read_counters(os.path.join(raw, c))
+        copy = [v for (name, cn), lst in vals.items() if "MulFunctor" in name and cn == c for v in lst]
+        gmax = max(g for g, _ in copy)
+        copy_kib = [v for g, v in copy if g == gmax]
+        calib[c] = CALIB_MIB * 1024.0 / (sum(copy_kib) / len(copy_kib))
+        for (name, cn), lst in vals.items():
+            if "msa::" in name and cn == c:
+                kib.setdefault(short(name), {})[c] = sum(v for _, v in lst) / len(lst)
+    shutil.rmtree(raw, ignore_errors=True)
+
+    kernels = {}
+    for name in sorted(set(stats) | set(kib)):
+        if "pack" in name:
+            continue
+        e = dict(stats.get(name, {}))
+        k = kib.get(name, {})
+        if "FETCH_SIZE" in k:
+            e["fetch_bytes"] = k["FETCH_SIZE"] * 1024.0 * calib["FETCH_SIZE"]
+        if "WRITE_SIZE" in k:
+            e["write_bytes"] = k["WRITE_SIZE"] * 1024.0 * calib["WRITE_SIZE"]
+        e["role"] = role_of(name)
+        kernels[name] = e
+    out = {"workload": w, "sources_sha256": sources_hash(), "calibration": calib,
+           "commands": {k: " ".join(v) for k, v in cmds.items()}, "kernels": kernels}
+    with open(os.path.join(args.out, f"decode_step_{w}_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+
+    lines = [f"# rocprofv3 summary: MSA layer step, workload {w}", "",
+             "Produced by `python profile_step.py --workload " + w + "` on one MI355X, which runs:", ""]
+    lines += ["    " + " ".join(c if not c.startswith(ROOT) else os.path.relpath(c, ROOT) for c in v)
+              .replace(py, "python3") for v in cmds.values()]
+    lines += ["", "(rocprofv3 runs from /tmp with TMPDIR=/tmp; raw output is summarised and deleted.)", "",
+              f"Counter calibration: the 512 MiB elementwise copy reads FETCH_SIZE x {calib['FETCH_SIZE']:.4f} and "
+              f"WRITE_SIZE x {calib['WRITE_SIZE']:.4f} of its true bytes' KiB, so per-kernel readings are "
+              "multiplied by these factors.", "",
+              f"Kernel sources sha256: `{out['sources_sha256']}`", "",
+              "| kernel | launches | avg us | min us | max us | HBM read B/launch | HBM write B/launch |",
+              "|---|---|---|---|---|---|---|"]
+    for name, e in kernels.items():
+        lines.append(f"| `{name}` | {e.get('calls', '')} | {e.get('avg_us', 0):.2f} | {e.get('min_us', 0):.2f} | "
+                     f"{e.get('max_us', 0):.2f} | {e.get('fetch_bytes', 0):,.0f} | {e.get('write_bytes', 0):,.0f} |")
+    with open(os.path.join(args.out, f"decode_step_{w}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    main()
