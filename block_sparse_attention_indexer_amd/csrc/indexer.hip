@@ -1,188 +1,20 @@
-// Steps 1+2 of MSA: index scores over the paged index-key cache, max-pooled
-// per 128-token block in the same pass.
+// Steps 1+2 of MSA for decode and speculative decode (T <= 4 query tokens):
+// index scores over the paged index-key cache, max-pooled per 128-token block
+// in the same pass.  (Many query tokens: indexer_prefill.hip.)
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer":
 // one index query per GQA group is dotted with every key of a single shared
 // index-key head, and the scores are max-pooled into one score per block.
 // Decode is bound by reading the index keys of the whole context (128 B per
-// token in FP8, 72 B in NVFP4), so this kernel is a coalesced streaming scan:
-// every page is read once, dequantised in registers, contracted on the f16
-// MFMA against all query rows (tokens x 4 groups) at once, and reduced to one
-// max per (row, block) before anything is written.  Per-key scores are
-// written only when the caller asks for them.
-//
-// Work split: grid (page chunk of 16 pages, sequence, row-tile group).  A
-// workgroup has 4 waves; each wave owns whole pages.  For a 16-key tile a
-// lane (quarter Q = lane/16, key j = lane%16) loads the 32 dims [32Q, 32Q+32)
-// of key j -- 16 contiguous bytes of NVFP4 codes or 32 bytes of FP8 -- which
-// is exactly its B operand of four 16x16x32 MFMAs (k-chunk c holds dims
-// 32Q+8c..32Q+8c+7).  The A operand (query rows) is loaded once.
+// token in FP8, 72 B in NVFP4), so these kernels are coalesced streaming
+// scans: every page is read once, dequantised in registers, contracted on f16
+// MFMAs against all query rows at once, and reduced to one max per (row,
+// block) before anything is written.  Per-key scores are written only when
+// the caller asks for them (a separate template instance).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace msa {
-
-constexpr int kIdxWaves = 4;
-constexpr int kIdxPagesPerWG = 16;
-
-__device__ __forceinline__ h8 reorder_like_lut(h8 a) {
-  return h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]};
-}
-
-// KT: 1 = FP8 keys, 2 = NVFP4 keys.  RT: 16-row tiles per workgroup (rows =
-// 4 tokens x 4 groups each).
-template <int KT, bool FP8MODE, int RT>
-__global__ __launch_bounds__(256) void indexer_mfma_kernel(
-    const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
-    const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
-    float* __restrict__ block_scores, float* __restrict__ token_scores) {
-  __shared__ uint32_t lut[FP8MODE ? 512 : 2];
-  if (FP8MODE) {
-    build_fp8_lut(lut);
-    __syncthreads();
-  }
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int Q = lane >> 4, j = lane & 15;
-  const int L = seq_lens[b];
-  const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
-  const int rt0 = blockIdx.z * RT;
-  const float NEG_INF = -__builtin_inff();
-  const float QNAN = __builtin_nanf("");
-
-  // A operand: row r = j -> token 4*(rt0+rt) + r/4, group r%4; k-chunk c of
-  // lane quarter Q holds dims 32Q + 8c .. 32Q + 8c + 7.
-  h8 A[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int t = 4 * (rt0 + rt) + (j >> 2), g = j & 3;
-    if (t < T) {
-      const uint4* src =
-          reinterpret_cast<const uint4*>(idx_q + (((size_t)b * T + t) * kGroups + g) * kHeadDim + 32 * Q);
-      const uint4 u0 = src[0], u1 = src[1];
-      const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const h8 a = fp8x8_to_h8(w[2 * c], w[2 * c + 1]);
-        A[rt][c] = (KT == 2 && FP8MODE) ? reorder_like_lut(a) : a;
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) A[rt][c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-  // last token of this row-tile group: pages after its own block are skipped
-  const int t_last = min(T - 1, 4 * (rt0 + RT) - 1);
-  const int own_last = (L - T + t_last) / kBlock;
-
-  const int i_begin = blockIdx.x * kIdxPagesPerWG;
-  const int i_end = min(i_begin + kIdxPagesPerWG, max_blocks);
-  for (int i = i_begin + wave; i < i_end; i += kIdxWaves) {
-    float bmax[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bmax[rt][r] = NEG_INF;
-    bool bad = false, computed = false;
-    if (i < nb && i <= own_last) {
-      const int pg = table[(size_t)b * max_blocks + i];
-      if (pg < 0 || (int64_t)pg >= num_pages) {
-        bad = true;
-      } else {
-        computed = true;
-        const size_t rowbase = (size_t)pg * kBlock;
-        uint4 cw0[8], cw1[8];
-        uint32_t sw[8];
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-          const size_t row = rowbase + kt * 16 + j;
-          if (KT == 2) {
-            cw0[kt] = *reinterpret_cast<const uint4*>(kdata + row * kNvfp4RowBytes + 16 * Q);
-            sw[kt] = *reinterpret_cast<const uint16_t*>(kscales + row * kNvfp4ScaleBytes + 2 * Q);
-          } else {
-            const uint4* src = reinterpret_cast<const uint4*>(kdata + row * kHeadDim + 32 * Q);
-            cw0[kt] = src[0];
-            cw1[kt] = src[1];
-          }
-        }
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-          h8 Bc[4];
-          if (KT == 2) {
-            const uint32_t w[4] = {cw0[kt].x, cw0[kt].y, cw0[kt].z, cw0[kt].w};
-            if (FP8MODE) {
-              const uint32_t s0 = sw[kt] & 0xFFu, s1 = (sw[kt] >> 8) & 0xFFu;
-              const uint32_t l0 = lut[2 * s0], h0 = lut[2 * s0 + 1];
-              const uint32_t l1 = lut[2 * s1], h1 = lut[2 * s1 + 1];
-              Bc[0] = fp4x8_lut_to_h8(w[0], l0, h0);
-              Bc[1] = fp4x8_lut_to_h8(w[1], l0, h0);
-              Bc[2] = fp4x8_lut_to_h8(w[2], l1, h1);
-              Bc[3] = fp4x8_lut_to_h8(w[3], l1, h1);
-            } else {
-              const h2 sc = fp8x2_to_h2<false>(sw[kt]);
-              const h8 s0 = h8{sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
-              const h8 s1 = h8{sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
-              Bc[0] = fp4x8_to_h8(w[0]) * s0;
-              Bc[1] = fp4x8_to_h8(w[1]) * s0;
-              Bc[2] = fp4x8_to_h8(w[2]) * s1;
-              Bc[3] = fp4x8_to_h8(w[3]) * s1;
-            }
-          } else {
-            Bc[0] = fp8x8_to_h8(cw0[kt].x, cw0[kt].y);
-            Bc[1] = fp8x8_to_h8(cw0[kt].z, cw0[kt].w);
-            Bc[2] = fp8x8_to_h8(cw1[kt].x, cw1[kt].y);
-            Bc[3] = fp8x8_to_h8(cw1[kt].z, cw1[kt].w);
-          }
-          const int key = i * kBlock + kt * 16 + j;
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(A[rt][c], Bc[c], acc);
-            // lane (Q, j) holds rows 4Q..4Q+3 = token 4*(rt0+rt)+Q, groups 0..3, key j
-            const int t = 4 * (rt0 + rt) + Q;
-            const int p = L - T + t;
-            const bool vis = (t < T) && (key <= p);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float v = vis ? acc[r] * sigma : NEG_INF;
-              bmax[rt][r] = fmaxf(bmax[rt][r], v);
-              if (token_scores != nullptr && t < T)
-                token_scores[(((size_t)b * T + t) * kGroups + r) * ((size_t)max_blocks * kBlock) + key] = v;
-            }
-          }
-        }
-      }
-    }
-    if (token_scores != nullptr && !computed) {
-      // every key of this block is past p, beyond the sequence, or unreadable
-      const float v = bad ? QNAN : NEG_INF;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int t = 4 * (rt0 + rt) + Q;
-        if (t < T) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float* dst = token_scores + (((size_t)b * T + t) * kGroups + r) * ((size_t)max_blocks * kBlock) +
-                         (size_t)i * kBlock;
-            for (int kk = j; kk < kBlock; kk += 16) dst[kk] = v;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int t = 4 * (rt0 + rt) + Q;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float m = max16(bmax[rt][r]);
-        if (j == 0 && t < T)
-          block_scores[(((size_t)b * T + t) * kGroups + r) * max_blocks + i] = bad ? QNAN : m;
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Decode and speculative decode (T <= 4): a streaming scan.
@@ -672,13 +504,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
                        p.block_table, p.max_blocks, p.T, sigma, block_scores, token_scores);
     return hipGetLastError();
   }
-  const unsigned gx = (unsigned)((p.max_blocks + kIdxPagesPerWG - 1) / kIdxPagesPerWG);
   const uint8_t* q8 = (const uint8_t*)idx_q;
-#define MSA_IDX_LAUNCH(KT, FM, RT)                                                          \
-  hipLaunchKernelGGL((indexer_mfma_kernel<KT, FM, RT>),                                     \
-                     dim3(gx, p.B, (unsigned)((p.T + 4 * RT - 1) / (4 * RT))), dim3(256), 0, s, q8, \
-                     k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, \
-                     sigma, block_scores, token_scores)
   if (p.T == 1 && !(k.dtype == 2 && fp8mode)) {
     // one token: 4x4x4 MFMA scan (the FP8-rounded NVFP4 reading keeps the 16-row path,
     // since its re-rounded values cannot take the scale after the dot)
@@ -712,11 +538,8 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     }
 #undef MSA_DEC_LAUNCH
   } else {
-    if (k.dtype == 1) MSA_IDX_LAUNCH(1, false, 2);
-    else if (fp8mode) MSA_IDX_LAUNCH(2, true, 2);
-    else MSA_IDX_LAUNCH(2, false, 2);
+    return launch_indexer_prefill(p, idx_q, k, fp8mode, sigma, block_scores, token_scores, s);
   }
-#undef MSA_IDX_LAUNCH
   return hipGetLastError();
 }
 

@@ -1,0 +1,293 @@
+// Steps 1+2 of MSA for many query tokens (chunked prefill): index scores
+// max-pooled per 128-key block, as a dense GEMM with the pooling fused into
+// its epilogue.
+//
+// Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
+// (one index query per GQA group dotted with every key of a single shared
+// index-key head, then max-pooled per block) and section "Performance
+// optimizations" (separate indexer prefill and decode kernels).
+//
+// For one sequence the scores are Q K^T with Q = [T tokens x 4 groups, 128]
+// and K = [L keys, 128]; only the per-(row, block) maxima are kept, so the
+// T x L score matrix never exists.  A workgroup owns 64 tokens x 4 groups =
+// 256 rows and a chunk of kPfChunk consecutive blocks.  Its 4 waves keep
+// their 64 rows of Q as f16 MFMA operands in registers for the whole chunk.
+// Per block the page is read once (the next page's raw bytes are prefetched
+// into registers while the current block is multiplied), dequantised into
+// an f16 tile in LDS (double-buffered, rows padded to 272 B so the operand
+// reads are free of bank conflicts), and contracted on 16x16x32 f16 MFMAs
+// (exact products, fp32 sums), 64 rows x 64 keys per wave at a time (two
+// halves per block keep the accumulator at 64 registers).  The epilogue takes
+// the max over the block's keys: in-lane over the key tiles and halves, then
+// a 4-step butterfly over the 16 key lanes that leaves one row per lane.
+// Causality is per key (key <= the token's position), applied only in the
+// blocks at or past the tile's first own block.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace msa {
+
+constexpr int kPfTokens = 64;                  // query tokens per workgroup (x 4 groups = 256 rows)
+constexpr int kPfChunk = 16;                   // blocks per workgroup
+constexpr int kPfRowHalves = kHeadDim + 8;     // f16 per LDS key row (272 B)
+constexpr int kPfTileHalves = kBlock * kPfRowHalves;
+
+// 8 NVFP4 codes (one dword, one scale) -> 8 FP8-rounded values as f16, in element order.
+__device__ __forceinline__ h8 fp4x8_lut_to_h8_ordered(uint32_t w, uint32_t lut_lo, uint32_t lut_hi) {
+  const uint32_t me = w & 0x07070707u, mo = (w >> 4) & 0x07070707u;
+  const uint32_t fe = __builtin_amdgcn_perm(lut_hi, lut_lo, me) ^ ((w << 4) & 0x80808080u);
+  const uint32_t fo = __builtin_amdgcn_perm(lut_hi, lut_lo, mo) ^ (w & 0x80808080u);
+  // interleave even (fe) and odd (fo) elements: bytes e0 e1 e2 e3 | e4 e5 e6 e7
+  return fp8x8_to_h8(__builtin_amdgcn_perm(fo, fe, 0x05010400u), __builtin_amdgcn_perm(fo, fe, 0x07030602u));
+}
+
+// The raw bytes of half a key row (64 dims) that one thread dequantises.
+template <int KT> struct PfRaw;
+template <> struct PfRaw<2> { uint4 c[2]; uint32_t s; };   // NVFP4: 32 B codes + 4 scale bytes
+template <> struct PfRaw<1> { uint4 c[4]; };               // FP8: 64 B
+
+template <int KT>
+__device__ __forceinline__ void pf_load(PfRaw<KT>& r, const uint8_t* __restrict__ kdata,
+                                        const uint8_t* __restrict__ kscales, size_t row, int half) {
+  if constexpr (KT == 2) {
+    const uint4* src = reinterpret_cast<const uint4*>(kdata + row * kNvfp4RowBytes + 32 * half);
+    r.c[0] = src[0];
+    r.c[1] = src[1];
+    r.s = *reinterpret_cast<const uint32_t*>(kscales + row * kNvfp4ScaleBytes + 4 * half);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(kdata + row * kHeadDim + 64 * half);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.c[q] = src[q];
+  }
+}
+
+// Dequantise 64 dims of one key into the f16 tile row.
+template <int KT, bool FP8MODE>
+__device__ __forceinline__ void pf_store(const PfRaw<KT>& r, const uint32_t* lut, _Float16* dst) {
+  h8 v[8];
+  if constexpr (KT == 2) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {                 // dword d: dims 8d .. 8d+7, scale byte d/2
+      const uint4& c = r.c[d >> 2];
+      const uint32_t w = (d & 3) == 0 ? c.x : (d & 3) == 1 ? c.y : (d & 3) == 2 ? c.z : c.w;
+      const uint32_t sb = (r.s >> (8 * (d >> 1))) & 0xFFu;
+      if constexpr (FP8MODE) {
+        v[d] = fp4x8_lut_to_h8_ordered(w, lut[2 * sb], lut[2 * sb + 1]);
+      } else {
+        const _Float16 sh = e4m3_to_h(sb);
+        v[d] = fp4x8_to_h8(w) * h8{sh, sh, sh, sh, sh, sh, sh, sh};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = fp8x8_to_h8(r.c[q].x, r.c[q].y);
+      v[2 * q + 1] = fp8x8_to_h8(r.c[q].z, r.c[q].w);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) *reinterpret_cast<h8*>(dst + 8 * d) = v[d];
+}
+
+// One butterfly step: lanes whose bit HALF is set keep the upper HALF values,
+// the others the lower ones; each receives its partner's copy of what it keeps.
+template <int HALF>
+__device__ __forceinline__ void butterfly_step(float (&v)[16], int n) {
+  const bool up = (n & HALF) != 0;
+#pragma unroll
+  for (int k = 0; k < HALF; ++k) {
+    const float keep = up ? v[k + HALF] : v[k];
+    const float send = up ? v[k] : v[k + HALF];
+    v[k] = fmaxf(keep, __shfl_xor(send, HALF));
+  }
+}
+// Max of 16 values per lane over the 16 lanes of each lane quarter; lane n of
+// a quarter returns the maximum of value n.
+__device__ __forceinline__ float butterfly_max16(float (&v)[16], int n) {
+  butterfly_step<8>(v, n);
+  butterfly_step<4>(v, n);
+  butterfly_step<2>(v, n);
+  butterfly_step<1>(v, n);
+  return v[0];
+}
+
+template <int KT, bool FP8MODE, bool TOKSC>
+__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
+    const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
+    float* __restrict__ block_scores, float* __restrict__ token_scores) {
+  __shared__ uint32_t lut[FP8MODE ? 512 : 2];
+  __shared__ __attribute__((aligned(16))) _Float16 tile[2][kPfTileHalves];
+  __shared__ int page_of[kPfChunk];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Q = lane >> 4, n = lane & 15;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.x * kPfTokens;
+  const int c0 = blockIdx.y * kPfChunk;
+  const int L = seq_lens[b];
+  const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
+  const int t_last = min(T, t0 + kPfTokens) - 1;
+  const int own_first = (L - T + t0) / kBlock;          // own block of the tile's first token
+  const int own_last = (L - T + t_last) / kBlock;
+  const int c_end = min(c0 + kPfChunk, max_blocks);
+  // blocks [c0, c_comp) of this chunk have visible keys; [c_comp, c_end) get -inf
+  const int c_comp = max(c0, min(c_end, min(nb, own_last + 1)));
+  const float NEG_INF = -__builtin_inff();
+  const float QNAN = __builtin_nanf("");
+  const size_t tstride = (size_t)max_blocks * kBlock;
+
+  if (FP8MODE) build_fp8_lut(lut);
+  if (tid < kPfChunk) {
+    int pg = -1;
+    if (c0 + tid < c_comp) {
+      pg = table[(size_t)b * max_blocks + c0 + tid];
+      if (pg < 0 || (int64_t)pg >= num_pages) pg = -2;     // unreadable page
+    }
+    page_of[tid] = pg;
+  }
+
+  // rows of this wave: 4 row tiles rr; row m of tile rr = token 4*(4*wave+rr) + m/4, group m%4
+  // A operand fragment [rr][ks]: lane (Q, m=n) holds dims 32ks + 8Q .. +7 of that row
+  h8 A[4][4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int t = t0 + 4 * (4 * wave + rr) + (n >> 2);
+    const int g = n & 3;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (t < T) {
+        const uint2 u = *reinterpret_cast<const uint2*>(idx_q + (((size_t)b * T + t) * kGroups + g) * kHeadDim +
+                                                        32 * ks + 8 * Q);
+        A[rr][ks] = fp8x8_to_h8(u.x, u.y);
+      } else {
+        A[rr][ks] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+  // this lane's token per row tile (rows 4Q..4Q+3 of tile rr share it) and its position
+  int p_of[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) p_of[rr] = L - T + t0 + 4 * (4 * wave + rr) + Q;
+  __syncthreads();
+
+  // blocks of the chunk with no visible key for any row: -inf
+  for (int e = tid; e < kPfTokens * kGroups * (c_end - c_comp); e += 256) {
+    const int nblk = c_end - c_comp;
+    const int row = e / nblk, i = c_comp + e % nblk;
+    const int t = t0 + (row >> 2);
+    if (t < T) block_scores[(((size_t)b * T + t) * kGroups + (row & 3)) * max_blocks + i] = NEG_INF;
+    if (TOKSC && t < T)
+      for (int kk = 0; kk < kBlock; ++kk)
+        token_scores[(((size_t)b * T + t) * kGroups + (row & 3)) * tstride + (size_t)i * kBlock + kk] = NEG_INF;
+  }
+  const int nblocks = c_comp - c0;
+  if (nblocks <= 0) return;
+
+  const int key_ld = tid >> 1, half_ld = tid & 1;   // the half key row this thread dequantises
+  auto page_row = [&](int k) -> size_t {
+    const int pg = page_of[k];
+    return (size_t)(pg < 0 ? 0 : pg) * kBlock + key_ld;
+  };
+  PfRaw<KT> raw;
+  pf_load<KT>(raw, kdata, kscales, page_row(0), half_ld);
+  pf_store<KT, FP8MODE>(raw, lut, &tile[0][key_ld * kPfRowHalves + 64 * half_ld]);
+  __syncthreads();
+
+  for (int k = 0; k < nblocks; ++k) {
+    const int i = c0 + k;
+    const _Float16* B = tile[k & 1];
+    if (k + 1 < nblocks) pf_load<KT>(raw, kdata, kscales, page_row(k + 1), half_ld);
+
+    // two halves of 64 keys; lane (Q, n) of a 16x16 output tile holds rows 4Q..4Q+3 of row
+    // tile rr (token p_of[rr]) for key kh*64 + kt*16 + n
+    const bool bad = page_of[k] == -2;
+    const bool all_visible = i < own_first;
+    float m[16];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      f4 acc[4][4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        h8 Bf[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          Bf[kt] = *reinterpret_cast<const h8*>(B + (kh * 64 + kt * 16 + n) * kPfRowHalves + 32 * ks + 8 * Q);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = mfma_16x16x32(A[rr][ks], Bf[kt], acc[rr][kt]);
+        // keep the next k-step's operand reads from being hoisted (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v;
+          if (all_visible) {
+            v = fmaxf(fmaxf(acc[rr][0][r], acc[rr][1][r]), fmaxf(acc[rr][2][r], acc[rr][3][r]));
+          } else {
+            v = NEG_INF;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+              v = fmaxf(v, (i * kBlock + kh * 64 + kt * 16 + n <= p_of[rr]) ? acc[rr][kt][r] : NEG_INF);
+          }
+          m[4 * rr + r] = kh == 0 ? v : fmaxf(m[4 * rr + r], v);
+        }
+      if constexpr (TOKSC) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = t0 + 4 * (4 * wave + rr) + Q;
+          if (t < T) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int kt = 0; kt < 4; ++kt) {
+                const int key = i * kBlock + kh * 64 + kt * 16 + n;
+                token_scores[(((size_t)b * T + t) * kGroups + r) * tstride + key] =
+                    bad ? QNAN : (key <= p_of[rr] ? acc[rr][kt][r] * sigma : NEG_INF);
+              }
+          }
+        }
+      }
+    }
+    const float mx = butterfly_max16(m, n);              // value n: tile n/4, group n%4
+    {
+      const int t = t0 + 4 * (4 * wave + (n >> 2)) + Q;
+      if (t < T) block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i] = bad ? QNAN : mx * sigma;
+    }
+
+    if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves + 64 * half_ld]);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const CacheArgs& k,
+                                  bool fp8mode, float sigma, float* block_scores, float* token_scores,
+                                  hipStream_t s) {
+  const dim3 grid((unsigned)((p.T + kPfTokens - 1) / kPfTokens),
+                  (unsigned)((p.max_blocks + kPfChunk - 1) / kPfChunk), (unsigned)p.B);
+  const uint8_t* q8 = static_cast<const uint8_t*>(idx_q);
+  const bool ts = token_scores != nullptr;
+#define MSA_PF_LAUNCH(KT, FM, TS)                                                                \
+  hipLaunchKernelGGL((indexer_prefill_kernel<KT, FM, TS>), grid, dim3(256), 0, s, q8, k.data,     \
+                     k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, sigma,  \
+                     block_scores, token_scores)
+  if (k.dtype == 1) {
+    if (ts) MSA_PF_LAUNCH(1, false, true); else MSA_PF_LAUNCH(1, false, false);
+  } else if (fp8mode) {
+    if (ts) MSA_PF_LAUNCH(2, true, true); else MSA_PF_LAUNCH(2, true, false);
+  } else {
+    if (ts) MSA_PF_LAUNCH(2, false, true); else MSA_PF_LAUNCH(2, false, false);
+  }
+#undef MSA_PF_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -32,6 +32,10 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
                           const CacheArgs& k, bool fp8mode, float* block_scores,
                           float* token_scores, hipStream_t s);
 
+hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const CacheArgs& k,
+                                  bool fp8mode, float sigma, float* block_scores, float* token_scores,
+                                  hipStream_t s);
+
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s);
 

@@ -80,6 +80,7 @@ WORKLOADS = {
     "tiny_nvfp4": Workload("tiny_nvfp4", 3, 1, (1500, 7000), "nvfp4", "fp8", 4, [], 0.05),
     "tiny_spec": Workload("tiny_spec", 2, 4, (2100, 6000), "nvfp4", "fp8", 4),
     "tiny_prefill": Workload("tiny_prefill", 2, 300, (2500, 4200), "nvfp4", "fp8", 8, [], 0.0, True, True),
+    "tiny_prefill_fp8": Workload("tiny_prefill_fp8", 2, 200, (1500, 3000), "fp8", "fp8", 8, [], 0.0, True, True),
 }
 
 
