@@ -31,7 +31,7 @@
 
 namespace msa {
 
-constexpr int kAttnWaves = 16;
+constexpr int kAttnManyRows = 8192;   // rows from which the 4-wave form is used
 constexpr int kVtDwords = kHeadDim * 8 + 64;   // 128 dims x 16 keys f16, padded per 16 dims
 
 __device__ __forceinline__ int vt_index(int d, int kp) {   // dword of (dim d, key pair kp)
@@ -54,36 +54,37 @@ template <int KT> struct VRaw;
 template <> struct VRaw<1> { uint4 c[2]; };
 template <> struct VRaw<2> { uint2 c[2]; uint32_t s[2]; };
 
+// Loads take the base of one (page, KV head) slice -- uniform across the wave
+// -- and a 32-bit row offset within it, so addresses are a scalar base plus a
+// per-lane offset.
 template <int KT>
-__device__ __forceinline__ KRaw<KT> load_k_tile(const uint8_t* kdata, const uint8_t* kscales,
-                                                 size_t krow, int Q) {
-  KRaw<KT> r;
+__device__ __forceinline__ KRaw<KT> load_k_tile(const uint8_t* kbase, const uint8_t* sbase, uint32_t r, int Q) {
+  KRaw<KT> t;
   if constexpr (KT == 2) {
-    r.c = *reinterpret_cast<const uint4*>(kdata + krow * kNvfp4RowBytes + 16 * Q);
-    r.s = *reinterpret_cast<const uint16_t*>(kscales + krow * kNvfp4ScaleBytes + 2 * Q);
+    t.c = *reinterpret_cast<const uint4*>(kbase + r * kNvfp4RowBytes + 16 * Q);
+    t.s = *reinterpret_cast<const uint16_t*>(sbase + r * kNvfp4ScaleBytes + 2 * Q);
   } else {
-    const uint4* src = reinterpret_cast<const uint4*>(kdata + krow * kHeadDim + 32 * Q);
-    r.c0 = src[0];
-    r.c1 = src[1];
+    const uint4* src = reinterpret_cast<const uint4*>(kbase + r * kHeadDim + 32 * Q);
+    t.c0 = src[0];
+    t.c1 = src[1];
   }
-  return r;
+  return t;
 }
 
 template <int KT>
-__device__ __forceinline__ VRaw<KT> load_v_tile(const uint8_t* vdata, const uint8_t* vscales,
-                                                 size_t vrow0, int dg) {
-  VRaw<KT> r;
+__device__ __forceinline__ VRaw<KT> load_v_tile(const uint8_t* vbase, const uint8_t* sbase, uint32_t r0, int dg) {
+  VRaw<KT> t;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const size_t vrow = vrow0 + u;
+    const uint32_t r = r0 + u;
     if constexpr (KT == 2) {
-      r.c[u] = *reinterpret_cast<const uint2*>(vdata + vrow * kNvfp4RowBytes + 8 * dg);
-      r.s[u] = vscales[vrow * kNvfp4ScaleBytes + dg];
+      t.c[u] = *reinterpret_cast<const uint2*>(vbase + r * kNvfp4RowBytes + 8 * dg);
+      t.s[u] = sbase[r * kNvfp4ScaleBytes + dg];
     } else {
-      r.c[u] = *reinterpret_cast<const uint4*>(vdata + vrow * kHeadDim + 16 * dg);
+      t.c[u] = *reinterpret_cast<const uint4*>(vbase + r * kHeadDim + 16 * dg);
     }
   }
-  return r;
+  return t;
 }
 
 // K tile -> the four 16x32 A fragments of S^T = K Q^T (k-chunk c = dims 32Q+8c .. +7).
@@ -158,20 +159,25 @@ __device__ __forceinline__ void stage_v_tile(const VRaw<KT>& r, const uint32_t* 
 template <int KT> constexpr int kVAhead = KT == 2 ? 4 : 2;
 constexpr int kMergeStride = kHeadDim + 4;   // fp32 row of one head in the merge buffer (padded)
 
-// KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).
-template <int KT, bool FP8MODE>
-__global__ __launch_bounds__(1024) void attn_mfma_kernel(
+// KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  WAVES waves per workgroup;
+// wave w takes selected blocks w, w + WAVES, ... and keeps a running (max,
+// sum, O) over them (online softmax); the WAVES states merge at the end.
+template <int KT, bool FP8MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_kernel(
     const uint8_t* __restrict__ q, float c_log2, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t kpages, const uint8_t* __restrict__ vdata,
     const uint8_t* __restrict__ vscales, int64_t vpages, float v_scale,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int T, float* __restrict__ out,
     float* __restrict__ lse) {
+  static_assert(kTopK % WAVES == 0, "blocks split evenly over the waves");
+  constexpr int kSmemDwords = WAVES * 16 * kMergeStride > WAVES * kVtDwords ? WAVES * 16 * kMergeStride
+                                                                             : WAVES * kVtDwords;
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
-  // V^T staging (16 x kVtDwords dwords), later reused as the merge buffer
-  // [16 waves][16 heads][kMergeStride] fp32.
-  __shared__ __attribute__((aligned(16))) uint32_t smem[kAttnWaves * 16 * kMergeStride];
-  __shared__ float m_sh[kAttnWaves][16], l_sh[kAttnWaves][16];
+  // V^T staging (WAVES x kVtDwords dwords), later reused as the merge buffer
+  // [WAVES][16 heads][kMergeStride] fp32.
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kSmemDwords];
+  __shared__ float m_sh[WAVES][16], l_sh[WAVES][16];
   __shared__ int nan_sh;
 
   const int row = blockIdx.x;   // (b*T + t)*4 + g
@@ -182,9 +188,11 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
   const int Q = lane >> 4, j = lane & 15;
   const float NEG_INF = -__builtin_inff();
 
-  // independent loads first: length, this wave's block, the query
+  // independent loads first: length, this wave's blocks, the query
   const int L = seq_lens[b];
-  const int blk = sel[(size_t)row * kTopK + w];
+  int blks[kTopK / WAVES];
+#pragma unroll
+  for (int u = 0; u < kTopK / WAVES; ++u) blks[u] = sel[(size_t)row * kTopK + w + u * WAVES];
   const uint4* qsrc =
       reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
   const uint4 qu0 = qsrc[0], qu1 = qsrc[1];
@@ -192,53 +200,68 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
   if (FP8MODE) build_fp8_lut(lut);
   __syncthreads();
 
-  const int p = L - T + t;
-  int nkeys = 0;
-  size_t rowbase = 0;
-  if (blk >= 0) {
-    if (blk >= max_blocks) {
-      nan_sh = 1;
-    } else {
-      const int pg = table[(size_t)b * max_blocks + blk];
-      if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
-        nan_sh = 1;
-      } else {
-        nkeys = min(kBlock, p + 1 - blk * kBlock);
-        rowbase = ((size_t)pg * kGroups + g) * kBlock;   // (page, KV head g)
-      }
+  // B operand of S^T = K Q^T: lane (Q, head j), k-chunk c = dims 32Q+8c..+7.
+  h8 Bq[4];
+  {
+    const uint32_t wq[8] = {qu0.x, qu0.y, qu0.z, qu0.w, qu1.x, qu1.y, qu1.z, qu1.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
+      Bq[c] = (KT == 2 && FP8MODE) ? reorder_like_lut_a(a) : a;
     }
   }
 
+  const int p = L - T + t;
+  const int kp = lane & 7;     // key pair within a V tile (keys 2kp, 2kp+1)
+  const int dg = lane >> 3;    // 16-dim group of a V tile
+  uint32_t* vt = smem + w * kVtDwords;
   float m = NEG_INF, l = 0.0f;
   f4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (nkeys > 0) {
-    const int kp = lane & 7;     // key pair within a V tile (keys 2kp, 2kp+1)
-    const int dg = lane >> 3;    // 16-dim group of a V tile
+#pragma unroll 1
+  for (int u = 0; u < kTopK / WAVES; ++u) {
+    const int blk = __builtin_amdgcn_readfirstlane(blks[u]);   // one value per wave
+    int nkeys = 0;
+    size_t rowbase = 0;
+    if (blk >= 0) {
+      if (blk >= max_blocks) {
+        nan_sh = 1;
+      } else {
+        const int pg = __builtin_amdgcn_readfirstlane(table[(size_t)b * max_blocks + blk]);
+        if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
+          nan_sh = 1;
+        } else {
+          nkeys = min(kBlock, p + 1 - blk * kBlock);
+          rowbase = ((size_t)pg * kGroups + g) * kBlock;   // (page, KV head g)
+        }
+      }
+    }
+    if (nkeys <= 0) continue;   // uniform per wave
+
     // Every K load and the first V tiles are issued before the first product.
     // All 128 rows of the page are read (they exist even when the block is
     // only partly visible), which keeps control flow uniform so that each
     // wait covers exactly the tile it needs.
+    // lane indices made opaque here so that the per-lane load offsets are
+    // recomputed per block instead of hoisted out of the loop (and spilled)
+    int jl = j, kpl = kp, dgl = dg, Ql = Q;
+    asm volatile("" : "+v"(jl), "+v"(kpl), "+v"(dgl), "+v"(Ql));
+    constexpr size_t kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
+    const uint8_t* kbase = kdata + rowbase * kRowBytes;
+    const uint8_t* vbase = vdata + rowbase * kRowBytes;
+    const uint8_t* ksb = KT == 2 ? kscales + rowbase * kNvfp4ScaleBytes : nullptr;
+    const uint8_t* vsb = KT == 2 ? vscales + rowbase * kNvfp4ScaleBytes : nullptr;
     KRaw<KT> kraw[8];
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) kraw[kt] = load_k_tile<KT>(kdata, kscales, rowbase + kt * 16 + j, Q);
+    for (int kt = 0; kt < 8; ++kt) kraw[kt] = load_k_tile<KT>(kbase, ksb, kt * 16 + jl, Ql);
     VRaw<KT> vraw[8];
 #pragma unroll
-    for (int kt = 0; kt < kVAhead<KT>; ++kt)
-      vraw[kt] = load_v_tile<KT>(vdata, vscales, rowbase + kt * 16 + 2 * kp, dg);
+    for (int kt = 0; kt < kVAhead<KT>; ++kt) vraw[kt] = load_v_tile<KT>(vbase, vsb, kt * 16 + 2 * kpl, dgl);
 
-    h8 Bq[4];
-    {
-      const uint32_t wq[8] = {qu0.x, qu0.y, qu0.z, qu0.w, qu1.x, qu1.y, qu1.z, qu1.w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
-        Bq[c] = (KT == 2 && FP8MODE) ? reorder_like_lut_a(a) : a;
-      }
-    }
-    // ---------------- S^T = K Q^T, 8 tiles of 16 keys
+    // ---------------- S^T = K Q^T, 8 tiles of 16 keys (exp2 domain)
+    const bool full = nkeys == kBlock;   // uniform: no key of the block is past p
     float x[8][4];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
@@ -248,36 +271,48 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
       // lane (Q, head j) holds keys kt*16 + 4Q + r
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[kt][r] = (kt * 16 + 4 * Q + r < nkeys) ? acc[r] * c_log2 : NEG_INF;
+        for (int r = 0; r < 4; ++r) x[kt][r] = acc[r] * c_log2;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[kt][r] = (kt * 16 + 4 * Q + r < nkeys) ? acc[r] * c_log2 : NEG_INF;
+      }
     }
-    // ---------------- softmax of this block (exp2 domain)
+    // ---------------- online softmax over this wave's blocks
     float mx = NEG_INF;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kt][r]);
     mx = max_over_quarters(mx);
+    const float m_new = fmaxf(m, mx);
+    if (m != NEG_INF && m_new != m) {          // rescale what earlier blocks left
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+    }
+    m = m_new;
     float s = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[kt][r] = exp2f(x[kt][r] - mx);
+        x[kt][r] = fast_exp2(x[kt][r] - m);
         s += x[kt][r];
       }
-    m = mx;
-    l = sum_over_quarters(s);
+    l += sum_over_quarters(s);
 
     // ---------------- O^T += V^T P^T, 8 tiles of 16 keys
-    uint32_t* vt = smem + w * kVtDwords;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
+      // keeps the V window at kVAhead tiles (hoisting further costs registers)
+      __builtin_amdgcn_sched_barrier(0);
       if (kt + kVAhead<KT> < 8)
-        vraw[kt + kVAhead<KT>] =
-            load_v_tile<KT>(vdata, vscales, rowbase + (kt + kVAhead<KT>) * 16 + 2 * kp, dg);
+        vraw[kt + kVAhead<KT>] = load_v_tile<KT>(vbase, vsb, (kt + kVAhead<KT>) * 16 + 2 * kpl, dgl);
       const int key0 = kt * 16 + 2 * kp;
-      stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt, kp, dg, key0 < nkeys, key0 + 1 < nkeys);
+      stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt, kp, dg, full || key0 < nkeys, full || key0 + 1 < nkeys);
       lds_wait();
       // P^T operand: lane (Q, head j) holds keys 4Q..4Q+3 of this tile
       h4 phi, plo;
@@ -299,7 +334,7 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
     }
   }
 
-  // ---------------- merge the 16 block states in a fixed order
+  // ---------------- merge the WAVES states in a fixed order
   if (Q == 0) {
     m_sh[w][j] = m;
     l_sh[w][j] = l;
@@ -308,34 +343,34 @@ __global__ __launch_bounds__(1024) void attn_mfma_kernel(
   {
     float M = NEG_INF;
 #pragma unroll
-    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, m_sh[ww][j]);
+    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][j]);
     const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
     float* red = reinterpret_cast<float*>(smem) + ((size_t)w * 16 + j) * kMergeStride;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(red + dt * 16 + 4 * Q) = O[dt] * f;
   }
   __syncthreads();
-  {
-    // thread -> head hh, dims 2*dl, 2*dl+1
-    const int hh = threadIdx.x >> 6, dl = threadIdx.x & 63;
+  const bool bad = nan_sh != 0;
+  for (int e = threadIdx.x; e < 16 * 64; e += WAVES * 64) {
+    // e -> head hh, dims 2*dl, 2*dl+1
+    const int hh = e >> 6, dl = e & 63;
     float M = NEG_INF;
 #pragma unroll
-    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, m_sh[ww][hh]);
+    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][hh]);
     float Lt = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < kAttnWaves; ++ww) {
+    for (int ww = 0; ww < WAVES; ++ww) {
       const float mw = m_sh[ww][hh];
       if (mw != NEG_INF) Lt += l_sh[ww][hh] * exp2f(mw - M);
     }
     const float* red = reinterpret_cast<const float*>(smem) + (size_t)hh * kMergeStride + 2 * dl;
     float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
-    for (int ww = 0; ww < kAttnWaves; ++ww) {
+    for (int ww = 0; ww < WAVES; ++ww) {
       const float2 v = *reinterpret_cast<const float2*>(red + (size_t)ww * 16 * kMergeStride);
       acc.x += v.x;
       acc.y += v.y;
     }
-    const bool bad = nan_sh != 0;
     const float inv = v_scale / Lt;
     float2 o = make_float2(acc.x * inv, acc.y * inv);
     if (bad) o = make_float2(__builtin_nanf(""), __builtin_nanf(""));
@@ -425,13 +460,23 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   }
   const float c_log2 = softmax_scale * q_scale * k.tensor_scale * 1.4426950408889634f;
   const uint8_t* q8 = (const uint8_t*)q;
-#define MSA_ATTN_LAUNCH(KT, FM)                                                                 \
-  hipLaunchKernelGGL((attn_mfma_kernel<KT, FM>), dim3(rows), dim3(1024), 0, s, q8, c_log2, k.data, \
-                     k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale, sel,      \
-                     p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse)
-  if (k.dtype == 1) MSA_ATTN_LAUNCH(1, false);
-  else if (fp8mode) MSA_ATTN_LAUNCH(2, true);
-  else MSA_ATTN_LAUNCH(2, false);
+  // Few rows (decode): 16 waves per row, one selected block each, so every
+  // block of the step is in flight at once.  Many rows (prefill): 4 waves per
+  // row with 4 blocks each and a 4-way merge -- a small LDS footprint and many
+  // resident rows per CU.  The choice depends only on the row count.
+  const bool many = rows >= kAttnManyRows;
+#define MSA_ATTN_LAUNCH(KT, FM)                                                                       \
+  if (many)                                                                                           \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4>), dim3(rows), dim3(256), 0, s, q8, c_log2, k.data, \
+                       k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale, sel,      \
+                       p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse);                        \
+  else                                                                                                \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16>), dim3(rows), dim3(1024), 0, s, q8, c_log2,       \
+                       k.data, k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale,   \
+                       sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse)
+  if (k.dtype == 1) { MSA_ATTN_LAUNCH(1, false); }
+  else if (fp8mode) { MSA_ATTN_LAUNCH(2, true); }
+  else { MSA_ATTN_LAUNCH(2, false); }
 #undef MSA_ATTN_LAUNCH
   return hipGetLastError();
 }

@@ -165,6 +165,10 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// 2^x with the hardware exponential alone (results below the smallest normal
+// float flush to zero; exact enough for softmax weights in [0, 1]).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------ waves
 __device__ __forceinline__ float max16(float v) {   // max over the 16 lanes of a row
   v = fmaxf(v, __shfl_xor(v, 1));

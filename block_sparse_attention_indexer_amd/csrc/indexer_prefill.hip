@@ -12,8 +12,8 @@
 // T x L score matrix never exists.  A workgroup owns 64 tokens x 4 groups =
 // 256 rows and a chunk of kPfChunk consecutive blocks.  Its 4 waves keep
 // their 64 rows of Q as f16 MFMA operands in registers for the whole chunk.
-// Per block the page is read once (the next page's raw bytes are prefetched
-// into registers while the current block is multiplied), dequantised into
+// Per block the page is read once (raw bytes are prefetched into registers
+// two blocks ahead of the block being multiplied), dequantised into
 // an f16 tile in LDS (double-buffered, rows padded to 272 B so the operand
 // reads are free of bank conflicts), and contracted on 16x16x32 f16 MFMAs
 // (exact products, fp32 sums), 64 rows x 64 keys per wave at a time (two
@@ -28,7 +28,13 @@
 namespace msa {
 
 constexpr int kPfTokens = 64;                  // query tokens per workgroup (x 4 groups = 256 rows)
-constexpr int kPfChunk = 16;                   // blocks per workgroup
+#ifndef MSA_PF_SCHED
+#define MSA_PF_SCHED 0
+#endif
+#ifndef MSA_PF_CHUNK
+#define MSA_PF_CHUNK 16
+#endif
+constexpr int kPfChunk = MSA_PF_CHUNK;         // blocks per workgroup
 constexpr int kPfRowHalves = kHeadDim + 8;     // f16 per LDS key row (272 B)
 constexpr int kPfTileHalves = kBlock * kPfRowHalves;
 
@@ -190,15 +196,18 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const int pg = page_of[k];
     return (size_t)(pg < 0 ? 0 : pg) * kBlock + key_ld;
   };
-  PfRaw<KT> raw;
+  // raw bytes run two blocks ahead of the block being multiplied
+  PfRaw<KT> raw, raw2;
   pf_load<KT>(raw, kdata, kscales, page_row(0), half_ld);
+  if (nblocks > 1) pf_load<KT>(raw2, kdata, kscales, page_row(1), half_ld);
   pf_store<KT, FP8MODE>(raw, lut, &tile[0][key_ld * kPfRowHalves + 64 * half_ld]);
+  raw = raw2;
   __syncthreads();
 
   for (int k = 0; k < nblocks; ++k) {
     const int i = c0 + k;
     const _Float16* B = tile[k & 1];
-    if (k + 1 < nblocks) pf_load<KT>(raw, kdata, kscales, page_row(k + 1), half_ld);
+    if (k + 2 < nblocks) pf_load<KT>(raw2, kdata, kscales, page_row(k + 2), half_ld);
 
     // two halves of 64 keys; lane (Q, n) of a 16x16 output tile holds rows 4Q..4Q+3 of row
     // tile rr (token p_of[rr]) for key kh*64 + kt*16 + n
@@ -222,8 +231,10 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = mfma_16x16x32(A[rr][ks], Bf[kt], acc[rr][kt]);
+#if MSA_PF_SCHED
         // keep the next k-step's operand reads from being hoisted (register pressure)
         __builtin_amdgcn_sched_barrier(0);
+#endif
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
@@ -264,6 +275,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     }
 
     if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves + 64 * half_ld]);
+    raw = raw2;
     __syncthreads();
   }
 }

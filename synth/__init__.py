@@ -81,6 +81,8 @@ WORKLOADS = {
     "tiny_spec": Workload("tiny_spec", 2, 4, (2100, 6000), "nvfp4", "fp8", 4),
     "tiny_prefill": Workload("tiny_prefill", 2, 300, (2500, 4200), "nvfp4", "fp8", 8, [], 0.0, True, True),
     "tiny_prefill_fp8": Workload("tiny_prefill_fp8", 2, 200, (1500, 3000), "fp8", "fp8", 8, [], 0.0, True, True),
+    # enough query rows (2 x 1,100 x 4) for the many-row attention form
+    "tiny_prefill_many": Workload("tiny_prefill_many", 2, 1100, (2300, 3600), "nvfp4", "fp8", 8, [], 0.0, True, True),
 }
 
 

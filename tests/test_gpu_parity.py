@@ -96,7 +96,8 @@ def test_unpack_fp8_every_code(M):
 
 SMALL = [("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"),
          ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"), ("tiny_spec", "fp8"),
-         ("tiny_prefill", "exact"), ("tiny_prefill", "fp8"), ("tiny_prefill_fp8", "exact")]
+         ("tiny_prefill", "exact"), ("tiny_prefill", "fp8"), ("tiny_prefill_fp8", "exact"),
+         ("tiny_prefill_many", "exact")]
 
 
 @pytest.mark.parametrize("wname,mode", SMALL)
