@@ -53,7 +53,7 @@ class Workload:
     name: str
     B: int
     T: int
-    lens: object                 # int, or (lo, hi) for uniform ragged lengths
+    lens: object                 # int, (lo, hi) for uniform ragged lengths, or a list per sequence
     kv_dtype: str                # 'f32' | 'fp8' | 'nvfp4'
     q_dtype: str                 # 'f32' | 'fp8'
     hot_per_seq: int = 0
@@ -81,6 +81,15 @@ WORKLOADS = {
     "tiny_spec": Workload("tiny_spec", 2, 4, (2100, 6000), "nvfp4", "fp8", 4),
     "tiny_prefill": Workload("tiny_prefill", 2, 300, (2500, 4200), "nvfp4", "fp8", 8, [], 0.0, True, True),
     "tiny_prefill_fp8": Workload("tiny_prefill_fp8", 2, 200, (1500, 3000), "fp8", "fp8", 8, [], 0.0, True, True),
+    # edge cases: T = 2 and 3; contexts of 1, 128, 129, 2,048 and 2,049 tokens (one key,
+    # exact block edges, 16 vs 17 blocks); a prefill with no cached context; a row of
+    # more than 2,048 blocks
+    "tiny_t2": Workload("tiny_t2", 2, 2, (130, 3000), "nvfp4", "fp8", 4, [], 0.05),
+    "tiny_t3": Workload("tiny_t3", 3, 3, (2200, 4000), "fp8", "fp8", 4),
+    "tiny_edge": Workload("tiny_edge", 5, 1, [1, 128, 129, 2048, 2049], "nvfp4", "fp8", 2, [], 0.0),
+    "tiny_prefill_nocache": Workload("tiny_prefill_nocache", 2, 129, [129, 700], "nvfp4", "fp8", 2, [], 0.0,
+                                     True, True),
+    "long_rows": Workload("long_rows", 1, 1, 300000, "fp8", "fp8", 8),
     # enough query rows (2 x 1,100 x 4) for the many-row attention form
     "tiny_prefill_many": Workload("tiny_prefill_many", 2, 1100, (2300, 3600), "nvfp4", "fp8", 8, [], 0.0, True, True),
 }
@@ -106,6 +115,9 @@ def make_layout(w: Workload, seed: int) -> Layout:
     if isinstance(w.lens, tuple):
         lo, hi = w.lens
         lens = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64)
+    elif isinstance(w.lens, list):
+        assert len(w.lens) == w.B
+        lens = torch.tensor(w.lens, dtype=torch.int64)
     else:
         lens = torch.full((w.B,), int(w.lens), dtype=torch.int64)
     assert int(lens.min()) >= w.T

@@ -97,7 +97,8 @@ def test_unpack_fp8_every_code(M):
 SMALL = [("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"),
          ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"), ("tiny_spec", "fp8"),
          ("tiny_prefill", "exact"), ("tiny_prefill", "fp8"), ("tiny_prefill_fp8", "exact"),
-         ("tiny_prefill_many", "exact")]
+         ("tiny_prefill_many", "exact"), ("tiny_t2", "exact"), ("tiny_t2", "fp8"), ("tiny_t3", "exact"),
+         ("tiny_edge", "exact"), ("tiny_prefill_nocache", "exact"), ("long_rows", "exact")]
 
 
 @pytest.mark.parametrize("wname,mode", SMALL)
