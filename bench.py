@@ -5,12 +5,15 @@ for the whole batch (one MSA layer).  Inputs are seeded synthetic data drawn
 and packed on the GPU before the timed region (resident in HBM).
 
     python bench.py [--steps K] [--warmup W] [--workload c3_128k]
-                    [--dequant exact|fp8] [--no-cpu-baseline]
+                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill]
 
-Prints one JSON line.  ``value`` is layer-steps/s; ``roofline`` describes the
-dominant kernel (the index-key scan) from HIP events recorded around each of
-its launches on the stream it runs on; ``cpu_baseline`` is the CPU fp64
-oracle timed on a bounded sample of the same workload.
+Prints one JSON line.  ``value`` is layer-steps/s over the timed steps (wall
+clock, synchronised on both sides); ``roofline`` describes the dominant kernel
+(the index-key scan) from HIP events recorded around each of its launches in
+the timed region, on the stream it runs on, and ``traffic`` from the rocprofv3
+counter summary under profiles/ (null once the kernel sources changed);
+``prefill`` times the chunked-prefill workload through the same calls;
+``cpu_baseline`` is the CPU fp64 oracle timed on a bounded sample.
 """
 import argparse
 import json
@@ -18,6 +21,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -35,6 +40,7 @@ def parse():
     ap.add_argument("--dequant", default="exact", choices=["exact", "fp8"])
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill section")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -113,7 +119,9 @@ class Workload:
         self.out = torch.empty((B, T, 64, 128), dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
 
-    def step(self, dequant, ev=None):
+    def step(self, dequant, ev=None, scan_only=False):
+        """One layer step on torch's current stream; `ev` events bracket the calls
+        (only the index scan when scan_only)."""
         M, w = self.M, self.w
         stream = None
         if ev is not None:
@@ -123,33 +131,55 @@ class Workload:
         if ev is not None:
             ev[1].record()
         M.msa_block_topk(self.prob, self.bs, self.sel, stream=stream)
-        if ev is not None:
+        if ev is not None and not scan_only:
             ev[2].record()
         fn = M.msa_sparse_attn_decode if w.T <= 8 else M.msa_sparse_attn_prefill
         fn(self.prob, self.q, w.q_dtype, 1.0, self.caches["k"][2], self.caches["v"][2], dequant, self.sel,
            1.0 / math.sqrt(128.0), self.out, None, stream=stream)
-        if ev is not None:
+        if ev is not None and not scan_only:
             ev[3].record()
 
 
+# Algorithmic bytes per element row of 128 dims (NVFP4: 64 B of E2M1 codes + 8 E4M3 scales).
+ROW_BYTES = {"f32": 512, "fp8": 128, "nvfp4": 72}
+F16_MFMA_PEAK_TFLOPS = 2500.0
+
+
 def algorithmic_bytes(wl, sel_host):
-    """Bytes the method must move per layer step (oracle.traffic's model)."""
-    from oracle import traffic as TR
+    """Bytes the method itself must move in one layer step: every index key of every
+    sequence once, the index queries, the block scores written (and read back by the
+    top-16), K and V rows of each distinct selected (sequence, group, block) once, the
+    queries, the fp32 outputs and the small tables.  Repeat reads are not counted."""
     w, lay = wl.w, wl.lay
     lens = [int(x) for x in lay.seq_lens]
     maxb = lay.max_blocks
-    idx = TR.indexer_bytes(lens, w.T, w.kv_dtype, w.q_dtype, 4, maxb)
-    topk = TR.topk_bytes(w.B, w.T, 4, maxb)
-    # distinct (sequence, group, block) rows read, each key once per KV head
-    keys = 0
+    qb = 4 if w.q_dtype == "f32" else 1
+    rows = w.B * w.T * 4
+    idx = (sum(lens) * ROW_BYTES[w.kv_dtype] + rows * 128 * qb + rows * maxb * 4 + w.B * maxb * 4 + w.B * 4)
+    topk = rows * maxb * 4 + rows * 16 * 4
+    keys = 0   # distinct selected keys, summed over (sequence, group)
     for b in range(w.B):
         L = lens[b]
         for g in range(4):
-            blocks = set(int(i) for i in sel_host[b, :, g].reshape(-1) if i >= 0)
-            for i in blocks:
+            for i in set(int(i) for i in sel_host[b, :, g].reshape(-1) if i >= 0):
                 keys += min(128, L - 128 * i)
-    attn = TR.attention_bytes(keys, w.kv_dtype, w.q_dtype, w.B, w.T, 64)
+    attn = 2 * keys * ROW_BYTES[w.kv_dtype] + w.B * w.T * 64 * 128 * (qb + 4)
     return idx, topk, attn
+
+
+def algorithmic_flops(wl, sel_host):
+    """Index scores: 2*128 flops per (token, group, visible key); attention: 4*128 flops
+    per (token, head, attended key) -- QK^T and PV."""
+    w, lay = wl.w, wl.lay
+    idx = attn = 0
+    for b in range(w.B):
+        L = int(lay.seq_lens[b])
+        p = np.arange(L - w.T, L, dtype=np.int64)                         # token positions
+        idx += 2 * 128 * 4 * int((p + 1).sum())
+        s = sel_host[b].astype(np.int64)                                   # [T, 4, 16]
+        nk = np.where(s >= 0, np.clip(p[:, None, None] + 1 - 128 * s, 0, 128), 0)
+        attn += 4 * 128 * 16 * int(nk.sum())
+    return idx, attn
 
 
 def indexer_kernel_name(w, dequant):
@@ -165,10 +195,10 @@ def indexer_kernel_name(w, dequant):
     return f"msa::indexer_mfma_kernel<{kt}, {str(fp8mode).lower()}, 2>"
 
 
-def measured_traffic(workload, role):
-    """Calibrated HBM bytes per launch (read + write) of one step's kernel, from the
-    rocprofv3 counter summary under profiles/ -- None when there is none or when the
-    kernel sources changed since the counters were taken."""
+def measured_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch (read + write) of one kernel, from the rocprofv3
+    counter summary under profiles/ -- None when there is none or when the kernel
+    sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -177,10 +207,40 @@ def measured_traffic(workload, role):
         d = json.load(fh)
     if d.get("sources_sha256") != profile_step.sources_hash():
         return None
-    for e in d["kernels"].values():
-        if e.get("role") == role and "fetch_bytes" in e and "write_bytes" in e:
-            return round(e["fetch_bytes"] + e["write_bytes"])
-    return None
+    e = d["kernels"].get(kernel)
+    if e is None or "fetch_bytes" not in e or "write_bytes" not in e:
+        return None
+    return round(e["fetch_bytes"] + e["write_bytes"])
+
+
+def prefill_section(dequant, seed, steps=5, warmup=2):
+    """The chunked-prefill workload (c5) through the same three calls: per-call
+    event timings and the MFMA rate of the two contractions (f16 MFMAs, exact
+    products) against the f16 dense peak."""
+    import torch
+    wl = Workload("c5", seed)
+    w = wl.w
+    for _ in range(warmup):
+        wl.step(dequant)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for k in range(steps):
+        wl.step(dequant, evs[k])
+    torch.cuda.synchronize()
+    t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(3)] for k in range(steps)]).mean(axis=0)
+    f_idx, f_attn = algorithmic_flops(wl, wl.sel.cpu().numpy())
+    tf_idx = f_idx / (t[0] * 1e-3) / 1e12
+    tf_attn = f_attn / (t[2] * 1e-3) / 1e12
+    return {"workload": f"c5: chunked prefill, batch {w.B}, {w.T} new query tokens per sequence on "
+                        f"{w.lens - w.T} cached ({w.lens} total), NVFP4 K/V and index keys, FP8 queries",
+            "ms_per_step": round(float(t.sum()), 4),
+            "indexer": {"kernel": "msa::indexer_prefill_kernel", "ms": round(float(t[0]), 4),
+                        "gflop": round(f_idx / 1e9, 1), "tflops": round(tf_idx, 1),
+                        "frac_of_f16_mfma_peak": round(tf_idx / F16_MFMA_PEAK_TFLOPS, 4)},
+            "topk_ms": round(float(t[1]), 4),
+            "attention": {"kernel": "msa::attn_mfma_kernel (4 waves per row)", "ms": round(float(t[2]), 4),
+                          "gflop": round(f_attn / 1e9, 1), "tflops": round(tf_attn, 1),
+                          "frac_of_f16_mfma_peak": round(tf_attn / F16_MFMA_PEAK_TFLOPS, 4)}}
 
 
 def cpu_baseline(wl, dequant, sample):
@@ -251,17 +311,25 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # Timed region: K whole steps; HIP events on the launching stream bracket only the
+    # index scan (the roofline kernel), so the step itself runs undisturbed.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        wl.step(args.dequant, evs[k])
+        wl.step(args.dequant, evs[k], scan_only=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
     k_idx = [evs[k][0].elapsed_time(evs[k][1]) for k in range(K)]
-    k_topk = [evs[k][1].elapsed_time(evs[k][2]) for k in range(K)]
-    k_attn = [evs[k][2].elapsed_time(evs[k][3]) for k in range(K)]
+    # after the timed region: every call bracketed, for the per-kernel breakdown
+    Kb = min(K, 20)
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(Kb)]
+    for k in range(Kb):
+        wl.step(args.dequant, evb[k])
+    torch.cuda.synchronize()
+    k_topk = [evb[k][1].elapsed_time(evb[k][2]) for k in range(Kb)]
+    k_attn = [evb[k][2].elapsed_time(evb[k][3]) for k in range(Kb)]
 
     sel = wl.sel.cpu().numpy()
     b_idx, b_topk, b_attn = algorithmic_bytes(wl, sel)
@@ -295,9 +363,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant) + " (index-key scan + block max-pool)",
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, "indexer")},
+                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant))},
         "cpu_baseline": None,
     }
+    if not args.no_prefill and args.workload != "c5":
+        out["prefill"] = prefill_section(args.dequant, args.seed)
     if sample:
         out["cpu_baseline"] = cpu_baseline(wl, args.dequant, sample)
     print(json.dumps(out), flush=True)

@@ -36,3 +36,33 @@ def test_nvfp4_is_four_and_a_half_bits():
 def test_dense_is_never_cheaper_past_2048():
     for L in [2049, 5000, 10 ** 6]:
         assert TR.sparse_decode_bytes(L, "fp8") < TR.dense_decode_bytes(L, "fp8") * (0.125 + 2048 / L + 1e-12)
+
+
+def test_bench_bytes_model_matches_the_oracle_model():
+    """bench.py restates the algorithmic bytes model (it may not import the oracle);
+    both must give the same figures for the same selection."""
+    import types
+    import numpy as np
+    import bench
+    from oracle import traffic as TR
+    rng = np.random.default_rng(4)
+    for kv, qd, T in (("nvfp4", "fp8", 1), ("fp8", "fp8", 4), ("f32", "f32", 1)):
+        lens = [1000, 3001, 129]
+        maxb = 24
+        B = len(lens)
+        sel = np.full((B, T, 4, 16), -1, np.int32)
+        for b, L in enumerate(lens):
+            nb = (L + 127) // 128
+            for t in range(T):
+                for g in range(4):
+                    k = min(16, nb)
+                    sel[b, t, g, :k] = np.sort(rng.choice(nb, k, replace=False))
+        w = types.SimpleNamespace(B=B, T=T, kv_dtype=kv, q_dtype=qd)
+        lay = types.SimpleNamespace(seq_lens=np.array(lens), max_blocks=maxb)
+        wl = types.SimpleNamespace(w=w, lay=lay)
+        idx, topk, attn = bench.algorithmic_bytes(wl, sel)
+        assert idx == TR.indexer_bytes(lens, T, kv, qd, 4, maxb)
+        assert topk == TR.topk_bytes(B, T, 4, maxb)
+        keys = sum(min(128, lens[b] - 128 * i) for b in range(B) for g in range(4)
+                   for i in set(int(x) for x in sel[b, :, g].reshape(-1) if x >= 0))
+        assert attn == TR.attention_bytes(keys, kv, qd, B, T, 64)
