@@ -1,11 +1,12 @@
 """Benchmark of the MSA decode layer step on one MI355X.
 
-One step = msa_indexer_scores -> msa_block_topk -> msa_sparse_attn_decode
-for the whole batch (one MSA layer).  Inputs are seeded synthetic data drawn
+One step = msa_indexer_scores (index scan and block max-pool) -> msa_block_topk
+(top-16 selection) -> msa_sparse_attn_decode for the whole batch (one MSA
+layer); with --fused the first two run as the single call msa_indexer_topk.  Inputs are seeded synthetic data drawn
 and packed on the GPU before the timed region (resident in HBM).
 
     python bench.py [--steps K] [--warmup W] [--workload c3_128k]
-                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill]
+                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill] [--fused]
 
 Prints one JSON line.  ``value`` is layer-steps/s over the timed steps (wall
 clock, synchronised on both sides); ``roofline`` describes the dominant kernel
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill section")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the scan and the top-16 as the one call msa_indexer_topk")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -117,27 +120,37 @@ class Workload:
         self.bs = torch.empty((B, T, 4, maxb), dtype=torch.float32, device=dev)
         self.sel = torch.empty((B, T, 4, 16), dtype=torch.int32, device=dev)
         self.out = torch.empty((B, T, 64, 128), dtype=torch.float32, device=dev)
+        # arrival counters of msa_indexer_topk: zero-filled once, left zero-filled by every call
+        self.ws = torch.zeros(max(1, M.msa_workspace_size(self.prob, M.MSA_CALL_INDEXER_TOPK) // 4),
+                              dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
 
-    def step(self, dequant, ev=None, scan_only=False):
-        """One layer step on torch's current stream; `ev` events bracket the calls
-        (only the index scan when scan_only)."""
+    def step(self, dequant, ev=None, scan_only=False, fused=False):
+        """One layer step on torch's current stream.  fused: msa_indexer_topk (scan +
+        selection) then attention; else the three separate calls.  `ev` events are
+        recorded before the first call and after each call (after the first only, when
+        scan_only)."""
         M, w = self.M, self.w
-        stream = None
         if ev is not None:
             ev[0].record()
-        M.msa_indexer_scores(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], dequant, self.bs,
-                             None, stream=stream)
-        if ev is not None:
-            ev[1].record()
-        M.msa_block_topk(self.prob, self.bs, self.sel, stream=stream)
-        if ev is not None and not scan_only:
-            ev[2].record()
+        if fused:
+            M.msa_indexer_topk(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], dequant, self.bs,
+                               self.sel, self.ws)
+            calls_done = 1
+        else:
+            M.msa_indexer_scores(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], dequant,
+                                 self.bs, None)
+            if ev is not None:
+                ev[1].record()
+            M.msa_block_topk(self.prob, self.bs, self.sel)
+            calls_done = 2
+        if ev is not None and (fused or not scan_only):
+            ev[calls_done].record()
         fn = M.msa_sparse_attn_decode if w.T <= 8 else M.msa_sparse_attn_prefill
         fn(self.prob, self.q, w.q_dtype, 1.0, self.caches["k"][2], self.caches["v"][2], dequant, self.sel,
-           1.0 / math.sqrt(128.0), self.out, None, stream=stream)
+           1.0 / math.sqrt(128.0), self.out, None)
         if ev is not None and not scan_only:
-            ev[3].record()
+            ev[calls_done + 1].record()
 
 
 # Algorithmic bytes per element row of 128 dims (NVFP4: 64 B of E2M1 codes + 8 E4M3 scales).
@@ -182,17 +195,17 @@ def algorithmic_flops(wl, sel_host):
     return idx, attn
 
 
-def indexer_kernel_name(w, dequant):
+def indexer_kernel_name(w, dequant, fused=False):
     """The index-scan kernel libmsa launches for this workload (as rocprofv3 names it)."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
     fp8mode = kt == 2 and dequant == "fp8"
     if w.T == 1 and not fp8mode:
-        return f"msa::indexer_decode1_kernel<{kt}, false>"
+        return f"msa::indexer_decode1_kernel<{kt}, false, {str(fused).lower()}>"
     if w.T <= 4:
         return f"msa::indexer_decode_kernel<{kt}, {str(fp8mode).lower()}, false>"
-    return f"msa::indexer_mfma_kernel<{kt}, {str(fp8mode).lower()}, 2>"
+    return f"msa::indexer_prefill_kernel<{kt}, {str(fp8mode).lower()}, false>"
 
 
 def measured_traffic(workload, kernel):
@@ -221,11 +234,11 @@ def prefill_section(dequant, seed, steps=5, warmup=2):
     wl = Workload("c5", seed)
     w = wl.w
     for _ in range(warmup):
-        wl.step(dequant)
+        wl.step(dequant, fused=False)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for k in range(steps):
-        wl.step(dequant, evs[k])
+        wl.step(dequant, evs[k], fused=False)
     torch.cuda.synchronize()
     t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(3)] for k in range(steps)]).mean(axis=0)
     f_idx, f_attn = algorithmic_flops(wl, wl.sel.cpu().numpy())
@@ -307,35 +320,38 @@ def main():
         del a, bbuf
 
     for _ in range(args.warmup):
-        wl.step(args.dequant)
+        wl.step(args.dequant, fused=args.fused)
     torch.cuda.synchronize()
 
     K = args.steps
+    fused = args.fused
+    ncalls = 2 if fused else 3
     # Timed region: K whole steps; HIP events on the launching stream bracket only the
-    # index scan (the roofline kernel), so the step itself runs undisturbed.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    # first call (the index scan, with the selection when fused: the roofline kernel),
+    # so the step itself runs undisturbed.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        wl.step(args.dequant, evs[k], scan_only=True)
+        wl.step(args.dequant, evs[k], scan_only=True, fused=fused)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
     k_idx = [evs[k][0].elapsed_time(evs[k][1]) for k in range(K)]
-    # after the timed region: every call bracketed, for the per-kernel breakdown
+    # after the timed region: every call bracketed, for the per-call breakdown
     Kb = min(K, 20)
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(Kb)]
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(Kb)]
     for k in range(Kb):
-        wl.step(args.dequant, evb[k])
+        wl.step(args.dequant, evb[k], fused=fused)
     torch.cuda.synchronize()
-    k_topk = [evb[k][1].elapsed_time(evb[k][2]) for k in range(Kb)]
-    k_attn = [evb[k][2].elapsed_time(evb[k][3]) for k in range(Kb)]
+    per_call = np.array([[evb[k][i].elapsed_time(evb[k][i + 1]) for i in range(ncalls)] for k in range(Kb)]).mean(axis=0)
 
     sel = wl.sel.cpu().numpy()
     b_idx, b_topk, b_attn = algorithmic_bytes(wl, sel)
     total_bytes = b_idx + b_topk + b_attn
     idx_ms = float(np.mean(k_idx))
-    achieved_idx = b_idx / (idx_ms * 1e-3) / 1e9
+    b_first = b_idx + b_topk if fused else b_idx          # bytes of the first (roofline) call
+    achieved_idx = b_first / (idx_ms * 1e-3) / 1e9
     step_tbps = total_bytes / (ms_step * 1e-3) / 1e12
 
     out = {
@@ -358,12 +374,14 @@ def main():
         "hbm_TBps_step": round(step_tbps, 3),
         "pct_of_peak_hbm_step": round(100 * step_tbps * 1e3 / HBM_PEAK_GBPS, 1),
         "bytes_per_step": {"indexer": b_idx, "topk": b_topk, "attention": b_attn},
-        "kernel_ms": {"indexer": round(idx_ms, 5), "topk": round(float(np.mean(k_topk)), 5),
-                      "attention": round(float(np.mean(k_attn)), 5)},
-        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant) + " (index-key scan + block max-pool)",
+        "call_ms": ({"indexer_topk": round(idx_ms, 5), "attention": round(float(per_call[1]), 5)} if fused else
+                    {"indexer": round(idx_ms, 5), "topk": round(float(per_call[1]), 5),
+                     "attention": round(float(per_call[2]), 5)}),
+        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, fused) +
+                     (" (index-key scan + block max-pool + top-16)" if fused else " (index-key scan + block max-pool)"),
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant))},
+                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, fused))},
         "cpu_baseline": None,
     }
     if not args.no_prefill and args.workload != "c5":

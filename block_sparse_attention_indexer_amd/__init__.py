@@ -5,7 +5,7 @@ Argument marshalling only: every step runs in the HIP kernels of libmsa.so
 memory and the current stream; nothing here computes on the CPU, and if the
 library is missing every call raises instead of falling back.
 
-The functions keep the C names: msa_indexer_scores, msa_block_topk,
+The functions keep the C names: msa_indexer_scores, msa_indexer_topk, msa_block_topk,
 msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_pack_fp8,
 msa_unpack_fp8, msa_pack_nvfp4, msa_unpack_nvfp4, msa_workspace_size.
 """
@@ -18,9 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
 MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
 MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
-MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN = 0, 1, 2
+MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK = 0, 1, 2, 3
 
-EXPORTED = ("msa_indexer_scores", "msa_block_topk", "msa_sparse_attn_decode",
+EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -62,6 +62,8 @@ def _lib():
         P = ctypes.POINTER
         sig = {
             "msa_indexer_scores": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp, vp],
+            "msa_indexer_topk": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp, vp,
+                                 sz, vp],
             "msa_block_topk": [P(msa_problem), vp, vp, vp],
             "msa_sparse_attn_decode": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
                                        ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
@@ -130,6 +132,16 @@ def msa_indexer_scores(prob, idx_q, q_dtype, q_scale, idx_k, dequant, block_scor
     _check(_lib().msa_indexer_scores(ctypes.byref(prob), _ptr(idx_q), DTYPES[q_dtype], float(q_scale),
                                      ctypes.byref(idx_k), DEQUANT[dequant], _ptr(block_scores),
                                      _ptr(token_scores), _stream(stream)), "msa_indexer_scores")
+
+
+def msa_indexer_topk(prob, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores, sel, workspace,
+                     stream=None):
+    """Steps 1-3 in one call; `workspace`: a zero-filled device tensor of at least
+    msa_workspace_size(prob, MSA_CALL_INDEXER_TOPK) bytes (left zero-filled)."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib().msa_indexer_topk(ctypes.byref(prob), _ptr(idx_q), DTYPES[q_dtype], float(q_scale),
+                                   ctypes.byref(idx_k), DEQUANT[dequant], _ptr(block_scores), _ptr(sel),
+                                   _ptr(workspace), ws_bytes, _stream(stream)), "msa_indexer_topk")
 
 
 def msa_block_topk(prob, block_scores, sel, stream=None):

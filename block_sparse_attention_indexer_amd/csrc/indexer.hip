@@ -13,6 +13,7 @@
 // the caller asks for them (a separate template instance).
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_wave.hpp"
 
 namespace msa {
 
@@ -353,12 +354,16 @@ __device__ __forceinline__ float wave_max4(f4 v, int lane) {
 #endif
 constexpr int kDec1PagesPerWave = MSA_DEC1_PAGES_PER_WAVE;
 
-template <int KT, bool TOKSC>
+// FUSE: the last workgroup of a sequence to finish (a per-sequence arrival
+// counter in `counters`, zero before the call and reset to zero by that
+// workgroup) also selects the sequence's top-16 blocks, one wave per group.
+// Nothing waits on another workgroup: the last arrival does the work.
+template <int KT, bool TOKSC, bool FUSE>
 __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, float sigma, float* __restrict__ block_scores,
-    float* __restrict__ token_scores) {
+    float* __restrict__ token_scores, int32_t* __restrict__ sel, uint32_t* __restrict__ counters) {
   static_assert(kDec1PagesPerWave >= 1 && kDec1PagesPerWave <= 64, "page ids are held one per lane");
   __shared__ float pooled[kDecWaves][kDec1PagesPerWave][kGroups];
   const int b = blockIdx.y;
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
   const int L = seq_lens[b];
   const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
   const int w0 = (blockIdx.x * kDecWaves + wave) * kDec1PagesPerWave;
-  if (w0 >= max_blocks) return;
+  if (w0 < max_blocks) {
   const int wend = min(w0 + kDec1PagesPerWave, max_blocks);
   const int nreal = max(0, min(wend, nb) - w0);
 
@@ -444,7 +449,36 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
   lds_wait();
   for (int e = lane; e < kGroups * nreal; e += 64) {
     const int g = e / nreal, i = e % nreal;
-    block_scores[((size_t)b * kGroups + g) * max_blocks + w0 + i] = pooled[wave][i][g];
+    float* dst = block_scores + ((size_t)b * kGroups + g) * max_blocks + w0 + i;
+    if (FUSE)   // device-coherent store: read back by another workgroup in this kernel
+      __hip_atomic_store(dst, pooled[wave][i][g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *dst = pooled[wave][i][g];
+  }
+  }   // w0 < max_blocks
+
+  if constexpr (FUSE) {
+    // The scores and -inf fills above are complete (not merely issued) before the
+    // count, and the count is taken at system scope, so the last arrival reads every
+    // workgroup's scores with device-coherent loads.  No cache-wide fence: on a GPU
+    // with one L2 per XCD that would write back and invalidate the whole L2.
+    __shared__ int last_sh;
+    __shared__ WaveTopkLds tk[kDecWaves];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last_sh = __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                        gridDim.x - 1 ? 1 : 0;
+    __syncthreads();
+    if (last_sh) {
+      if (threadIdx.x == 0) __hip_atomic_store(&counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      const int own = max(0, min((L - 1) / kBlock, max_blocks - 1));
+      const size_t r = (size_t)b * kGroups + wave;   // one group per wave
+      if (own <= 64 * 16)
+        wave_topk_row_regs<16>(block_scores + r * max_blocks, own, sel + r * kTopK, tk[wave], lane);
+      else
+        wave_topk_row(block_scores + r * max_blocks, own, sel + r * kTopK, tk[wave], lane);
+    }
   }
 }
 
@@ -494,9 +528,13 @@ __global__ __launch_bounds__(128) void indexer_f32_kernel(
   }
 }
 
+bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mode) {
+  return p.T == 1 && k.dtype != 0 && !(k.dtype == 2 && fp8mode);
+}
+
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
-                          float* token_scores, hipStream_t s) {
+                          float* token_scores, hipStream_t s, int32_t* sel, uint32_t* counters) {
   const float sigma = q_scale * k.tensor_scale;
   if (k.dtype == 0) {
     hipLaunchKernelGGL(indexer_f32_kernel, dim3(p.max_blocks, p.B), dim3(128), 0, s,
@@ -511,14 +549,15 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     const unsigned per_wg = kDecWaves * kDec1PagesPerWave;
     const dim3 grid((unsigned)((p.max_blocks + per_wg - 1) / per_wg), (unsigned)p.B);
     const bool ts = token_scores != nullptr;
-#define MSA_DEC1_LAUNCH(KT, TS)                                                                  \
-  hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS>), grid, dim3(kDecWaves * 64), 0, s, q8, k.data, \
-                     k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,        \
-                     block_scores, token_scores)
+#define MSA_DEC1_LAUNCH(KT, TS, FU)                                                                  \
+  hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS, FU>), grid, dim3(kDecWaves * 64), 0, s, q8, k.data, \
+                     k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,            \
+                     block_scores, token_scores, sel, counters)
+    const bool fu = sel != nullptr;
     if (k.dtype == 1) {
-      if (ts) MSA_DEC1_LAUNCH(1, true); else MSA_DEC1_LAUNCH(1, false);
+      if (ts) MSA_DEC1_LAUNCH(1, true, false); else if (fu) MSA_DEC1_LAUNCH(1, false, true); else MSA_DEC1_LAUNCH(1, false, false);
     } else {
-      if (ts) MSA_DEC1_LAUNCH(2, true); else MSA_DEC1_LAUNCH(2, false);
+      if (ts) MSA_DEC1_LAUNCH(2, true, false); else if (fu) MSA_DEC1_LAUNCH(2, false, true); else MSA_DEC1_LAUNCH(2, false, false);
     }
 #undef MSA_DEC1_LAUNCH
   } else if (p.T <= 4) {

@@ -28,9 +28,13 @@ hipError_t launch_pack_nvfp4(const float* x, int64_t groups, float tensor_scale,
 hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t groups,
                                float tensor_scale, bool fp8mode, float* out, hipStream_t s);
 
+// With sel and counters non-null (only where indexer_can_fuse_topk), the scan also
+// writes the top-16 selection; counters: one zeroed uint32 per sequence, left zeroed.
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
-                          float* token_scores, hipStream_t s);
+                          float* token_scores, hipStream_t s, int32_t* sel = nullptr,
+                          uint32_t* counters = nullptr);
+bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mode);
 
 hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const CacheArgs& k,
                                   bool fp8mode, float sigma, float* block_scores, float* token_scores,

@@ -1,0 +1,187 @@
+// Top-16 selection for one row by a single wavefront (step 3 of MSA).
+//
+// Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer":
+// attention runs over the top 16 blocks and the most recent block is always
+// kept.  With own+1 <= 16 visible blocks all are selected; otherwise the own
+// block joins the 15 best older blocks under (score descending, block index
+// ascending).  NaN ranks below every number.
+//
+// Each older block i is a 64-bit key: order-preserving score bits above the
+// complemented index, so keys are distinct and the order above is integer
+// order.  A most-significant-digit radix select over 8-bit digits narrows a
+// key prefix until exactly 15 keys lie at or above it; each pass streams the
+// row from memory (written just before by other workgroups), counts
+// digits in a 256-bin histogram in LDS, and lets one wave scan find the digit.
+// Only one wave takes part, so no workgroup barrier is needed.
+#pragma once
+#include "common.hpp"
+
+namespace msa {
+
+struct WaveTopkLds {
+  uint32_t hist[256];
+  int32_t won[kTopK];
+  uint32_t n_won;
+};
+
+__device__ __forceinline__ uint64_t topk_key(float s, int i) {
+  return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// Scores written by other workgroups of the same kernel are read with
+// device-coherent loads (they bypass the per-XCD caches that may hold stale
+// lines); no cache-wide fence is needed.
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Writes out[0..15] (ascending block ids, -1 padded) for one row of scores S.
+__device__ inline void wave_topk_row(const float* S, int own, int32_t* out, WaveTopkLds& sh, int lane) {
+  if (own + 1 <= kTopK) {
+    if (lane < kTopK) out[lane] = lane <= own ? lane : -1;
+    return;
+  }
+  const int n = own;               // candidates: blocks 0 .. own-1
+  uint64_t prefix = 0, mask = 0;
+  uint32_t need = kTopK - 1;
+#pragma unroll 1
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sh.hist[4 * lane + u] = 0;
+    lds_wait();
+    for (int i = lane; i < n; i += 64) {
+      const uint64_t key = topk_key(coherent_load(S + i), i);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(key >> shift) & 255u], 1u);
+    }
+    lds_wait();
+    // lane l holds bins 4l..4l+3; find digit d with above(d) < need <= above(d) + hist[d]
+    uint32_t h[4], s = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { h[u] = sh.hist[4 * lane + u]; s += h[u]; }
+    uint32_t incl = s;             // suffix sum over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(incl, off);
+      if (lane + off < 64) incl += o;
+    }
+    uint32_t above = incl - s;     // keys in bins of higher lanes
+    uint32_t d = 0, a = 0, c = 0;
+    bool found = false;
+#pragma unroll
+    for (int u = 3; u >= 0; --u) {
+      if (!found && above < need && need <= above + h[u]) {
+        found = true;
+        d = 4 * lane + u;
+        a = above;
+        c = h[u];
+      }
+      above += h[u];
+    }
+    const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
+    d = __shfl(d, src);
+    a = __shfl(a, src);
+    c = __shfl(c, src);
+    prefix |= (uint64_t)d << shift;
+    mask |= 255ull << shift;
+    need -= a;
+    if (c == need) break;          // wave-uniform
+  }
+  // exactly 15 keys satisfy (key & mask) >= prefix
+  if (lane == 0) sh.n_won = 0;
+  lds_wait();
+  for (int i = lane; i < n; i += 64) {
+    const uint64_t key = topk_key(coherent_load(S + i), i);
+    if ((key & mask) >= prefix) {
+      const uint32_t slot = atomicAdd(&sh.n_won, 1u);
+      if (slot < (uint32_t)(kTopK - 1)) sh.won[slot] = i;
+    }
+  }
+  lds_wait();
+  const int32_t mine = lane < kTopK - 1 ? sh.won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
+  int rank = 0;
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
+  if (lane < kTopK) out[rank] = mine;
+}
+
+// The same selection with the row held in registers: each lane loads its
+// E scores once (lane + 64e), all loads in flight together, and the radix
+// passes run on registers.  For rows of up to 64*E older blocks.
+template <int E>
+__device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out, WaveTopkLds& sh, int lane) {
+  if (own + 1 <= kTopK) {
+    if (lane < kTopK) out[lane] = lane <= own ? lane : -1;
+    return;
+  }
+  const int n = own;
+  uint32_t k32[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    k32[e] = i < n ? order_key(coherent_load(S + i)) : 0u;
+  }
+  auto key_of = [&](int e) -> uint64_t {
+    return ((uint64_t)k32[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * e));
+  };
+  uint64_t prefix = 0, mask = 0;
+  uint32_t need = kTopK - 1;
+#pragma unroll 1
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sh.hist[4 * lane + u] = 0;
+    lds_wait();
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t key = key_of(e);
+      if (lane + 64 * e < n && (key & mask) == prefix) atomicAdd(&sh.hist[(uint32_t)(key >> shift) & 255u], 1u);
+    }
+    lds_wait();
+    uint32_t h[4], s = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { h[u] = sh.hist[4 * lane + u]; s += h[u]; }
+    uint32_t incl = s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(incl, off);
+      if (lane + off < 64) incl += o;
+    }
+    uint32_t above = incl - s;
+    uint32_t d = 0, a = 0, c = 0;
+    bool found = false;
+#pragma unroll
+    for (int u = 3; u >= 0; --u) {
+      if (!found && above < need && need <= above + h[u]) {
+        found = true;
+        d = 4 * lane + u;
+        a = above;
+        c = h[u];
+      }
+      above += h[u];
+    }
+    const int src = __ffsll((unsigned long long)__ballot(found)) - 1;
+    d = __shfl(d, src);
+    a = __shfl(a, src);
+    c = __shfl(c, src);
+    prefix |= (uint64_t)d << shift;
+    mask |= 255ull << shift;
+    need -= a;
+    if (c == need) break;
+  }
+  if (lane == 0) sh.n_won = 0;
+  lds_wait();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (lane + 64 * e < n && (key_of(e) & mask) >= prefix) {
+      const uint32_t slot = atomicAdd(&sh.n_won, 1u);
+      if (slot < (uint32_t)(kTopK - 1)) sh.won[slot] = lane + 64 * e;
+    }
+  }
+  lds_wait();
+  const int32_t mine = lane < kTopK - 1 ? sh.won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
+  int rank = 0;
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
+  if (lane < kTopK) out[rank] = mine;
+}
+
+}  // namespace msa

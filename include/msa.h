@@ -154,7 +154,29 @@ msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_d
                                    float* out, float* lse, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
-typedef enum { MSA_CALL_INDEXER = 0, MSA_CALL_TOPK = 1, MSA_CALL_ATTN = 2 } msa_call;
+/* Steps 1-3 in one call ("MSA primer": score, max-pool per block, keep the top
+ * 16 blocks with the most recent one forced): the same block_scores and sel as
+ * msa_indexer_scores followed by msa_block_topk, bit for bit.  For one query
+ * token with FP8 or NVFP4-exact keys a single kernel does both -- the last
+ * workgroup to finish a sequence selects that sequence's blocks -- which
+ * removes the separate selection pass from the decode step; otherwise the two
+ * kernels run back to back.
+ *   workspace  device, at least msa_workspace_size(prob, MSA_CALL_INDEXER_TOPK)
+ *              bytes (4 per sequence), zero-filled before its first use; every
+ *              call leaves it zero-filled again.  Calls that share a workspace
+ *              must not overlap (they are ordered on one stream).
+ * Other arguments as for msa_indexer_scores and msa_block_topk. */
+msa_status msa_indexer_topk(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
+                            float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                            float* block_scores, int32_t* sel, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+typedef enum {
+  MSA_CALL_INDEXER = 0,
+  MSA_CALL_TOPK = 1,
+  MSA_CALL_ATTN = 2,
+  MSA_CALL_INDEXER_TOPK = 3
+} msa_call;
 
 /* Bytes of device workspace a call needs for this problem (0 = none).
  * Reads only host-visible fields of prob. */

@@ -117,3 +117,17 @@ def test_pack_validation(lib):
     assert lib.msa_pack_fp8(64, -1, 1.0, 64, None) == M.MSA_ERR_INVALID_ARG
     assert lib.msa_pack_fp8(64, 0, 1.0, 64, None) == M.MSA_OK
     assert lib.msa_unpack_fp8(64, 4, float("nan"), 64, None) == M.MSA_ERR_INVALID_ARG
+
+
+def test_indexer_topk_validation(lib):
+    p = _prob()
+    c = _cache()
+    def call(prob=p, sel=4096, ws=8192, ws_bytes=64):
+        return lib.msa_indexer_topk(ctypes.byref(prob), 1024, M.MSA_FP8_E4M3, 1.0, ctypes.byref(c), 0, 2048, sel,
+                                    ws, ws_bytes, None)
+    assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_INDEXER_TOPK) == 2 * 4
+    assert call(sel=None) == M.MSA_ERR_INVALID_ARG
+    assert call(ws=None) == M.MSA_ERR_WORKSPACE
+    assert call(ws_bytes=4) == M.MSA_ERR_WORKSPACE
+    assert call(ws=8193) == M.MSA_ERR_WORKSPACE
+    assert call(prob=_prob(topk=8)) == M.MSA_ERR_UNSUPPORTED

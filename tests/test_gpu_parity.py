@@ -193,3 +193,51 @@ def test_full_size_sampled(M, wname, samples):
             H.compare_out(res["out"][b, t], o[0])
             assert np.abs(res["lse"][b, t] - lse[0]).max() <= 1e-4
         _say(wname, "sample", b, "ok")
+
+
+# ------------------------------------------------------------------ fused scan + selection
+
+def _fused(M, case, ws, B=None, dequant="exact"):
+    w, lay = case.w, case.lay
+    B = w.B if B is None else B
+    prob = M.problem(case.d_seq[:B], case.d_table[:B], w.T)
+    bs = torch.empty((B, w.T, 4, lay.max_blocks), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, w.T, 4, 16), dtype=torch.int32, device="cuda")
+    M.msa_indexer_topk(prob, case.d_idx_q[:B], w.q_dtype, 1.0, case.d_caches["idx_k"][2], dequant, bs, sel, ws)
+    torch.cuda.synchronize()
+    return bs.cpu().numpy(), sel.cpu().numpy()
+
+
+@pytest.mark.parametrize("wname,mode", [("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"), ("tiny_edge", "exact"),
+                                        ("long_rows", "exact"), ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"),
+                                        ("c1", "exact")])
+def test_indexer_topk_equals_the_separate_calls(M, wname, mode):
+    """msa_indexer_topk gives the block scores and selection of msa_indexer_scores +
+    msa_block_topk bit for bit, call after call, and leaves its workspace zeroed --
+    also when a later call covers fewer sequences."""
+    _say("indexer_topk", wname, mode)
+    case = H.HostCase(wname).upload()
+    ref = H.to_host(H.run_path(case, mode, attention=False))
+    B = case.w.B
+    ws = torch.zeros(M.msa_workspace_size(M.problem(case.d_seq, case.d_table, case.w.T), M.MSA_CALL_INDEXER_TOPK) // 4,
+                     dtype=torch.int32, device="cuda")
+    for rep in range(3):
+        bs, sel = _fused(M, case, ws, dequant=mode)
+        assert np.array_equal(bs, ref["block_scores"], equal_nan=True), rep
+        assert np.array_equal(sel, ref["sel"]), rep
+        assert int(ws.abs().sum()) == 0
+    if B > 1:
+        bs, sel = _fused(M, case, ws, B=B - 1, dequant=mode)
+        assert np.array_equal(sel, ref["sel"][:B - 1])
+        assert int(ws.abs().sum()) == 0
+
+
+def test_indexer_topk_full_size(M):
+    _say("indexer_topk full size c3_128k")
+    case = H.DeviceCase("c3_128k", keep_fp32=False)
+    ref = H.to_host(H.run_path(case, "exact", attention=False))
+    ws = torch.zeros(case.w.B, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        bs, sel = _fused(M, case, ws)
+        assert np.array_equal(bs, ref["block_scores"]) and np.array_equal(sel, ref["sel"]), rep
+    assert int(ws.abs().sum()) == 0
