@@ -208,11 +208,12 @@ def indexer_kernel_name(w, dequant, fused=False):
     return f"msa::indexer_prefill_kernel<{kt}, {str(fp8mode).lower()}, false>"
 
 
-def measured_traffic(workload, kernel):
-    """Calibrated HBM bytes per launch (read + write) of one kernel, from the rocprofv3
-    counter summary under profiles/ -- None when there is none or when the kernel
+def measured_traffic(workload, kernel=None, role=None):
+    """Calibrated HBM bytes per launch (read + write) of one kernel -- named, or the
+    only kernel of a role ("indexer", "topk", "attention") -- from the rocprofv3
+    counter summary under profiles/; None when there is none or when the kernel
     sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"layer_step_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     import profile_step
@@ -220,6 +221,11 @@ def measured_traffic(workload, kernel):
         d = json.load(fh)
     if d.get("sources_sha256") != profile_step.sources_hash():
         return None
+    if kernel is None:
+        names = [n for n, e in d["kernels"].items() if e.get("role") == role]
+        if len(names) != 1:
+            return None
+        kernel = names[0]
     e = d["kernels"].get(kernel)
     if e is None or "fetch_bytes" not in e or "write_bytes" not in e:
         return None
@@ -249,11 +255,13 @@ def prefill_section(dequant, seed, steps=5, warmup=2):
             "ms_per_step": round(float(t.sum()), 4),
             "indexer": {"kernel": "msa::indexer_prefill_kernel", "ms": round(float(t[0]), 4),
                         "gflop": round(f_idx / 1e9, 1), "tflops": round(tf_idx, 1),
-                        "frac_of_f16_mfma_peak": round(tf_idx / F16_MFMA_PEAK_TFLOPS, 4)},
+                        "frac_of_f16_mfma_peak": round(tf_idx / F16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic("c5", role="indexer")},
             "topk_ms": round(float(t[1]), 4),
             "attention": {"kernel": "msa::attn_mfma_kernel (4 waves per row)", "ms": round(float(t[2]), 4),
                           "gflop": round(f_attn / 1e9, 1), "tflops": round(tf_attn, 1),
-                          "frac_of_f16_mfma_peak": round(tf_attn / F16_MFMA_PEAK_TFLOPS, 4)}}
+                          "frac_of_f16_mfma_peak": round(tf_attn / F16_MFMA_PEAK_TFLOPS, 4),
+                          "traffic": measured_traffic("c5", role="attention")}}
 
 
 def cpu_baseline(wl, dequant, sample):

@@ -5,8 +5,8 @@
 Runs bench.py three times as a child process under rocprofv3 (this process
 never touches the GPU):
 
-  1. --kernel-trace --stats      bench.py --steps 10 --warmup 2 --no-cpu-baseline
-  2. --pmc FETCH_SIZE            bench.py --steps 3 --warmup 1 --no-cpu-baseline --calib-copy-mib 512
+  1. --kernel-trace --stats      bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-prefill
+  2. --pmc FETCH_SIZE            bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-prefill --calib-copy-mib 512
   3. --pmc WRITE_SIZE            (same)
 
 Counter readings are per dispatch, in KiB.  Each is scaled by what the same
@@ -14,10 +14,10 @@ counter reads for the 512 MiB elementwise copy that bench.py launches with
 --calib-copy-mib (which reads and writes exactly 512 MiB), so the reported
 bytes are calibrated HBM bytes per launch.  Writes, into --out:
 
-  decode_step_<workload>.md          per-kernel launches and durations, calibrated HBM
+  layer_step_<workload>.md           per-kernel launches and durations, calibrated HBM
                           bytes per launch, the calibration factors and the
                           commands that produced them;
-  decode_step_<workload>_traffic.json the same numbers for bench.py, with a hash of the
+  layer_step_<workload>_traffic.json the same numbers for bench.py, with a hash of the
                           kernel sources they were measured on.
 Raw rocprofv3 output is deleted once summarised.
 """
@@ -105,8 +105,8 @@ def main():
 
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(raw, "trace"), "-o", "run",
                  "-f", "csv", "--", py, bench, "--workload", w, "--steps", "10", "--warmup", "2",
-                 "--no-cpu-baseline"]
-    pmc_bench = [py, bench, "--workload", w, "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+                 "--no-cpu-baseline", "--no-prefill"]
+    pmc_bench = [py, bench, "--workload", w, "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-prefill",
                  "--calib-copy-mib", str(CALIB_MIB)]
     cmds = {"trace": trace_cmd}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -151,7 +151,7 @@ def main():
         kernels[name] = e
     out = {"workload": w, "sources_sha256": sources_hash(), "calibration": calib,
            "commands": {k: " ".join(v) for k, v in cmds.items()}, "kernels": kernels}
-    with open(os.path.join(args.out, f"decode_step_{w}_traffic.json"), "w") as fh:
+    with open(os.path.join(args.out, f"layer_step_{w}_traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
 
     lines = [f"# rocprofv3 summary: MSA layer step, workload {w}", "",
@@ -168,7 +168,7 @@ def main():
     for name, e in kernels.items():
         lines.append(f"| `{name}` | {e.get('calls', '')} | {e.get('avg_us', 0):.2f} | {e.get('min_us', 0):.2f} | "
                      f"{e.get('max_us', 0):.2f} | {e.get('fetch_bytes', 0):,.0f} | {e.get('write_bytes', 0):,.0f} |")
-    with open(os.path.join(args.out, f"decode_step_{w}.md"), "w") as fh:
+    with open(os.path.join(args.out, f"layer_step_{w}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
 
