@@ -283,22 +283,29 @@ __device__ __forceinline__ float e4m3_byte_to_f(uint32_t w, int k) {
   }
 }
 
+#ifndef MSA_DEC1_CHAINS
+#define MSA_DEC1_CHAINS 2
+#endif
+constexpr int kDec1Chains = MSA_DEC1_CHAINS;   // independent MFMA accumulation chains (divides 8)
+
 // The 4 group scores of this lane's key (before the tensor scales).
 // A[c] gives dims 4c .. 4c+3 of this lane's group (lane % 4).
 template <int KT, typename ASrc>
 __device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const ASrc& A) {
   f4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (KT == 2) {
-    // two scale groups at a time, their MFMA chains interleaved
+    // kDec1Chains scale groups at a time, their MFMA chains interleaved
 #pragma unroll
-    for (int s0 = 0; s0 < 8; s0 += 2) {
-      f4 part[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int s0 = 0; s0 < 8; s0 += kDec1Chains) {
+      f4 part[kDec1Chains];
+#pragma unroll
+      for (int g = 0; g < kDec1Chains; ++g) part[g] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {               // dword 2s+h: dims 16s+8h .. +7, low nibble first
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
 #pragma unroll
-          for (int g = 0; g < 2; ++g) {
+          for (int g = 0; g < kDec1Chains; ++g) {
             const int s = s0 + g;
             const uint32_t w = dword_of(u.c[s >> 1], 2 * (s & 1) + h);
             const h4 bv = e == 0 ? cat4(fp4x2_to_h2<0>(w), fp4x2_to_h2<1>(w)) : cat4(fp4x2_to_h2<2>(w), fp4x2_to_h2<3>(w));
@@ -307,7 +314,7 @@ __device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const ASrc& A) 
         }
       }
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < kDec1Chains; ++g) {
         const int s = s0 + g;
         const float sc = e4m3_byte_to_f(s < 4 ? u.s.x : u.s.y, s & 3);
 #pragma unroll
@@ -350,16 +357,24 @@ __device__ __forceinline__ float wave_max4(f4 v, int lane) {
 }
 
 #ifndef MSA_DEC1_PAGES_PER_WAVE
-#define MSA_DEC1_PAGES_PER_WAVE 8
+#define MSA_DEC1_PAGES_PER_WAVE 16
 #endif
 constexpr int kDec1PagesPerWave = MSA_DEC1_PAGES_PER_WAVE;
+
+// Each wave keeps a ring of kDec1Ring key sets in registers, kDec1Ring - 1 of
+// them in flight while one is contracted; at ~170 VGPRs that is two
+// workgroups per CU, so about 24 sets (110 KB) are in flight per CU.
+#ifndef MSA_DEC1_RING
+#define MSA_DEC1_RING 4
+#endif
+constexpr int kDec1Ring = MSA_DEC1_RING;
 
 // FUSE: the last workgroup of a sequence to finish (a per-sequence arrival
 // counter in `counters`, zero before the call and reset to zero by that
 // workgroup) also selects the sequence's top-16 blocks, one wave per group.
 // Nothing waits on another workgroup: the last arrival does the work.
 template <int KT, bool TOKSC, bool FUSE>
-__global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
+__global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, float sigma, float* __restrict__ block_scores,
@@ -367,7 +382,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
   static_assert(kDec1PagesPerWave >= 1 && kDec1PagesPerWave <= 64, "page ids are held one per lane");
   __shared__ float pooled[kDecWaves][kDec1PagesPerWave][kGroups];
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float NEG_INF = -__builtin_inff();
   const float QNAN = __builtin_nanf("");
   const int L = seq_lens[b];
@@ -410,16 +425,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
   }
 
   const int nsets = 2 * nreal;               // two 64-key sets per page
-  KeySet<KT> cur, nxt;
-  load_key_set<KT>(cur, kdata, kscales, (size_t)__builtin_amdgcn_readlane(pid_safe, 0) * kBlock + lane);
   f4 bmax = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
-  for (int u = 0; u < nsets; ++u) {
+  // score set u (64 keys of block u/2) and fold it into the block maxima
+  auto consume = [&](int u, const KeySet<KT>& cur) {
     const int blk = u >> 1, half = u & 1;
-    {
-      const int un = min(u + 1, nsets - 1);
-      load_key_set<KT>(nxt, kdata, kscales,
-                       (size_t)__builtin_amdgcn_readlane(pid_safe, un >> 1) * kBlock + (un & 1) * 64 + lane);
-    }
     f4 sc = score_key_set<KT>(cur, A);
     const int key = (w0 + blk) * kBlock + half * 64 + lane;
     if (w0 + blk == nb - 1) {                    // only the last block can hold keys past L - 1
@@ -433,7 +442,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) tsc[g * tstride + key] = key < L ? sc[g] * sigma : NEG_INF;
     }
-    cur = nxt;
     if (half == 1) {
       const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
       const float m = wave_max4(bmax, lane);
@@ -444,6 +452,27 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode1_kernel(
           for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)(w0 + blk) * kBlock + kk] = QNAN;
       }
       bmax = f4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    }
+  };
+  {
+    // a ring of kDec1Ring key sets in registers, kDec1Ring - 1 loads ahead; loads
+    // past the wave's last set re-read that set (cache hits), so that every
+    // load is unconditional and each wait covers exactly one set
+    constexpr int R = kDec1Ring;
+    KeySet<KT> buf[R];
+    auto load_set = [&](KeySet<KT>& dst, int u) {
+      const int uc = min(u, nsets - 1);
+      load_key_set<KT>(dst, kdata, kscales,
+                       (size_t)__builtin_amdgcn_readlane(pid_safe, uc >> 1) * kBlock + (uc & 1) * 64 + lane);
+    };
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r) load_set(buf[r], r);
+    for (int u0 = 0; u0 < nsets; u0 += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        load_set(buf[(r + R - 1) % R], u0 + r + R - 1);
+        if (u0 + r < nsets) consume(u0 + r, buf[r]);
+      }
     }
   }
   lds_wait();
