@@ -14,16 +14,21 @@
 //         from the page: lane quarter Q loads dims [32Q, 32Q+32) of its key;
 //         B = Q^T, the 16 heads of the group);
 //   softmax over the block's <= 128 keys in fp32 (exp2 domain);
-//   O^T += V^T P^T on 16x16x16 f16 MFMAs.  The lane layout of S^T is exactly
-//         the B operand P^T of the next product, so P never leaves registers;
-//         P is split into f16 hi + lo parts (two MFMAs) to keep ~2^-22
-//         relative precision.  V^T is staged per 16-key tile through a
-//         wave-private LDS slice (dequantised, transposed); keys past the
-//         query's position are staged as zeros.
+//   O^T += V^T P^T on 16x16x32 f16 MFMAs, two 16-key tiles per product.  The
+//         lane layout of S^T is the B operand P^T of the next product, so P
+//         never leaves registers; it enters as f16 (round to nearest, at most
+//         2^-12 relative error per element; the softmax sum stays fp32).
+//         Each 16-key V tile is dequantised into a wave-private LDS slice in
+//         its natural [key][dim] f16 layout (16-byte writes, chunks
+//         XOR-swizzled per key so that neither the writes nor the reads meet
+//         bank conflicts) and read back with gfx950's transposing LDS read
+//         (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of
+//         one dim: the A operand of V^T.  Keys past the query's position are
+//         zeroed before decoding (their scale byte, or their FP8 bytes).
 // The 16 per-block partial states (max, sum, O) are merged in one pass over
 // LDS, summed in wave order, so results are deterministic.
-// FP8 and NVFP4 values are exact in f16; the products are exact and the
-// accumulation is fp32.
+// FP8 and NVFP4 values are exact in f16, so Q K^T is exact up to its fp32
+// accumulation; P V carries P's f16 rounding.
 #include <math.h>
 
 #include "common.hpp"
@@ -32,16 +37,28 @@
 namespace msa {
 
 constexpr int kAttnManyRows = 8192;   // rows from which the 4-wave form is used
-constexpr int kVtDwords = kHeadDim * 8 + 64;   // 128 dims x 16 keys f16, padded per 16 dims
 
-__device__ __forceinline__ int vt_index(int d, int kp) {   // dword of (dim d, key pair kp)
-  return d * 8 + kp + ((d >> 4) << 3);
+// One 16-key V tile in LDS: f16 [16 keys][128 dims], 256 B per key.  The
+// 16-byte chunk c of key k sits at chunk c ^ vt_swizzle(k): with it the
+// 16-byte writes (8 keys per phase) and the transposing 8-byte reads (4 keys
+// x 4 chunks per phase) each touch every bank once.
+constexpr int kVtBytes = 16 * kHeadDim * 2;
+constexpr int kVtSlotBytes = 2 * kVtBytes;   // per wave: the two tiles of one PV product
+__device__ __forceinline__ int vt_swizzle(int k) { return (2 * k + (k >> 2) + 4 * (k >> 3)) & 15; }
+__device__ __forceinline__ int vt_offset(int k, int chunk) { return k * 256 + 16 * (chunk ^ vt_swizzle(k)); }
+
+// gfx950 transposing LDS read: in each group of 16 lanes, lane i receives for
+// e = 0..3 the 16-bit element (i mod 4) of the 8-byte chunk addressed by lane
+// 4e + i/4 of its group (fixed by an in-bounds probe).  With lane l pointing
+// at key l/4, dims 4(l mod 4) .. +3 of a 16-dim tile, lane l gets dim l mod 16
+// of keys 4(l/16) .. +3.
+__device__ __forceinline__ h4 lds_read_tr16(const uint8_t* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)p);
+  return __builtin_bit_cast(h4, v);
 }
 __device__ __forceinline__ h8 reorder_like_lut_a(h8 a) {
   return h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]};
-}
-__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
 // One 16-key tile of K or V as loaded from a page, before decoding.
@@ -115,43 +132,43 @@ __device__ __forceinline__ void decode_k_tile(const KRaw<KT>& r, const uint32_t*
   }
 }
 
-// V tile -> this lane's 2 keys x 16 dims as f16, written transposed (V^T,
-// dim-major, key pairs packed in one dword) into the wave's LDS slice.
-// Keys at or past `valid` are written as zeros, so unwritten rows of a
-// partly filled page never reach the product (0 * NaN would).
+// V tile -> this lane's 2 keys x 16 dims as f16, written in [key][dim]
+// layout into the wave's LDS slice (woff[u][hh]: byte offsets of key 2kp+u,
+// dims 16dg+8hh .. +7).  Keys that are not kept are zeroed before decoding:
+// an NVFP4 key through its scale bytes (E2M1 codes are always finite), an
+// FP8 key through its bytes, so unwritten rows of a partly filled page never
+// reach the product (0 * NaN would).
 template <int KT, bool FP8MODE>
-__device__ __forceinline__ void stage_v_tile(const VRaw<KT>& r, const uint32_t* lut, uint32_t* vt,
-                                             int kp, int dg, bool keep0, bool keep1) {
-  h8 v0[2], v1[2];
+__device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, uint8_t* vt,
+                                             const int (&woff)[2][2], bool keep0, bool keep1) {
+  if constexpr (KT == 2) {
+    r.s[0] = keep0 ? r.s[0] : 0u;
+    r.s[1] = keep1 ? r.s[1] : 0u;
+  } else {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    r.c[0] = keep0 ? r.c[0] : z;
+    r.c[1] = keep1 ? r.c[1] : z;
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    h8* dst = u == 0 ? v0 : v1;
+    h8 v[2];
     if constexpr (KT == 2) {
       const uint32_t sb = r.s[u];
       if constexpr (FP8MODE) {
-        dst[0] = fp4x8_lut_to_h8(r.c[u].x, lut[2 * sb], lut[2 * sb + 1]);
-        dst[1] = fp4x8_lut_to_h8(r.c[u].y, lut[2 * sb], lut[2 * sb + 1]);
+        v[0] = fp4x8_lut_to_h8(r.c[u].x, lut[2 * sb], lut[2 * sb + 1]);
+        v[1] = fp4x8_lut_to_h8(r.c[u].y, lut[2 * sb], lut[2 * sb + 1]);
       } else {
         const _Float16 sh = e4m3_to_h(sb);
         const h8 ss = h8{sh, sh, sh, sh, sh, sh, sh, sh};
-        dst[0] = fp4x8_to_h8(r.c[u].x) * ss;
-        dst[1] = fp4x8_to_h8(r.c[u].y) * ss;
+        v[0] = fp4x8_to_h8(r.c[u].x) * ss;
+        v[1] = fp4x8_to_h8(r.c[u].y) * ss;
       }
     } else {
-      dst[0] = fp8x8_to_h8(r.c[u].x, r.c[u].y);
-      dst[1] = fp8x8_to_h8(r.c[u].z, r.c[u].w);
+      v[0] = fp8x8_to_h8(r.c[u].x, r.c[u].y);
+      v[1] = fp8x8_to_h8(r.c[u].z, r.c[u].w);
     }
-  }
-  const h8 zero = h8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const h8 a = keep0 ? v0[hh] : zero;
-    const h8 c = keep1 ? v1[hh] : zero;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 16 * dg + 8 * hh + ((KT == 2 && FP8MODE) ? lut_perm(e) : e);
-      vt[vt_index(d, kp)] = pack_h2(a[e], c[e]);
-    }
+    for (int hh = 0; hh < 2; ++hh) *reinterpret_cast<h8*>(vt + woff[u][hh]) = v[hh];
   }
 }
 
@@ -171,10 +188,10 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_ker
     const int32_t* __restrict__ table, int max_blocks, int T, float* __restrict__ out,
     float* __restrict__ lse) {
   static_assert(kTopK % WAVES == 0, "blocks split evenly over the waves");
-  constexpr int kSmemDwords = WAVES * 16 * kMergeStride > WAVES * kVtDwords ? WAVES * 16 * kMergeStride
-                                                                             : WAVES * kVtDwords;
+  constexpr int kSmemDwords = WAVES * 16 * kMergeStride > WAVES * kVtSlotBytes / 4 ? WAVES * 16 * kMergeStride
+                                                                                    : WAVES * kVtSlotBytes / 4;
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
-  // V^T staging (WAVES x kVtDwords dwords), later reused as the merge buffer
+  // V tile staging (WAVES x kVtSlotBytes), later reused as the merge buffer
   // [WAVES][16 heads][kMergeStride] fp32.
   __shared__ __attribute__((aligned(16))) uint32_t smem[kSmemDwords];
   __shared__ float m_sh[WAVES][16], l_sh[WAVES][16];
@@ -214,7 +231,17 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_ker
   const int p = L - T + t;
   const int kp = lane & 7;     // key pair within a V tile (keys 2kp, 2kp+1)
   const int dg = lane >> 3;    // 16-dim group of a V tile
-  uint32_t* vt = smem + w * kVtDwords;
+  uint8_t* vt = reinterpret_cast<uint8_t*>(smem) + w * kVtSlotBytes;
+  // LDS byte offsets, fixed per lane: where this lane writes its V values
+  // (keys 2kp+u, dims 16dg+8hh..) and where its transposing reads point
+  // (key lane/4, dims 16dt + 4(lane mod 4)..; the chunk index 2dt + x XORs as
+  // a bit field, so dt enters as "^ 32dt")
+  int woff[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) woff[u][hh] = vt_offset(2 * kp + u, 2 * dg + hh);
+  const int roff = vt_offset(lane >> 2, (lane & 3) >> 1) + 8 * (lane & 1);
   float m = NEG_INF, l = 0.0f;
   f4 O[8];
 #pragma unroll
@@ -304,31 +331,35 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_ker
       }
     l += sum_over_quarters(s);
 
-    // ---------------- O^T += V^T P^T, 8 tiles of 16 keys
+    // ---------------- O^T += V^T P^T, 4 pairs of 16-key tiles
+    // One 16x16x32 MFMA covers two tiles: lane (Q, j) takes keys 4Q..4Q+3 of
+    // each tile of the pair, in P^T (from S^T's layout) and in V^T (two
+    // transposing reads) alike.
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      // keeps the V window at kVAhead tiles (hoisting further costs registers)
-      __builtin_amdgcn_sched_barrier(0);
-      if (kt + kVAhead<KT> < 8)
-        vraw[kt + kVAhead<KT>] = load_v_tile<KT>(vbase, vsb, (kt + kVAhead<KT>) * 16 + 2 * kpl, dgl);
-      const int key0 = kt * 16 + 2 * kp;
-      stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt, kp, dg, full || key0 < nkeys, full || key0 + 1 < nkeys);
-      lds_wait();
-      // P^T operand: lane (Q, head j) holds keys 4Q..4Q+3 of this tile
-      h4 phi, plo;
+    for (int kt2 = 0; kt2 < 8; kt2 += 2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const _Float16 hv = (_Float16)x[kt][r];
-        phi[r] = hv;
-        plo[r] = (_Float16)(x[kt][r] - (float)hv);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int kt = kt2 + t2;
+        // keeps the V window at kVAhead tiles (hoisting further costs registers)
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + kVAhead<KT> < 8)
+          vraw[kt + kVAhead<KT>] = load_v_tile<KT>(vbase, vsb, (kt + kVAhead<KT>) * 16 + 2 * kpl, dgl);
+        const int key0 = kt * 16 + 2 * kp;
+        stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt + t2 * kVtBytes, woff, full || key0 < nkeys,
+                                  full || key0 + 1 < nkeys);
       }
+      lds_wait();
+      // P^T operand in f16 (P in (0, 1], rounded to nearest)
+      h8 ph;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ph[e] = (_Float16)x[kt2 + (e >> 2)][e & 3];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int d = dt * 16 + j;   // A row = dim
-        const uint2 av = *reinterpret_cast<const uint2*>(vt + vt_index(d, 2 * Q));
-        const h4 a = __builtin_bit_cast(h4, av);
-        O[dt] = mfma_16x16x16(a, phi, O[dt]);
-        O[dt] = mfma_16x16x16(a, plo, O[dt]);
+        // A operand: lane (Q, j) gets dim 16dt + j of keys 4Q .. 4Q+3 of both tiles
+        const h4 a0 = lds_read_tr16(vt + (roff ^ (32 * dt)));
+        const h4 a1 = lds_read_tr16(vt + kVtBytes + (roff ^ (32 * dt)));
+        const h8 a = h8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        O[dt] = mfma_16x16x32(a, ph, O[dt]);
       }
       lds_wait();
     }
@@ -346,8 +377,17 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_ker
     for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][j]);
     const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
     float* red = reinterpret_cast<float*>(smem) + ((size_t)w * 16 + j) * kMergeStride;
+    if constexpr (KT == 2 && FP8MODE) {
+      // the table decode leaves each 8-dim chunk in the order (0,2,4,6 | 1,3,5,7),
+      // so row 4Q + r of a tile is dim 8(Q/2) + (Q%2) + 2r
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(red + dt * 16 + 4 * Q) = O[dt] * f;
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[dt * 16 + 8 * (Q >> 1) + (Q & 1) + 2 * r] = O[dt][r] * f;
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(red + dt * 16 + 4 * Q) = O[dt] * f;
+    }
   }
   __syncthreads();
   const bool bad = nan_sh != 0;
