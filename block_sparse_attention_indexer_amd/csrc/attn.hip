@@ -36,7 +36,10 @@
 
 namespace msa {
 
-constexpr int kAttnManyRows = 8192;   // rows from which the 4-wave form is used
+#ifndef MSA_ATTN_MANY_ROWS
+#define MSA_ATTN_MANY_ROWS 8192
+#endif
+constexpr int kAttnManyRows = MSA_ATTN_MANY_ROWS;   // rows from which the 4-wave form is used
 
 // One 16-key V tile in LDS: f16 [16 keys][128 dims], 256 B per key.  The
 // 16-byte chunk c of key k sits at chunk c ^ vt_swizzle(k): with it the
@@ -173,14 +176,24 @@ __device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, ui
 }
 
 // V tiles in flight ahead of the one being multiplied.
-template <int KT> constexpr int kVAhead = KT == 2 ? 4 : 2;
+#ifndef MSA_ATTN_VAHEAD
+#define MSA_ATTN_VAHEAD 4
+#endif
+#ifndef MSA_ATTN_KRING
+#define MSA_ATTN_KRING 8
+#endif
+template <int KT> constexpr int kVAhead = KT == 2 ? MSA_ATTN_VAHEAD : 2;
+constexpr int kKRing = MSA_ATTN_KRING;   // K tiles of a block in flight (divides 8)
 constexpr int kMergeStride = kHeadDim + 4;   // fp32 row of one head in the merge buffer (padded)
 
 // KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  WAVES waves per workgroup;
 // wave w takes selected blocks w, w + WAVES, ... and keeps a running (max,
 // sum, O) over them (online softmax); the WAVES states merge at the end.
+#ifndef MSA_ATTN_MANY_WG
+#define MSA_ATTN_MANY_WG 3
+#endif
 template <int KT, bool FP8MODE, int WAVES>
-__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_kernel(
+__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : MSA_ATTN_MANY_WG) void attn_mfma_kernel(
     const uint8_t* __restrict__ q, float c_log2, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t kpages, const uint8_t* __restrict__ vdata,
     const uint8_t* __restrict__ vscales, int64_t vpages, float v_scale,
@@ -280,9 +293,11 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_ker
     const uint8_t* vbase = vdata + rowbase * kRowBytes;
     const uint8_t* ksb = KT == 2 ? kscales + rowbase * kNvfp4ScaleBytes : nullptr;
     const uint8_t* vsb = KT == 2 ? vscales + rowbase * kNvfp4ScaleBytes : nullptr;
-    KRaw<KT> kraw[8];
+    // K tiles in a ring of kKRing slots: tile kt + kKRing is loaded into the
+    // slot tile kt leaves once decoded
+    KRaw<KT> kraw[kKRing];
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) kraw[kt] = load_k_tile<KT>(kbase, ksb, kt * 16 + jl, Ql);
+    for (int kt = 0; kt < kKRing; ++kt) kraw[kt] = load_k_tile<KT>(kbase, ksb, kt * 16 + jl, Ql);
     VRaw<KT> vraw[8];
 #pragma unroll
     for (int kt = 0; kt < kVAhead<KT>; ++kt) vraw[kt] = load_v_tile<KT>(vbase, vsb, kt * 16 + 2 * kpl, dgl);
@@ -293,17 +308,18 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : 3) void attn_mfma_ker
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       h8 Ak[4];
-      decode_k_tile<KT, FP8MODE>(kraw[kt], lut, Ak);
+      decode_k_tile<KT, FP8MODE>(kraw[kt % kKRing], lut, Ak);
+      if (kt + kKRing < 8) kraw[kt % kKRing] = load_k_tile<KT>(kbase, ksb, (kt + kKRing) * 16 + jl, Ql);
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
       // lane (Q, head j) holds keys kt*16 + 4Q + r
-      if (full) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[kt][r] = acc[r] * c_log2;
-      } else {
+      for (int r = 0; r < 4; ++r) x[kt][r] = acc[r] * c_log2;
+      if (!full) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) x[kt][r] = (kt * 16 + 4 * Q + r < nkeys) ? acc[r] * c_log2 : NEG_INF;
+        for (int r = 0; r < 4; ++r)
+          if (kt * 16 + 4 * Q + r >= nkeys) x[kt][r] = NEG_INF;
       }
     }
     // ---------------- online softmax over this wave's blocks
