@@ -187,6 +187,29 @@ __device__ __forceinline__ float sum_over_quarters(float v) {
   v += __shfl_xor(v, 32);
   return v;
 }
+// Lane l = 16Q + n returns the maximum of value Q over lanes n, n+16, n+32,
+// n+48: 3 exchanges (each lane keeps the half of its values that its side
+// of the exchange owns).
+__device__ __forceinline__ float quarter_max4(f4 v, int lane) {
+  const bool up = lane & 32;
+  float a = up ? v[2] : v[0], b = up ? v[3] : v[1];          // keep these two
+  const float sa = up ? v[0] : v[2], sb = up ? v[1] : v[3];  // partner keeps these
+  a = fmaxf(a, __shfl_xor(sa, 32));
+  b = fmaxf(b, __shfl_xor(sb, 32));
+  const bool up16 = lane & 16;
+  const float m = up16 ? b : a;
+  return fmaxf(m, __shfl_xor(up16 ? a : b, 16));
+}
+// Max over the 64 lanes of 4 values: 7 exchanges.  Lane l returns the
+// maximum of value g = 2*(l/32) + (l/16)%2.
+__device__ __forceinline__ float wave_max4(f4 v, int lane) {
+  float m = quarter_max4(v, lane);
+  m = fmaxf(m, __shfl_xor(m, 8));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 1));
+  return m;
+}
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_wave_barrier();

@@ -338,24 +338,6 @@ struct AInRegs {
   __device__ __forceinline__ h4 operator[](int c) const { return v[c]; }
 };
 
-// Max over the 64 lanes of 4 values: 7 exchanges.  Lane l returns the
-// maximum of value g = 2*(l/32) + (l/16)%2.
-__device__ __forceinline__ float wave_max4(f4 v, int lane) {
-  const bool up = lane & 32;
-  float a = up ? v[2] : v[0], b = up ? v[3] : v[1];          // keep these two
-  const float sa = up ? v[0] : v[2], sb = up ? v[1] : v[3];  // partner keeps these
-  a = fmaxf(a, __shfl_xor(sa, 32));
-  b = fmaxf(b, __shfl_xor(sb, 32));
-  const bool up16 = lane & 16;
-  float m = up16 ? b : a;
-  m = fmaxf(m, __shfl_xor(up16 ? a : b, 16));
-  m = fmaxf(m, __shfl_xor(m, 8));
-  m = fmaxf(m, __shfl_xor(m, 4));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 1));
-  return m;
-}
-
 #ifndef MSA_DEC1_PAGES_PER_WAVE
 #define MSA_DEC1_PAGES_PER_WAVE 16
 #endif

@@ -13,15 +13,16 @@
 // 256 rows and a chunk of kPfChunk consecutive blocks.  Its 4 waves keep
 // their 64 rows of Q as f16 MFMA operands in registers for the whole chunk.
 // Per block the page is read once (raw bytes are prefetched into registers
-// two blocks ahead of the block being multiplied), dequantised into
-// an f16 tile in LDS (double-buffered, rows padded to 272 B so the operand
-// reads are free of bank conflicts), and contracted on 16x16x32 f16 MFMAs
-// (exact products, fp32 sums), 64 rows x 64 keys per wave at a time (two
-// halves per block keep the accumulator at 64 registers).  The epilogue takes
-// the max over the block's keys: in-lane over the key tiles and halves, then
-// a 4-step butterfly over the 16 key lanes that leaves one row per lane.
-// Causality is per key (key <= the token's position), applied only in the
-// blocks at or past the tile's first own block.
+// two blocks ahead of the block being multiplied), dequantised into an f16
+// tile in LDS (double-buffered; rows padded to 272 B and the second half of
+// each row rotated by 4 chunks, so neither the stores nor the operand reads
+// meet bank conflicts), and contracted on 16x16x32 f16 MFMAs (exact
+// products, fp32 sums) as S^T = K Q^T: keys are the MFMA rows, so a lane
+// holds 16 keys of one query row per 64-key half.  The epilogue takes the
+// max over the block's keys in-lane, then across the four lane quarters
+// (3 exchanges, leaving one query row per lane).  Causality is per key
+// (key <= the token's position), applied only in the blocks at or past the
+// tile's first own block.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -67,9 +68,13 @@ __device__ __forceinline__ void pf_load(PfRaw<KT>& r, const uint8_t* __restrict_
   }
 }
 
-// Dequantise 64 dims of one key into the f16 tile row.
+// LDS offset (in f16) of the 16-byte chunk c (dims 8c .. 8c+7) of a tile row:
+// chunks of the second half are rotated by 4.
+__device__ __forceinline__ int pf_chunk(int c) { return 8 * ((c & 8) | ((c + ((c >> 3) << 2)) & 7)); }
+
+// Dequantise 64 dims (half `half`) of one key into its f16 tile row.
 template <int KT, bool FP8MODE>
-__device__ __forceinline__ void pf_store(const PfRaw<KT>& r, const uint32_t* lut, _Float16* dst) {
+__device__ __forceinline__ void pf_store(const PfRaw<KT>& r, const uint32_t* lut, _Float16* row, int half) {
   h8 v[8];
   if constexpr (KT == 2) {
 #pragma unroll
@@ -92,29 +97,7 @@ __device__ __forceinline__ void pf_store(const PfRaw<KT>& r, const uint32_t* lut
     }
   }
 #pragma unroll
-  for (int d = 0; d < 8; ++d) *reinterpret_cast<h8*>(dst + 8 * d) = v[d];
-}
-
-// One butterfly step: lanes whose bit HALF is set keep the upper HALF values,
-// the others the lower ones; each receives its partner's copy of what it keeps.
-template <int HALF>
-__device__ __forceinline__ void butterfly_step(float (&v)[16], int n) {
-  const bool up = (n & HALF) != 0;
-#pragma unroll
-  for (int k = 0; k < HALF; ++k) {
-    const float keep = up ? v[k + HALF] : v[k];
-    const float send = up ? v[k] : v[k + HALF];
-    v[k] = fmaxf(keep, __shfl_xor(send, HALF));
-  }
-}
-// Max of 16 values per lane over the 16 lanes of each lane quarter; lane n of
-// a quarter returns the maximum of value n.
-__device__ __forceinline__ float butterfly_max16(float (&v)[16], int n) {
-  butterfly_step<8>(v, n);
-  butterfly_step<4>(v, n);
-  butterfly_step<2>(v, n);
-  butterfly_step<1>(v, n);
-  return v[0];
+  for (int d = 0; d < 8; ++d) *reinterpret_cast<h8*>(row + pf_chunk(8 * half + d)) = v[d];
 }
 
 template <int KT, bool FP8MODE, bool TOKSC>
@@ -172,10 +155,14 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
       }
     }
   }
-  // this lane's token per row tile (rows 4Q..4Q+3 of tile rr share it) and its position
+  // the position of this lane's query row (row n of each row tile: token n/4)
   int p_of[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) p_of[rr] = L - T + t0 + 4 * (4 * wave + rr) + Q;
+  for (int rr = 0; rr < 4; ++rr) p_of[rr] = L - T + t0 + 4 * (4 * wave + rr) + (n >> 2);
+  // LDS offsets of this lane's operand chunks (dims 32ks + 8Q .. +7)
+  int kofs[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) kofs[ks] = pf_chunk(4 * ks + Q);
   __syncthreads();
 
   // blocks of the chunk with no visible key for any row: -inf
@@ -200,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   PfRaw<KT> raw, raw2;
   pf_load<KT>(raw, kdata, kscales, page_row(0), half_ld);
   if (nblocks > 1) pf_load<KT>(raw2, kdata, kscales, page_row(1), half_ld);
-  pf_store<KT, FP8MODE>(raw, lut, &tile[0][key_ld * kPfRowHalves + 64 * half_ld]);
+  pf_store<KT, FP8MODE>(raw, lut, &tile[0][key_ld * kPfRowHalves], half_ld);
   raw = raw2;
   __syncthreads();
 
@@ -209,11 +196,11 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const _Float16* B = tile[k & 1];
     if (k + 2 < nblocks) pf_load<KT>(raw2, kdata, kscales, page_row(k + 2), half_ld);
 
-    // two halves of 64 keys; lane (Q, n) of a 16x16 output tile holds rows 4Q..4Q+3 of row
-    // tile rr (token p_of[rr]) for key kh*64 + kt*16 + n
+    // two halves of 64 keys; in the 16x16 output tile (kt, rr), lane (Q, n) holds keys
+    // kh*64 + kt*16 + 4Q + r (r = 0..3) of query row n of row tile rr
     const bool bad = page_of[k] == -2;
     const bool all_visible = i < own_first;
-    float m[16];
+    f4 m;   // per row tile rr: this lane's running max over its keys
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       f4 acc[4][4];
@@ -223,58 +210,62 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        h8 Bf[4];
+        h8 Kf[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          Bf[kt] = *reinterpret_cast<const h8*>(B + (kh * 64 + kt * 16 + n) * kPfRowHalves + 32 * ks + 8 * Q);
+          Kf[kt] = *reinterpret_cast<const h8*>(B + (kh * 64 + kt * 16 + n) * kPfRowHalves + kofs[ks]);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = mfma_16x16x32(A[rr][ks], Bf[kt], acc[rr][kt]);
+          for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = mfma_16x16x32(Kf[kt], A[rr][ks], acc[rr][kt]);
 #if MSA_PF_SCHED
         // keep the next k-step's operand reads from being hoisted (register pressure)
         __builtin_amdgcn_sched_barrier(0);
 #endif
       }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
+      for (int rr = 0; rr < 4; ++rr) {
+        float v;
+        if (all_visible) {
+          float u[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v;
-          if (all_visible) {
-            v = fmaxf(fmaxf(acc[rr][0][r], acc[rr][1][r]), fmaxf(acc[rr][2][r], acc[rr][3][r]));
-          } else {
-            v = NEG_INF;
+          for (int kt = 0; kt < 4; ++kt)
+            u[kt] = fmaxf(fmaxf(acc[rr][kt][0], acc[rr][kt][1]), fmaxf(acc[rr][kt][2], acc[rr][kt][3]));
+          v = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+        } else {
+          v = NEG_INF;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-              v = fmaxf(v, (i * kBlock + kh * 64 + kt * 16 + n <= p_of[rr]) ? acc[rr][kt][r] : NEG_INF);
-          }
-          m[4 * rr + r] = kh == 0 ? v : fmaxf(m[4 * rr + r], v);
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v = fmaxf(v, (i * kBlock + kh * 64 + kt * 16 + 4 * Q + r <= p_of[rr]) ? acc[rr][kt][r] : NEG_INF);
         }
+        m[rr] = kh == 0 ? v : fmaxf(m[rr], v);
+      }
       if constexpr (TOKSC) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int t = t0 + 4 * (4 * wave + rr) + Q;
+          const int t = t0 + 4 * (4 * wave + rr) + (n >> 2);
           if (t < T) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-              for (int kt = 0; kt < 4; ++kt) {
-                const int key = i * kBlock + kh * 64 + kt * 16 + n;
-                token_scores[(((size_t)b * T + t) * kGroups + r) * tstride + key] =
+              for (int r = 0; r < 4; ++r) {
+                const int key = i * kBlock + kh * 64 + kt * 16 + 4 * Q + r;
+                token_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * tstride + key] =
                     bad ? QNAN : (key <= p_of[rr] ? acc[rr][kt][r] * sigma : NEG_INF);
               }
           }
         }
       }
     }
-    const float mx = butterfly_max16(m, n);              // value n: tile n/4, group n%4
+    const float mx = quarter_max4(m, lane);              // query row n of row tile Q
     {
-      const int t = t0 + 4 * (4 * wave + (n >> 2)) + Q;
+      const int t = t0 + 4 * (4 * wave + Q) + (n >> 2);
       if (t < T) block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i] = bad ? QNAN : mx * sigma;
     }
 
-    if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves + 64 * half_ld]);
+    if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves], half_ld);
     raw = raw2;
     __syncthreads();
   }
