@@ -7,23 +7,25 @@
 // select them all.  Otherwise the own block is joined by the 15 best older
 // blocks under the strict order (score descending, block index ascending).
 //
-// One workgroup of 256 threads per row.  Each older block becomes a 64-bit
-// key: order-preserving score bits above the complemented block index, so
-// the keys are distinct and the order above is plain integer order.  The row
-// is read once into registers; a most-significant-digit radix select over
-// 8-bit digits (LDS histogram, one wave finds the digit) narrows a key prefix
-// until exactly 15 keys lie at or above it -- usually after two or three
-// digits.  The 15 winners plus the own block are then ranked and written
-// ascending.
+// Each older block becomes a 64-bit key: order-preserving score bits above
+// the complemented block index, so the keys are distinct and the order above
+// is plain integer order.  The row is read once into registers; a
+// most-significant-digit radix select over 8-bit digits (LDS histogram, the
+// digit found by one wave) narrows a key prefix until exactly 15 keys lie at
+// or above it -- usually after two or three digits.  The 15 winners plus the
+// own block are then ranked and written ascending.  Rows of up to 2,048
+// blocks take one wave each (topk_wave_kernel; no workgroup barrier), longer
+// rows one workgroup of 256 threads (topk_radix_kernel).
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_wave.hpp"
 
 namespace msa {
 
 constexpr int kTopkThreads = 256;
 
-template <int E>   // keys per thread: rows of up to 256*E older blocks
-__global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(
+template <int E, int NT = kTopkThreads>   // keys per thread: rows of up to NT*E older blocks
+__global__ __launch_bounds__(NT) void topk_radix_kernel(
     const float* __restrict__ block_scores, int32_t* __restrict__ sel,
     const int32_t* __restrict__ seq_lens, int T, int max_blocks) {
   __shared__ uint32_t hist[256];
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = tid + e * kTopkThreads;
+    const int i = tid + e * NT;
     key[e] = i < n ? ((uint64_t)order_key(S[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
   }
   // Index 0xFFFFFFFF is never a block, so a real key is never 0: 0 marks "no key".
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(
   if (tid == 0) n_won = 0;
 #pragma unroll 1
   for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(
   for (int e = 0; e < E; ++e) {
     if (key[e] != 0ull && (key[e] & mask) >= prefix) {
       const uint32_t slot = atomicAdd(&n_won, 1u);
-      if (slot < (uint32_t)(kTopK - 1)) won[slot] = tid + e * kTopkThreads;
+      if (slot < (uint32_t)(kTopK - 1)) won[slot] = tid + e * NT;
     }
   }
   __syncthreads();
@@ -113,11 +115,43 @@ __global__ __launch_bounds__(kTopkThreads) void topk_radix_kernel(
   }
 }
 
+// Rows of up to 64*E blocks: one wave per row, the row held in registers and
+// the digit search done with wave operations only (no workgroup barrier).
+constexpr int kTopkWaveRows = 4;   // rows (waves) per workgroup
+#ifndef MSA_TOPK_MANY_ROWS
+#define MSA_TOPK_MANY_ROWS 4096
+#endif
+constexpr int kTopkManyRows = MSA_TOPK_MANY_ROWS;
+
+template <int E>
+__global__ __launch_bounds__(64 * kTopkWaveRows) void topk_wave_kernel(
+    const float* __restrict__ block_scores, int32_t* __restrict__ sel,
+    const int32_t* __restrict__ seq_lens, int T, int max_blocks, int64_t rows) {
+  __shared__ WaveTopkLds sh[kTopkWaveRows];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kTopkWaveRows + w;
+  if (row >= rows) return;   // whole wave
+  const int b = (int)(row / ((int64_t)T * kGroups));
+  const int t = (int)((row / kGroups) % T);
+  const int own = max(0, min((seq_lens[b] - T + t) / kBlock, max_blocks - 1));
+  wave_topk_row_regs<E, false>(block_scores + row * max_blocks, own, sel + row * kTopK, sh[w], lane);
+}
+
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.T * kGroups;
   const dim3 grid((unsigned)rows), block(kTopkThreads);
-  if (p.max_blocks <= 8 * kTopkThreads)
+  const dim3 wgrid((unsigned)((rows + kTopkWaveRows - 1) / kTopkWaveRows)), wblock(64 * kTopkWaveRows);
+  // Many rows: a wave per row keeps every CU busy.  Few rows (decode): a
+  // workgroup per row shortens each row's critical path.
+  const bool many = rows >= kTopkManyRows;
+  if (many && p.max_blocks <= 64 * 16)
+    hipLaunchKernelGGL(topk_wave_kernel<16>, wgrid, wblock, 0, s, block_scores, sel, p.seq_lens, p.T,
+                       p.max_blocks, rows);
+  else if (many && p.max_blocks <= 64 * 32)
+    hipLaunchKernelGGL(topk_wave_kernel<32>, wgrid, wblock, 0, s, block_scores, sel, p.seq_lens, p.T,
+                       p.max_blocks, rows);
+  else if (p.max_blocks <= 8 * kTopkThreads)
     hipLaunchKernelGGL(topk_radix_kernel<8>, grid, block, 0, s, block_scores, sel, p.seq_lens, p.T,
                        p.max_blocks);
   else

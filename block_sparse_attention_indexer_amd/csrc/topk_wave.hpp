@@ -106,8 +106,9 @@ __device__ inline void wave_topk_row(const float* S, int own, int32_t* out, Wave
 
 // The same selection with the row held in registers: each lane loads its
 // E scores once (lane + 64e), all loads in flight together, and the radix
-// passes run on registers.  For rows of up to 64*E older blocks.
-template <int E>
+// passes run on registers.  For rows of up to 64*E older blocks.  COHERENT:
+// the scores were written by other workgroups of the running kernel.
+template <int E, bool COHERENT = true>
 __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out, WaveTopkLds& sh, int lane) {
   if (own + 1 <= kTopK) {
     if (lane < kTopK) out[lane] = lane <= own ? lane : -1;
@@ -118,7 +119,7 @@ __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out,
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = lane + 64 * e;
-    k32[e] = i < n ? order_key(coherent_load(S + i)) : 0u;
+    k32[e] = i < n ? order_key(COHERENT ? coherent_load(S + i) : S[i]) : 0u;
   }
   auto key_of = [&](int e) -> uint64_t {
     return ((uint64_t)k32[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * e));
