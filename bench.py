@@ -2,11 +2,12 @@
 
 One step = msa_indexer_scores (index scan and block max-pool) -> msa_block_topk
 (top-16 selection) -> msa_sparse_attn_decode for the whole batch (one MSA
-layer); with --fused the first two run as the single call msa_indexer_topk.  Inputs are seeded synthetic data drawn
+layer); with --fused the first two run as the single call msa_indexer_topk,
+with --mono all three as the single call msa_decode_step.  Inputs are seeded synthetic data drawn
 and packed on the GPU before the timed region (resident in HBM).
 
     python bench.py [--steps K] [--warmup W] [--workload c3_128k]
-                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill] [--fused]
+                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill] [--fused | --mono]
 
 Prints one JSON line.  ``value`` is layer-steps/s over the timed steps (wall
 clock, synchronised on both sides); ``roofline`` describes the dominant kernel
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill section")
     ap.add_argument("--fused", action="store_true",
                     help="run the scan and the top-16 as the one call msa_indexer_topk")
+    ap.add_argument("--mono", action="store_true",
+                    help="run the whole step as the one call msa_decode_step")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -123,16 +126,27 @@ class Workload:
         # arrival counters of msa_indexer_topk: zero-filled once, left zero-filled by every call
         self.ws = torch.zeros(max(1, M.msa_workspace_size(self.prob, M.MSA_CALL_INDEXER_TOPK) // 4),
                               dtype=torch.int32, device=dev)
+        # work counters and flags of msa_decode_step: likewise
+        self.ws_step = torch.zeros(max(1, M.msa_workspace_size(self.prob, M.MSA_CALL_DECODE_STEP) // 4),
+                                   dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
 
-    def step(self, dequant, ev=None, scan_only=False, fused=False):
-        """One layer step on torch's current stream.  fused: msa_indexer_topk (scan +
-        selection) then attention; else the three separate calls.  `ev` events are
-        recorded before the first call and after each call (after the first only, when
-        scan_only)."""
+    def step(self, dequant, ev=None, scan_only=False, path="calls"):
+        """One layer step on torch's current stream.  path "calls": the three separate
+        calls; "fused": msa_indexer_topk (scan + selection) then attention; "mono":
+        msa_decode_step.  `ev` events are recorded before the first call and after each
+        call (after the first only, when scan_only)."""
         M, w = self.M, self.w
         if ev is not None:
             ev[0].record()
+        if path == "mono":
+            M.msa_decode_step(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], self.q, w.q_dtype,
+                              1.0, self.caches["k"][2], self.caches["v"][2], dequant, 1.0 / math.sqrt(128.0),
+                              self.bs, self.sel, self.out, None, self.ws_step)
+            if ev is not None:
+                ev[1].record()
+            return
+        fused = path == "fused"
         if fused:
             M.msa_indexer_topk(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], dequant, self.bs,
                                self.sel, self.ws)
@@ -195,12 +209,16 @@ def algorithmic_flops(wl, sel_host):
     return idx, attn
 
 
-def indexer_kernel_name(w, dequant, fused=False):
-    """The index-scan kernel libmsa launches for this workload (as rocprofv3 names it)."""
+def indexer_kernel_name(w, dequant, path="calls"):
+    """The first kernel of the step (the index scan, or the whole step for "mono") that
+    libmsa launches for this workload, as rocprofv3 names it."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
     fp8mode = kt == 2 and dequant == "fp8"
+    fused = path == "fused"
+    if path == "mono" and w.T == 1 and not fp8mode:
+        return f"msa::decode_step_kernel<{kt}>"
     if w.T == 1 and not fp8mode:
         return f"msa::indexer_decode1_kernel<{kt}, false, {str(fused).lower()}>"
     if w.T <= 4:
@@ -240,11 +258,11 @@ def prefill_section(dequant, seed, steps=5, warmup=2):
     wl = Workload("c5", seed)
     w = wl.w
     for _ in range(warmup):
-        wl.step(dequant, fused=False)
+        wl.step(dequant)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for k in range(steps):
-        wl.step(dequant, evs[k], fused=False)
+        wl.step(dequant, evs[k])
     torch.cuda.synchronize()
     t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(3)] for k in range(steps)]).mean(axis=0)
     f_idx, f_attn = algorithmic_flops(wl, wl.sel.cpu().numpy())
@@ -327,13 +345,14 @@ def main():
         torch.cuda.synchronize()
         del a, bbuf
 
+    path = "mono" if args.mono else "fused" if args.fused else "calls"
     for _ in range(args.warmup):
-        wl.step(args.dequant, fused=args.fused)
+        wl.step(args.dequant, path=path)
     torch.cuda.synchronize()
 
     K = args.steps
-    fused = args.fused
-    ncalls = 2 if fused else 3
+    fused = path == "fused"
+    ncalls = {"calls": 3, "fused": 2, "mono": 1}[path]
     # Timed region: K whole steps; HIP events on the launching stream bracket only the
     # first call (the index scan, with the selection when fused: the roofline kernel),
     # so the step itself runs undisturbed.
@@ -341,7 +360,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        wl.step(args.dequant, evs[k], scan_only=True, fused=fused)
+        wl.step(args.dequant, evs[k], scan_only=True, path=path)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
@@ -350,7 +369,7 @@ def main():
     Kb = min(K, 20)
     evb = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(Kb)]
     for k in range(Kb):
-        wl.step(args.dequant, evb[k], fused=fused)
+        wl.step(args.dequant, evb[k], path=path)
     torch.cuda.synchronize()
     per_call = np.array([[evb[k][i].elapsed_time(evb[k][i + 1]) for i in range(ncalls)] for k in range(Kb)]).mean(axis=0)
 
@@ -358,7 +377,8 @@ def main():
     b_idx, b_topk, b_attn = algorithmic_bytes(wl, sel)
     total_bytes = b_idx + b_topk + b_attn
     idx_ms = float(np.mean(k_idx))
-    b_first = b_idx + b_topk if fused else b_idx          # bytes of the first (roofline) call
+    # bytes of the first (roofline) call
+    b_first = total_bytes if path == "mono" else b_idx + b_topk if fused else b_idx
     achieved_idx = b_first / (idx_ms * 1e-3) / 1e9
     step_tbps = total_bytes / (ms_step * 1e-3) / 1e12
 
@@ -382,14 +402,17 @@ def main():
         "hbm_TBps_step": round(step_tbps, 3),
         "pct_of_peak_hbm_step": round(100 * step_tbps * 1e3 / HBM_PEAK_GBPS, 1),
         "bytes_per_step": {"indexer": b_idx, "topk": b_topk, "attention": b_attn},
-        "call_ms": ({"indexer_topk": round(idx_ms, 5), "attention": round(float(per_call[1]), 5)} if fused else
+        "call_ms": ({"decode_step": round(idx_ms, 5)} if path == "mono" else
+                    {"indexer_topk": round(idx_ms, 5), "attention": round(float(per_call[1]), 5)} if fused else
                     {"indexer": round(idx_ms, 5), "topk": round(float(per_call[1]), 5),
                      "attention": round(float(per_call[2]), 5)}),
-        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, fused) +
-                     (" (index-key scan + block max-pool + top-16)" if fused else " (index-key scan + block max-pool)"),
+        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, path) +
+                     {"mono": " (the whole step: scan, pool, top-16, attention)",
+                      "fused": " (index-key scan + block max-pool + top-16)",
+                      "calls": " (index-key scan + block max-pool)"}[path],
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, fused))},
+                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, path))},
         "cpu_baseline": None,
     }
     if not args.no_prefill and args.workload != "c5":

@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
 MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
 MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
-MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK = 0, 1, 2, 3
+MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK, MSA_CALL_DECODE_STEP = 0, 1, 2, 3, 4
 
 EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
+            "msa_decode_step",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -69,6 +70,8 @@ def _lib():
                                        ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
             "msa_sparse_attn_prefill": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
                                         ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
+            "msa_decode_step": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), vp, ctypes.c_int, f32,
+                                P(msa_cache), P(msa_cache), ctypes.c_int, f32, vp, vp, vp, vp, vp, sz, vp],
             "msa_workspace_size": [P(msa_problem), ctypes.c_int],
             "msa_pack_fp8": [vp, i64, f32, vp, vp],
             "msa_unpack_fp8": [vp, i64, f32, vp, vp],
@@ -164,6 +167,19 @@ def msa_sparse_attn_decode(*args, **kw):
 
 def msa_sparse_attn_prefill(*args, **kw):
     _attn("msa_sparse_attn_prefill", *args, **kw)
+
+
+def msa_decode_step(prob, idx_q, idx_q_dtype, idx_q_scale, idx_k, q, q_dtype, q_scale, k, v, dequant,
+                    softmax_scale, block_scores, sel, out, lse, workspace, stream=None):
+    """One decode layer step (steps 1-4) in one call; `workspace`: a zero-filled device
+    tensor of at least msa_workspace_size(prob, MSA_CALL_DECODE_STEP) bytes (left
+    zero-filled)."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib().msa_decode_step(ctypes.byref(prob), _ptr(idx_q), DTYPES[idx_q_dtype], float(idx_q_scale),
+                                  ctypes.byref(idx_k), _ptr(q), DTYPES[q_dtype], float(q_scale), ctypes.byref(k),
+                                  ctypes.byref(v), DEQUANT[dequant], float(softmax_scale), _ptr(block_scores),
+                                  _ptr(sel), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
+           "msa_decode_step")
 
 
 def msa_workspace_size(prob, which):

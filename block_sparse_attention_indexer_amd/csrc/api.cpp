@@ -153,9 +153,50 @@ msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_d
                    workspace, workspace_bytes, stream, 262144);
 }
 
+msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype idx_q_dtype,
+                           float idx_q_scale, const msa_cache* idx_k, const void* q, msa_dtype q_dtype,
+                           float q_scale, const msa_cache* k, const msa_cache* v, msa_dequant dequant,
+                           float softmax_scale, float* block_scores, int32_t* sel, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (prob->tokens > 8) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
+  if ((st = check_pair(idx_q_dtype, idx_k->dtype)) != MSA_OK) return st;
+  if ((st = check_cache(k, 4)) != MSA_OK) return st;
+  if ((st = check_cache(v, 4)) != MSA_OK) return st;
+  if (k->dtype != v->dtype) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_pair(q_dtype, k->dtype)) != MSA_OK) return st;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (idx_q == nullptr || q == nullptr || block_scores == nullptr || sel == nullptr || out == nullptr)
+    return MSA_ERR_INVALID_ARG;
+  if (!aligned(idx_q, 16) || !aligned(q, 16) || !aligned(block_scores, 4) || !aligned(sel, 4) ||
+      !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return MSA_ERR_INVALID_ARG;
+  if (!good_scale(idx_q_scale) || !good_scale(q_scale) || !good_scale(softmax_scale)) return MSA_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned(workspace, 4) ||
+      workspace_bytes < msa_workspace_size(prob, MSA_CALL_DECODE_STEP))
+    return MSA_ERR_WORKSPACE;
+  const ProblemArgs pa = to_args(prob);
+  const CacheArgs ia = to_args(idx_k), ka = to_args(k), va = to_args(v);
+  const bool fp8 = dequant == MSA_DQ_FP8;
+  if (msa::decode_step_fits(pa, ia, ka, va, fp8))
+    return hip_status(msa::launch_decode_step(pa, idx_q, idx_q_scale, ia, q, q_scale, ka, va, softmax_scale,
+                                              block_scores, sel, out, lse, static_cast<uint32_t*>(workspace),
+                                              stream));
+  hipError_t e = msa::launch_indexer(pa, idx_q, (int)idx_q_dtype, idx_q_scale, ia, fp8, block_scores, nullptr, stream);
+  if (e == hipSuccess) e = msa::launch_topk(pa, block_scores, sel, stream);
+  if (e == hipSuccess)
+    e = msa::launch_attention(pa, q, (int)q_dtype, q_scale, ka, va, fp8, sel, softmax_scale, out, lse, stream);
+  return hip_status(e);
+}
+
 size_t msa_workspace_size(const msa_problem* prob, msa_call which) {
-  if (which == MSA_CALL_INDEXER_TOPK && prob != nullptr && prob->batch > 0)
+  if (prob == nullptr || prob->batch <= 0) return 0;
+  if (which == MSA_CALL_INDEXER_TOPK)
     return (size_t)prob->batch * sizeof(uint32_t);   // one arrival counter per sequence
+  if (which == MSA_CALL_DECODE_STEP)
+    return msa::decode_step_workspace_words(prob->batch) * sizeof(uint32_t);
   return 0;
 }
 

@@ -1,0 +1,476 @@
+// Step 4 of MSA: exact attention over the selected blocks -- device code
+// shared by the attention kernel and the one-launch decode step.
+//
+// Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
+// and its Figure 1 caption: attention runs exactly, but only over the top
+// blocks; every query head of a GQA group attends over its group's block
+// set, so a query reads full K/V for at most 2,048 keys.
+//
+// One workgroup per (sequence, query token, group) with 16 waves; wave w
+// takes the w-th selected block.  All of a block's K loads and the first V
+// tiles are issued together right after the block-table lookup, so a wave
+// waits on memory about twice (K, then the rest of V) rather than once per
+// tile.  Per block (one KV head, 16 query heads):
+//   S^T = K Q^T on 16x16x32 f16 MFMAs (A = 16 keys x 32 dims of K, straight
+//         from the page: lane quarter Q loads dims [32Q, 32Q+32) of its key;
+//         B = Q^T, the 16 heads of the group);
+//   softmax over the block's <= 128 keys in fp32 (exp2 domain);
+//   O^T += V^T P^T on 16x16x32 f16 MFMAs, two 16-key tiles per product.  The
+//         lane layout of S^T is the B operand P^T of the next product, so P
+//         never leaves registers; it enters as f16 (round to nearest, at most
+//         2^-12 relative error per element; the softmax sum stays fp32).
+//         Each 16-key V tile is dequantised into a wave-private LDS slice in
+//         its natural [key][dim] f16 layout (16-byte writes, chunks
+//         XOR-swizzled per key so that neither the writes nor the reads meet
+//         bank conflicts) and read back with gfx950's transposing LDS read
+//         (ds_read_b64_tr_b16), which hands each lane 4 consecutive keys of
+//         one dim: the A operand of V^T.  Keys past the query's position are
+//         zeroed before decoding (their scale byte, or their FP8 bytes).
+// The 16 per-block partial states (max, sum, O) are merged in one pass over
+// LDS, summed in wave order, so results are deterministic.
+// FP8 and NVFP4 values are exact in f16, so Q K^T is exact up to its fp32
+// accumulation; P V carries P's f16 rounding.
+#pragma once
+#include "common.hpp"
+
+namespace msa {
+
+#ifndef MSA_ATTN_MANY_ROWS
+#define MSA_ATTN_MANY_ROWS 8192
+#endif
+constexpr int kAttnManyRows = MSA_ATTN_MANY_ROWS;   // rows from which the 4-wave form is used
+
+// One 16-key V tile in LDS: f16 [16 keys][128 dims], 256 B per key.  The
+// 16-byte chunk c of key k sits at chunk c ^ vt_swizzle(k): with it the
+// 16-byte writes (8 keys per phase) and the transposing 8-byte reads (4 keys
+// x 4 chunks per phase) each touch every bank once.
+constexpr int kVtBytes = 16 * kHeadDim * 2;
+constexpr int kVtSlotBytes = 2 * kVtBytes;   // per wave: the two tiles of one PV product
+__device__ __forceinline__ int vt_swizzle(int k) { return (2 * k + (k >> 2) + 4 * (k >> 3)) & 15; }
+__device__ __forceinline__ int vt_offset(int k, int chunk) { return k * 256 + 16 * (chunk ^ vt_swizzle(k)); }
+
+// gfx950 transposing LDS read: in each group of 16 lanes, lane i receives for
+// e = 0..3 the 16-bit element (i mod 4) of the 8-byte chunk addressed by lane
+// 4e + i/4 of its group (fixed by an in-bounds probe).  With lane l pointing
+// at key l/4, dims 4(l mod 4) .. +3 of a 16-dim tile, lane l gets dim l mod 16
+// of keys 4(l/16) .. +3.
+__device__ __forceinline__ h4 lds_read_tr16(const uint8_t* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)p);
+  return __builtin_bit_cast(h4, v);
+}
+__device__ __forceinline__ h8 reorder_like_lut_a(h8 a) {
+  return h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]};
+}
+
+// One 16-key tile of K or V as loaded from a page, before decoding.
+//   K tile, lane (quarter Q, key j): dims [32Q, 32Q+32) of key j.
+//   V tile, lane (key pair kp, 16-dim group dg): dims [16dg, 16dg+16) of keys 2kp, 2kp+1.
+template <int KT> struct KRaw;
+template <> struct KRaw<1> { uint4 c0, c1; };
+template <> struct KRaw<2> { uint4 c; uint32_t s; };
+template <int KT> struct VRaw;
+template <> struct VRaw<1> { uint4 c[2]; };
+template <> struct VRaw<2> { uint2 c[2]; uint32_t s[2]; };
+
+// Loads take the base of one (page, KV head) slice -- uniform across the wave
+// -- and a 32-bit row offset within it, so addresses are a scalar base plus a
+// per-lane offset.
+template <int KT>
+__device__ __forceinline__ KRaw<KT> load_k_tile(const uint8_t* kbase, const uint8_t* sbase, uint32_t r, int Q) {
+  KRaw<KT> t;
+  if constexpr (KT == 2) {
+    t.c = *reinterpret_cast<const uint4*>(kbase + r * kNvfp4RowBytes + 16 * Q);
+    t.s = *reinterpret_cast<const uint16_t*>(sbase + r * kNvfp4ScaleBytes + 2 * Q);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(kbase + r * kHeadDim + 32 * Q);
+    t.c0 = src[0];
+    t.c1 = src[1];
+  }
+  return t;
+}
+
+template <int KT>
+__device__ __forceinline__ VRaw<KT> load_v_tile(const uint8_t* vbase, const uint8_t* sbase, uint32_t r0, int dg) {
+  VRaw<KT> t;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t r = r0 + u;
+    if constexpr (KT == 2) {
+      t.c[u] = *reinterpret_cast<const uint2*>(vbase + r * kNvfp4RowBytes + 8 * dg);
+      t.s[u] = sbase[r * kNvfp4ScaleBytes + dg];
+    } else {
+      t.c[u] = *reinterpret_cast<const uint4*>(vbase + r * kHeadDim + 16 * dg);
+    }
+  }
+  return t;
+}
+
+// K tile -> the four 16x32 A fragments of S^T = K Q^T (k-chunk c = dims 32Q+8c .. +7).
+template <int KT, bool FP8MODE>
+__device__ __forceinline__ void decode_k_tile(const KRaw<KT>& r, const uint32_t* lut, h8 (&Ak)[4]) {
+  if constexpr (KT == 2) {
+    const uint32_t wv[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
+    if constexpr (FP8MODE) {
+      const uint32_t s0 = r.s & 0xFFu, s1 = (r.s >> 8) & 0xFFu;
+      Ak[0] = fp4x8_lut_to_h8(wv[0], lut[2 * s0], lut[2 * s0 + 1]);
+      Ak[1] = fp4x8_lut_to_h8(wv[1], lut[2 * s0], lut[2 * s0 + 1]);
+      Ak[2] = fp4x8_lut_to_h8(wv[2], lut[2 * s1], lut[2 * s1 + 1]);
+      Ak[3] = fp4x8_lut_to_h8(wv[3], lut[2 * s1], lut[2 * s1 + 1]);
+    } else {
+      const h2 sc = fp8x2_to_h2<false>(r.s);
+      const h8 s0 = h8{sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+      const h8 s1 = h8{sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+      Ak[0] = fp4x8_to_h8(wv[0]) * s0;
+      Ak[1] = fp4x8_to_h8(wv[1]) * s0;
+      Ak[2] = fp4x8_to_h8(wv[2]) * s1;
+      Ak[3] = fp4x8_to_h8(wv[3]) * s1;
+    }
+  } else {
+    Ak[0] = fp8x8_to_h8(r.c0.x, r.c0.y);
+    Ak[1] = fp8x8_to_h8(r.c0.z, r.c0.w);
+    Ak[2] = fp8x8_to_h8(r.c1.x, r.c1.y);
+    Ak[3] = fp8x8_to_h8(r.c1.z, r.c1.w);
+  }
+}
+
+// V tile -> this lane's 2 keys x 16 dims as f16, written in [key][dim]
+// layout into the wave's LDS slice (woff[u][hh]: byte offsets of key 2kp+u,
+// dims 16dg+8hh .. +7).  Keys that are not kept are zeroed before decoding:
+// an NVFP4 key through its scale bytes (E2M1 codes are always finite), an
+// FP8 key through its bytes, so unwritten rows of a partly filled page never
+// reach the product (0 * NaN would).
+template <int KT, bool FP8MODE>
+__device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, uint8_t* vt,
+                                             const int (&woff)[2][2], bool keep0, bool keep1) {
+  if constexpr (KT == 2) {
+    r.s[0] = keep0 ? r.s[0] : 0u;
+    r.s[1] = keep1 ? r.s[1] : 0u;
+  } else {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    r.c[0] = keep0 ? r.c[0] : z;
+    r.c[1] = keep1 ? r.c[1] : z;
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    h8 v[2];
+    if constexpr (KT == 2) {
+      const uint32_t sb = r.s[u];
+      if constexpr (FP8MODE) {
+        v[0] = fp4x8_lut_to_h8(r.c[u].x, lut[2 * sb], lut[2 * sb + 1]);
+        v[1] = fp4x8_lut_to_h8(r.c[u].y, lut[2 * sb], lut[2 * sb + 1]);
+      } else {
+        const _Float16 sh = e4m3_to_h(sb);
+        const h8 ss = h8{sh, sh, sh, sh, sh, sh, sh, sh};
+        v[0] = fp4x8_to_h8(r.c[u].x) * ss;
+        v[1] = fp4x8_to_h8(r.c[u].y) * ss;
+      }
+    } else {
+      v[0] = fp8x8_to_h8(r.c[u].x, r.c[u].y);
+      v[1] = fp8x8_to_h8(r.c[u].z, r.c[u].w);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) *reinterpret_cast<h8*>(vt + woff[u][hh]) = v[hh];
+  }
+}
+
+// V tiles in flight ahead of the one being multiplied.
+#ifndef MSA_ATTN_VAHEAD
+#define MSA_ATTN_VAHEAD 4
+#endif
+#ifndef MSA_ATTN_KRING
+#define MSA_ATTN_KRING 8
+#endif
+template <int KT> constexpr int kVAhead = KT == 2 ? MSA_ATTN_VAHEAD : 2;
+constexpr int kKRing = MSA_ATTN_KRING;   // K tiles of a block in flight (divides 8)
+constexpr int kMergeStride = kHeadDim + 4;   // fp32 row of one head in the merge buffer (padded)
+
+// KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  WAVES waves per workgroup;
+// wave w takes selected blocks w, w + WAVES, ... and keeps a running (max,
+// sum, O) over them (online softmax); the WAVES states merge at the end.
+// Everything the attention of one row needs.
+struct AttnArgs {
+  const uint8_t* q;
+  float c_log2;
+  const uint8_t* kdata;
+  const uint8_t* kscales;
+  int64_t kpages;
+  const uint8_t* vdata;
+  const uint8_t* vscales;
+  int64_t vpages;
+  float v_scale;
+  const int32_t* sel;
+  const int32_t* seq_lens;
+  const int32_t* table;
+  int max_blocks;
+  int T;
+  float* out;
+  float* lse;
+};
+
+// Attention of one row (b*T + t)*4 + g by a workgroup of WAVES waves (all
+// of which call it): KT 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  Wave w
+// takes selected blocks w, w + WAVES, ... and keeps a running (max, sum, O)
+// over them (online softmax); the WAVES states merge at the end.
+// COHERENT_SEL: the selection was written by another workgroup of the
+// running kernel (device-coherent loads).
+template <int KT, bool FP8MODE, int WAVES, bool COHERENT_SEL>
+__device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
+  const uint8_t* __restrict__ q = args.q;
+  const float c_log2 = args.c_log2;
+  const uint8_t* __restrict__ kdata = args.kdata;
+  const uint8_t* __restrict__ kscales = args.kscales;
+  const int64_t kpages = args.kpages;
+  const uint8_t* __restrict__ vdata = args.vdata;
+  const uint8_t* __restrict__ vscales = args.vscales;
+  const int64_t vpages = args.vpages;
+  const float v_scale = args.v_scale;
+  const int32_t* __restrict__ sel = args.sel;
+  const int32_t* __restrict__ seq_lens = args.seq_lens;
+  const int32_t* __restrict__ table = args.table;
+  const int max_blocks = args.max_blocks;
+  const int T = args.T;
+  float* __restrict__ out = args.out;
+  float* __restrict__ lse = args.lse;
+  static_assert(kTopK % WAVES == 0, "blocks split evenly over the waves");
+  constexpr int kSmemDwords = WAVES * 16 * kMergeStride > WAVES * kVtSlotBytes / 4 ? WAVES * 16 * kMergeStride
+                                                                                    : WAVES * kVtSlotBytes / 4;
+  __shared__ uint32_t lut[FP8MODE ? 512 : 2];
+  // V tile staging (WAVES x kVtSlotBytes), later reused as the merge buffer
+  // [WAVES][16 heads][kMergeStride] fp32.
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kSmemDwords];
+  __shared__ float m_sh[WAVES][16], l_sh[WAVES][16];
+  __shared__ int nan_sh;
+
+  const int g = row & 3;
+  const int bt = row >> 2;
+  const int t = bt % T, b = bt / T;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int Q = lane >> 4, j = lane & 15;
+  const float NEG_INF = -__builtin_inff();
+
+  // independent loads first: length, this wave's blocks, the query
+  const int L = seq_lens[b];
+  int blks[kTopK / WAVES];
+#pragma unroll
+  for (int u = 0; u < kTopK / WAVES; ++u) {
+    const int32_t* sp = sel + (size_t)row * kTopK + w + u * WAVES;
+    blks[u] = COHERENT_SEL ? __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sp;
+  }
+  const uint4* qsrc =
+      reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
+  const uint4 qu0 = qsrc[0], qu1 = qsrc[1];
+  if (threadIdx.x == 0) nan_sh = 0;
+  if (FP8MODE) build_fp8_lut(lut);
+  __syncthreads();
+
+  // B operand of S^T = K Q^T: lane (Q, head j), k-chunk c = dims 32Q+8c..+7.
+  h8 Bq[4];
+  {
+    const uint32_t wq[8] = {qu0.x, qu0.y, qu0.z, qu0.w, qu1.x, qu1.y, qu1.z, qu1.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
+      Bq[c] = (KT == 2 && FP8MODE) ? reorder_like_lut_a(a) : a;
+    }
+  }
+
+  const int p = L - T + t;
+  const int kp = lane & 7;     // key pair within a V tile (keys 2kp, 2kp+1)
+  const int dg = lane >> 3;    // 16-dim group of a V tile
+  uint8_t* vt = reinterpret_cast<uint8_t*>(smem) + w * kVtSlotBytes;
+  // LDS byte offsets, fixed per lane: where this lane writes its V values
+  // (keys 2kp+u, dims 16dg+8hh..) and where its transposing reads point
+  // (key lane/4, dims 16dt + 4(lane mod 4)..; the chunk index 2dt + x XORs as
+  // a bit field, so dt enters as "^ 32dt")
+  int woff[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) woff[u][hh] = vt_offset(2 * kp + u, 2 * dg + hh);
+  const int roff = vt_offset(lane >> 2, (lane & 3) >> 1) + 8 * (lane & 1);
+  float m = NEG_INF, l = 0.0f;
+  f4 O[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) O[dt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll 1
+  for (int u = 0; u < kTopK / WAVES; ++u) {
+    const int blk = __builtin_amdgcn_readfirstlane(blks[u]);   // one value per wave
+    int nkeys = 0;
+    size_t rowbase = 0;
+    if (blk >= 0) {
+      if (blk >= max_blocks) {
+        nan_sh = 1;
+      } else {
+        const int pg = __builtin_amdgcn_readfirstlane(table[(size_t)b * max_blocks + blk]);
+        if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
+          nan_sh = 1;
+        } else {
+          nkeys = min(kBlock, p + 1 - blk * kBlock);
+          rowbase = ((size_t)pg * kGroups + g) * kBlock;   // (page, KV head g)
+        }
+      }
+    }
+    if (nkeys <= 0) continue;   // uniform per wave
+
+    // Every K load and the first V tiles are issued before the first product.
+    // All 128 rows of the page are read (they exist even when the block is
+    // only partly visible), which keeps control flow uniform so that each
+    // wait covers exactly the tile it needs.
+    // lane indices made opaque here so that the per-lane load offsets are
+    // recomputed per block instead of hoisted out of the loop (and spilled)
+    int jl = j, kpl = kp, dgl = dg, Ql = Q;
+    asm volatile("" : "+v"(jl), "+v"(kpl), "+v"(dgl), "+v"(Ql));
+    constexpr size_t kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
+    const uint8_t* kbase = kdata + rowbase * kRowBytes;
+    const uint8_t* vbase = vdata + rowbase * kRowBytes;
+    const uint8_t* ksb = KT == 2 ? kscales + rowbase * kNvfp4ScaleBytes : nullptr;
+    const uint8_t* vsb = KT == 2 ? vscales + rowbase * kNvfp4ScaleBytes : nullptr;
+    // K tiles in a ring of kKRing slots: tile kt + kKRing is loaded into the
+    // slot tile kt leaves once decoded
+    KRaw<KT> kraw[kKRing];
+#pragma unroll
+    for (int kt = 0; kt < kKRing; ++kt) kraw[kt] = load_k_tile<KT>(kbase, ksb, kt * 16 + jl, Ql);
+    VRaw<KT> vraw[8];
+#pragma unroll
+    for (int kt = 0; kt < kVAhead<KT>; ++kt) vraw[kt] = load_v_tile<KT>(vbase, vsb, kt * 16 + 2 * kpl, dgl);
+
+    // ---------------- S^T = K Q^T, 8 tiles of 16 keys (exp2 domain)
+    const bool full = nkeys == kBlock;   // uniform: no key of the block is past p
+    float x[8][4];
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt) {
+      h8 Ak[4];
+      decode_k_tile<KT, FP8MODE>(kraw[kt % kKRing], lut, Ak);
+      if (kt + kKRing < 8) kraw[kt % kKRing] = load_k_tile<KT>(kbase, ksb, (kt + kKRing) * 16 + jl, Ql);
+      f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
+      // lane (Q, head j) holds keys kt*16 + 4Q + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[kt][r] = acc[r] * c_log2;
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kt * 16 + 4 * Q + r >= nkeys) x[kt][r] = NEG_INF;
+      }
+    }
+    // ---------------- online softmax over this wave's blocks
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kt][r]);
+    mx = max_over_quarters(mx);
+    const float m_new = fmaxf(m, mx);
+    if (m != NEG_INF && m_new != m) {          // rescale what earlier blocks left
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+    }
+    m = m_new;
+    float s = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[kt][r] = fast_exp2(x[kt][r] - m);
+        s += x[kt][r];
+      }
+    l += sum_over_quarters(s);
+
+    // ---------------- O^T += V^T P^T, 4 pairs of 16-key tiles
+    // One 16x16x32 MFMA covers two tiles: lane (Q, j) takes keys 4Q..4Q+3 of
+    // each tile of the pair, in P^T (from S^T's layout) and in V^T (two
+    // transposing reads) alike.
+#pragma unroll
+    for (int kt2 = 0; kt2 < 8; kt2 += 2) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int kt = kt2 + t2;
+        // keeps the V window at kVAhead tiles (hoisting further costs registers)
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + kVAhead<KT> < 8)
+          vraw[kt + kVAhead<KT>] = load_v_tile<KT>(vbase, vsb, (kt + kVAhead<KT>) * 16 + 2 * kpl, dgl);
+        const int key0 = kt * 16 + 2 * kp;
+        stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt + t2 * kVtBytes, woff, full || key0 < nkeys,
+                                  full || key0 + 1 < nkeys);
+      }
+      lds_wait();
+      // P^T operand in f16 (P in (0, 1], rounded to nearest)
+      h8 ph;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ph[e] = (_Float16)x[kt2 + (e >> 2)][e & 3];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        // A operand: lane (Q, j) gets dim 16dt + j of keys 4Q .. 4Q+3 of both tiles
+        const h4 a0 = lds_read_tr16(vt + (roff ^ (32 * dt)));
+        const h4 a1 = lds_read_tr16(vt + kVtBytes + (roff ^ (32 * dt)));
+        const h8 a = h8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        O[dt] = mfma_16x16x32(a, ph, O[dt]);
+      }
+      lds_wait();
+    }
+  }
+
+  // ---------------- merge the WAVES states in a fixed order
+  if (Q == 0) {
+    m_sh[w][j] = m;
+    l_sh[w][j] = l;
+  }
+  __syncthreads();   // also: every wave is done with its V^T slice
+  {
+    float M = NEG_INF;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][j]);
+    const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
+    float* red = reinterpret_cast<float*>(smem) + ((size_t)w * 16 + j) * kMergeStride;
+    if constexpr (KT == 2 && FP8MODE) {
+      // the table decode leaves each 8-dim chunk in the order (0,2,4,6 | 1,3,5,7),
+      // so row 4Q + r of a tile is dim 8(Q/2) + (Q%2) + 2r
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[dt * 16 + 8 * (Q >> 1) + (Q & 1) + 2 * r] = O[dt][r] * f;
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f4*>(red + dt * 16 + 4 * Q) = O[dt] * f;
+    }
+  }
+  __syncthreads();
+  const bool bad = nan_sh != 0;
+  for (int e = threadIdx.x; e < 16 * 64; e += WAVES * 64) {
+    // e -> head hh, dims 2*dl, 2*dl+1
+    const int hh = e >> 6, dl = e & 63;
+    float M = NEG_INF;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][hh]);
+    float Lt = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) {
+      const float mw = m_sh[ww][hh];
+      if (mw != NEG_INF) Lt += l_sh[ww][hh] * exp2f(mw - M);
+    }
+    const float* red = reinterpret_cast<const float*>(smem) + (size_t)hh * kMergeStride + 2 * dl;
+    float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) {
+      const float2 v = *reinterpret_cast<const float2*>(red + (size_t)ww * 16 * kMergeStride);
+      acc.x += v.x;
+      acc.y += v.y;
+    }
+    const float inv = v_scale / Lt;
+    float2 o = make_float2(acc.x * inv, acc.y * inv);
+    if (bad) o = make_float2(__builtin_nanf(""), __builtin_nanf(""));
+    const size_t orow = ((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + hh;
+    *reinterpret_cast<float2*>(out + orow * kHeadDim + 2 * dl) = o;
+    if (lse != nullptr && dl == 0) {
+      const float v = (M + log2f(Lt)) * 0.69314718055994530942f;
+      lse[orow] = bad ? __builtin_nanf("") : v;
+    }
+  }
+}
+
+}  // namespace msa

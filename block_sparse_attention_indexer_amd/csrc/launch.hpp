@@ -2,6 +2,7 @@
 // surface is include/msa.h).  Each returns hipGetLastError() after enqueueing.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace msa {
@@ -47,5 +48,16 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
                             const CacheArgs& k, const CacheArgs& v, bool fp8mode,
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
                             hipStream_t s);
+
+// One decode layer step (T = 1) in one launch: block_scores, sel and out as the
+// three calls above leave them.  ws: decode_step_workspace_words(B) zeroed
+// uint32 words, left zeroed.  Only where decode_step_fits.
+bool decode_step_fits(const ProblemArgs& p, const CacheArgs& idx_k, const CacheArgs& k, const CacheArgs& v,
+                      bool fp8mode);
+size_t decode_step_workspace_words(int B);
+hipError_t launch_decode_step(const ProblemArgs& p, const void* idx_q, float idx_q_scale, const CacheArgs& idx_k,
+                              const void* q, float q_scale, const CacheArgs& k, const CacheArgs& v,
+                              float softmax_scale, float* block_scores, int32_t* sel, float* out, float* lse,
+                              uint32_t* ws, hipStream_t s);
 
 }  // namespace msa

@@ -35,10 +35,12 @@ __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Writes out[0..15] (ascending block ids, -1 padded) for one row of scores S.
+// Writes out[0..15] (ascending block ids, -1 padded) for one row of scores S;
+// the scores were written, and the selection is read, by other workgroups of
+// the running kernel (device-coherent loads and stores).
 __device__ inline void wave_topk_row(const float* S, int own, int32_t* out, WaveTopkLds& sh, int lane) {
   if (own + 1 <= kTopK) {
-    if (lane < kTopK) out[lane] = lane <= own ? lane : -1;
+    if (lane < kTopK) __hip_atomic_store(out + lane, lane <= own ? lane : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   const int n = own;               // candidates: blocks 0 .. own-1
@@ -101,17 +103,21 @@ __device__ inline void wave_topk_row(const float* S, int own, int32_t* out, Wave
   int rank = 0;
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
-  if (lane < kTopK) out[rank] = mine;
+  if (lane < kTopK) __hip_atomic_store(out + rank, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The same selection with the row held in registers: each lane loads its
 // E scores once (lane + 64e), all loads in flight together, and the radix
 // passes run on registers.  For rows of up to 64*E older blocks.  COHERENT:
-// the scores were written by other workgroups of the running kernel.
+// the scores were written, and the selection is read, by other workgroups of
+// the running kernel (device-coherent loads and stores).
 template <int E, bool COHERENT = true>
 __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out, WaveTopkLds& sh, int lane) {
   if (own + 1 <= kTopK) {
-    if (lane < kTopK) out[lane] = lane <= own ? lane : -1;
+    if (lane < kTopK) {
+      if (COHERENT) __hip_atomic_store(out + lane, lane <= own ? lane : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else out[lane] = lane <= own ? lane : -1;
+    }
     return;
   }
   const int n = own;
@@ -182,7 +188,10 @@ __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out,
   int rank = 0;
 #pragma unroll
   for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
-  if (lane < kTopK) out[rank] = mine;
+  if (lane < kTopK) {
+    if (COHERENT) __hip_atomic_store(out + rank, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else out[rank] = mine;
+  }
 }
 
 }  // namespace msa

@@ -131,3 +131,27 @@ def test_indexer_topk_validation(lib):
     assert call(ws_bytes=4) == M.MSA_ERR_WORKSPACE
     assert call(ws=8193) == M.MSA_ERR_WORKSPACE
     assert call(prob=_prob(topk=8)) == M.MSA_ERR_UNSUPPORTED
+
+
+def test_decode_step_validation(lib):
+    p = _prob()
+    ik = _cache()
+    kv = _cache(heads=4)
+    def call(prob=p, idx_k=ik, k=kv, v=kv, sel=4096, out=8192, ws=16384, ws_bytes=64, qs=1.0, sm=0.1,
+             q_dtype=M.MSA_FP8_E4M3):
+        return lib.msa_decode_step(ctypes.byref(prob), 1024, M.MSA_FP8_E4M3, 1.0, ctypes.byref(idx_k), 3072,
+                                   q_dtype, qs, ctypes.byref(k), ctypes.byref(v), M.MSA_DQ_EXACT, sm, 2048, sel,
+                                   out, None, ws, ws_bytes, None)
+    # 4 counters + an arrival counter and 4 row flags per sequence
+    assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_DECODE_STEP) == (4 + 5 * 2) * 4
+    assert call(sel=None) == M.MSA_ERR_INVALID_ARG
+    assert call(out=None) == M.MSA_ERR_INVALID_ARG
+    assert call(out=8196) == M.MSA_ERR_INVALID_ARG          # misaligned
+    assert call(ws=None) == M.MSA_ERR_WORKSPACE
+    assert call(ws_bytes=40) == M.MSA_ERR_WORKSPACE
+    assert call(qs=0.0) == M.MSA_ERR_INVALID_ARG
+    assert call(sm=float("nan")) == M.MSA_ERR_INVALID_ARG
+    assert call(prob=_prob(tokens=9)) == M.MSA_ERR_UNSUPPORTED
+    assert call(v=_cache(heads=4, dtype=M.MSA_FP8_E4M3)) == M.MSA_ERR_UNSUPPORTED   # K and V differ
+    assert call(k=_cache(heads=1)) == M.MSA_ERR_INVALID_ARG                          # K/V need 4 heads
+    assert call(q_dtype=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED
