@@ -249,6 +249,47 @@ def decode_query(qarr, dtype, scale):
     raise ValueError(dtype)
 
 
+def cache_insert(cache, x, seq_lens, block_table, T):
+    """Quantise-and-insert: the new tokens' rows written into a paged cache.
+
+    Source: section "QKV GEMM + norm + RoPE + KV insert fusion" -- K, V and the
+    index key are quantised (to NVFP4) as they are written into their caches.
+    x: fp32 [B, T, heads, 128], the rows of the T new tokens of each sequence;
+    token t of sequence b sits at position p = seq_lens[b] - T + t, which is
+    row p % 128 of page block_table[b][p // 128] (as for every other step).
+    Each row is quantised on its own with the cache's tensor scale
+    (formats.fp8_quantize / formats.nvfp4_quantize; fp32 rows are copied).
+    Returns a new cache dict; rows whose page id is outside the pool are
+    skipped, and nothing else changes.
+    """
+    from . import formats
+    out = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+    dt = cache["dtype"]
+    S = float(cache.get("tensor_scale", 1.0))
+    P = out["data"].shape[0]
+    x = np.asarray(x, dtype=np.float32)
+    for b in range(len(seq_lens)):
+        for t in range(T):
+            p = int(seq_lens[b]) - T + t
+            page = int(block_table[b][p // BLOCK])
+            if page < 0 or page >= P:
+                continue
+            r = p % BLOCK
+            for h in range(x.shape[2]):
+                row = x[b, t, h]
+                if dt == "f32":
+                    out["data"][page, h, r] = row
+                elif dt == "fp8":
+                    out["data"][page, h, r] = formats.fp8_quantize(row, S)
+                elif dt == "nvfp4":
+                    codes, sc = formats.nvfp4_quantize(row, S)
+                    out["data"][page, h, r] = codes
+                    out["scales"][page, h, r] = sc
+                else:
+                    raise ValueError(dt)
+    return out
+
+
 def sequence_view(cache, block_table_row, L, mode="exact"):
     """[heads, L, 128] decoded rows of one sequence, logical order."""
     nb = num_blocks(L)

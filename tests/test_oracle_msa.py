@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import formats as F
 from oracle import msa as M
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")))
@@ -236,3 +237,69 @@ def test_chunked_pooling_equals_unchunked():
         assert np.array_equal(np.isneginf(got), np.isneginf(full))
         fin = np.isfinite(full)
         assert np.abs(got[fin] - full[fin]).max() < 1e-12
+
+
+def _insert_pool(dtype, P, heads, rng):
+    """A page pool filled with arbitrary (valid) bytes, and its tensor scale."""
+    S = 0.25
+    if dtype == "f32":
+        return {"dtype": "f32", "data": rng.normal(size=(P, heads, 128, 128)).astype(np.float32), "tensor_scale": 1.0}
+    if dtype == "fp8":
+        data = rng.integers(0, 256, size=(P, heads, 128, 128), dtype=np.uint8)
+        data[(data & 0x7F) == 0x7F] = 0          # no NaN bytes
+        return {"dtype": "fp8", "data": data, "tensor_scale": S}
+    return {"dtype": "nvfp4", "data": rng.integers(0, 256, size=(P, heads, 128, 64), dtype=np.uint8),
+            "scales": rng.integers(0, 0x7F, size=(P, heads, 128, 8), dtype=np.uint8), "tensor_scale": S}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "fp8", "nvfp4"])
+def test_insert_then_read_back_equals_quantised_rows(dtype):
+    """Inserting a whole sequence and reading it back through the (separately pinned)
+    paged reader gives the rows quantised and decoded in one piece, in logical order."""
+    rng = np.random.default_rng(21)
+    heads, L = 4, 128 * 3 + 17
+    nb = (L + 127) // 128
+    P = nb + 3
+    table = np.array([rng.permutation(P)[:nb]], np.int32)
+    pool = _insert_pool(dtype, P, heads, rng)
+    x = (3.0 * rng.normal(size=(1, L, heads, 128))).astype(np.float32)
+    got = M.sequence_view(M.cache_insert(pool, x, [L], table, L), table[0], L)
+    rows = x[0].transpose(1, 0, 2)                      # [heads, L, 128]
+    S = pool["tensor_scale"]
+    if dtype == "f32":
+        ref = rows.astype(np.float64)
+    elif dtype == "fp8":
+        ref = F.fp8_dequantize(F.fp8_quantize(rows, S), S)
+    else:
+        c, sc = F.nvfp4_quantize(rows, S)
+        ref = F.nvfp4_dequantize(c, sc, S)
+    assert np.array_equal(got, ref)
+
+
+def test_insert_in_steps_equals_insert_at_once_and_touches_nothing_else():
+    """Growing a sequence token by token (decode) or a chunk at a time (prefill) gives
+    the same pool as one insert; pages of other sequences and free slots stay as they
+    were; a row whose page id is outside the pool is skipped."""
+    rng = np.random.default_rng(22)
+    heads, L = 1, 300
+    nb = (L + 127) // 128
+    P = 6
+    table = np.array([[4, 1, 3]], np.int32)
+    pool = _insert_pool("nvfp4", P, heads, rng)
+    x = rng.normal(size=(1, L, heads, 128)).astype(np.float32)
+    once = M.cache_insert(pool, x, [L], table, L)
+    step = pool
+    for n in [1, 2, 130, 290, 299, 300]:
+        prev = step
+        T = n - (0 if prev is pool else last)
+        step = M.cache_insert(prev, x[:, n - T:n], [n], table, T)
+        last = n
+    for k in ("data", "scales"):
+        assert np.array_equal(step[k], once[k])
+        untouched = np.ones(P, bool)
+        untouched[table[0]] = False
+        assert np.array_equal(once[k][untouched], pool[k][untouched])
+        # slots past the sequence in its last page
+        assert np.array_equal(once[k][3, :, L - 256:], pool[k][3, :, L - 256:])
+    bad = M.cache_insert(pool, x[:, :5], [5], np.array([[P + 2, 0, 0]], np.int32), 5)
+    assert all(np.array_equal(bad[k], pool[k]) for k in ("data", "scales"))

@@ -49,6 +49,33 @@ def _sparse_attention_wrong_gqa(q, K, V, sel, L, T, scale):
 
 
 _orig_attention = M.sparse_attention
+_orig_insert = M.cache_insert
+
+
+def _insert_one_token_late(cache, x, seq_lens, block_table, T):
+    # the new tokens placed one position too far
+    return _orig_insert(cache, x, [int(L) + 1 for L in seq_lens], block_table, T)
+
+
+def _insert_one_scale_per_row(cache, x, seq_lens, block_table, T):
+    # NVFP4 with one scale byte for the whole 128-dim row instead of one per 16 dims
+    if cache["dtype"] != "nvfp4":
+        return _orig_insert(cache, x, seq_lens, block_table, T)
+    out = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in cache.items()}
+    S = np.float32(cache["tensor_scale"])
+    x = np.asarray(x, np.float32)
+    for b in range(len(seq_lens)):
+        for t in range(T):
+            p = int(seq_lens[b]) - T + t
+            page, r = int(block_table[b][p // 128]), p % 128
+            for h in range(x.shape[2]):
+                row = x[b, t, h]
+                sb = F.e4m3_encode(np.float64(np.abs(row).max() / (np.float32(6.0) * S)))
+                denom = np.float32(F.e4m3_value(sb)) * S
+                codes = F.e2m1_encode((row / denom).astype(np.float64)) if denom > 0 else np.zeros(128, np.int64)
+                out["data"][page, h, r] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+                out["scales"][page, h, r] = sb
+    return out
 
 
 @pytest.mark.parametrize("target,mutant,pin", [
@@ -57,6 +84,8 @@ _orig_attention = M.sparse_attention
     (M, ("attended_keys", _attended_keys_ignoring_causality), lambda: TM.test_short_context_equals_dense_causal_attention(2048, 4)),
     (M, ("sparse_attention", _sparse_attention_wrong_gqa), TM.test_sparse_attention_equals_masked_sdpa_from_selection),
     (F, ("e4m3_encode", _e4m3_ties_away), TF.test_e4m3_encode_matches_torch_rne_in_range),
+    (M, ("cache_insert", _insert_one_token_late), lambda: TM.test_insert_then_read_back_equals_quantised_rows("fp8")),
+    (M, ("cache_insert", _insert_one_scale_per_row), lambda: TM.test_insert_then_read_back_equals_quantised_rows("nvfp4")),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, mutant, pin):
     name, fn = mutant
