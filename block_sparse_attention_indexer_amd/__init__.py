@@ -21,7 +21,7 @@ MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
 MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK, MSA_CALL_DECODE_STEP = 0, 1, 2, 3, 4
 
 EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
-            "msa_decode_step",
+            "msa_decode_step", "msa_cache_insert",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -72,6 +72,7 @@ def _lib():
                                         ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
             "msa_decode_step": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), vp, ctypes.c_int, f32,
                                 P(msa_cache), P(msa_cache), ctypes.c_int, f32, vp, vp, vp, vp, vp, sz, vp],
+            "msa_cache_insert": [P(msa_problem), vp, P(msa_cache), vp],
             "msa_workspace_size": [P(msa_problem), ctypes.c_int],
             "msa_pack_fp8": [vp, i64, f32, vp, vp],
             "msa_unpack_fp8": [vp, i64, f32, vp, vp],
@@ -180,6 +181,13 @@ def msa_decode_step(prob, idx_q, idx_q_dtype, idx_q_scale, idx_k, q, q_dtype, q_
                                   ctypes.byref(v), DEQUANT[dequant], float(softmax_scale), _ptr(block_scores),
                                   _ptr(sel), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
            "msa_decode_step")
+
+
+def msa_cache_insert(prob, x, cache_, stream=None):
+    """Quantise the fp32 rows x [B, T, heads, 128] of the T new tokens and write them
+    into their slots of the paged cache `cache_` (its data and scales are written)."""
+    _check(_lib().msa_cache_insert(ctypes.byref(prob), _ptr(x), ctypes.byref(cache_), _stream(stream)),
+           "msa_cache_insert")
 
 
 def msa_workspace_size(prob, which):

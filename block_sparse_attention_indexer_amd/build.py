@@ -17,8 +17,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are kept out of the device code on purpose.
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["pack.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "attn.hip", "decode_step.hip",
-           "api.cpp"]
+SOURCES = ["pack.hip", "insert.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "attn.hip",
+           "decode_step.hip", "api.cpp"]
 
 
 def _compile(src):

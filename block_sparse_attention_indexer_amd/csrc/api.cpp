@@ -191,6 +191,16 @@ msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype
   return hip_status(e);
 }
 
+msa_status msa_cache_insert(const msa_problem* prob, const float* x, const msa_cache* cache, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (cache == nullptr) return MSA_ERR_INVALID_ARG;
+  if (cache->heads != 1 && cache->heads != 4) return MSA_ERR_INVALID_ARG;
+  if ((st = check_cache(cache, cache->heads)) != MSA_OK) return st;
+  if (x == nullptr || !aligned(x, 16)) return MSA_ERR_INVALID_ARG;
+  return hip_status(msa::launch_insert(to_args(prob), x, to_args(cache), cache->heads, stream));
+}
+
 size_t msa_workspace_size(const msa_problem* prob, msa_call which) {
   if (prob == nullptr || prob->batch <= 0) return 0;
   if (which == MSA_CALL_INDEXER_TOPK)

@@ -133,6 +133,21 @@ __host__ __device__ inline uint32_t e2m1_encode(float x) {
                         (uint32_t)(a > 5.0f);
   return ((bits >> 31) << 3) | code;
 }
+// The two roundings above with gfx950's conversion instructions, two values
+// at a time.  For every input that is not NaN they give the same bits as
+// e4m3_encode / e2m1_encode (compared over all 2^32 float patterns); NaN
+// inputs have no defined code in either.  The E4M3 instruction turns
+// magnitudes beyond 464 into the NaN code, so its inputs are first clamped
+// to +-448, which is where the saturating encoder sends them; the E2M1 one
+// saturates at 6 by itself (its scale operand is 1, i.e. none).
+__device__ __forceinline__ uint32_t e4m3_encode2(float a, float b) {   // byte 0: a, byte 1: b
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                                   __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f), 0, false) &
+         0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e2m1_encode2(float a, float b) {   // low nibble: a, high nibble: b
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
 __host__ __device__ inline float e2m1_magnitude(uint32_t m) {
   const float t[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
   return t[m & 7u];

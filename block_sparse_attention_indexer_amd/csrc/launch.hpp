@@ -49,6 +49,10 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
                             hipStream_t s);
 
+// Quantise the fp32 rows x [B, T, heads, 128] of the T new tokens and write them
+// into their slots of cache c (heads = c's heads per page).
+hipError_t launch_insert(const ProblemArgs& p, const float* x, const CacheArgs& c, int heads, hipStream_t s);
+
 // One decode layer step (T = 1) in one launch: block_scores, sel and out as the
 // three calls above leave them.  ws: decode_step_workspace_words(B) zeroed
 // uint32 words, left zeroed.  Only where decode_step_fits.

@@ -16,7 +16,7 @@ __global__ void pack_fp8_kernel(const float* __restrict__ x, int64_t n, float sc
                                 uint8_t* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    out[i] = (uint8_t)e4m3_encode(x[i] / scale);
+    out[i] = (uint8_t)e4m3_encode2(x[i] / scale, 0.0f);
   }
 }
 
@@ -45,15 +45,13 @@ __global__ void pack_nvfp4_kernel(const float* __restrict__ x, int64_t groups, f
     for (int k = 0; k < 16; ++k) amax = fmaxf(amax, __builtin_fabsf(v[k]));
     const float six_s = 6.0f * tensor_scale;
     const float t = amax / six_s;
-    const uint32_t sb = e4m3_encode(t);
+    const uint32_t sb = e4m3_encode2(t, 0.0f) & 0xFFu;
     const float denom = e4m3_value(sb) * tensor_scale;
     uint32_t w[2] = {0u, 0u};
     if (denom > 0.0f) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t c = e2m1_encode(v[k] / denom);
-        w[k >> 3] |= c << (4 * (k & 7));
-      }
+      for (int j = 0; j < 8; ++j)   // elements 2j, 2j+1: byte j of the group's 8
+        w[j >> 2] |= e2m1_encode2(v[2 * j] / denom, v[2 * j + 1] / denom) << (8 * (j & 3));
     }
     reinterpret_cast<uint2*>(codes)[gi] = make_uint2(w[0], w[1]);
     scales[gi] = (uint8_t)sb;

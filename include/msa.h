@@ -197,6 +197,24 @@ msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype
                            float softmax_scale, float* block_scores, int32_t* sel, float* out,
                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Quantise-and-insert (section "QKV GEMM + norm + RoPE + KV insert fusion": K,
+ * V and the index key are quantised to NVFP4 as they are written into their
+ * caches; this is that insert step without the GEMM, norm and RoPE).
+ *   x      device fp32 [batch, tokens, cache->heads, 128], contiguous and
+ *          16-byte aligned (MSA_ERR_INVALID_ARG otherwise): the rows
+ *          of the `tokens` new tokens of each sequence; token t of sequence b
+ *          sits at position seq_lens[b] - tokens + t (seq_lens include them).
+ *   cache  FP8, NVFP4 or fp32, heads 1 (index keys) or 4 (K or V).  Its data
+ *          (and NVFP4 scales) are WRITTEN: the row of position p goes to row
+ *          p % 128 of page block_table[b][p / 128], every head of it; nothing
+ *          else is touched.  Quantisation as msa_pack_fp8 / msa_pack_nvfp4 with
+ *          the cache's tensor_scale, so inserted rows are bit-identical to the
+ *          same rows packed in one piece; fp32 rows are copied.
+ * A row whose page id lies outside [0, num_pages) is not written (page ids
+ * are device data: not checked on the host).  Rows of different calls may
+ * share pages; rows of one call must not share a slot. */
+msa_status msa_cache_insert(const msa_problem* prob, const float* x, const msa_cache* cache, hipStream_t stream);
+
 typedef enum {
   MSA_CALL_INDEXER = 0,
   MSA_CALL_TOPK = 1,

@@ -155,3 +155,16 @@ def test_decode_step_validation(lib):
     assert call(v=_cache(heads=4, dtype=M.MSA_FP8_E4M3)) == M.MSA_ERR_UNSUPPORTED   # K and V differ
     assert call(k=_cache(heads=1)) == M.MSA_ERR_INVALID_ARG                          # K/V need 4 heads
     assert call(q_dtype=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED
+
+
+def test_cache_insert_validation(lib):
+    p = _prob()
+    def call(prob=p, x=1024, c=None):
+        c = _cache(heads=4) if c is None else c
+        return lib.msa_cache_insert(ctypes.byref(prob), x, ctypes.byref(c), None)
+    assert call(x=None) == M.MSA_ERR_INVALID_ARG
+    assert call(x=1032) == M.MSA_ERR_INVALID_ARG                       # rows need 16-byte alignment
+    assert call(c=_cache(heads=2)) == M.MSA_ERR_INVALID_ARG            # 1 (index keys) or 4 (K, V)
+    assert call(c=_cache(heads=4, scales=None)) == M.MSA_ERR_INVALID_ARG
+    assert call(c=_cache(heads=4, tensor_scale=0.0)) == M.MSA_ERR_INVALID_ARG
+    assert call(prob=_prob(block_size=64)) == M.MSA_ERR_UNSUPPORTED

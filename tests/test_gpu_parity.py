@@ -68,6 +68,55 @@ def test_pack_nvfp4_bit_exact(M, S):
     assert np.array_equal(codes.cpu().numpy(), oc)
 
 
+def _tie_sweep(lo_exp, hi_exp):
+    """Every float32 of both signs with biased exponent in [lo_exp, hi_exp], any of the
+    top 11 mantissa bits and the low 12 bits in {0, 1, 0x7FF, 0x800, 0x801, 0xFFF}: all
+    the E4M3 and E2M1 rounding ties of that range and their float neighbours."""
+    e = np.arange(lo_exp, hi_exp + 1, dtype=np.uint32)
+    top = np.arange(2048, dtype=np.uint32) << 12
+    low = np.array([0, 1, 0x7FF, 0x800, 0x801, 0xFFF], dtype=np.uint32)
+    bits = ((e[:, None, None] << 23) | top[None, :, None] | low[None, None, :]).ravel()
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000), np.array([0, 0x80000000], dtype=np.uint32)])
+    return bits.view(np.float32)
+
+
+def test_pack_fp8_rounding_ties(M):
+    """Magnitudes 2^-27 .. 2^14 (past the saturation point) at and beside every tie."""
+    x = _tie_sweep(100, 141)
+    d = torch.from_numpy(x).cuda()
+    out = torch.empty(len(x), dtype=torch.uint8, device="cuda")
+    M.msa_pack_fp8(d, 1.0, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), OF.fp8_quantize(x, 1.0))
+
+
+def test_pack_nvfp4_rounding_ties(M):
+    """Groups whose largest magnitude is 6 * 2^k (scale byte exactly 2^k) around values
+    at and beside every E2M1 tie, and groups whose scale rounds down (codes saturate)."""
+    v = _tie_sweep(100, 129)
+    v = v[np.abs(v) < 6.0]
+    groups = []
+    for k in (-3, 0, 4):
+        f = np.float32(2.0 ** k)
+        body = v * f
+        body = np.concatenate([body, np.zeros((-len(body)) % 15, dtype=np.float32)]).reshape(-1, 15)
+        groups.append(np.concatenate([np.full((len(body), 1), 6 * f, dtype=np.float32), body], axis=1))
+        sat = np.array([6.375, 6.2, -6.375, 6.0, 5.9, -6.1, 0.25, -0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 0.0, -0.0],
+                       dtype=np.float32) * f                 # amax/6 = 1.0625: the scale rounds down to 1
+        groups.append(sat[None, :])
+    g = np.concatenate(groups)
+    g = np.concatenate([g, np.zeros(((-len(g)) % 8, 16), dtype=np.float32)])
+    x = np.ascontiguousarray(g.reshape(-1, 128))
+    d = torch.from_numpy(x).cuda()
+    codes = torch.empty((len(x), 64), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((len(x), 8), dtype=torch.uint8, device="cuda")
+    M.msa_pack_nvfp4(d, 1.0, codes, sc)
+    torch.cuda.synchronize()
+    oc, os_ = OF.nvfp4_quantize(x, 1.0)
+    assert np.array_equal(sc.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)
+
+
 @pytest.mark.parametrize("mode", ["exact", "fp8"])
 def test_unpack_nvfp4_every_scale_and_code(M, mode):
     scales = np.array([s for s in range(256) if not (s & 0x80) and s != 0x7F], dtype=np.uint8)
@@ -315,3 +364,44 @@ def test_decode_step_full_size(M, wname):
         assert np.array_equal(bs, ref["block_scores"]) and np.array_equal(sel, ref["sel"]), rep
         _same_attention(out, lse, ref["out"], ref["lse"])
     assert int(ws.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("dtype,heads,T,lens", [
+    ("nvfp4", 4, 1, [300, 129, 5000, 128]),          # decode: one token per sequence
+    ("nvfp4", 1, 130, [300, 700]),                  # a chunk spanning block boundaries
+    ("fp8", 4, 5, [127, 128, 129]),
+    ("fp8", 1, 1, [1, 64]),
+    ("f32", 4, 3, [260]),
+    ("nvfp4", 4, 4096, [4096 + 65536, 4096 + 1000]),  # c5-sized prefill chunk, K or V
+])
+def test_cache_insert_bit_exact(M, dtype, heads, T, lens):
+    """msa_cache_insert writes exactly the oracle's quantised rows into exactly their
+    slots; every other byte of the pool (arbitrary contents) is left alone, and a
+    row whose page id is outside the pool is not written."""
+    _say("cache_insert", dtype, heads, T, lens)
+    from tests.test_oracle_msa import _insert_pool
+    rng = np.random.default_rng(31 + T)
+    B = len(lens)
+    nbs = [(L + 127) // 128 for L in lens]
+    maxb = max(nbs)
+    P = sum(nbs) + 3
+    perm = rng.permutation(P)
+    table = np.full((B, maxb), -1, np.int32)
+    off = 0
+    for b, n in enumerate(nbs):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    if B > 1:
+        table[1, nbs[1] - 1] = P + 7        # the last block of sequence 1 has no page in this pool
+    pool = _insert_pool(dtype, P, heads, rng)
+    x = (3.0 * rng.normal(size=(B, T, heads, 128))).astype(np.float32)
+    want = OM.cache_insert(pool, x, lens, table, T)
+    d_data = torch.from_numpy(pool["data"]).cuda()
+    d_sc = torch.from_numpy(pool["scales"]).cuda() if dtype == "nvfp4" else None
+    c = M.cache(dtype, d_data, d_sc, pool["tensor_scale"], heads)
+    prob = M.problem(torch.tensor(lens, dtype=torch.int32, device="cuda"), torch.from_numpy(table).cuda(), T)
+    M.msa_cache_insert(prob, torch.from_numpy(x).cuda(), c)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_data.cpu().numpy(), want["data"])
+    if dtype == "nvfp4":
+        assert np.array_equal(d_sc.cpu().numpy(), want["scales"])
