@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--mono", action="store_true",
                     help="run the whole step as the one call msa_decode_step")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
+    ap.add_argument("--only", choices=["insert"], default=None,
+                    help="run one side section alone and print its JSON (for profiling), not the step line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -382,6 +384,9 @@ def main():
     import numpy as np
     import torch
     torch.cuda.set_device(0)
+    if args.only == "insert":
+        print(json.dumps({"insert": insert_section(args.seed, steps=args.steps)}), flush=True)
+        return
     sample = [] if args.no_cpu_baseline else list(range(0, 64, 64 // max(1, args.cpu_sample)))[: args.cpu_sample]
     wl = Workload(args.workload, args.seed, keep_sequences=sample)
     w = wl.w

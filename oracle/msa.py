@@ -152,6 +152,81 @@ def select_all(block_scores, L, T, k=TOPK):
     return out
 
 
+# ---------------------------------------------------------------- DCP selection
+#
+# Source: sections "NVFP4 indexer DCP" (NVIDIA part and AMD part): with
+# decode context parallelism each of P GPUs scores all four groups over its
+# share of the pages; every GPU sends its local top-16 per group to the GPU
+# that owns the group, which merges them into the final top-16, and the
+# selection stays exact (on AMD the block scores themselves are written to
+# the owner and are bit-identical to a single-GPU run).
+# Readings where the pages are silent:
+#   * block i of every sequence belongs to shard i % P;
+#   * a shard's candidates for a row are its blocks older than the row's own
+#     block (the own block is forced by the owner, not sent);
+#   * a shard sends its 16 best candidates by (score descending, block index
+#     ascending), best first, fewer when it has fewer (padded with block -1,
+#     score NaN);
+#   * the owner applies the single-GPU rule to the union of the candidates:
+#     all blocks when own+1 <= 16, else the own block plus the 15 best
+#     candidates, reported ascending.
+
+
+def shard_blocks(nblocks, shard, num_shards):
+    """Logical block ids < nblocks that belong to `shard` of `num_shards`."""
+    assert 0 <= shard < num_shards
+    return np.arange(shard, nblocks, num_shards, dtype=np.int64)
+
+
+def shard_candidates(block_scores_row, own, shard, num_shards, k=TOPK):
+    """The shard's k best blocks older than `own` for one (token, group) row.
+
+    Returns (scores [k] float64, blocks [k] int32), best first, padded with
+    (NaN, -1)."""
+    S = np.asarray(block_scores_row, dtype=np.float64)
+    blocks = shard_blocks(own, shard, num_shards)
+    cs = S[blocks]
+    assert np.all(np.isfinite(cs)), "visible blocks must have finite scores"
+    order = np.lexsort((blocks, -cs))[:k]     # score descending, then block ascending
+    scores = np.full(k, np.nan)
+    ids = np.full(k, -1, dtype=np.int32)
+    scores[: len(order)] = cs[order]
+    ids[: len(order)] = blocks[order]
+    return scores, ids
+
+
+def merge_candidates(cand_scores, cand_blocks, own, k=TOPK):
+    """The owner's merge for one row: cand_* [P, k] from shard_candidates.
+
+    Returns k block ids, ascending, padded with -1 -- the same layout as
+    select_blocks."""
+    if own + 1 <= k:
+        chosen = list(range(own + 1))
+    else:
+        ids = np.asarray(cand_blocks).ravel()
+        sc = np.asarray(cand_scores, dtype=np.float64).ravel()
+        keep = ids >= 0
+        ids, sc = ids[keep].astype(np.int64), sc[keep]
+        order = np.lexsort((ids, -sc))[: k - 1]
+        chosen = sorted([int(i) for i in ids[order]] + [int(own)])
+    return np.array(chosen + [-1] * (k - len(chosen)), dtype=np.int32)
+
+
+def dcp_select_all(block_scores, L, T, num_shards, k=TOPK):
+    """sel[t, g, :] of one sequence by the sharded route: every shard's
+    candidates, then the merge."""
+    Tn, G, _ = block_scores.shape
+    own = own_blocks(L, T)
+    out = np.empty((Tn, G, k), dtype=np.int32)
+    for t in range(Tn):
+        for g in range(G):
+            parts = [shard_candidates(block_scores[t, g], int(own[t]), s, num_shards, k)
+                     for s in range(num_shards)]
+            out[t, g] = merge_candidates(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
+                                         int(own[t]), k)
+    return out
+
+
 def attended_keys(sel_row, p):
     """Key positions a query at position p attends through one selection row."""
     keys = []

@@ -303,3 +303,75 @@ def test_insert_in_steps_equals_insert_at_once_and_touches_nothing_else():
         assert np.array_equal(once[k][3, :, L - 256:], pool[k][3, :, L - 256:])
     bad = M.cache_insert(pool, x[:, :5], [5], np.array([[P + 2, 0, 0]], np.int32), 5)
     assert all(np.array_equal(bad[k], pool[k]) for k in ("data", "scales"))
+
+
+# ---------------------------------------------------------------- DCP selection
+
+
+def test_shards_partition_the_blocks():
+    for n in (0, 1, 7, 16, 1000):
+        for P in (1, 2, 3, 4, 8):
+            parts = [M.shard_blocks(n, s, P) for s in range(P)]
+            assert np.array_equal(np.sort(np.concatenate(parts)), np.arange(n))
+            sizes = [len(p) for p in parts]
+            assert max(sizes) - min(sizes) <= 1
+
+
+def test_shard_candidates_and_merge_worked_example():
+    # Blocks 0..9, own block 9, two shards (even / odd blocks), 4 kept (k = 4).
+    # Shard 0 holds blocks 0,2,4,6,8 with scores 5,5,2,0,5: best first by
+    # (score desc, block asc) that is 0,2,8,4.  Shard 1 holds 1,3,5,7 with
+    # scores 1,3,3,4: 7,3,5,1.  The owner keeps block 9 and the 3 best of the
+    # union -- blocks 0, 2 and 8 (score 5) -- and reports 0,2,8,9.
+    S = np.array([5, 1, 5, 3, 2, 3, 0, 4, 5, 9], dtype=float)
+    s0, b0 = M.shard_candidates(S, 9, 0, 2, k=4)
+    s1, b1 = M.shard_candidates(S, 9, 1, 2, k=4)
+    assert b0.tolist() == [0, 2, 8, 4] and s0.tolist() == [5, 5, 5, 2]
+    assert b1.tolist() == [7, 3, 5, 1] and s1.tolist() == [4, 3, 3, 1]
+    sel = M.merge_candidates(np.stack([s0, s1]), np.stack([b0, b1]), 9, k=4)
+    assert sel.tolist() == [0, 2, 8, 9]
+    assert np.array_equal(sel, M.select_blocks(S, 9, k=4))
+
+
+def test_shard_candidates_brute_force():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        P = int(rng.integers(1, 5))
+        shard = int(rng.integers(0, P))
+        own = int(rng.integers(0, 60))
+        S = rng.integers(0, 4, own + 1).astype(float)
+        ranked = sorted((-S[i], i) for i in range(shard, own, P))[:16]
+        sc, ids = M.shard_candidates(S, own, shard, P)
+        n = len(ranked)
+        assert ids[:n].tolist() == [i for _, i in ranked] and np.all(ids[n:] == -1)
+        assert sc[:n].tolist() == [-v for v, _ in ranked] and np.all(np.isnan(sc[n:]))
+
+
+def _dcp_route(S, own, P):
+    parts = [M.shard_candidates(S, own, s, P) for s in range(P)]
+    return M.merge_candidates(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]), own)
+
+
+def test_dcp_merge_equals_single_gpu_selection():
+    """The pages' claim: merging the shards' local top-16s selects exactly what
+    one GPU selects from all the scores -- here against select_blocks."""
+    rng = np.random.default_rng(11)
+    for P in (1, 2, 3, 4, 5, 8):
+        for trial in range(120):
+            own = int(rng.integers(0, 400))
+            S = rng.integers(0, 6, own + 1).astype(float) if trial % 2 else rng.normal(size=own + 1)
+            assert np.array_equal(_dcp_route(S, own, P), M.select_blocks(S, own)), (P, trial)
+        # every one of the 15 best older blocks on one shard, the own block scoring highest
+        own = 300
+        S = rng.normal(size=own + 1)
+        S[0:own:P] += 100.0
+        S[own] = 1e3
+        assert np.array_equal(_dcp_route(S, own, P), M.select_blocks(S, own)), P
+
+
+def test_dcp_select_all_equals_select_all():
+    rng = np.random.default_rng(12)
+    L, T = 40 * 128 + 17, 4
+    S = rng.integers(0, 8, (T, 4, M.num_blocks(L))).astype(float)
+    for P in (2, 4):
+        assert np.array_equal(M.dcp_select_all(S, L, T, P), M.select_all(S, L, T))

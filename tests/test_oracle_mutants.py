@@ -78,6 +78,36 @@ def _insert_one_scale_per_row(cache, x, seq_lens, block_table, T):
     return out
 
 
+_orig_shard_candidates = M.shard_candidates
+_orig_merge = M.merge_candidates
+
+
+def _shard_sends_top8(S, own, shard, P, k=16):
+    sc, ids = _orig_shard_candidates(S, own, shard, P, k)
+    sc[8:], ids[8:] = np.nan, -1
+    return sc, ids
+
+
+def _shard_includes_own_block(S, own, shard, P, k=16):
+    S = np.asarray(S, float)
+    blocks = np.arange(shard, own + 1, P)
+    order = np.lexsort((blocks, -S[blocks]))[:k]
+    sc, ids = np.full(k, np.nan), np.full(k, -1, np.int32)
+    sc[: len(order)], ids[: len(order)] = S[blocks][order], blocks[order]
+    return sc, ids
+
+
+def _merge_ties_to_higher_block(cs, cb, own, k=16):
+    if own + 1 <= k:
+        return _orig_merge(cs, cb, own, k)
+    ids, sc = np.asarray(cb).ravel(), np.asarray(cs, float).ravel()
+    keep = ids >= 0
+    ids, sc = ids[keep], sc[keep]
+    order = np.lexsort((-ids, -sc))[: k - 1]
+    ch = sorted([int(i) for i in ids[order]] + [own])
+    return np.array(ch + [-1] * (k - len(ch)), np.int32)
+
+
 @pytest.mark.parametrize("target,mutant,pin", [
     (M, ("select_blocks", _select_ties_to_higher_index), TM.test_selection_boundary_tie_goes_to_lower_block),
     (M, ("select_blocks", _select_without_forcing_own), TM.test_selection_invariants_random_rows),
@@ -86,6 +116,9 @@ def _insert_one_scale_per_row(cache, x, seq_lens, block_table, T):
     (F, ("e4m3_encode", _e4m3_ties_away), TF.test_e4m3_encode_matches_torch_rne_in_range),
     (M, ("cache_insert", _insert_one_token_late), lambda: TM.test_insert_then_read_back_equals_quantised_rows("fp8")),
     (M, ("cache_insert", _insert_one_scale_per_row), lambda: TM.test_insert_then_read_back_equals_quantised_rows("nvfp4")),
+    (M, ("shard_candidates", _shard_sends_top8), TM.test_dcp_merge_equals_single_gpu_selection),
+    (M, ("shard_candidates", _shard_includes_own_block), TM.test_dcp_merge_equals_single_gpu_selection),
+    (M, ("merge_candidates", _merge_ties_to_higher_block), TM.test_dcp_merge_equals_single_gpu_selection),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, mutant, pin):
     name, fn = mutant
