@@ -6,7 +6,8 @@ memory and the current stream; nothing here computes on the CPU, and if the
 library is missing every call raises instead of falling back.
 
 The functions keep the C names: msa_indexer_scores, msa_indexer_topk, msa_block_topk,
-msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_pack_fp8,
+msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_decode_step, msa_cache_insert,
+msa_indexer_scores_shard, msa_shard_topk, msa_topk_merge, msa_pack_fp8,
 msa_unpack_fp8, msa_pack_nvfp4, msa_unpack_nvfp4, msa_workspace_size.
 """
 import ctypes
@@ -18,10 +19,12 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
 MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
 MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
+MSA_MAX_SHARDS = 8
 MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK, MSA_CALL_DECODE_STEP = 0, 1, 2, 3, 4
 
 EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
-            "msa_decode_step", "msa_cache_insert",
+            "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
+            "msa_topk_merge",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -73,6 +76,10 @@ def _lib():
             "msa_decode_step": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), vp, ctypes.c_int, f32,
                                 P(msa_cache), P(msa_cache), ctypes.c_int, f32, vp, vp, vp, vp, vp, sz, vp],
             "msa_cache_insert": [P(msa_problem), vp, P(msa_cache), vp],
+            "msa_indexer_scores_shard": [P(msa_problem), i32, i32, vp, ctypes.c_int, f32, P(msa_cache),
+                                         ctypes.c_int, vp, vp],
+            "msa_shard_topk": [P(msa_problem), i32, i32, vp, vp, vp, vp],
+            "msa_topk_merge": [P(msa_problem), i32, vp, vp, vp, vp],
             "msa_workspace_size": [P(msa_problem), ctypes.c_int],
             "msa_pack_fp8": [vp, i64, f32, vp, vp],
             "msa_unpack_fp8": [vp, i64, f32, vp, vp],
@@ -146,6 +153,24 @@ def msa_indexer_topk(prob, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores
     _check(_lib().msa_indexer_topk(ctypes.byref(prob), _ptr(idx_q), DTYPES[q_dtype], float(q_scale),
                                    ctypes.byref(idx_k), DEQUANT[dequant], _ptr(block_scores), _ptr(sel),
                                    _ptr(workspace), ws_bytes, _stream(stream)), "msa_indexer_topk")
+
+
+def msa_indexer_scores_shard(prob, shard, num_shards, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores,
+                             stream=None):
+    _check(_lib().msa_indexer_scores_shard(ctypes.byref(prob), int(shard), int(num_shards), _ptr(idx_q),
+                                           DTYPES[q_dtype], float(q_scale), ctypes.byref(idx_k),
+                                           DEQUANT[dequant], _ptr(block_scores), _stream(stream)),
+           "msa_indexer_scores_shard")
+
+
+def msa_shard_topk(prob, shard, num_shards, block_scores, cand_scores, cand_blocks, stream=None):
+    _check(_lib().msa_shard_topk(ctypes.byref(prob), int(shard), int(num_shards), _ptr(block_scores),
+                                 _ptr(cand_scores), _ptr(cand_blocks), _stream(stream)), "msa_shard_topk")
+
+
+def msa_topk_merge(prob, num_shards, cand_scores, cand_blocks, sel, stream=None):
+    _check(_lib().msa_topk_merge(ctypes.byref(prob), int(num_shards), _ptr(cand_scores), _ptr(cand_blocks),
+                                 _ptr(sel), _stream(stream)), "msa_topk_merge")
 
 
 def msa_block_topk(prob, block_scores, sel, stream=None):

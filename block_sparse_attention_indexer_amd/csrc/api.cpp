@@ -135,6 +135,46 @@ msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, in
   return hip_status(msa::launch_topk(to_args(prob), block_scores, sel, stream));
 }
 
+msa_status msa_indexer_scores_shard(const msa_problem* prob, int32_t shard, int32_t num_shards,
+                                    const void* idx_q, msa_dtype q_dtype, float q_scale,
+                                    const msa_cache* idx_k, msa_dequant dequant, float* block_scores,
+                                    hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (num_shards < 1 || num_shards > MSA_MAX_SHARDS || shard < 0 || shard >= num_shards) return MSA_ERR_INVALID_ARG;
+  if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
+  if ((st = check_pair(q_dtype, idx_k->dtype)) != MSA_OK) return st;
+  if (idx_k->dtype == MSA_F32 || prob->tokens > 4) return MSA_ERR_UNSUPPORTED;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (idx_q == nullptr || block_scores == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(idx_q, 16) || !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale)) return MSA_ERR_INVALID_ARG;
+  return hip_status(msa::launch_indexer(to_args(prob), idx_q, (int)q_dtype, q_scale, to_args(idx_k),
+                                        dequant == MSA_DQ_FP8, block_scores, nullptr, stream, nullptr,
+                                        nullptr, shard, num_shards));
+}
+
+msa_status msa_shard_topk(const msa_problem* prob, int32_t shard, int32_t num_shards, const float* block_scores,
+                          float* cand_scores, int32_t* cand_blocks, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (num_shards < 1 || num_shards > MSA_MAX_SHARDS || shard < 0 || shard >= num_shards) return MSA_ERR_INVALID_ARG;
+  if (block_scores == nullptr || cand_scores == nullptr || cand_blocks == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(block_scores, 4) || !aligned(cand_scores, 4) || !aligned(cand_blocks, 4)) return MSA_ERR_INVALID_ARG;
+  return hip_status(msa::launch_shard_topk(to_args(prob), shard, num_shards, block_scores, cand_scores,
+                                           cand_blocks, stream));
+}
+
+msa_status msa_topk_merge(const msa_problem* prob, int32_t num_shards, const float* cand_scores,
+                          const int32_t* cand_blocks, int32_t* sel, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (num_shards < 1 || num_shards > MSA_MAX_SHARDS) return MSA_ERR_INVALID_ARG;
+  if (cand_scores == nullptr || cand_blocks == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(cand_scores, 4) || !aligned(cand_blocks, 4) || !aligned(sel, 4)) return MSA_ERR_INVALID_ARG;
+  return hip_status(msa::launch_topk_merge(to_args(prob), num_shards, cand_scores, cand_blocks, sel, stream));
+}
+
 msa_status msa_sparse_attn_decode(const msa_problem* prob, const void* q, msa_dtype q_dtype,
                                   float q_scale, const msa_cache* k, const msa_cache* v,
                                   msa_dequant dequant, const int32_t* sel, float softmax_scale,

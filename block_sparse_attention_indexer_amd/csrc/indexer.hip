@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
-    float* __restrict__ block_scores, float* __restrict__ token_scores) {
+    float* __restrict__ block_scores, float* __restrict__ token_scores, int blk_off, int blk_step) {
   constexpr int UPP = 8 / TPU;             // units per page
   static_assert(kDecPagesPerWave >= 1 && kDecPagesPerWave <= 64, "page ids are held one per lane");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
@@ -142,14 +142,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   const float QNAN = __builtin_nanf("");
   const int L = seq_lens[b];
   const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
+  // shard (context-parallel) view: local block j is logical block gblk(j); w0,
+  // wend and nreal count local blocks (blk_off 0, blk_step 1: the whole context)
+  auto gblk = [&](int jj) { return blk_off + blk_step * jj; };
+  const int nloc = shard_count(max_blocks, blk_off, blk_step);
   const int w0 = (blockIdx.x * kDecWaves + wave) * kDecPagesPerWave;   // first block of this wave
-  if (w0 >= max_blocks) return;
-  const int wend = min(w0 + kDecPagesPerWave, max_blocks);
-  const int nreal = max(0, min(wend, nb) - w0);                        // blocks with keys
+  if (w0 >= nloc) return;
+  const int wend = min(w0 + kDecPagesPerWave, nloc);
+  const int nreal = max(0, min(wend, shard_count(nb, blk_off, blk_step)) - w0);   // blocks with keys
 
   // page ids of this wave's blocks: lane i holds block w0 + i; bad ids read page 0
   int pid = 0;
-  if (lane < nreal) pid = table[(size_t)b * max_blocks + w0 + lane];
+  if (lane < nreal) pid = table[(size_t)b * max_blocks + gblk(w0 + lane)];
   const int pid_bad = (pid < 0 || (int64_t)pid >= num_pages) ? 1 : 0;
   const int pid_safe = pid_bad ? 0 : pid;
 
@@ -182,11 +186,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     for (int i = w0 + nreal; i < wend; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)i * kBlock + kk] = NEG_INF;
+        for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)gblk(i) * kBlock + kk] = NEG_INF;
   }
   for (int e = lane; e < 16 * (wend - w0 - nreal); e += 64) {
     const int n = wend - w0 - nreal;
-    const int rowi = e / n, i = w0 + nreal + e % n;
+    const int rowi = e / n, i = gblk(w0 + nreal + e % n);
     if ((rowi >> 2) < T) block_scores[(((size_t)b * T + (rowi >> 2)) * kGroups + (rowi & 3)) * max_blocks + i] = NEG_INF;
   }
 
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
       const size_t row0 = (size_t)__builtin_amdgcn_readlane(pid_safe, blk) * kBlock + part * (16 * TPU) + j;
       load_idx_unit<KT, TPU>(buf0, kdata, kscales, row0, Q);
     }
-    contract_idx_unit<KT, FP8MODE, TOKSC, TPU>(buf0, A, lut, (w0 + blk) * kBlock + part * (16 * TPU) + j,
+    contract_idx_unit<KT, FP8MODE, TOKSC, TPU>(buf0, A, lut, gblk(w0 + blk) * kBlock + part * (16 * TPU) + j,
                                                p_tok, tok_ok, sigma, bmax, tsc_row, tstride);
     if (PIPE) buf0 = buf1;
     if (part == UPP - 1) {
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
         bmax[r] = NEG_INF;
       }
       if (TOKSC && bad && tok_ok) {
-        const int i = w0 + blk;
+        const int i = gblk(w0 + blk);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)i * kBlock + kk] = QNAN;
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   for (int e = lane; e < 16 * nreal; e += 64) {
     const int rowi = e / nreal, i = e % nreal;
     const int tt = rowi >> 2, g = rowi & 3;
-    if (tt < T) block_scores[(((size_t)b * T + tt) * kGroups + g) * max_blocks + w0 + i] = pooled[wave][i][rowi];
+    if (tt < T) block_scores[(((size_t)b * T + tt) * kGroups + g) * max_blocks + gblk(w0 + i)] = pooled[wave][i][rowi];
   }
 }
 
@@ -298,8 +302,12 @@ bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mod
 
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
-                          float* token_scores, hipStream_t s, int32_t* sel, uint32_t* counters) {
+                          float* token_scores, hipStream_t s, int32_t* sel, uint32_t* counters,
+                          int shard, int num_shards) {
   const float sigma = q_scale * k.tensor_scale;
+  const int nloc = shard_count(p.max_blocks, shard, num_shards);   // blocks of the shard
+  if (num_shards != 1 && (k.dtype == 0 || p.T > 4 || sel != nullptr)) return hipErrorInvalidValue;
+  if (nloc == 0) return hipSuccess;   // a shard past the last block has nothing to score
   if (k.dtype == 0) {
     hipLaunchKernelGGL(indexer_f32_kernel, dim3(p.max_blocks, p.B), dim3(128), 0, s,
                        (const float*)idx_q, (const float*)k.data, k.num_pages, p.seq_lens,
@@ -311,10 +319,10 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     // one token: 4x4x4 MFMA scan (the FP8-rounded NVFP4 reading keeps the 16-row path,
     // since its re-rounded values cannot take the scale after the dot)
     const unsigned per_wg = kScan1Blocks;
-    const dim3 grid((unsigned)((p.max_blocks + per_wg - 1) / per_wg), (unsigned)p.B);
+    const dim3 grid((unsigned)((nloc + per_wg - 1) / per_wg), (unsigned)p.B);
     const bool ts = token_scores != nullptr;
     const Scan1Args sa{q8, k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,
-                       block_scores, token_scores};
+                       block_scores, token_scores, shard, num_shards};
 #define MSA_DEC1_LAUNCH(KT, TS, FU) \
   hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS, FU>), grid, dim3(kDecWaves * 64), 0, s, sa, sel, counters)
     const bool fu = sel != nullptr;
@@ -326,11 +334,11 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
 #undef MSA_DEC1_LAUNCH
   } else if (p.T <= 4) {
     const unsigned per_wg = kDecWaves * kDecPagesPerWave;
-    const dim3 grid((unsigned)((p.max_blocks + per_wg - 1) / per_wg), (unsigned)p.B);
+    const dim3 grid((unsigned)((nloc + per_wg - 1) / per_wg), (unsigned)p.B);
 #define MSA_DEC_LAUNCH(KT, FM, TS)                                                              \
   hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2), MSA_DEC_PIPE != 0>), grid, dim3(kDecWaves * 64), 0, s, q8,  \
                      k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, \
-                     sigma, block_scores, token_scores)
+                     sigma, block_scores, token_scores, shard, num_shards)
     const bool ts = token_scores != nullptr;
     if (k.dtype == 1) {
       if (ts) MSA_DEC_LAUNCH(1, false, true); else MSA_DEC_LAUNCH(1, false, false);

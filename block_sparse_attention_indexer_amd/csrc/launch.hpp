@@ -31,10 +31,20 @@ hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int6
 
 // With sel and counters non-null (only where indexer_can_fuse_topk), the scan also
 // writes the top-16 selection; counters: one zeroed uint32 per sequence, left zeroed.
+// num_shards > 1: only the logical blocks i with i % num_shards == shard are scored
+// (FP8 / NVFP4 keys, T <= 4, no fused selection).
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
                           float* token_scores, hipStream_t s, int32_t* sel = nullptr,
-                          uint32_t* counters = nullptr);
+                          uint32_t* counters = nullptr, int shard = 0, int num_shards = 1);
+
+// Context-parallel selection: the local top-16 of one shard's blocks per row
+// (cand_* [rows][16], best first, padded with NaN / -1), and the owner's merge of
+// num_shards such lists (cand_* [num_shards][rows][16]) into sel.
+hipError_t launch_shard_topk(const ProblemArgs& p, int shard, int num_shards, const float* block_scores,
+                             float* cand_scores, int32_t* cand_blocks, hipStream_t s);
+hipError_t launch_topk_merge(const ProblemArgs& p, int num_shards, const float* cand_scores,
+                             const int32_t* cand_blocks, int32_t* sel, hipStream_t s);
 bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mode);
 
 hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const CacheArgs& k,

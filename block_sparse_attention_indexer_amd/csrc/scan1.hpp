@@ -145,10 +145,19 @@ struct Scan1Args {
   float sigma;
   float* block_scores;
   float* token_scores;
+  // Context-parallel shard: the scan covers logical blocks blk_off + blk_step*j
+  // (j = 0, 1, ...) only, writing their scores at those positions; 0 and 1 for
+  // the whole context.
+  int blk_off = 0;
+  int blk_step = 1;
 };
+// Blocks of the shard among the first n logical blocks.
+__host__ __device__ __forceinline__ int shard_count(int n, int off, int step) {
+  return n > off ? (n - off + step - 1) / step : 0;
+}
 constexpr int kScan1Blocks = kDecWaves * kDec1PagesPerWave;   // blocks per workgroup chunk
 
-// One workgroup's chunk of the scan: blocks [kScan1Blocks*chunk, +kScan1Blocks)
+// One workgroup's chunk of the scan: shard blocks [kScan1Blocks*chunk, +kScan1Blocks)
 // of sequence b (blocks past the sequence get -inf).  COHERENT: the pooled
 // scores are stored device-coherently, for another workgroup of the same
 // kernel to read.
@@ -161,13 +170,17 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   const float QNAN = __builtin_nanf("");
   const int L = a.seq_lens[b];
   const int nb = min((L + kBlock - 1) / kBlock, a.max_blocks);
+  // local index j of the shard is logical block gblk(j); w0, wend, nreal count local blocks
+  auto gblk = [&](int j) { return a.blk_off + a.blk_step * j; };
+  const int nloc = shard_count(a.max_blocks, a.blk_off, a.blk_step);
+  const int nb_loc = shard_count(nb, a.blk_off, a.blk_step);
   const int w0 = (chunk * kDecWaves + wave) * kDec1PagesPerWave;
-  if (w0 < a.max_blocks) {
-  const int wend = min(w0 + kDec1PagesPerWave, a.max_blocks);
-  const int nreal = max(0, min(wend, nb) - w0);
+  if (w0 < nloc) {
+  const int wend = min(w0 + kDec1PagesPerWave, nloc);
+  const int nreal = max(0, min(wend, nb_loc) - w0);
 
   int pid = 0;
-  if (lane < nreal) pid = a.table[(size_t)b * a.max_blocks + w0 + lane];
+  if (lane < nreal) pid = a.table[(size_t)b * a.max_blocks + gblk(w0 + lane)];
   const int pid_bad = (pid < 0 || (int64_t)pid >= a.num_pages) ? 1 : 0;
   const int pid_safe = pid_bad ? 0 : pid;
 
@@ -189,13 +202,13 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   // blocks of this wave past the sequence: -inf
   for (int e = lane; e < kGroups * (wend - w0 - nreal); e += 64) {
     const int n = wend - w0 - nreal;
-    a.block_scores[((size_t)b * kGroups + e / n) * a.max_blocks + w0 + nreal + e % n] = NEG_INF;
+    a.block_scores[((size_t)b * kGroups + e / n) * a.max_blocks + gblk(w0 + nreal + e % n)] = NEG_INF;
   }
   if (TOKSC) {
     for (int i = w0 + nreal; i < wend; ++i)
 #pragma unroll
       for (int g = 0; g < kGroups; ++g)
-        for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)i * kBlock + kk] = NEG_INF;
+        for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)gblk(i) * kBlock + kk] = NEG_INF;
   }
 
   const int nsets = 2 * nreal;               // two 64-key sets per page
@@ -204,8 +217,8 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   auto consume = [&](int u, const KeySet<KT>& cur) {
     const int blk = u >> 1, half = u & 1;
     f4 sc = score_key_set<KT>(cur, A);
-    const int key = (w0 + blk) * kBlock + half * 64 + lane;
-    if (w0 + blk == nb - 1) {                    // only the last block can hold keys past L - 1
+    const int key = gblk(w0 + blk) * kBlock + half * 64 + lane;
+    if (gblk(w0 + blk) == nb - 1) {              // only the last block can hold keys past L - 1
       if (key >= L) sc = f4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
     }
     bmax[0] = fmaxf(bmax[0], sc[0]);
@@ -223,7 +236,7 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
       if (TOKSC && bad) {
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
-          for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)(w0 + blk) * kBlock + kk] = QNAN;
+          for (int kk = lane; kk < kBlock; kk += 64) tsc[g * tstride + (size_t)gblk(w0 + blk) * kBlock + kk] = QNAN;
       }
       bmax = f4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
     }
@@ -252,13 +265,13 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   lds_wait();
   for (int e = lane; e < kGroups * nreal; e += 64) {
     const int g = e / nreal, i = e % nreal;
-    float* dst = a.block_scores + ((size_t)b * kGroups + g) * a.max_blocks + w0 + i;
+    float* dst = a.block_scores + ((size_t)b * kGroups + g) * a.max_blocks + gblk(w0 + i);
     if (COHERENT)   // device-coherent store: read back by another workgroup in this kernel
       __hip_atomic_store(dst, pooled[wave][i][g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
       *dst = pooled[wave][i][g];
   }
-  }   // w0 < a.max_blocks
+  }   // w0 < nloc
 
 }
 

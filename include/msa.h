@@ -113,7 +113,7 @@ typedef struct {
  *                wholly after p and for i >= ceil(L_b/128).
  *   token_scores device out, nullable, [B][T][4][max_blocks*128] fp32:
  *                the per-key scores (-inf past p), for inspection only.
- * Any T >= 1: T <= 8 runs the decode scan, larger T the prefill kernel. */
+ * Any T >= 1: T <= 4 runs the decode scan, larger T the prefill kernel. */
 msa_status msa_indexer_scores(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
                               float q_scale, const msa_cache* idx_k, msa_dequant dequant,
                               float* block_scores, float* token_scores, hipStream_t stream);
@@ -153,6 +153,46 @@ msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_d
                                    msa_dequant dequant, const int32_t* sel, float softmax_scale,
                                    float* out, float* lse, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* Indexer decode context parallelism (DCP), on one GPU (sections "NVFP4
+ * indexer DCP", NVIDIA and AMD parts: each of P GPUs scores all four groups
+ * over its share of the pages; each sends its local top-16 per group to the
+ * group's owner, which merges them into the final top-16 -- an exact
+ * selection; on AMD the scores themselves, bit-identical to a single-GPU
+ * run, are written into the owner's buffer).  Shard s of num_shards holds
+ * the logical blocks i with i % num_shards == s.  1 <= num_shards <=
+ * MSA_MAX_SHARDS and 0 <= shard < num_shards, else MSA_ERR_INVALID_ARG.
+ *
+ * msa_indexer_scores_shard: msa_indexer_scores restricted to the shard's
+ *   blocks: their entries of block_scores [B][T][4][max_blocks] are written
+ *   (the same bits as one msa_indexer_scores call writes there, -inf past the
+ *   sequence); every other entry is left untouched, so running every shard
+ *   once fills block_scores exactly as msa_indexer_scores does.  FP8 or NVFP4
+ *   index keys and tokens <= 4 (decode and speculative decode), else
+ *   MSA_ERR_UNSUPPORTED; no per-key scores.
+ * msa_shard_topk: the shard's local top-16 per (sequence, token, group) row
+ *   of block_scores: among the shard's blocks older than the row's own block
+ *   (p / 128), the 16 best by (score descending, block ascending), best
+ *   first, as cand_scores [B][T][4][16] fp32 (the score bits as read) and
+ *   cand_blocks [B][T][4][16] int32; a shard with fewer candidates pads with
+ *   NaN / -1.  NaN ranks below every number.  Reads only the shard's entries.
+ * msa_topk_merge: the owner's merge.  cand_scores / cand_blocks are
+ *   [num_shards][B][T][4][16], shard s's lists from msa_shard_topk at offset
+ *   s*B*T*4*16.  Writes sel [B][T][4][16] equal to msa_block_topk on the full
+ *   block_scores: with own+1 <= 16 visible blocks 0..own, else the own block
+ *   and the 15 best candidates, ascending, -1 padded.  Candidates that are
+ *   not older than the row's own block are ignored; the lists must come from
+ *   distinct shards of one partition. */
+#define MSA_MAX_SHARDS 8
+msa_status msa_indexer_scores_shard(const msa_problem* prob, int32_t shard, int32_t num_shards,
+                                    const void* idx_q, msa_dtype q_dtype, float q_scale,
+                                    const msa_cache* idx_k, msa_dequant dequant, float* block_scores,
+                                    hipStream_t stream);
+msa_status msa_shard_topk(const msa_problem* prob, int32_t shard, int32_t num_shards,
+                          const float* block_scores, float* cand_scores, int32_t* cand_blocks,
+                          hipStream_t stream);
+msa_status msa_topk_merge(const msa_problem* prob, int32_t num_shards, const float* cand_scores,
+                          const int32_t* cand_blocks, int32_t* sel, hipStream_t stream);
 
 /* Steps 1-3 in one call ("MSA primer": score, max-pool per block, keep the top
  * 16 blocks with the most recent one forced): the same block_scores and sel as

@@ -168,3 +168,37 @@ def test_cache_insert_validation(lib):
     assert call(c=_cache(heads=4, scales=None)) == M.MSA_ERR_INVALID_ARG
     assert call(c=_cache(heads=4, tensor_scale=0.0)) == M.MSA_ERR_INVALID_ARG
     assert call(prob=_prob(block_size=64)) == M.MSA_ERR_UNSUPPORTED
+
+
+def test_dcp_validation(lib):
+    p = _prob()
+    c = _cache()
+
+    def shard_scan(prob=p, shard=0, n=4, q=1024, cache=c, bs=2048, qd=M.MSA_FP8_E4M3):
+        return lib.msa_indexer_scores_shard(ctypes.byref(prob), shard, n, q, qd, 1.0, ctypes.byref(cache),
+                                            M.MSA_DQ_EXACT, bs, None)
+
+    assert shard_scan(n=0) == M.MSA_ERR_INVALID_ARG
+    assert shard_scan(n=M.MSA_MAX_SHARDS + 1) == M.MSA_ERR_INVALID_ARG
+    assert shard_scan(shard=4) == M.MSA_ERR_INVALID_ARG
+    assert shard_scan(shard=-1) == M.MSA_ERR_INVALID_ARG
+    assert shard_scan(prob=_prob(tokens=5)) == M.MSA_ERR_UNSUPPORTED          # decode and speculative only
+    assert shard_scan(cache=_cache(dtype=M.MSA_F32, scales=None), qd=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED
+    assert shard_scan(bs=None) == M.MSA_ERR_INVALID_ARG
+    assert shard_scan(q=1032) == M.MSA_ERR_INVALID_ARG
+
+    def local(prob=p, shard=1, n=4, bs=2048, cs=4096, cb=8192):
+        return lib.msa_shard_topk(ctypes.byref(prob), shard, n, bs, cs, cb, None)
+
+    assert local(shard=4) == M.MSA_ERR_INVALID_ARG
+    assert local(cs=None) == M.MSA_ERR_INVALID_ARG
+    assert local(cb=8194) == M.MSA_ERR_INVALID_ARG
+    assert local(prob=_prob(topk=8)) == M.MSA_ERR_UNSUPPORTED
+
+    def merge(prob=p, n=4, cs=4096, cb=8192, sel=16384):
+        return lib.msa_topk_merge(ctypes.byref(prob), n, cs, cb, sel, None)
+
+    assert merge(n=0) == M.MSA_ERR_INVALID_ARG
+    assert merge(n=9) == M.MSA_ERR_INVALID_ARG
+    assert merge(sel=None) == M.MSA_ERR_INVALID_ARG
+    assert merge(prob=_prob(batch=0)) == M.MSA_ERR_INVALID_ARG

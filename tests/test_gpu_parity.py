@@ -405,3 +405,83 @@ def test_cache_insert_bit_exact(M, dtype, heads, T, lens):
     assert np.array_equal(d_data.cpu().numpy(), want["data"])
     if dtype == "nvfp4":
         assert np.array_equal(d_sc.cpu().numpy(), want["scales"])
+
+
+# ------------------------------------------------------------------ context parallelism (DCP) on one GPU
+
+SENTINEL = 12345.0
+
+
+def _dcp_run(M, case, P, dequant="exact"):
+    """Every shard's scan into one buffer (prefilled with a sentinel), then every
+    shard's local top-16 and the merge.  Returns host copies."""
+    w, lay = case.w, case.lay
+    B, T, maxb = w.B, w.T, lay.max_blocks
+    prob = M.problem(case.d_seq, case.d_table, T)
+    bs = torch.full((B, T, 4, maxb), SENTINEL, dtype=torch.float32, device="cuda")
+    owned = []
+    for s in range(P):
+        M.msa_indexer_scores_shard(prob, s, P, case.d_idx_q, w.q_dtype, 1.0, case.d_caches["idx_k"][2], dequant, bs)
+        torch.cuda.synchronize()
+        host = bs.cpu().numpy()
+        mine = np.zeros(maxb, bool)
+        mine[s::P] = True
+        owned.append(mine)
+        # no entry of a shard that has not run yet is touched
+        later = ~np.any(np.stack(owned), axis=0)
+        assert np.all(host[..., later] == SENTINEL), s
+    cs = torch.empty((P, B, T, 4, 16), dtype=torch.float32, device="cuda")
+    cb = torch.empty((P, B, T, 4, 16), dtype=torch.int32, device="cuda")
+    for s in range(P):
+        M.msa_shard_topk(prob, s, P, bs, cs[s], cb[s])
+    sel = torch.empty((B, T, 4, 16), dtype=torch.int32, device="cuda")
+    M.msa_topk_merge(prob, P, cs, cb, sel)
+    torch.cuda.synchronize()
+    return bs.cpu().numpy(), cs.cpu().numpy(), cb.cpu().numpy(), sel.cpu().numpy()
+
+
+def _check_dcp(case, ref, bs, cs, cb, sel, P, rows=None):
+    w = case.w
+    seq = case.lay.seq_lens.numpy()
+    # the pages' claim: shard scores are bit-identical to the single-GPU scan ...
+    assert np.array_equal(bs, ref["block_scores"], equal_nan=True)
+    # ... and the merged selection is the single-GPU selection
+    assert np.array_equal(sel, ref["sel"])
+    # local lists and merge against the oracle, on the same (GPU) scores
+    for b in (range(w.B) if rows is None else rows):
+        L = int(seq[b])
+        own = OM.own_blocks(L, w.T)
+        for t in range(w.T):
+            for g in range(4):
+                for s in range(P):
+                    os_, ob = OM.shard_candidates(bs[b, t, g], int(own[t]), s, P)
+                    assert np.array_equal(cb[s, b, t, g], ob), (b, t, g, s)
+                    n = int((ob >= 0).sum())
+                    assert np.array_equal(cs[s, b, t, g, :n], os_[:n].astype(np.float32)), (b, t, g, s)
+                    assert np.all(np.isnan(cs[s, b, t, g, n:]))
+                assert np.array_equal(sel[b, t, g], OM.merge_candidates(cs[:, b, t, g], cb[:, b, t, g], int(own[t])))
+
+
+@pytest.mark.parametrize("wname,mode,P", [("tiny_nvfp4", "exact", 4), ("tiny_nvfp4", "exact", 1),
+                                          ("tiny_nvfp4", "fp8", 3), ("tiny_fp8", "exact", 2),
+                                          ("tiny_spec", "exact", 4), ("tiny_spec", "fp8", 8),
+                                          ("tiny_t3", "exact", 5), ("tiny_edge", "exact", 4),
+                                          ("long_rows", "exact", 4), ("long_rows", "exact", 2)])
+def test_dcp_shards_and_merge(M, wname, mode, P):
+    """Shard scans write only their own blocks and, together, the unsharded scores bit
+    for bit; local top-16s and the merge match the oracle; the merged selection
+    equals msa_block_topk's."""
+    _say("dcp", wname, mode, P)
+    case = H.HostCase(wname).upload()
+    ref = H.to_host(H.run_path(case, mode, attention=False))
+    _check_dcp(case, ref, *_dcp_run(M, case, P, mode), P)
+
+
+@pytest.mark.parametrize("wname,rows", [("c3_128k", [0, 33, 63]), ("c4", [2, 15])])
+def test_dcp_full_size(M, wname, rows):
+    """At full size (one token over 131,072-token contexts; 4 tokens over 262,144):
+    four shards against the unsharded scan and selection."""
+    _say("dcp full size", wname)
+    case = H.DeviceCase(wname, keep_fp32=False)
+    ref = H.to_host(H.run_path(case, "exact", attention=False))
+    _check_dcp(case, ref, *_dcp_run(M, case, 4), 4, rows=rows)
