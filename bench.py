@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--mono", action="store_true",
                     help="run the whole step as the one call msa_decode_step")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
-    ap.add_argument("--only", choices=["insert"], default=None,
+    ap.add_argument("--only", choices=["insert", "dcp"], default=None,
                     help="run one side section alone and print its JSON (for profiling), not the step line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -211,21 +211,31 @@ def algorithmic_flops(wl, sel_host):
     return idx, attn
 
 
-def indexer_kernel_name(w, dequant, path="calls"):
+def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
     """The first kernel of the step (the index scan, or the whole step for "mono") that
-    libmsa launches for this workload, as rocprofv3 names it."""
+    libmsa launches for this workload, as rocprofv3 names it.  The pages-per-wave
+    template argument follows the launcher's rule: the largest of its three sizes
+    whose grid gives every CU two workgroups."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
     fp8mode = kt == 2 and dequant == "fp8"
-    fused = path == "fused"
+    fused = path == "fused" and not fp8mode
+    nb = max_blocks if max_blocks is not None else -(-max(np.atleast_1d(w.lens)) // 128)
+
+    def ppw(big):
+        for p_ in (big, big // 2):
+            if w.B * -(-nb // (4 * p_)) >= 2 * cus:
+                return p_
+        return big // 4
+    b = lambda x: str(x).lower()
     if path == "mono" and w.T == 1 and not fp8mode:
         return f"msa::decode_step_kernel<{kt}>"
-    if w.T == 1 and not fp8mode:
-        return f"msa::indexer_decode1_kernel<{kt}, false, {str(fused).lower()}>"
+    if w.T == 1:
+        return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16)}, {b(fp8mode)}>"
     if w.T <= 4:
-        return f"msa::indexer_decode_kernel<{kt}, {str(fp8mode).lower()}, false>"
-    return f"msa::indexer_prefill_kernel<{kt}, {str(fp8mode).lower()}, false>"
+        return f"msa::indexer_decode_kernel<{kt}, {b(fp8mode)}, false, {4 if kt == 2 else 2}, true, {ppw(8)}>"
+    return f"msa::indexer_prefill_kernel<{kt}, {b(fp8mode)}, false>"
 
 
 def measured_traffic(workload, kernel=None, role=None):
@@ -337,6 +347,81 @@ def insert_section(seed, steps=20):
     return {"kernel": "msa::insert_rows_kernel<2> (3 launches: K, V, index keys; timed as graph replays)", **out}
 
 
+def dcp_section(wl, dequant, P=4, steps=20):
+    """Decode context parallelism on one GPU: the P shard scans of the index cache
+    (each the work one of P GPUs would do), every shard's local top-16 and the
+    owner's merge, each bracketed by HIP events on the launching stream, against the
+    unsharded scan + top-16 of the same batch.  The exchange between GPUs is not
+    part of it.  Algorithmic bytes of a shard scan: the index keys of its blocks, the
+    index queries and the block scores it writes."""
+    import torch
+    M, w, lay = wl.M, wl.w, wl.lay
+    B, T, maxb = w.B, w.T, lay.max_blocks
+    ik = wl.caches["idx_k"][2]
+    bs = torch.empty_like(wl.bs)
+    cs = torch.empty((P, B, T, 4, 16), dtype=torch.float32, device="cuda")
+    cb = torch.empty((P, B, T, 4, 16), dtype=torch.int32, device="cuda")
+    sel = torch.empty_like(wl.sel)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def once(rec):
+        t = [ev() for _ in range(2 * P + 2)] if rec else None
+        for s_ in range(P):
+            if rec: t[s_].record()
+            M.msa_indexer_scores_shard(wl.prob, s_, P, wl.idx_q, w.q_dtype, 1.0, ik, dequant, bs)
+        if rec: t[P].record()
+        for s_ in range(P):
+            M.msa_shard_topk(wl.prob, s_, P, bs, cs[s_], cb[s_])
+            if rec: t[P + 1 + s_].record()
+        M.msa_topk_merge(wl.prob, P, cs, cb, sel)
+        if rec: t[2 * P + 1].record()
+        return t
+
+    for _ in range(3):
+        once(False)
+    full_ev = [[ev() for _ in range(3)] for _ in range(steps)]
+    runs = []
+    for k in range(steps):
+        runs.append(once(True))
+        e = full_ev[k]
+        e[0].record()
+        M.msa_indexer_scores(wl.prob, wl.idx_q, w.q_dtype, 1.0, ik, dequant, wl.bs, None)
+        e[1].record()
+        M.msa_block_topk(wl.prob, wl.bs, wl.sel)
+        e[2].record()
+    torch.cuda.synchronize()
+    scan = np.array([[r[s_].elapsed_time(r[s_ + 1]) for s_ in range(P)] for r in runs]).mean(axis=0)
+    local = np.array([[r[P + s_].elapsed_time(r[P + 1 + s_]) for s_ in range(P)] for r in runs]).mean(axis=0)
+    merge = float(np.mean([r[2 * P].elapsed_time(r[2 * P + 1]) for r in runs]))
+    full_scan = float(np.mean([e[0].elapsed_time(e[1]) for e in full_ev]))
+    full_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in full_ev]))
+    exact = bool(torch.equal(bs, wl.bs)) and bool(torch.equal(sel, wl.sel))
+    lens = [int(x) for x in lay.seq_lens]
+    shard_keys = np.zeros(P)
+    for L in lens:
+        nb = (L + 127) // 128
+        for s_ in range(P):
+            blocks = np.arange(s_, nb, P)
+            shard_keys[s_] += np.minimum(128, L - 128 * blocks).sum()
+    qb = 4 if w.q_dtype == "f32" else 1
+    shard_bytes = shard_keys * ROW_BYTES[w.kv_dtype] + B * T * 4 * 128 * qb + \
+        np.array([B * T * 4 * len(range(s_, maxb, P)) * 4 for s_ in range(P)])
+    gbps = shard_bytes / (scan * 1e-3) / 1e9
+    return {"workload": w.name, "shards": P,
+            "kernels": {"scan": indexer_kernel_name(w, dequant, max_blocks=-(-maxb // P)),
+                        "local_top16": "msa::shard_topk_kernel<4>" if -(-maxb // P) <= 1024 else
+                        "msa::shard_topk_kernel<32>",
+                        "merge": "msa::topk_merge_kernel"},
+            "shard_scan_ms": [round(float(x), 5) for x in scan],
+            "shard_scan_GBps": [round(float(x), 1) for x in gbps],
+            "shard_scan_frac_of_hbm_peak": round(float(gbps.mean()) / HBM_PEAK_GBPS, 4),
+            "local_top16_ms": [round(float(x), 5) for x in local], "merge_ms": round(merge, 5),
+            "unsharded_scan_ms": round(full_scan, 5), "unsharded_top16_ms": round(full_topk, 5),
+            "per_gpu_ms": round(float(scan.max() + local.max() + merge), 5),
+            "scan_speedup_per_gpu": round(full_scan / float(scan.max()), 3),
+            "bit_identical_scores_and_selection": exact}
+
+
 def cpu_baseline(wl, dequant, sample):
     """The oracle on `sample` sequences of the same workload, packed by the
     oracle itself from the fp32 sources; timed from decode to attention."""
@@ -384,17 +469,9 @@ def main():
     import numpy as np
     import torch
     torch.cuda.set_device(0)
-    if args.only == "insert":
-        print(json.dumps({"insert": insert_section(args.seed, steps=args.steps)}), flush=True)
-        return
-    sample = [] if args.no_cpu_baseline else list(range(0, 64, 64 // max(1, args.cpu_sample)))[: args.cpu_sample]
-    wl = Workload(args.workload, args.seed, keep_sequences=sample)
-    w = wl.w
-    print(f"[bench] workload {w.name} ready: B={w.B} T={w.T} pages={wl.lay.num_pages}", file=sys.stderr, flush=True)
-
     if args.calib_copy_mib:
         # a plain elementwise copy kernel (reads and writes calib_copy_mib MiB each) whose
-        # FETCH_SIZE / WRITE_SIZE counter readings calibrate the counters of the kernels above
+        # FETCH_SIZE / WRITE_SIZE counter readings calibrate the counters of the MSA kernels
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
         bbuf = torch.empty_like(a)
@@ -402,6 +479,17 @@ def main():
             torch.mul(a, 1.0, out=bbuf)
         torch.cuda.synchronize()
         del a, bbuf
+    if args.only == "insert":
+        print(json.dumps({"insert": insert_section(args.seed, steps=args.steps)}), flush=True)
+        return
+    if args.only == "dcp":
+        wl = Workload(args.workload, args.seed)
+        print(json.dumps({"dcp": dcp_section(wl, args.dequant, steps=args.steps)}), flush=True)
+        return
+    sample = [] if args.no_cpu_baseline else list(range(0, 64, 64 // max(1, args.cpu_sample)))[: args.cpu_sample]
+    wl = Workload(args.workload, args.seed, keep_sequences=sample)
+    w = wl.w
+    print(f"[bench] workload {w.name} ready: B={w.B} T={w.T} pages={wl.lay.num_pages}", file=sys.stderr, flush=True)
 
     path = "mono" if args.mono else "fused" if args.fused else "calls"
     for _ in range(args.warmup):
@@ -464,15 +552,18 @@ def main():
                     {"indexer_topk": round(idx_ms, 5), "attention": round(float(per_call[1]), 5)} if fused else
                     {"indexer": round(idx_ms, 5), "topk": round(float(per_call[1]), 5),
                      "attention": round(float(per_call[2]), 5)}),
-        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, path) +
+        "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, path, wl.lay.max_blocks) +
                      {"mono": " (the whole step: scan, pool, top-16, attention)",
                       "fused": " (index-key scan + block max-pool + top-16)",
                       "calls": " (index-key scan + block max-pool)"}[path],
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, path))},
+                     "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, path,
+                                                                              wl.lay.max_blocks))},
         "cpu_baseline": None,
     }
+    if w.T <= 4 and w.kv_dtype != "f32":
+        out["dcp"] = dcp_section(wl, args.dequant)
     if not args.no_prefill and args.workload != "c5":
         out["prefill"] = prefill_section(args.dequant, args.seed)
         out["insert"] = insert_section(args.seed)

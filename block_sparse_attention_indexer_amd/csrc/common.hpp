@@ -163,7 +163,7 @@ __device__ inline void build_fp8_lut(uint32_t* lut) {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const uint32_t byte = bad ? 0x7Fu : e4m3_encode(e2m1_magnitude((uint32_t)m) * sv);
+      const uint32_t byte = bad ? 0x7Fu : e4m3_encode2(e2m1_magnitude((uint32_t)m) * sv, 0.0f) & 0xFFu;
       w[m >> 2] |= byte << (8 * (m & 3));
     }
     lut[2 * s] = w[0];

@@ -20,8 +20,9 @@ namespace msa {
 // ---------------------------------------------------------------------------
 // Decode and speculative decode (T <= 4): a streaming scan.
 //
-// Grid (page range, sequence); each of the 4 waves of a workgroup owns
-// kDecPagesPerWave consecutive logical blocks.  A wave reads its page ids
+// Grid (page range, sequence); each of the 4 waves of a workgroup owns PPW
+// consecutive blocks (kDecPagesPerWave, or a half or a quarter of it when the
+// grid would otherwise leave CUs idle).  A wave reads its page ids
 // once (one lane per block), then walks its pages in units of TPU key tiles
 // (16 keys each).  With PIPE the next unit's loads are issued before the
 // current unit is contracted, so memory and math overlap inside the wave;
@@ -120,17 +121,17 @@ __device__ __forceinline__ void contract_idx_unit(const IdxUnit<KT, TPU>& u, con
   }
 }
 
-template <int KT, bool FP8MODE, bool TOKSC, int TPU, bool PIPE>
+template <int KT, bool FP8MODE, bool TOKSC, int TPU, bool PIPE, int PPW>
 __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
     float* __restrict__ block_scores, float* __restrict__ token_scores, int blk_off, int blk_step) {
   constexpr int UPP = 8 / TPU;             // units per page
-  static_assert(kDecPagesPerWave >= 1 && kDecPagesPerWave <= 64, "page ids are held one per lane");
+  static_assert(PPW >= 1 && PPW <= 64, "page ids are held one per lane");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
   // pooled scores of each wave's blocks, [block][token*4 + group], written out at the end
-  __shared__ float pooled[kDecWaves][kDecPagesPerWave][16];
+  __shared__ float pooled[kDecWaves][PPW][16];
   if (FP8MODE) {
     build_fp8_lut(lut);
     __syncthreads();
@@ -146,9 +147,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   // wend and nreal count local blocks (blk_off 0, blk_step 1: the whole context)
   auto gblk = [&](int jj) { return blk_off + blk_step * jj; };
   const int nloc = shard_count(max_blocks, blk_off, blk_step);
-  const int w0 = (blockIdx.x * kDecWaves + wave) * kDecPagesPerWave;   // first block of this wave
+  const int w0 = (blockIdx.x * kDecWaves + wave) * PPW;   // first block of this wave
   if (w0 >= nloc) return;
-  const int wend = min(w0 + kDecPagesPerWave, nloc);
+  const int wend = min(w0 + PPW, nloc);
   const int nreal = max(0, min(wend, shard_count(nb, blk_off, blk_step)) - w0);   // blocks with keys
 
   // page ids of this wave's blocks: lane i holds block w0 + i; bad ids read page 0
@@ -243,10 +244,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
 // per-sequence arrival counter in `counters`, zero before the call and reset
 // to zero by that workgroup) also selects the sequence's top-16 blocks.
 // Nothing waits on another workgroup: the last arrival does the work.
-template <int KT, bool TOKSC, bool FUSE>
+template <int KT, bool TOKSC, bool FUSE, int PPW, bool FP8MODE = false>
 __global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_kernel(Scan1Args a, int32_t* __restrict__ sel,
                                                                             uint32_t* __restrict__ counters) {
-  scan1_chunk<KT, TOKSC, FUSE>(a, blockIdx.y, blockIdx.x);
+  __shared__ __align__(8) uint32_t lut[FP8MODE ? 512 : 2];
+  if constexpr (FP8MODE) {
+    build_fp8_lut(lut);
+    __syncthreads();
+  }
+  scan1_chunk<KT, TOKSC, FUSE, PPW, FP8MODE>(a, blockIdx.y, blockIdx.x, lut);
   if constexpr (FUSE) scan1_select_if_last(a, blockIdx.y, gridDim.x, sel, counters);
 }
 
@@ -315,38 +321,67 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     return hipGetLastError();
   }
   const uint8_t* q8 = (const uint8_t*)idx_q;
-  if (p.T == 1 && !(k.dtype == 2 && fp8mode)) {
-    // one token: 4x4x4 MFMA scan (the FP8-rounded NVFP4 reading keeps the 16-row path,
-    // since its re-rounded values cannot take the scale after the dot)
-    const unsigned per_wg = kScan1Blocks;
-    const dim3 grid((unsigned)((nloc + per_wg - 1) / per_wg), (unsigned)p.B);
+  // Pages per wave: the largest of the kernel's three sizes whose grid still gives
+  // every CU two workgroups (a shard, or few long sequences, has few chunks).
+  const int want = 2 * current_cu_count();
+  auto pick_ppw = [&](int big) {
+    for (int ppw = big; ppw > big / 4; ppw /= 2)
+      if ((int64_t)p.B * ((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)) >= want) return ppw;
+    return big / 4;
+  };
+  if (p.T == 1 && !(fp8mode && k.dtype == 2 && sel != nullptr)) {
+    // one token: 4x4x4 MFMA scan; the FP8-rounded NVFP4 reading decodes through the
+    // LDS table instead of scaling partial dots (not fused with the selection)
+    const int ppw = pick_ppw(kDec1PagesPerWave);
+    const bool f8 = fp8mode && k.dtype == 2;
+    const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
     const bool ts = token_scores != nullptr;
+    const bool fu = sel != nullptr;
     const Scan1Args sa{q8, k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,
                        block_scores, token_scores, shard, num_shards};
-#define MSA_DEC1_LAUNCH(KT, TS, FU) \
-  hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS, FU>), grid, dim3(kDecWaves * 64), 0, s, sa, sel, counters)
-    const bool fu = sel != nullptr;
+#define MSA_DEC1_LAUNCH(KT, TS, FU, PPW, FM)                                                        \
+  hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS, FU, PPW, FM>), grid, dim3(kDecWaves * 64), 0, s, sa, sel, \
+                     counters)
+#define MSA_DEC1_PPW(KT, TS, FU, FM)                                                                \
+  do {                                                                                              \
+    if (ppw == kDec1PagesPerWave) MSA_DEC1_LAUNCH(KT, TS, FU, kDec1PagesPerWave, FM);               \
+    else if (ppw == kDec1PagesPerWave / 2) MSA_DEC1_LAUNCH(KT, TS, FU, kDec1PagesPerWave / 2, FM);  \
+    else MSA_DEC1_LAUNCH(KT, TS, FU, kDec1PagesPerWave / 4, FM);                                    \
+  } while (0)
     if (k.dtype == 1) {
-      if (ts) MSA_DEC1_LAUNCH(1, true, false); else if (fu) MSA_DEC1_LAUNCH(1, false, true); else MSA_DEC1_LAUNCH(1, false, false);
+      if (ts) MSA_DEC1_PPW(1, true, false, false); else if (fu) MSA_DEC1_PPW(1, false, true, false);
+      else MSA_DEC1_PPW(1, false, false, false);
+    } else if (f8) {
+      if (ts) MSA_DEC1_PPW(2, true, false, true); else MSA_DEC1_PPW(2, false, false, true);
     } else {
-      if (ts) MSA_DEC1_LAUNCH(2, true, false); else if (fu) MSA_DEC1_LAUNCH(2, false, true); else MSA_DEC1_LAUNCH(2, false, false);
+      if (ts) MSA_DEC1_PPW(2, true, false, false); else if (fu) MSA_DEC1_PPW(2, false, true, false);
+      else MSA_DEC1_PPW(2, false, false, false);
     }
+#undef MSA_DEC1_PPW
 #undef MSA_DEC1_LAUNCH
   } else if (p.T <= 4) {
-    const unsigned per_wg = kDecWaves * kDecPagesPerWave;
-    const dim3 grid((unsigned)((nloc + per_wg - 1) / per_wg), (unsigned)p.B);
-#define MSA_DEC_LAUNCH(KT, FM, TS)                                                              \
-  hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2), MSA_DEC_PIPE != 0>), grid, dim3(kDecWaves * 64), 0, s, q8,  \
-                     k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, \
+    const int ppw = pick_ppw(kDecPagesPerWave);
+    const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
+#define MSA_DEC_LAUNCH(KT, FM, TS, PPW)                                                                      \
+  hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2),            \
+                                            MSA_DEC_PIPE != 0, PPW>), grid, dim3(kDecWaves * 64), 0, s, q8,   \
+                     k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T,             \
                      sigma, block_scores, token_scores, shard, num_shards)
+#define MSA_DEC_PPW(KT, FM, TS)                                                                   \
+  do {                                                                                            \
+    if (ppw == kDecPagesPerWave) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave);                    \
+    else if (ppw == kDecPagesPerWave / 2) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave / 2);       \
+    else MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave / 4);                                        \
+  } while (0)
     const bool ts = token_scores != nullptr;
     if (k.dtype == 1) {
-      if (ts) MSA_DEC_LAUNCH(1, false, true); else MSA_DEC_LAUNCH(1, false, false);
+      if (ts) MSA_DEC_PPW(1, false, true); else MSA_DEC_PPW(1, false, false);
     } else if (fp8mode) {
-      if (ts) MSA_DEC_LAUNCH(2, true, true); else MSA_DEC_LAUNCH(2, true, false);
+      if (ts) MSA_DEC_PPW(2, true, true); else MSA_DEC_PPW(2, true, false);
     } else {
-      if (ts) MSA_DEC_LAUNCH(2, false, true); else MSA_DEC_LAUNCH(2, false, false);
+      if (ts) MSA_DEC_PPW(2, false, true); else MSA_DEC_PPW(2, false, false);
     }
+#undef MSA_DEC_PPW
 #undef MSA_DEC_LAUNCH
   } else {
     return launch_indexer_prefill(p, idx_q, k, fp8mode, sigma, block_scores, token_scores, s);

@@ -22,6 +22,20 @@ struct ProblemArgs {
   const int32_t* block_table;
 };
 
+// Compute units of the current device, queried once per device (256 on MI355X;
+// 256 is also the answer if the query fails).
+inline int current_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) return 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_pack_fp8(const float* x, int64_t n, float scale, uint8_t* out, hipStream_t s);
 hipError_t launch_unpack_fp8(const uint8_t* x, int64_t n, float scale, float* out, hipStream_t s);
 hipError_t launch_pack_nvfp4(const float* x, int64_t groups, float tensor_scale, uint8_t* codes,

@@ -67,11 +67,32 @@ __device__ __forceinline__ float e4m3_byte_to_f(uint32_t w, int k) {
 constexpr int kDec1Chains = MSA_DEC1_CHAINS;   // independent MFMA accumulation chains (divides 8)
 
 // The 4 group scores of this lane's key (before the tensor scales).
-// A[c] gives dims 4c .. 4c+3 of this lane's group (lane % 4).
-template <int KT, typename ASrc>
-__device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const ASrc& A) {
+// A[c] gives dims 4c .. 4c+3 of this lane's group (lane % 4) -- for the
+// FP8-rounded NVFP4 reading (FP8MODE) dims 8i + {0,2,4,6} (c = 2i) and
+// 8i + {1,3,5,7} (c = 2i+1), the order the table decode produces.
+// FP8MODE: each element is the E4M3 re-rounding of e2m1 x scale, read from
+// the 2 KB table in LDS (`lut`, two words per scale byte), so the scale
+// cannot be applied after the dot: all 32 MFMAs take decoded values.
+template <int KT, bool FP8MODE, typename ASrc>
+__device__ __forceinline__ f4 score_key_set(const KeySet<KT>& u, const ASrc& A, const uint32_t* lut) {
   f4 tot = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (KT == 2) {
+  if constexpr (KT == 2 && FP8MODE) {
+    f4 part[2] = {f4{0.0f, 0.0f, 0.0f, 0.0f}, f4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {              // scale group sg: dims 16sg .. 16sg+15
+      const uint32_t sb = ((sg < 4 ? u.s.x : u.s.y) >> (8 * (sg & 3))) & 0xFFu;
+      const uint2 lh = reinterpret_cast<const uint2*>(lut)[sb];   // one 8-byte LDS read
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const h8 v = fp4x8_lut_to_h8(dword_of(u.c[sg >> 1], 2 * (sg & 1) + h), lh.x, lh.y);
+        const int c = 4 * sg + 2 * h;
+        part[h] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[c], h4{v[0], v[1], v[2], v[3]}, part[h], 0, 0, 0);
+        part[h] = __builtin_amdgcn_mfma_f32_4x4x4f16(A[c + 1], h4{v[4], v[5], v[6], v[7]}, part[h], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] = part[0][i] + part[1][i];
+  } else if constexpr (KT == 2) {
     // kDec1Chains scale groups at a time, their MFMA chains interleaved
 #pragma unroll
     for (int s0 = 0; s0 < 8; s0 += kDec1Chains) {
@@ -157,14 +178,15 @@ __host__ __device__ __forceinline__ int shard_count(int n, int off, int step) {
 }
 constexpr int kScan1Blocks = kDecWaves * kDec1PagesPerWave;   // blocks per workgroup chunk
 
-// One workgroup's chunk of the scan: shard blocks [kScan1Blocks*chunk, +kScan1Blocks)
-// of sequence b (blocks past the sequence get -inf).  COHERENT: the pooled
-// scores are stored device-coherently, for another workgroup of the same
-// kernel to read.
-template <int KT, bool TOKSC, bool COHERENT>
-__device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk) {
-  static_assert(kDec1PagesPerWave >= 1 && kDec1PagesPerWave <= 64, "page ids are held one per lane");
-  __shared__ float pooled[kDecWaves][kDec1PagesPerWave][kGroups];
+// One workgroup's chunk of the scan: shard blocks [4*PPW*chunk, +4*PPW) of
+// sequence b, PPW per wave (blocks past the sequence get -inf).  Smaller PPW
+// gives more, shorter chunks: used when the grid would not fill the chip.
+// COHERENT: the pooled scores are stored device-coherently, for another
+// workgroup of the same kernel to read.
+template <int KT, bool TOKSC, bool COHERENT, int PPW = kDec1PagesPerWave, bool FP8MODE = false>
+__device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk, const uint32_t* lut = nullptr) {
+  static_assert(PPW >= 1 && PPW <= 64, "page ids are held one per lane");
+  __shared__ float pooled[kDecWaves][PPW][kGroups];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float NEG_INF = -__builtin_inff();
   const float QNAN = __builtin_nanf("");
@@ -174,9 +196,9 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   auto gblk = [&](int j) { return a.blk_off + a.blk_step * j; };
   const int nloc = shard_count(a.max_blocks, a.blk_off, a.blk_step);
   const int nb_loc = shard_count(nb, a.blk_off, a.blk_step);
-  const int w0 = (chunk * kDecWaves + wave) * kDec1PagesPerWave;
+  const int w0 = (chunk * kDecWaves + wave) * PPW;
   if (w0 < nloc) {
-  const int wend = min(w0 + kDec1PagesPerWave, nloc);
+  const int wend = min(w0 + PPW, nloc);
   const int nreal = max(0, min(wend, nb_loc) - w0);
 
   int pid = 0;
@@ -192,8 +214,17 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
     for (int q = 0; q < 8; ++q) {
       const uint4 v = src[q];
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (FP8MODE) {   // dims 16q+8h + {0,2,4,6} then + {1,3,5,7}
 #pragma unroll
-      for (int k = 0; k < 4; ++k) A.v[4 * q + k] = cat4(fp8x2_to_h2<false>(wv[k]), fp8x2_to_h2<true>(wv[k]));
+        for (int h = 0; h < 2; ++h) {
+          const h8 d = fp8x8_to_h8(wv[2 * h], wv[2 * h + 1]);
+          A.v[4 * q + 2 * h] = h4{d[0], d[2], d[4], d[6]};
+          A.v[4 * q + 2 * h + 1] = h4{d[1], d[3], d[5], d[7]};
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) A.v[4 * q + k] = cat4(fp8x2_to_h2<false>(wv[k]), fp8x2_to_h2<true>(wv[k]));
+      }
     }
   }
   const size_t tstride = (size_t)a.max_blocks * kBlock;
@@ -216,7 +247,7 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   // score set u (64 keys of block u/2) and fold it into the block maxima
   auto consume = [&](int u, const KeySet<KT>& cur) {
     const int blk = u >> 1, half = u & 1;
-    f4 sc = score_key_set<KT>(cur, A);
+    f4 sc = score_key_set<KT, FP8MODE>(cur, A, lut);
     const int key = gblk(w0 + blk) * kBlock + half * 64 + lane;
     if (gblk(w0 + blk) == nb - 1) {              // only the last block can hold keys past L - 1
       if (key >= L) sc = f4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};

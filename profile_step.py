@@ -1,6 +1,6 @@
 """Collect the rocprofv3 figures that bench.py reports, for one workload.
 
-    python profile_step.py [--workload c3_128k] [--out gpurun_out/profile]
+    python profile_step.py [--workload c3_128k] [--only insert|dcp] [--out gpurun_out/profile]
 
 Runs bench.py three times as a child process under rocprofv3 (this process
 never touches the GPU):
@@ -13,6 +13,9 @@ Counter readings are per dispatch, in KiB.  Each is scaled by what the same
 counter reads for the 512 MiB elementwise copy that bench.py launches with
 --calib-copy-mib (which reads and writes exactly 512 MiB), so the reported
 bytes are calibrated HBM bytes per launch.  Writes, into --out:
+
+With --only, bench.py runs that side section alone (bench.py --only ...) and the
+files are named insert_rows_c5_chunk_and_c3_decode.* or dcp_<workload>.* instead.
 
   layer_step_<workload>.md           per-kernel launches and durations, calibrated HBM
                           bytes per launch, the calibration factors and the
@@ -94,6 +97,7 @@ def read_counters(d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="c3_128k")
+    ap.add_argument("--only", choices=["insert", "dcp"], default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
@@ -103,17 +107,22 @@ def main():
     raw = os.path.join(args.out, "raw")
     shutil.rmtree(raw, ignore_errors=True)
 
+    only = ["--only", args.only] if args.only else []
+    tag = {None: f"layer_step_{w}", "insert": "insert_rows_c5_chunk_and_c3_decode", "dcp": f"dcp_{w}"}[args.only]
+    title = {None: f"MSA layer step, workload {w}",
+             "insert": "quantise-and-insert (msa_cache_insert), c5 prefill chunk and c3_128k decode token",
+             "dcp": f"single-GPU DCP (4 shard scans, local top-16s, merge), workload {w}"}[args.only]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(raw, "trace"), "-o", "run",
                  "-f", "csv", "--", py, bench, "--workload", w, "--steps", "10", "--warmup", "2",
-                 "--no-cpu-baseline", "--no-prefill"]
+                 "--no-cpu-baseline", "--no-prefill"] + only
     pmc_bench = [py, bench, "--workload", w, "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-prefill",
-                 "--calib-copy-mib", str(CALIB_MIB)]
+                 "--calib-copy-mib", str(CALIB_MIB)] + only
     cmds = {"trace": trace_cmd}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds[c] = ["rocprofv3", "--pmc", c, "-d", os.path.join(raw, c), "-o", "run", "-f", "csv", "--"] + pmc_bench
     for k, cmd in cmds.items():
-        if run(cmd, os.path.join(args.out, f"{w}_{k}.log")) != 0:
-            sys.exit(f"rocprofv3 pass {k} failed; see {args.out}/{w}_{k}.log")
+        if run(cmd, os.path.join(args.out, f"{tag}_{k}.log")) != 0:
+            sys.exit(f"rocprofv3 pass {k} failed; see {args.out}/{tag}_{k}.log")
 
     # kernel trace statistics
     stats = {}
@@ -151,11 +160,12 @@ def main():
         kernels[name] = e
     out = {"workload": w, "sources_sha256": sources_hash(), "calibration": calib,
            "commands": {k: " ".join(v) for k, v in cmds.items()}, "kernels": kernels}
-    with open(os.path.join(args.out, f"layer_step_{w}_traffic.json"), "w") as fh:
+    with open(os.path.join(args.out, f"{tag}_traffic.json"), "w") as fh:
         json.dump(out, fh, indent=1)
 
-    lines = [f"# rocprofv3 summary: MSA layer step, workload {w}", "",
-             "Produced by `python profile_step.py --workload " + w + "` on one MI355X, which runs:", ""]
+    lines = [f"# rocprofv3 summary: {title}", "",
+             "Produced by `python profile_step.py --workload " + w + " ".join([""] + only) +
+             "` on one MI355X, which runs:", ""]
     lines += ["    " + " ".join(c if not c.startswith(ROOT) else os.path.relpath(c, ROOT) for c in v)
               .replace(py, "python3") for v in cmds.values()]
     lines += ["", "(rocprofv3 runs from /tmp with TMPDIR=/tmp; raw output is summarised and deleted.)", "",
@@ -168,7 +178,7 @@ def main():
     for name, e in kernels.items():
         lines.append(f"| `{name}` | {e.get('calls', '')} | {e.get('avg_us', 0):.2f} | {e.get('min_us', 0):.2f} | "
                      f"{e.get('max_us', 0):.2f} | {e.get('fetch_bytes', 0):,.0f} | {e.get('write_bytes', 0):,.0f} |")
-    with open(os.path.join(args.out, f"layer_step_{w}.md"), "w") as fh:
+    with open(os.path.join(args.out, f"{tag}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
 

@@ -211,21 +211,22 @@ def test_out_of_range_page_gives_nan_not_a_fault(M):
 
 # ------------------------------------------------------------------ full sizes, sampled
 
-FULL = [("c2", [0, 17, 31]), ("c3", [0, 21, 63]), ("c3_128k", [5, 40]), ("c4", [3, 11]), ("c5", [1])]
+FULL = [("c2", [0, 17, 31], "exact"), ("c3", [0, 21, 63], "exact"), ("c3_128k", [5, 40], "exact"),
+        ("c3_128k", [7], "fp8"), ("c4", [3, 11], "exact"), ("c5", [1], "exact")]
 
 
-@pytest.mark.parametrize("wname,samples", FULL)
-def test_full_size_sampled(M, wname, samples):
-    _say("full-size case", wname, "samples", samples)
+@pytest.mark.parametrize("wname,samples,mode", FULL)
+def test_full_size_sampled(M, wname, samples, mode):
+    _say("full-size case", wname, "samples", samples, mode)
     case = H.DeviceCase(wname)
     w, lay = case.w, case.lay
-    res = H.to_host(H.run_path(case, "exact"))
+    res = H.to_host(H.run_path(case, mode))
     T = w.T
     for b in samples:
         gsel = res["sel"][b]
         # oracle scores over the whole sequence, K/V packed for the oracle's and GPU's blocks
         inp = case.oracle_inputs(b, kv_blocks=None if w.kv_dtype == "f32" else [])
-        ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], T, "exact", w.q_dtype)
+        ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], T, mode, w.q_dtype)
         H.compare_scores(res["block_scores"][b:b + 1], ora["block_scores"])
         H.compare_selection(gsel[None], ora["sel"], ora["block_scores"], ora["near_tie"], inp["seq_lens"], T)
         blocks = np.union1d(gsel[gsel >= 0], ora["sel"][ora["sel"] >= 0])
@@ -234,8 +235,8 @@ def test_full_size_sampled(M, wname, samples):
         for t in rows:
             qq = OM.decode_query(inp["q"][0, t:t + 1], w.q_dtype, 1.0)
             L = int(inp["seq_lens"][0])
-            K = OM.sequence_view(inp["caches"]["k"], inp["kv_table"][0], L)
-            V = OM.sequence_view(inp["caches"]["v"], inp["kv_table"][0], L)
+            K = OM.sequence_view(inp["caches"]["k"], inp["kv_table"][0], L, mode)
+            V = OM.sequence_view(inp["caches"]["v"], inp["kv_table"][0], L, mode)
             # a single query token at position L - T + t: view the sequence as ending there
             Lt = L - T + t + 1
             o, lse = OM.sparse_attention(qq, K[:, :Lt], V[:, :Lt], gsel[t:t + 1], Lt, 1, H.SOFTMAX_SCALE)
