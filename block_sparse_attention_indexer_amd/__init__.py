@@ -7,7 +7,7 @@ library is missing every call raises instead of falling back.
 
 The functions keep the C names: msa_indexer_scores, msa_indexer_topk, msa_block_topk,
 msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_decode_step, msa_cache_insert,
-msa_indexer_scores_shard, msa_shard_topk, msa_topk_merge, msa_pack_fp8,
+msa_indexer_scores_shard, msa_shard_topk, msa_topk_merge, msa_indexer_scores_prefix, msa_pack_fp8,
 msa_unpack_fp8, msa_pack_nvfp4, msa_unpack_nvfp4, msa_workspace_size.
 """
 import ctypes
@@ -21,10 +21,12 @@ MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
 MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
 MSA_MAX_SHARDS = 8
 MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK, MSA_CALL_DECODE_STEP = 0, 1, 2, 3, 4
+MSA_CALL_INDEXER_PREFIX = 5
+MSA_MAX_PREFIX_GROUPS = MSA_MAX_PREFIX_SEQS = 64
 
 EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
             "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
-            "msa_topk_merge",
+            "msa_topk_merge", "msa_indexer_scores_prefix",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -80,6 +82,8 @@ def _lib():
                                          ctypes.c_int, vp, vp],
             "msa_shard_topk": [P(msa_problem), i32, i32, vp, vp, vp, vp],
             "msa_topk_merge": [P(msa_problem), i32, vp, vp, vp, vp],
+            "msa_indexer_scores_prefix": [P(msa_problem), i32, vp, vp, vp, ctypes.c_int, f32, P(msa_cache),
+                                          ctypes.c_int, vp, vp, sz, vp],
             "msa_workspace_size": [P(msa_problem), ctypes.c_int],
             "msa_pack_fp8": [vp, i64, f32, vp, vp],
             "msa_unpack_fp8": [vp, i64, f32, vp, vp],
@@ -171,6 +175,22 @@ def msa_shard_topk(prob, shard, num_shards, block_scores, cand_scores, cand_bloc
 def msa_topk_merge(prob, num_shards, cand_scores, cand_blocks, sel, stream=None):
     _check(_lib().msa_topk_merge(ctypes.byref(prob), int(num_shards), _ptr(cand_scores), _ptr(cand_blocks),
                                  _ptr(sel), _stream(stream)), "msa_topk_merge")
+
+
+def msa_indexer_scores_prefix(prob, group_start, prefix_blocks, idx_q, q_dtype, q_scale, idx_k, dequant,
+                              block_scores, workspace, stream=None):
+    """group_start / prefix_blocks: host sequences of ints (num_groups + 1 and num_groups
+    entries); workspace: a device tensor of at least
+    msa_workspace_size(prob, MSA_CALL_INDEXER_PREFIX) bytes."""
+    n = len(prefix_blocks)
+    gs = (ctypes.c_int32 * (n + 1))(*[int(x) for x in group_start])
+    pb = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in prefix_blocks])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib().msa_indexer_scores_prefix(ctypes.byref(prob), n, ctypes.cast(gs, ctypes.c_void_p),
+                                            ctypes.cast(pb, ctypes.c_void_p), _ptr(idx_q), DTYPES[q_dtype],
+                                            float(q_scale), ctypes.byref(idx_k), DEQUANT[dequant],
+                                            _ptr(block_scores), _ptr(workspace), ws_bytes, _stream(stream)),
+           "msa_indexer_scores_prefix")
 
 
 def msa_block_topk(prob, block_scores, sel, stream=None):

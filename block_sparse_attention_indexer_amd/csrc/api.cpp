@@ -154,6 +154,52 @@ msa_status msa_indexer_scores_shard(const msa_problem* prob, int32_t shard, int3
                                         nullptr, shard, num_shards));
 }
 
+msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups, const int32_t* group_start,
+                                     const int32_t* prefix_blocks, const void* idx_q, msa_dtype q_dtype,
+                                     float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                                     float* block_scores, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
+  if ((st = check_pair(q_dtype, idx_k->dtype)) != MSA_OK) return st;
+  if (idx_k->dtype == MSA_F32 || prob->tokens > 4) return MSA_ERR_UNSUPPORTED;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (idx_q == nullptr || block_scores == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(idx_q, 16) || !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale)) return MSA_ERR_INVALID_ARG;
+  if (num_groups < 0 || num_groups > MSA_MAX_PREFIX_GROUPS) return MSA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (group_start == nullptr || prefix_blocks == nullptr)) return MSA_ERR_INVALID_ARG;
+  msa::PrefixGroups g{};
+  g.n = num_groups;
+  for (int k = 0; num_groups > 0 && k <= num_groups; ++k) {
+    g.start[k] = group_start[k];
+    if (g.start[k] < 0 || g.start[k] > prob->batch) return MSA_ERR_INVALID_ARG;
+    if (k > 0) {
+      const int n = g.start[k] - g.start[k - 1];
+      if (n < 1 || n > MSA_MAX_PREFIX_SEQS) return MSA_ERR_INVALID_ARG;
+    }
+  }
+  for (int k = 0; k < num_groups; ++k) {
+    g.blocks[k] = prefix_blocks[k];
+    if (g.blocks[k] < 0 || g.blocks[k] > prob->max_blocks) return MSA_ERR_INVALID_ARG;
+  }
+  if (workspace == nullptr || !aligned(workspace, 4) ||
+      workspace_bytes < msa_workspace_size(prob, MSA_CALL_INDEXER_PREFIX))
+    return MSA_ERR_WORKSPACE;
+  const msa::ProblemArgs pa = to_args(prob);
+  const msa::CacheArgs ka = to_args(idx_k);
+  const bool fp8 = dequant == MSA_DQ_FP8;
+  int32_t* skip = static_cast<int32_t*>(workspace);
+  hipError_t e = msa::launch_fill_skip(g, prob->batch, skip, stream);
+  if (e == hipSuccess)
+    e = msa::launch_indexer_shared(pa, idx_q, ka, fp8, q_scale * idx_k->tensor_scale, g, block_scores, stream);
+  if (e == hipSuccess)
+    e = msa::launch_indexer(pa, idx_q, (int)q_dtype, q_scale, ka, fp8, block_scores, nullptr, stream, nullptr,
+                            nullptr, 0, 1, skip);
+  return hip_status(e);
+}
+
 msa_status msa_shard_topk(const msa_problem* prob, int32_t shard, int32_t num_shards, const float* block_scores,
                           float* cand_scores, int32_t* cand_blocks, hipStream_t stream) {
   msa_status st = check_problem(prob);
@@ -247,6 +293,8 @@ size_t msa_workspace_size(const msa_problem* prob, msa_call which) {
     return (size_t)prob->batch * sizeof(uint32_t);   // one arrival counter per sequence
   if (which == MSA_CALL_DECODE_STEP)
     return msa::decode_step_workspace_words(prob->batch) * sizeof(uint32_t);
+  if (which == MSA_CALL_INDEXER_PREFIX)
+    return (size_t)prob->batch * sizeof(int32_t);     // shared block count per sequence
   return 0;
 }
 

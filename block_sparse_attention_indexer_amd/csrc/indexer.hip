@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
-    float* __restrict__ block_scores, float* __restrict__ token_scores, int blk_off, int blk_step) {
+    float* __restrict__ block_scores, float* __restrict__ token_scores, int blk_off, int blk_step,
+    const int32_t* __restrict__ skip) {
   constexpr int UPP = 8 / TPU;             // units per page
   static_assert(PPW >= 1 && PPW <= 64, "page ids are held one per lane");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
@@ -147,9 +148,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   // wend and nreal count local blocks (blk_off 0, blk_step 1: the whole context)
   auto gblk = [&](int jj) { return blk_off + blk_step * jj; };
   const int nloc = shard_count(max_blocks, blk_off, blk_step);
-  const int w0 = (blockIdx.x * kDecWaves + wave) * PPW;   // first block of this wave
-  if (w0 >= nloc) return;
-  const int wend = min(w0 + PPW, nloc);
+  const int wbase = (blockIdx.x * kDecWaves + wave) * PPW;
+  const int wend = min(wbase + PPW, nloc);
+  // first block of this wave (local blocks below skip[b] belong to the shared-prefix kernel)
+  const int w0 = skip == nullptr ? wbase : max(wbase, shard_count(skip[b], blk_off, blk_step));
+  if (w0 >= wend) return;
   const int nreal = max(0, min(wend, shard_count(nb, blk_off, blk_step)) - w0);   // blocks with keys
 
   // page ids of this wave's blocks: lane i holds block w0 + i; bad ids read page 0
@@ -302,6 +305,21 @@ __global__ __launch_bounds__(128) void indexer_f32_kernel(
   }
 }
 
+// skip[b] = the shared block count of b's prefix group (0 outside every group).
+__global__ void fill_skip_kernel(PrefixGroups g, int B, int32_t* __restrict__ skip) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int v = 0;
+  for (int k = 0; k < g.n; ++k)
+    if (b >= g.start[k] && b < g.start[k + 1]) v = g.blocks[k];
+  skip[b] = v;
+}
+
+hipError_t launch_fill_skip(const PrefixGroups& g, int B, int32_t* skip, hipStream_t s) {
+  hipLaunchKernelGGL(fill_skip_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s, g, B, skip);
+  return hipGetLastError();
+}
+
 bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mode) {
   return p.T == 1 && k.dtype != 0 && !(k.dtype == 2 && fp8mode);
 }
@@ -309,10 +327,10 @@ bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mod
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
                           float* token_scores, hipStream_t s, int32_t* sel, uint32_t* counters,
-                          int shard, int num_shards) {
+                          int shard, int num_shards, const int32_t* skip) {
   const float sigma = q_scale * k.tensor_scale;
   const int nloc = shard_count(p.max_blocks, shard, num_shards);   // blocks of the shard
-  if (num_shards != 1 && (k.dtype == 0 || p.T > 4 || sel != nullptr)) return hipErrorInvalidValue;
+  if ((num_shards != 1 || skip != nullptr) && (k.dtype == 0 || p.T > 4 || sel != nullptr)) return hipErrorInvalidValue;
   if (nloc == 0) return hipSuccess;   // a shard past the last block has nothing to score
   if (k.dtype == 0) {
     hipLaunchKernelGGL(indexer_f32_kernel, dim3(p.max_blocks, p.B), dim3(128), 0, s,
@@ -338,7 +356,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     const bool ts = token_scores != nullptr;
     const bool fu = sel != nullptr;
     const Scan1Args sa{q8, k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,
-                       block_scores, token_scores, shard, num_shards};
+                       block_scores, token_scores, shard, num_shards, skip};
 #define MSA_DEC1_LAUNCH(KT, TS, FU, PPW, FM)                                                        \
   hipLaunchKernelGGL((indexer_decode1_kernel<KT, TS, FU, PPW, FM>), grid, dim3(kDecWaves * 64), 0, s, sa, sel, \
                      counters)
@@ -366,7 +384,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2),            \
                                             MSA_DEC_PIPE != 0, PPW>), grid, dim3(kDecWaves * 64), 0, s, q8,   \
                      k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T,             \
-                     sigma, block_scores, token_scores, shard, num_shards)
+                     sigma, block_scores, token_scores, shard, num_shards, skip)
 #define MSA_DEC_PPW(KT, FM, TS)                                                                   \
   do {                                                                                            \
     if (ppw == kDecPagesPerWave) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave);                    \

@@ -100,27 +100,52 @@ __device__ __forceinline__ void pf_store(const PfRaw<KT>& r, const uint32_t* lut
   for (int d = 0; d < 8; ++d) *reinterpret_cast<h8*>(row + pf_chunk(8 * half + d)) = v[d];
 }
 
-template <int KT, bool FP8MODE, bool TOKSC>
+// SHARED (shared-prefix decode): the workgroup's rows are the query rows of
+// prefix group blockIdx.z -- sequences [start, start + n), whose first
+// `blocks` logical blocks are the same pages -- taken as n*T row tokens in
+// batch order (row token t = token t % T of sequence start + t / T, which is
+// row start*T + t of idx_q and block_scores, the same linear index as for one
+// sequence).  Only those shared blocks are scored, each page read and
+// dequantised once for all n sequences; each row keeps its own position.
+template <int KT, bool FP8MODE, bool TOKSC, bool SHARED = false, int CHUNK = kPfChunk>
 __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
-    float* __restrict__ block_scores, float* __restrict__ token_scores) {
+    float* __restrict__ block_scores, float* __restrict__ token_scores, PrefixGroups groups) {
+  static_assert(!(SHARED && TOKSC), "per-key scores are not written for shared prefixes");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
   __shared__ __attribute__((aligned(16))) _Float16 tile[2][kPfTileHalves];
-  __shared__ int page_of[kPfChunk];
+  __shared__ int page_of[CHUNK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Q = lane >> 4, n = lane & 15;
-  const int b = blockIdx.z;
+  // b: the sequence of row token 0 (whose block-table row gives the pages); Tn: row tokens
+  const int b = SHARED ? groups.start[blockIdx.z] : (int)blockIdx.z;
+  const int Tn = SHARED ? (groups.start[blockIdx.z + 1] - b) * T : T;
+  const int blim = SHARED ? min(groups.blocks[blockIdx.z], max_blocks) : max_blocks;
   const int t0 = blockIdx.x * kPfTokens;
-  const int c0 = blockIdx.y * kPfChunk;
+  const int c0 = blockIdx.y * CHUNK;
+  if (SHARED && (t0 >= Tn || c0 >= blim)) return;   // the grid covers the largest group
   const int L = seq_lens[b];
-  const int nb = min((L + kBlock - 1) / kBlock, max_blocks);
-  const int t_last = min(T, t0 + kPfTokens) - 1;
-  const int own_first = (L - T + t0) / kBlock;          // own block of the tile's first token
-  const int own_last = (L - T + t_last) / kBlock;
-  const int c_end = min(c0 + kPfChunk, max_blocks);
+  // position of row token t (t < Tn)
+  auto pos = [&](int t) { return SHARED ? seq_lens[b + t / T] - T + t % T : L - T + t; };
+  const int t_last = min(Tn, t0 + kPfTokens) - 1;
+  int own_first, own_last;   // smallest and largest own block of the tile's rows
+  if constexpr (SHARED) {
+    own_first = 0x7FFFFFFF;
+    own_last = -1;
+    for (int t = t0; t <= t_last; ++t) {
+      const int o = pos(t) / kBlock;
+      own_first = min(own_first, o);
+      own_last = max(own_last, o);
+    }
+  } else {
+    own_first = (L - T + t0) / kBlock;          // own block of the tile's first token
+    own_last = (L - T + t_last) / kBlock;
+  }
+  const int nb = SHARED ? blim : min((L + kBlock - 1) / kBlock, max_blocks);
+  const int c_end = min(c0 + CHUNK, blim);
   // blocks [c0, c_comp) of this chunk have visible keys; [c_comp, c_end) get -inf
   const int c_comp = max(c0, min(c_end, min(nb, own_last + 1)));
   const float NEG_INF = -__builtin_inff();
@@ -128,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   const size_t tstride = (size_t)max_blocks * kBlock;
 
   if (FP8MODE) build_fp8_lut(lut);
-  if (tid < kPfChunk) {
+  if (tid < CHUNK) {
     int pg = -1;
     if (c0 + tid < c_comp) {
       pg = table[(size_t)b * max_blocks + c0 + tid];
@@ -146,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const int g = n & 3;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (t < T) {
+      if (t < Tn) {
         const uint2 u = *reinterpret_cast<const uint2*>(idx_q + (((size_t)b * T + t) * kGroups + g) * kHeadDim +
                                                         32 * ks + 8 * Q);
         A[rr][ks] = fp8x8_to_h8(u.x, u.y);
@@ -158,7 +183,10 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   // the position of this lane's query row (row n of each row tile: token n/4)
   int p_of[4];
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) p_of[rr] = L - T + t0 + 4 * (4 * wave + rr) + (n >> 2);
+  for (int rr = 0; rr < 4; ++rr) {
+    const int t = t0 + 4 * (4 * wave + rr) + (n >> 2);
+    p_of[rr] = t < Tn ? pos(t) : -1;   // rows past the last token see nothing
+  }
   // LDS offsets of this lane's operand chunks (dims 32ks + 8Q .. +7)
   int kofs[4];
 #pragma unroll
@@ -170,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const int nblk = c_end - c_comp;
     const int row = e / nblk, i = c_comp + e % nblk;
     const int t = t0 + (row >> 2);
-    if (t < T) block_scores[(((size_t)b * T + t) * kGroups + (row & 3)) * max_blocks + i] = NEG_INF;
+    if (t < Tn) block_scores[(((size_t)b * T + t) * kGroups + (row & 3)) * max_blocks + i] = NEG_INF;
     if (TOKSC && t < T)
       for (int kk = 0; kk < kBlock; ++kk)
         token_scores[(((size_t)b * T + t) * kGroups + (row & 3)) * tstride + (size_t)i * kBlock + kk] = NEG_INF;
@@ -262,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const float mx = quarter_max4(m, lane);              // query row n of row tile Q
     {
       const int t = t0 + 4 * (4 * wave + Q) + (n >> 2);
-      if (t < T) block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i] = bad ? QNAN : mx * sigma;
+      if (t < Tn) block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i] = bad ? QNAN : mx * sigma;
     }
 
     if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves], half_ld);
@@ -278,10 +306,11 @@ hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const
                   (unsigned)((p.max_blocks + kPfChunk - 1) / kPfChunk), (unsigned)p.B);
   const uint8_t* q8 = static_cast<const uint8_t*>(idx_q);
   const bool ts = token_scores != nullptr;
+  const PrefixGroups none{};
 #define MSA_PF_LAUNCH(KT, FM, TS)                                                                \
   hipLaunchKernelGGL((indexer_prefill_kernel<KT, FM, TS>), grid, dim3(256), 0, s, q8, k.data,     \
                      k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, sigma,  \
-                     block_scores, token_scores)
+                     block_scores, token_scores, none)
   if (k.dtype == 1) {
     if (ts) MSA_PF_LAUNCH(1, false, true); else MSA_PF_LAUNCH(1, false, false);
   } else if (fp8mode) {
@@ -290,6 +319,41 @@ hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const
     if (ts) MSA_PF_LAUNCH(2, false, true); else MSA_PF_LAUNCH(2, false, false);
   }
 #undef MSA_PF_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_shared(const ProblemArgs& p, const void* idx_q, const CacheArgs& k, bool fp8mode,
+                                 float sigma, const PrefixGroups& g, float* block_scores, hipStream_t s) {
+  int max_rows = 0, max_blocks = 0;
+  for (int i = 0; i < g.n; ++i) {
+    max_rows = max(max_rows, (g.start[i + 1] - g.start[i]) * p.T);
+    max_blocks = max(max_blocks, min(g.blocks[i], p.max_blocks));
+  }
+  if (g.n == 0 || max_rows == 0 || max_blocks == 0) return hipSuccess;
+  const unsigned gx = (unsigned)((max_rows + kPfTokens - 1) / kPfTokens);
+  // blocks per workgroup: the largest of 16, 8, 4, 2 that still gives every CU two workgroups
+  const int want = 2 * current_cu_count();
+  int chunk = 2;
+  for (int c = 16; c > 2; c /= 2)
+    if ((int64_t)gx * ((max_blocks + c - 1) / c) * g.n >= want) { chunk = c; break; }
+  const dim3 grid(gx, (unsigned)((max_blocks + chunk - 1) / chunk), (unsigned)g.n);
+  const uint8_t* q8 = static_cast<const uint8_t*>(idx_q);
+#define MSA_SH_LAUNCH(KT, FM, C)                                                                      \
+  hipLaunchKernelGGL((indexer_prefill_kernel<KT, FM, false, true, C>), grid, dim3(256), 0, s, q8, k.data, \
+                     k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, sigma,          \
+                     block_scores, nullptr, g)
+#define MSA_SH_CHUNK(KT, FM)                                                 \
+  do {                                                                       \
+    if (chunk == 16) MSA_SH_LAUNCH(KT, FM, 16);                              \
+    else if (chunk == 8) MSA_SH_LAUNCH(KT, FM, 8);                           \
+    else if (chunk == 4) MSA_SH_LAUNCH(KT, FM, 4);                           \
+    else MSA_SH_LAUNCH(KT, FM, 2);                                           \
+  } while (0)
+  if (k.dtype == 1) MSA_SH_CHUNK(1, false);
+  else if (fp8mode) MSA_SH_CHUNK(2, true);
+  else MSA_SH_CHUNK(2, false);
+#undef MSA_SH_CHUNK
+#undef MSA_SH_LAUNCH
   return hipGetLastError();
 }
 

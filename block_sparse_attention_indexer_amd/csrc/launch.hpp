@@ -22,6 +22,15 @@ struct ProblemArgs {
   const int32_t* block_table;
 };
 
+// Shared-prefix groups of one call: sequences [start[k], start[k+1]) share
+// their first blocks[k] logical blocks (the same page ids).  Passed by value.
+constexpr int kMaxPrefixGroups = 64;
+struct PrefixGroups {
+  int n;
+  int start[kMaxPrefixGroups + 1];
+  int blocks[kMaxPrefixGroups];
+};
+
 // Compute units of the current device, queried once per device (256 on MI355X;
 // 256 is also the answer if the query fails).
 inline int current_cu_count() {
@@ -46,11 +55,13 @@ hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int6
 // With sel and counters non-null (only where indexer_can_fuse_topk), the scan also
 // writes the top-16 selection; counters: one zeroed uint32 per sequence, left zeroed.
 // num_shards > 1: only the logical blocks i with i % num_shards == shard are scored
-// (FP8 / NVFP4 keys, T <= 4, no fused selection).
+// (FP8 / NVFP4 keys, T <= 4, no fused selection).  skip (device [B], nullable): the
+// first skip[b] blocks of sequence b are left to another kernel (same restrictions).
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
                           float* token_scores, hipStream_t s, int32_t* sel = nullptr,
-                          uint32_t* counters = nullptr, int shard = 0, int num_shards = 1);
+                          uint32_t* counters = nullptr, int shard = 0, int num_shards = 1,
+                          const int32_t* skip = nullptr);
 
 // Context-parallel selection: the local top-16 of one shard's blocks per row
 // (cand_* [rows][16], best first, padded with NaN / -1), and the owner's merge of
@@ -64,6 +75,13 @@ bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mod
 hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const CacheArgs& k,
                                   bool fp8mode, float sigma, float* block_scores, float* token_scores,
                                   hipStream_t s);
+
+// Shared-prefix decode: the shared blocks of every prefix group scored once for all
+// of the group's query rows (T <= 4); skip: device [B] int32 filled with the shared
+// block count of each sequence (0 outside the groups), for the per-sequence scans.
+hipError_t launch_indexer_shared(const ProblemArgs& p, const void* idx_q, const CacheArgs& k, bool fp8mode,
+                                 float sigma, const PrefixGroups& g, float* block_scores, hipStream_t s);
+hipError_t launch_fill_skip(const PrefixGroups& g, int B, int32_t* skip, hipStream_t s);
 
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s);

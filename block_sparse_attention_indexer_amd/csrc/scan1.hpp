@@ -171,6 +171,9 @@ struct Scan1Args {
   // the whole context.
   int blk_off = 0;
   int blk_step = 1;
+  // Shared-prefix decode: device [B], nullable -- the first skip[b] logical
+  // blocks of sequence b are scored by another kernel and left untouched here.
+  const int32_t* skip = nullptr;
 };
 // Blocks of the shard among the first n logical blocks.
 __host__ __device__ __forceinline__ int shard_count(int n, int off, int step) {
@@ -196,9 +199,11 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   auto gblk = [&](int j) { return a.blk_off + a.blk_step * j; };
   const int nloc = shard_count(a.max_blocks, a.blk_off, a.blk_step);
   const int nb_loc = shard_count(nb, a.blk_off, a.blk_step);
-  const int w0 = (chunk * kDecWaves + wave) * PPW;
-  if (w0 < nloc) {
-  const int wend = min(w0 + PPW, nloc);
+  const int wbase = (chunk * kDecWaves + wave) * PPW;
+  const int wend = min(wbase + PPW, nloc);
+  // local blocks below skip[b] belong to the shared-prefix kernel
+  const int w0 = a.skip == nullptr ? wbase : max(wbase, shard_count(a.skip[b], a.blk_off, a.blk_step));
+  if (w0 < wend) {
   const int nreal = max(0, min(wend, nb_loc) - w0);
 
   int pid = 0;
@@ -302,7 +307,7 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
     else
       *dst = pooled[wave][i][g];
   }
-  }   // w0 < nloc
+  }   // w0 < wend
 
 }
 

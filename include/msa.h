@@ -194,6 +194,37 @@ msa_status msa_shard_topk(const msa_problem* prob, int32_t shard, int32_t num_sh
 msa_status msa_topk_merge(const msa_problem* prob, int32_t num_shards, const float* cand_scores,
                           const int32_t* cand_blocks, int32_t* sel, hipStream_t stream);
 
+/* Shared-prefix decode for the index scan (section "NVFP4 MSA kernel": a
+ * shared-prefix page is dequantised only once for up to 64 requests that
+ * share it).  Sequences [group_start[k], group_start[k+1]) of the batch form
+ * prefix group k; their block-table rows hold the same page ids in their
+ * first prefix_blocks[k] logical blocks (the caller's promise: the pages are
+ * read through the group's first row).  Writes the same block_scores as
+ * msa_indexer_scores: the shared blocks are scored once for the whole group,
+ * as one GEMM over all of its query rows (every shared page read and
+ * dequantised once), each row keeping its own causal position; the other
+ * blocks of every sequence by the decode scan.  Shared-block scores equal
+ * msa_indexer_scores' within fp32 summation order (a different MFMA shape);
+ * the -inf pattern is identical.
+ *   num_groups     0 .. MSA_MAX_PREFIX_GROUPS;
+ *   group_start    HOST [num_groups+1], strictly increasing, within
+ *                  [0, batch]; each group holds 1 .. MSA_MAX_PREFIX_SEQS
+ *                  sequences; sequences outside every group are scanned alone;
+ *   prefix_blocks  HOST [num_groups], each in [0, max_blocks];
+ *   workspace      device, at least msa_workspace_size(prob,
+ *                  MSA_CALL_INDEXER_PREFIX) bytes (4 per sequence), scratch:
+ *                  overwritten by every call, so calls that share it must not
+ *                  overlap.
+ * FP8 or NVFP4 index keys and tokens <= 4, else MSA_ERR_UNSUPPORTED; other
+ * arguments as for msa_indexer_scores (no per-key scores). */
+#define MSA_MAX_PREFIX_GROUPS 64
+#define MSA_MAX_PREFIX_SEQS 64
+msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups, const int32_t* group_start,
+                                     const int32_t* prefix_blocks, const void* idx_q, msa_dtype q_dtype,
+                                     float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                                     float* block_scores, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* Steps 1-3 in one call ("MSA primer": score, max-pool per block, keep the top
  * 16 blocks with the most recent one forced): the same block_scores and sel as
  * msa_indexer_scores followed by msa_block_topk, bit for bit.  For one query
@@ -260,7 +291,8 @@ typedef enum {
   MSA_CALL_TOPK = 1,
   MSA_CALL_ATTN = 2,
   MSA_CALL_INDEXER_TOPK = 3,
-  MSA_CALL_DECODE_STEP = 4
+  MSA_CALL_DECODE_STEP = 4,
+  MSA_CALL_INDEXER_PREFIX = 5
 } msa_call;
 
 /* Bytes of device workspace a call needs for this problem (0 = none).

@@ -202,3 +202,32 @@ def test_dcp_validation(lib):
     assert merge(n=9) == M.MSA_ERR_INVALID_ARG
     assert merge(sel=None) == M.MSA_ERR_INVALID_ARG
     assert merge(prob=_prob(batch=0)) == M.MSA_ERR_INVALID_ARG
+
+
+def test_indexer_prefix_validation(lib):
+    p = _prob(batch=4)
+    ws_need = lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_INDEXER_PREFIX)
+    assert ws_need == 16
+
+    def call(prob=p, gs=(0, 2, 4), pb=(3, 1), ws=4096, wsb=16, cache=None, qd=M.MSA_FP8_E4M3):
+        n = len(pb)
+        g = (ctypes.c_int32 * (n + 1))(*gs) if gs is not None else None
+        b = (ctypes.c_int32 * max(n, 1))(*pb) if pb is not None else None
+        c = _cache() if cache is None else cache
+        return lib.msa_indexer_scores_prefix(ctypes.byref(prob), n, ctypes.cast(g, ctypes.c_void_p) if g else None,
+                                             ctypes.cast(b, ctypes.c_void_p) if b else None, 1024, qd, 1.0,
+                                             ctypes.byref(c), M.MSA_DQ_EXACT, 2048, ws, wsb, None)
+
+    assert call(gs=(0, 2, 2)) == M.MSA_ERR_INVALID_ARG              # empty group
+    assert call(gs=(0, 2, 5)) == M.MSA_ERR_INVALID_ARG              # past the batch
+    assert call(gs=(1, 0, 4)) == M.MSA_ERR_INVALID_ARG              # decreasing
+    assert call(pb=(3, 9)) == M.MSA_ERR_INVALID_ARG                 # more blocks than max_blocks
+    assert call(pb=(-1, 1)) == M.MSA_ERR_INVALID_ARG
+    assert call(gs=None) == M.MSA_ERR_INVALID_ARG
+    assert call(wsb=12) == M.MSA_ERR_WORKSPACE
+    assert call(ws=None) == M.MSA_ERR_WORKSPACE
+    assert call(prob=_prob(batch=4, tokens=5)) == M.MSA_ERR_UNSUPPORTED
+    assert call(cache=_cache(dtype=M.MSA_F32, scales=None), qd=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED
+    big = _prob(batch=70)
+    gs = (0, 65)
+    assert call(prob=big, gs=gs, pb=(1,), wsb=4 * 70) == M.MSA_ERR_INVALID_ARG   # more than 64 sequences

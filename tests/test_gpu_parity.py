@@ -486,3 +486,81 @@ def test_dcp_full_size(M, wname, rows):
     case = H.DeviceCase(wname, keep_fp32=False)
     ref = H.to_host(H.run_path(case, "exact", attention=False))
     _check_dcp(case, ref, *_dcp_run(M, case, 4), 4, rows=rows)
+
+
+# ------------------------------------------------------------------ shared-prefix decode (index scan)
+
+def _share_prefixes(case, groups):
+    """Make every sequence of each group (first, end, blocks) read the same pages in its first
+    `blocks` logical blocks -- those of the group's longest member -- in the host table (the
+    oracle's) and its device copy.  Shorter members use only the blocks they reach."""
+    tab = case.lay.block_table
+    lens = case.lay.seq_lens
+    for s, e, pb in groups:
+        donor = s + int(torch.argmax(lens[s:e]))
+        assert (int(lens[donor]) + 127) // 128 >= pb
+        for b in range(s, e):
+            tab[b, :pb] = tab[donor, :pb]
+    case.d_table = tab.to("cuda")
+
+
+def _prefix_run(M, case, groups, mode):
+    w = case.w
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.full((w.B, w.T, 4, case.lay.max_blocks), 777.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.msa_workspace_size(prob, M.MSA_CALL_INDEXER_PREFIX) // 4, dtype=torch.int32, device="cuda")
+    starts = [g[0] for g in groups] + [groups[-1][1]]
+    M.msa_indexer_scores_prefix(prob, starts, [g[2] for g in groups], case.d_idx_q, w.q_dtype, 1.0,
+                                case.d_caches["idx_k"][2], mode, bs, ws)
+    torch.cuda.synchronize()
+    return bs.cpu().numpy()
+
+
+def _check_prefix(got, ref, groups, B):
+    assert not (got == 777.0).any(), "an entry was not written"
+    skip = np.zeros(B, int)
+    for s, e, pb in groups:
+        skip[s:e] = pb
+    for b in range(B):   # blocks outside the shared prefix: the decode scan's own bits
+        assert np.array_equal(got[b, ..., skip[b]:], ref[b, ..., skip[b]:], equal_nan=True), b
+    H.compare_scores(got, ref)   # shared blocks: same -inf pattern, values within summation order
+
+
+PREFIX = [("tiny_nvfp4", "exact", [(0, 3, 8)]), ("tiny_nvfp4", "fp8", [(0, 2, 12)]),
+          ("tiny_fp8", "exact", [(0, 2, 5)]), ("tiny_spec", "exact", [(0, 2, 10)]),
+          ("tiny_spec", "fp8", [(0, 2, 17)]), ("tiny_t3", "exact", [(0, 1, 4), (1, 3, 12)]),
+          ("tiny_edge", "exact", [(0, 5, 16)]), ("long_rows", "exact", [(0, 1, 2000)])]
+
+
+@pytest.mark.parametrize("wname,mode,groups", PREFIX)
+def test_indexer_prefix(M, wname, mode, groups):
+    """msa_indexer_scores_prefix writes every block score; blocks outside the shared
+    prefixes equal msa_indexer_scores bit for bit, shared ones within fp32 summation
+    order, and all of them match the oracle on the sharing block table (including
+    sequences whose own block lies inside the shared prefix)."""
+    _say("prefix", wname, mode, groups)
+    case = H.HostCase(wname).upload()
+    _share_prefixes(case, groups)
+    w, lay = case.w, case.lay
+    ref = H.to_host(H.run_path(case, mode, attention=False))
+    got = _prefix_run(M, case, groups, mode)
+    _check_prefix(got, ref["block_scores"], groups, w.B)
+    ora = H.oracle_scores(case.caches, case.idx_q, lay.seq_lens.numpy(), lay.block_table.numpy(), w.T, mode,
+                          w.q_dtype)
+    H.compare_scores(got, ora["block_scores"])
+
+
+@pytest.mark.parametrize("wname,groups,samples", [("c3_128k", [(0, 64, 512)], [0, 37, 63]),
+                                                  ("c4", [(0, 8, 1024), (8, 16, 1536)], [5, 12])])
+def test_indexer_prefix_full_size(M, wname, groups, samples):
+    _say("prefix full size", wname, groups)
+    case = H.DeviceCase(wname)
+    _share_prefixes(case, groups)
+    w = case.w
+    ref = H.to_host(H.run_path(case, "exact", attention=False))
+    got = _prefix_run(M, case, groups, "exact")
+    _check_prefix(got, ref["block_scores"], groups, w.B)
+    for b in samples:
+        inp = case.oracle_inputs(b, kv_blocks=[])
+        ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], w.T, "exact", w.q_dtype)
+        H.compare_scores(got[b:b + 1], ora["block_scores"])
