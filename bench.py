@@ -1,21 +1,26 @@
 """Benchmark of the MSA decode layer step on one MI355X.
 
-One step = msa_indexer_scores (index scan and block max-pool) -> msa_block_topk
-(top-16 selection) -> msa_sparse_attn_decode for the whole batch (one MSA
-layer); with --fused the first two run as the single call msa_indexer_topk,
-with --mono all three as the single call msa_decode_step.  Inputs are seeded synthetic data drawn
-and packed on the GPU before the timed region (resident in HBM).
+One step = msa_indexer_scores (index scan and block max-pool) ->
+msa_topk_sparse_attn (each attention workgroup selects its row's top-16 blocks,
+then attends over them) for the whole batch (one MSA layer).  --path calls runs
+the selection as its own launch (msa_block_topk, then msa_sparse_attn_decode);
+--path fused runs the scan and selection as msa_indexer_topk; --path mono runs
+the step as msa_decode_step.  Inputs are seeded synthetic data drawn and packed
+on the GPU before the timed region (resident in HBM).
 
     python bench.py [--steps K] [--warmup W] [--workload c3_128k]
-                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill] [--fused | --mono]
+                    [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill]
+                    [--path select|calls|fused|mono] [--only insert|dcp|prefix]
 
 Prints one JSON line.  ``value`` is layer-steps/s over the timed steps (wall
 clock, synchronised on both sides); ``roofline`` describes the dominant kernel
 (the index-key scan) from HIP events recorded around each of its launches in
 the timed region, on the stream it runs on, and ``traffic`` from the rocprofv3
 counter summary under profiles/ (null once the kernel sources changed);
-``prefill`` times the chunked-prefill workload through the same calls;
-``cpu_baseline`` is the CPU fp64 oracle timed on a bounded sample.
+``dcp``, ``prefix``, ``prefill`` and ``insert`` time the side sections
+(context-parallel shards, shared-prefix scan, the chunked-prefill workload,
+the cache insert); ``cpu_baseline`` is the CPU fp64 oracle timed on a bounded
+sample.
 """
 import argparse
 import json
@@ -43,12 +48,12 @@ def parse():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill section")
-    ap.add_argument("--fused", action="store_true",
-                    help="run the scan and the top-16 as the one call msa_indexer_topk")
-    ap.add_argument("--mono", action="store_true",
-                    help="run the whole step as the one call msa_decode_step")
+    ap.add_argument("--path", default="select", choices=["select", "calls", "fused", "mono"],
+                    help="select: msa_indexer_scores + msa_topk_sparse_attn (the selection inside the "
+                         "attention launch); calls: the three calls msa_indexer_scores, msa_block_topk, "
+                         "msa_sparse_attn_decode; fused: msa_indexer_topk + attention; mono: msa_decode_step")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
-    ap.add_argument("--only", choices=["insert", "dcp"], default=None,
+    ap.add_argument("--only", choices=["insert", "dcp", "prefix"], default=None,
                     help="run one side section alone and print its JSON (for profiling), not the step line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -147,6 +152,17 @@ class Workload:
                               self.bs, self.sel, self.out, None, self.ws_step)
             if ev is not None:
                 ev[1].record()
+            return
+        if path == "select":
+            # the scan, then one launch that selects each row's blocks and attends over them
+            M.msa_indexer_scores(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], dequant,
+                                 self.bs, None)
+            if ev is not None:
+                ev[1].record()
+            M.msa_topk_sparse_attn(self.prob, self.bs, self.sel, self.q, w.q_dtype, 1.0, self.caches["k"][2],
+                                   self.caches["v"][2], dequant, 1.0 / math.sqrt(128.0), self.out, None)
+            if ev is not None and not scan_only:
+                ev[2].record()
             return
         fused = path == "fused"
         if fused:
@@ -422,6 +438,63 @@ def dcp_section(wl, dequant, P=4, steps=20):
             "bit_identical_scores_and_selection": exact}
 
 
+def prefix_section(wl, dequant, shared_blocks=512, steps=20):
+    """Shared-prefix decode of the index scan: every sequence of the decode workload
+    reads the same pages in its first `shared_blocks` blocks (one prefix group per 64
+    sequences).  Times msa_indexer_scores on that block table (each sequence scans
+    the shared pages itself; repeated pages may hit in L2 / Infinity Cache) against
+    msa_indexer_scores_prefix (shared blocks scored once per group), both bracketed by
+    HIP events.  Algorithmic bytes of the prefix call: the shared index keys once per
+    group, every other visible key once, queries and scores."""
+    import torch
+    M, w, lay = wl.M, wl.w, wl.lay
+    B, T, maxb = w.B, w.T, lay.max_blocks
+    lens = [int(x) for x in lay.seq_lens]
+    sb = min(shared_blocks, min((L - T) // 128 for L in lens))
+    tab = lay.block_table.clone()
+    groups = [(s_, min(s_ + 64, B)) for s_ in range(0, B, 64)]
+    for s_, e_ in groups:
+        tab[s_:e_, :sb] = tab[s_, :sb]
+    d_tab = tab.to("cuda")
+    prob = M.problem(wl.seq, d_tab, T)
+    ik = wl.caches["idx_k"][2]
+    bs_u = torch.empty_like(wl.bs)
+    bs_p = torch.empty_like(wl.bs)
+    ws = torch.empty(M.msa_workspace_size(prob, M.MSA_CALL_INDEXER_PREFIX) // 4, dtype=torch.int32, device="cuda")
+    starts = [g[0] for g in groups] + [groups[-1][1]]
+    blocks = [sb] * len(groups)
+    for _ in range(3):
+        M.msa_indexer_scores(prob, wl.idx_q, w.q_dtype, 1.0, ik, dequant, bs_u, None)
+        M.msa_indexer_scores_prefix(prob, starts, blocks, wl.idx_q, w.q_dtype, 1.0, ik, dequant, bs_p, ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record()
+        M.msa_indexer_scores(prob, wl.idx_q, w.q_dtype, 1.0, ik, dequant, bs_u, None)
+        ev[k][1].record()
+        M.msa_indexer_scores_prefix(prob, starts, blocks, wl.idx_q, w.q_dtype, 1.0, ik, dequant, bs_p, ws)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    t_u = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_p = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    fin = torch.isfinite(bs_u)
+    same_inf = bool(torch.equal(torch.isneginf(bs_u), torch.isneginf(bs_p)))
+    rel = float(((bs_p[fin] - bs_u[fin]).abs() / (1 + bs_u[fin].abs())).max()) if bool(fin.any()) else 0.0
+    qb = 4 if w.q_dtype == "f32" else 1
+    other = B * T * 4 * (128 * qb + maxb * 4)
+    keys_shared = len(groups) * sb * 128 + sum(L - sb * 128 for L in lens)
+    b_prefix = keys_shared * ROW_BYTES[w.kv_dtype] + other
+    b_plain = sum(lens) * ROW_BYTES[w.kv_dtype] + other
+    return {"workload": w.name, "shared_blocks": sb, "groups": len(groups),
+            "kernels": {"shared": f"msa::indexer_prefill_kernel<{2 if w.kv_dtype == 'nvfp4' else 1}, "
+                                  f"{str(dequant == 'fp8' and w.kv_dtype == 'nvfp4').lower()}, false, true, C>",
+                        "rest": indexer_kernel_name(w, dequant, max_blocks=maxb)},
+            "unshared_scan_ms": round(t_u, 5), "prefix_scan_ms": round(t_p, 5),
+            "speedup": round(t_u / t_p, 3),
+            "prefix_algorithmic_bytes": int(b_prefix), "unshared_algorithmic_bytes": int(b_plain),
+            "prefix_GBps": round(b_prefix / (t_p * 1e-3) / 1e9, 1),
+            "max_rel_diff_vs_unshared": rel, "same_inf_pattern": same_inf}
+
+
 def cpu_baseline(wl, dequant, sample):
     """The oracle on `sample` sequences of the same workload, packed by the
     oracle itself from the fp32 sources; timed from decode to attention."""
@@ -482,23 +555,24 @@ def main():
     if args.only == "insert":
         print(json.dumps({"insert": insert_section(args.seed, steps=args.steps)}), flush=True)
         return
-    if args.only == "dcp":
+    if args.only in ("dcp", "prefix"):
         wl = Workload(args.workload, args.seed)
-        print(json.dumps({"dcp": dcp_section(wl, args.dequant, steps=args.steps)}), flush=True)
+        fn = dcp_section if args.only == "dcp" else prefix_section
+        print(json.dumps({args.only: fn(wl, args.dequant, steps=args.steps)}), flush=True)
         return
     sample = [] if args.no_cpu_baseline else list(range(0, 64, 64 // max(1, args.cpu_sample)))[: args.cpu_sample]
     wl = Workload(args.workload, args.seed, keep_sequences=sample)
     w = wl.w
     print(f"[bench] workload {w.name} ready: B={w.B} T={w.T} pages={wl.lay.num_pages}", file=sys.stderr, flush=True)
 
-    path = "mono" if args.mono else "fused" if args.fused else "calls"
+    path = args.path
     for _ in range(args.warmup):
         wl.step(args.dequant, path=path)
     torch.cuda.synchronize()
 
     K = args.steps
     fused = path == "fused"
-    ncalls = {"calls": 3, "fused": 2, "mono": 1}[path]
+    ncalls = {"calls": 3, "fused": 2, "mono": 1, "select": 2}[path]
     # Timed region: K whole steps; HIP events on the launching stream bracket only the
     # first call (the index scan, with the selection when fused: the roofline kernel),
     # so the step itself runs undisturbed.
@@ -550,12 +624,15 @@ def main():
         "bytes_per_step": {"indexer": b_idx, "topk": b_topk, "attention": b_attn},
         "call_ms": ({"decode_step": round(idx_ms, 5)} if path == "mono" else
                     {"indexer_topk": round(idx_ms, 5), "attention": round(float(per_call[1]), 5)} if fused else
+                    {"indexer": round(idx_ms, 5), "topk_attention": round(float(per_call[1]), 5)}
+                    if path == "select" else
                     {"indexer": round(idx_ms, 5), "topk": round(float(per_call[1]), 5),
                      "attention": round(float(per_call[2]), 5)}),
         "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, path, wl.lay.max_blocks) +
                      {"mono": " (the whole step: scan, pool, top-16, attention)",
                       "fused": " (index-key scan + block max-pool + top-16)",
-                      "calls": " (index-key scan + block max-pool)"}[path],
+                      "calls": " (index-key scan + block max-pool)",
+                      "select": " (index-key scan + block max-pool)"}[path],
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, path,
@@ -564,6 +641,7 @@ def main():
     }
     if w.T <= 4 and w.kv_dtype != "f32":
         out["dcp"] = dcp_section(wl, args.dequant)
+        out["prefix"] = prefix_section(wl, args.dequant)
     if not args.no_prefill and args.workload != "c5":
         out["prefill"] = prefill_section(args.dequant, args.seed)
         out["insert"] = insert_section(args.seed)

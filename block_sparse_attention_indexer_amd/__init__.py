@@ -7,7 +7,8 @@ library is missing every call raises instead of falling back.
 
 The functions keep the C names: msa_indexer_scores, msa_indexer_topk, msa_block_topk,
 msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_decode_step, msa_cache_insert,
-msa_indexer_scores_shard, msa_shard_topk, msa_topk_merge, msa_indexer_scores_prefix, msa_pack_fp8,
+msa_indexer_scores_shard, msa_shard_topk, msa_topk_merge, msa_indexer_scores_prefix,
+msa_topk_sparse_attn, msa_pack_fp8,
 msa_unpack_fp8, msa_pack_nvfp4, msa_unpack_nvfp4, msa_workspace_size.
 """
 import ctypes
@@ -26,7 +27,7 @@ MSA_MAX_PREFIX_GROUPS = MSA_MAX_PREFIX_SEQS = 64
 
 EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
             "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
-            "msa_topk_merge", "msa_indexer_scores_prefix",
+            "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -84,6 +85,8 @@ def _lib():
             "msa_topk_merge": [P(msa_problem), i32, vp, vp, vp, vp],
             "msa_indexer_scores_prefix": [P(msa_problem), i32, vp, vp, vp, ctypes.c_int, f32, P(msa_cache),
                                           ctypes.c_int, vp, vp, sz, vp],
+            "msa_topk_sparse_attn": [P(msa_problem), vp, vp, vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
+                                     ctypes.c_int, f32, vp, vp, vp],
             "msa_workspace_size": [P(msa_problem), ctypes.c_int],
             "msa_pack_fp8": [vp, i64, f32, vp, vp],
             "msa_unpack_fp8": [vp, i64, f32, vp, vp],
@@ -191,6 +194,14 @@ def msa_indexer_scores_prefix(prob, group_start, prefix_blocks, idx_q, q_dtype, 
                                             float(q_scale), ctypes.byref(idx_k), DEQUANT[dequant],
                                             _ptr(block_scores), _ptr(workspace), ws_bytes, _stream(stream)),
            "msa_indexer_scores_prefix")
+
+
+def msa_topk_sparse_attn(prob, block_scores, sel, q, q_dtype, q_scale, k, v, dequant, softmax_scale, out,
+                         lse=None, stream=None):
+    _check(_lib().msa_topk_sparse_attn(ctypes.byref(prob), _ptr(block_scores), _ptr(sel), _ptr(q), DTYPES[q_dtype],
+                                       float(q_scale), ctypes.byref(k), ctypes.byref(v), DEQUANT[dequant],
+                                       float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "msa_topk_sparse_attn")
 
 
 def msa_block_topk(prob, block_scores, sel, stream=None):

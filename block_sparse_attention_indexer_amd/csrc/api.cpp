@@ -59,7 +59,8 @@ msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_
 msa_status attention(const msa_problem* prob, const void* q, msa_dtype q_dtype, float q_scale,
                      const msa_cache* k, const msa_cache* v, msa_dequant dequant,
                      const int32_t* sel, float softmax_scale, float* out, float* lse,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream, int max_t) {
+                     void* workspace, size_t workspace_bytes, hipStream_t stream, int max_t,
+                     const float* block_scores = nullptr) {
   msa_status st = check_problem(prob);
   if (st != MSA_OK) return st;
   if (prob->tokens > max_t) return MSA_ERR_UNSUPPORTED;
@@ -71,12 +72,14 @@ msa_status attention(const msa_problem* prob, const void* q, msa_dtype q_dtype, 
   if (q == nullptr || sel == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(sel, 4) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
     return MSA_ERR_INVALID_ARG;
+  if (block_scores != nullptr && !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;
   if (!good_scale(q_scale) || !good_scale(softmax_scale)) return MSA_ERR_INVALID_ARG;
   if (msa_workspace_size(prob, MSA_CALL_ATTN) > workspace_bytes) return MSA_ERR_WORKSPACE;
   (void)workspace;
   return hip_status(msa::launch_attention(to_args(prob), q, (int)q_dtype, q_scale, to_args(k),
                                           to_args(v), dequant == MSA_DQ_FP8, sel, softmax_scale,
-                                          out, lse, stream));
+                                          out, lse, stream, block_scores,
+                                          block_scores != nullptr ? const_cast<int32_t*>(sel) : nullptr));
 }
 
 }  // namespace
@@ -133,6 +136,15 @@ msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, in
   if (block_scores == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
   if (!aligned(block_scores, 4) || !aligned(sel, 4)) return MSA_ERR_INVALID_ARG;
   return hip_status(msa::launch_topk(to_args(prob), block_scores, sel, stream));
+}
+
+msa_status msa_topk_sparse_attn(const msa_problem* prob, const float* block_scores, int32_t* sel, const void* q,
+                                msa_dtype q_dtype, float q_scale, const msa_cache* k, const msa_cache* v,
+                                msa_dequant dequant, float softmax_scale, float* out, float* lse,
+                                hipStream_t stream) {
+  if (block_scores == nullptr) return MSA_ERR_INVALID_ARG;
+  return attention(prob, q, q_dtype, q_scale, k, v, dequant, sel, softmax_scale, out, lse, nullptr, 0, stream,
+                   1 << 30, block_scores);
 }
 
 msa_status msa_indexer_scores_shard(const msa_problem* prob, int32_t shard, int32_t num_shards,
@@ -270,10 +282,11 @@ msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype
     return hip_status(msa::launch_decode_step(pa, idx_q, idx_q_scale, ia, q, q_scale, ka, va, softmax_scale,
                                               block_scores, sel, out, lse, static_cast<uint32_t*>(workspace),
                                               stream));
+  // otherwise: the scan, then one launch that selects each row's blocks and attends
   hipError_t e = msa::launch_indexer(pa, idx_q, (int)idx_q_dtype, idx_q_scale, ia, fp8, block_scores, nullptr, stream);
-  if (e == hipSuccess) e = msa::launch_topk(pa, block_scores, sel, stream);
   if (e == hipSuccess)
-    e = msa::launch_attention(pa, q, (int)q_dtype, q_scale, ka, va, fp8, sel, softmax_scale, out, lse, stream);
+    e = msa::launch_attention(pa, q, (int)q_dtype, q_scale, ka, va, fp8, sel, softmax_scale, out, lse, stream,
+                              block_scores, sel);
   return hip_status(e);
 }
 

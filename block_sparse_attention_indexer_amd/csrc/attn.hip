@@ -40,9 +40,11 @@ namespace msa {
 #ifndef MSA_ATTN_MANY_WG
 #define MSA_ATTN_MANY_WG 3
 #endif
-template <int KT, bool FP8MODE, int WAVES>
+// SELECT: each workgroup first selects its row's 16 blocks from the block
+// scores (msa_topk_sparse_attn), so the selection needs no launch of its own.
+template <int KT, bool FP8MODE, int WAVES, bool SELECT = false>
 __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : MSA_ATTN_MANY_WG) void attn_mfma_kernel(AttnArgs a) {
-  attend_row<KT, FP8MODE, WAVES, false>(a, blockIdx.x);
+  attend_row<KT, FP8MODE, WAVES, false, SELECT>(a, blockIdx.x);
 }
 
 // fp32 queries and caches: plain fp32 arithmetic on the vector ALUs.  One
@@ -111,8 +113,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
 hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, float q_scale,
                             const CacheArgs& k, const CacheArgs& v, bool fp8mode,
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
-                            hipStream_t s) {
+                            hipStream_t s, const float* block_scores, int32_t* sel_out) {
   const unsigned rows = (unsigned)((int64_t)p.B * p.T * kGroups);
+  const bool select = block_scores != nullptr;
+  if (select && k.dtype == 0) {   // the fp32 kernel takes a selection: select first
+    const hipError_t e = launch_topk(p, block_scores, sel_out, s);
+    if (e != hipSuccess) return e;
+    sel = sel_out;
+  }
   if (k.dtype == 0) {
     const float c_nat = softmax_scale * q_scale * k.tensor_scale;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(rows), dim3(256), 0, s, (const float*)q, c_nat,
@@ -128,16 +136,20 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   // resident rows per CU.  The choice depends only on the row count.
   const bool many = rows >= kAttnManyRows;
   const AttnArgs aa{q8, c_log2, k.data, k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale,
-                    sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse};
-#define MSA_ATTN_LAUNCH(KT, FM)                                                                    \
-  if (many)                                                                                        \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4>), dim3(rows), dim3(256), 0, s, aa);             \
-  else                                                                                             \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16>), dim3(rows), dim3(1024), 0, s, aa)
+                    sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse, block_scores, sel_out};
+#define MSA_ATTN_LAUNCH2(KT, FM, SE)                                                                 \
+  if (many)                                                                                          \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4, SE>), dim3(rows), dim3(256), 0, s, aa);           \
+  else                                                                                               \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16, SE>), dim3(rows), dim3(1024), 0, s, aa)
+#define MSA_ATTN_LAUNCH(KT, FM)                  \
+  if (select) { MSA_ATTN_LAUNCH2(KT, FM, true); } \
+  else { MSA_ATTN_LAUNCH2(KT, FM, false); }
   if (k.dtype == 1) { MSA_ATTN_LAUNCH(1, false); }
   else if (fp8mode) { MSA_ATTN_LAUNCH(2, true); }
   else { MSA_ATTN_LAUNCH(2, false); }
 #undef MSA_ATTN_LAUNCH
+#undef MSA_ATTN_LAUNCH2
   return hipGetLastError();
 }
 

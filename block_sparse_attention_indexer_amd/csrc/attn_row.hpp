@@ -32,6 +32,7 @@
 // accumulation; P V carries P's f16 rounding.
 #pragma once
 #include "common.hpp"
+#include "select.hpp"
 
 namespace msa {
 
@@ -206,6 +207,10 @@ struct AttnArgs {
   int T;
   float* out;
   float* lse;
+  // SELECT: the row's block scores are read from here and its selection is
+  // written to sel_out (sel is not read)
+  const float* block_scores = nullptr;
+  int32_t* sel_out = nullptr;
 };
 
 // Attention of one row (b*T + t)*4 + g by a workgroup of WAVES waves (all
@@ -213,8 +218,10 @@ struct AttnArgs {
 // takes selected blocks w, w + WAVES, ... and keeps a running (max, sum, O)
 // over them (online softmax); the WAVES states merge at the end.
 // COHERENT_SEL: the selection was written by another workgroup of the
-// running kernel (device-coherent loads).
-template <int KT, bool FP8MODE, int WAVES, bool COHERENT_SEL>
+// running kernel (device-coherent loads).  SELECT: the workgroup first
+// selects the row's blocks itself from args.block_scores (select_row, the
+// same rule and keys as msa_block_topk) and writes them to args.sel_out.
+template <int KT, bool FP8MODE, int WAVES, bool COHERENT_SEL, bool SELECT = false>
 __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
   const uint8_t* __restrict__ q = args.q;
   const float c_log2 = args.c_log2;
@@ -249,17 +256,28 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
   const int Q = lane >> 4, j = lane & 15;
   const float NEG_INF = -__builtin_inff();
 
-  // independent loads first: length, this wave's blocks, the query
+  // independent loads first: length, the query, this wave's blocks
   const int L = seq_lens[b];
-  int blks[kTopK / WAVES];
-#pragma unroll
-  for (int u = 0; u < kTopK / WAVES; ++u) {
-    const int32_t* sp = sel + (size_t)row * kTopK + w + u * WAVES;
-    blks[u] = COHERENT_SEL ? __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sp;
-  }
   const uint4* qsrc =
       reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
   const uint4 qu0 = qsrc[0], qu1 = qsrc[1];
+  int blks[kTopK / WAVES];
+  if constexpr (SELECT) {
+    __shared__ int32_t sel_sh[kTopK];
+    const int own = max(0, min((L - T + t) / kBlock, max_blocks - 1));
+    select_row<WAVES * 64, kMaxBlocksSelect / (WAVES * 64)>(args.block_scores + (size_t)row * max_blocks, own,
+                                                            sel_sh);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kTopK / WAVES; ++u) blks[u] = sel_sh[w + u * WAVES];
+    if (threadIdx.x < kTopK) args.sel_out[(size_t)row * kTopK + threadIdx.x] = sel_sh[threadIdx.x];
+  } else {
+#pragma unroll
+    for (int u = 0; u < kTopK / WAVES; ++u) {
+      const int32_t* sp = sel + (size_t)row * kTopK + w + u * WAVES;
+      blks[u] = COHERENT_SEL ? __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sp;
+    }
+  }
   if (threadIdx.x == 0) nan_sh = 0;
   if (FP8MODE) build_fp8_lut(lut);
   __syncthreads();

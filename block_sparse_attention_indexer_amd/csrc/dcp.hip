@@ -13,70 +13,14 @@
 // the 15 best older blocks overall, since each of those is among its own
 // shard's 16 best -- and reports them ascending, as msa_block_topk does.
 //
-// Both kernels turn (score, block) into one distinct 64-bit key
-// (order-preserving score bits over the complemented block id), narrow a key
-// prefix by most-significant-digit radix select until exactly `need` keys
-// lie at or above it, then rank the winners.
+// Both kernels rank (score, block) pairs by select.hpp's 64-bit keys and
+// narrow them with its radix cut, then rank the winners.
 #include "common.hpp"
 #include "launch.hpp"
 #include "scan1.hpp"
+#include "select.hpp"
 
 namespace msa {
-
-__device__ __forceinline__ uint64_t dcp_key(float score, int block) {
-  return ((uint64_t)order_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)block);
-}
-__device__ __forceinline__ int dcp_key_block(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-
-// The workgroup's keys (E per thread of NT, 0 = none, others distinct) hold at
-// least `need` >= 1 keys.  Returns prefix/mask such that exactly `need` keys
-// satisfy (key & mask) >= prefix.  Every thread of the workgroup calls it.
-template <int NT, int E>
-__device__ void radix_cut(const uint64_t (&key)[E], uint32_t need, uint64_t& prefix, uint64_t& mask) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t pick[3];
-  const int tid = threadIdx.x, lane = tid & 63;
-  prefix = 0;
-  mask = 0;
-#pragma unroll 1
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] != 0ull && (key[e] & mask) == prefix) atomicAdd(&hist[(uint32_t)(key[e] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (tid < 64) {
-      // lane l holds bins 4l..4l+3; find digit d with above(d) < need <= above(d) + hist[d]
-      uint32_t h[4], sum = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) { h[u] = hist[4 * lane + u]; sum += h[u]; }
-      uint32_t incl = sum;             // suffix sum over lanes >= this one
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(incl, off);
-        if (lane + off < 64) incl += o;
-      }
-      uint32_t above = incl - sum;
-#pragma unroll
-      for (int u = 3; u >= 0; --u) {
-        if (above < need && need <= above + h[u]) {
-          pick[0] = 4 * lane + u;
-          pick[1] = above;
-          pick[2] = h[u];
-        }
-        above += h[u];
-      }
-    }
-    __syncthreads();
-    const uint32_t d = pick[0], a = pick[1], c = pick[2];
-    prefix |= (uint64_t)d << shift;
-    mask |= 255ull << shift;
-    need -= a;
-    // pick is written again only after two more barriers
-    if (c == need) break;   // uniform across the workgroup
-  }
-}
 
 // One workgroup per row: the shard's 16 best blocks older than the own block.
 constexpr int kShardThreads = 256;
@@ -99,7 +43,7 @@ __global__ __launch_bounds__(kShardThreads) void shard_topk_kernel(
   for (int e = 0; e < E; ++e) {
     const int j = tid + e * kShardThreads;
     const int blk = shard + num_shards * j;
-    key[e] = j < nc ? dcp_key(S[blk], blk) : 0ull;
+    key[e] = j < nc ? select_key(S[blk], blk) : 0ull;
   }
   const uint32_t need = (uint32_t)min(nc, kTopK);
   uint64_t prefix = 0, mask = 0;   // nc <= 16: every candidate wins
@@ -122,7 +66,7 @@ __global__ __launch_bounds__(kShardThreads) void shard_topk_kernel(
     float* cs = cand_scores + row * kTopK;
     int32_t* cb = cand_blocks + row * kTopK;
     if (mine_ok) {
-      const int blk = dcp_key_block(mine);
+      const int blk = select_key_block(mine);
       cs[rank] = S[blk];
       cb[rank] = blk;
     } else if (tid < kTopK) {
@@ -164,7 +108,7 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(
       const size_t at = ((size_t)sh * rows + row) * kTopK + (c % kTopK);
       const int blk = cand_blocks[at];
       // only older blocks are candidates; anything else is ignored (the own block is added below)
-      if (blk >= 0 && blk < own) key[e] = dcp_key(cand_scores[at], blk);
+      if (blk >= 0 && blk < own) key[e] = select_key(cand_scores[at], blk);
     }
     nvalid += (uint32_t)__popcll(__ballot(key[e] != 0ull));
   }
@@ -177,7 +121,7 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(
   for (int e = 0; e < E; ++e) {
     if (key[e] != 0ull && (key[e] & mask) >= prefix) {
       const uint32_t slot = atomicAdd(&n_won, 1u);
-      if (slot < need) won[slot] = dcp_key_block(key[e]);
+      if (slot < need) won[slot] = select_key_block(key[e]);
     }
   }
   __syncthreads();

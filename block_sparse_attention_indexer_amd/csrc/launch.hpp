@@ -86,10 +86,12 @@ hipError_t launch_fill_skip(const PrefixGroups& g, int B, int32_t* skip, hipStre
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s);
 
+// With block_scores non-null the selection is made inside the attention launch
+// (each workgroup selects its own row; written to sel_out) and sel is not read.
 hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, float q_scale,
                             const CacheArgs& k, const CacheArgs& v, bool fp8mode,
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
-                            hipStream_t s);
+                            hipStream_t s, const float* block_scores = nullptr, int32_t* sel_out = nullptr);
 
 // Quantise the fp32 rows x [B, T, heads, 128] of the T new tokens and write them
 // into their slots of cache c (heads = c's heads per page).

@@ -225,6 +225,22 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
                                      float* block_scores, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* Steps 3+4 in one launch ("MSA primer": keep the top 16 blocks with the most
+ * recent one forced, then attend exactly over them): what msa_block_topk
+ * followed by msa_sparse_attn_decode / _prefill computes, with sel written
+ * as msa_block_topk writes it (bit for bit) and out / lse as the attention
+ * call writes them given that selection (bit for bit).  Each attention
+ * workgroup first selects its own row's blocks from block_scores, so the
+ * selection needs no launch of its own.  Any T >= 1; fp32 caches run the two
+ * kernels back to back.
+ *   block_scores  device [B][T][4][max_blocks], as msa_indexer_scores writes;
+ *   sel           device out [B][T][4][16];
+ * other arguments as for msa_sparse_attn_decode (no workspace). */
+msa_status msa_topk_sparse_attn(const msa_problem* prob, const float* block_scores, int32_t* sel, const void* q,
+                                msa_dtype q_dtype, float q_scale, const msa_cache* k, const msa_cache* v,
+                                msa_dequant dequant, float softmax_scale, float* out, float* lse,
+                                hipStream_t stream);
+
 /* Steps 1-3 in one call ("MSA primer": score, max-pool per block, keep the top
  * 16 blocks with the most recent one forced): the same block_scores and sel as
  * msa_indexer_scores followed by msa_block_topk, bit for bit.  For one query
@@ -251,8 +267,8 @@ msa_status msa_indexer_topk(const msa_problem* prob, const void* idx_q, msa_dtyp
  * (tokens == 1) with FP8 caches, or NVFP4 caches read exactly, and index keys
  * of the same dtype as K/V, one persistent kernel does all of it: as soon as
  * a sequence's blocks are scored and selected, its rows are attended while
- * other sequences are still being scanned.  Otherwise the three kernels run
- * back to back.
+ * other sequences are still being scanned.  Otherwise the scan runs, then
+ * one launch selects and attends (as msa_topk_sparse_attn).
  *   idx_q, idx_q_dtype, idx_q_scale, idx_k  as for msa_indexer_scores;
  *   q, q_dtype, q_scale, k, v, softmax_scale, out, lse  as for
  *                msa_sparse_attn_decode (k, v: same dtype);

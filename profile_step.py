@@ -15,7 +15,8 @@ counter reads for the 512 MiB elementwise copy that bench.py launches with
 bytes are calibrated HBM bytes per launch.  Writes, into --out:
 
 With --only, bench.py runs that side section alone (bench.py --only ...) and the
-files are named insert_rows_c5_chunk_and_c3_decode.* or dcp_<workload>.* instead.
+files are named insert_rows_c5_chunk_and_c3_decode.*, dcp_<workload>.* or prefix_<workload>.*
+instead.
 
   layer_step_<workload>.md           per-kernel launches and durations, calibrated HBM
                           bytes per launch, the calibration factors and the
@@ -97,7 +98,7 @@ def read_counters(d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="c3_128k")
-    ap.add_argument("--only", choices=["insert", "dcp"], default=None)
+    ap.add_argument("--only", choices=["insert", "dcp", "prefix"], default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
@@ -108,10 +109,12 @@ def main():
     shutil.rmtree(raw, ignore_errors=True)
 
     only = ["--only", args.only] if args.only else []
-    tag = {None: f"layer_step_{w}", "insert": "insert_rows_c5_chunk_and_c3_decode", "dcp": f"dcp_{w}"}[args.only]
+    tag = {None: f"layer_step_{w}", "insert": "insert_rows_c5_chunk_and_c3_decode", "dcp": f"dcp_{w}",
+           "prefix": f"prefix_{w}"}[args.only]
     title = {None: f"MSA layer step, workload {w}",
              "insert": "quantise-and-insert (msa_cache_insert), c5 prefill chunk and c3_128k decode token",
-             "dcp": f"single-GPU DCP (4 shard scans, local top-16s, merge), workload {w}"}[args.only]
+             "dcp": f"single-GPU DCP (4 shard scans, local top-16s, merge), workload {w}",
+             "prefix": f"shared-prefix index scan against the unshared scan, workload {w}"}[args.only]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(raw, "trace"), "-o", "run",
                  "-f", "csv", "--", py, bench, "--workload", w, "--steps", "10", "--warmup", "2",
                  "--no-cpu-baseline", "--no-prefill"] + only

@@ -231,3 +231,21 @@ def test_indexer_prefix_validation(lib):
     big = _prob(batch=70)
     gs = (0, 65)
     assert call(prob=big, gs=gs, pb=(1,), wsb=4 * 70) == M.MSA_ERR_INVALID_ARG   # more than 64 sequences
+
+
+def test_topk_sparse_attn_validation(lib):
+    p = _prob()
+    k = _cache(heads=4)
+
+    def call(bs=2048, sel=4096, q=8192, out=16384, kk=None, vv=None, prob=p):
+        kk = k if kk is None else kk
+        vv = k if vv is None else vv
+        return lib.msa_topk_sparse_attn(ctypes.byref(prob), bs, sel, q, M.MSA_FP8_E4M3, 1.0, ctypes.byref(kk),
+                                        ctypes.byref(vv), M.MSA_DQ_EXACT, 0.088, out, None, None)
+
+    assert call(bs=None) == M.MSA_ERR_INVALID_ARG
+    assert call(bs=2050) == M.MSA_ERR_INVALID_ARG
+    assert call(sel=None) == M.MSA_ERR_INVALID_ARG
+    assert call(out=16388) == M.MSA_ERR_INVALID_ARG
+    assert call(kk=_cache(heads=1)) == M.MSA_ERR_INVALID_ARG
+    assert call(vv=_cache(heads=4, dtype=M.MSA_FP8_E4M3, scales=None)) == M.MSA_ERR_UNSUPPORTED

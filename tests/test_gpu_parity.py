@@ -564,3 +564,46 @@ def test_indexer_prefix_full_size(M, wname, groups, samples):
         inp = case.oracle_inputs(b, kv_blocks=[])
         ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], w.T, "exact", w.q_dtype)
         H.compare_scores(got[b:b + 1], ora["block_scores"])
+
+
+# ------------------------------------------------------------------ selection inside the attention launch
+
+@pytest.mark.parametrize("wname,mode", [("tiny_nvfp4", "exact"), ("tiny_nvfp4", "fp8"), ("tiny_fp8", "exact"),
+                                        ("tiny_spec", "exact"), ("tiny_edge", "exact"), ("tiny_prefill", "exact"),
+                                        ("tiny_prefill_many", "exact"), ("long_rows", "exact"), ("c1", "exact"),
+                                        ("tiny_t3", "exact")])
+def test_topk_sparse_attn_equals_the_two_calls(M, wname, mode):
+    """msa_topk_sparse_attn writes msa_block_topk's selection and the attention call's
+    out / lse for it, bit for bit (decode and prefill forms, fp32 fallback)."""
+    _say("topk_sparse_attn", wname, mode)
+    case = H.HostCase(wname).upload()
+    w, lay = case.w, case.lay
+    ref = H.to_host(H.run_path(case, mode))
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.from_numpy(ref["block_scores"]).cuda()
+    sel = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.T, 64), dtype=torch.float32, device="cuda")
+    M.msa_topk_sparse_attn(prob, bs, sel, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2], case.d_caches["v"][2],
+                           mode, H.SOFTMAX_SCALE, out, lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref["sel"])
+    assert np.array_equal(out.cpu().numpy(), ref["out"], equal_nan=True)
+    assert np.array_equal(lse.cpu().numpy(), ref["lse"], equal_nan=True)
+
+
+def test_topk_sparse_attn_full_size(M):
+    _say("topk_sparse_attn full size c3_128k")
+    case = H.DeviceCase("c3_128k", keep_fp32=False)
+    w = case.w
+    ref = H.to_host(H.run_path(case, "exact"))
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.from_numpy(ref["block_scores"]).cuda()
+    sel = torch.empty((w.B, w.T, 4, 16), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.T, 64), dtype=torch.float32, device="cuda")
+    M.msa_topk_sparse_attn(prob, bs, sel, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2], case.d_caches["v"][2],
+                           "exact", H.SOFTMAX_SCALE, out, lse)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref["sel"])
+    assert np.array_equal(out.cpu().numpy(), ref["out"]) and np.array_equal(lse.cpu().numpy(), ref["lse"])
