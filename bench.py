@@ -296,6 +296,16 @@ def prefill_section(dequant, seed, steps=5, warmup=2):
     f_idx, f_attn = algorithmic_flops(wl, wl.sel.cpu().numpy())
     tf_idx = f_idx / (t[0] * 1e-3) / 1e12
     tf_attn = f_attn / (t[2] * 1e-3) / 1e12
+    # the selection inside the attention launch, on the same block scores
+    M = wl.M
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for k in range(steps):
+        ev2[k][0].record()
+        M.msa_topk_sparse_attn(wl.prob, wl.bs, wl.sel, wl.q, w.q_dtype, 1.0, wl.caches["k"][2], wl.caches["v"][2],
+                               dequant, 1.0 / math.sqrt(128.0), wl.out, None)
+        ev2[k][1].record()
+    torch.cuda.synchronize()
+    t_sel = float(np.mean([e[0].elapsed_time(e[1]) for e in ev2]))
     return {"workload": f"c5: chunked prefill, batch {w.B}, {w.T} new query tokens per sequence on "
                         f"{w.lens - w.T} cached ({w.lens} total), NVFP4 K/V and index keys, FP8 queries",
             "ms_per_step": round(float(t.sum()), 4),
@@ -304,6 +314,7 @@ def prefill_section(dequant, seed, steps=5, warmup=2):
                         "frac_of_f16_mfma_peak": round(tf_idx / F16_MFMA_PEAK_TFLOPS, 4),
                         "traffic": measured_traffic("c5", role="indexer")},
             "topk_ms": round(float(t[1]), 4),
+            "topk_inside_attention_ms": round(t_sel, 4),
             "attention": {"kernel": "msa::attn_mfma_kernel (4 waves per row)", "ms": round(float(t[2]), 4),
                           "gflop": round(f_attn / 1e9, 1), "tflops": round(tf_attn, 1),
                           "frac_of_f16_mfma_peak": round(tf_attn / F16_MFMA_PEAK_TFLOPS, 4),

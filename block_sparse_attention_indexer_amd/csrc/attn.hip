@@ -115,11 +115,17 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
                             hipStream_t s, const float* block_scores, int32_t* sel_out) {
   const unsigned rows = (unsigned)((int64_t)p.B * p.T * kGroups);
-  const bool select = block_scores != nullptr;
-  if (select && k.dtype == 0) {   // the fp32 kernel takes a selection: select first
+  const bool many = rows >= kAttnManyRows;
+  // The selection inside the attention launch pays off for decode (few rows: it
+  // saves a launch); with many rows (prefill) each workgroup's selection latency
+  // adds up (c5: 1.94 ms against 0.10 + 1.68 ms), and the fp32 kernel takes a
+  // selection -- there the top-16 kernel runs first.
+  bool select = block_scores != nullptr;
+  if (select && (k.dtype == 0 || many)) {
     const hipError_t e = launch_topk(p, block_scores, sel_out, s);
     if (e != hipSuccess) return e;
     sel = sel_out;
+    select = false;
   }
   if (k.dtype == 0) {
     const float c_nat = softmax_scale * q_scale * k.tensor_scale;
@@ -134,22 +140,19 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   // block of the step is in flight at once.  Many rows (prefill): 4 waves per
   // row with 4 blocks each and a 4-way merge -- a small LDS footprint and many
   // resident rows per CU.  The choice depends only on the row count.
-  const bool many = rows >= kAttnManyRows;
   const AttnArgs aa{q8, c_log2, k.data, k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale,
                     sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse, block_scores, sel_out};
-#define MSA_ATTN_LAUNCH2(KT, FM, SE)                                                                 \
-  if (many)                                                                                          \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4, SE>), dim3(rows), dim3(256), 0, s, aa);           \
-  else                                                                                               \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16, SE>), dim3(rows), dim3(1024), 0, s, aa)
-#define MSA_ATTN_LAUNCH(KT, FM)                  \
-  if (select) { MSA_ATTN_LAUNCH2(KT, FM, true); } \
-  else { MSA_ATTN_LAUNCH2(KT, FM, false); }
+#define MSA_ATTN_LAUNCH(KT, FM)                                                                        \
+  if (many)                                                                                            \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4, false>), dim3(rows), dim3(256), 0, s, aa);          \
+  else if (select)                                                                                     \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16, true>), dim3(rows), dim3(1024), 0, s, aa);         \
+  else                                                                                                 \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16, false>), dim3(rows), dim3(1024), 0, s, aa)
   if (k.dtype == 1) { MSA_ATTN_LAUNCH(1, false); }
   else if (fp8mode) { MSA_ATTN_LAUNCH(2, true); }
   else { MSA_ATTN_LAUNCH(2, false); }
 #undef MSA_ATTN_LAUNCH
-#undef MSA_ATTN_LAUNCH2
   return hipGetLastError();
 }
 

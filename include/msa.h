@@ -229,10 +229,11 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
  * recent one forced, then attend exactly over them): what msa_block_topk
  * followed by msa_sparse_attn_decode / _prefill computes, with sel written
  * as msa_block_topk writes it (bit for bit) and out / lse as the attention
- * call writes them given that selection (bit for bit).  Each attention
- * workgroup first selects its own row's blocks from block_scores, so the
- * selection needs no launch of its own.  Any T >= 1; fp32 caches run the two
- * kernels back to back.
+ * call writes them given that selection (bit for bit).  With fewer than
+ * 8,192 (sequence, token, group) rows (decode) each attention workgroup first
+ * selects its own row's blocks from block_scores, so the selection needs no
+ * launch of its own; with more rows (prefill), and for fp32 caches, the
+ * top-16 kernel runs first (there it is the faster way).  Any T >= 1.
  *   block_scores  device [B][T][4][max_blocks], as msa_indexer_scores writes;
  *   sel           device out [B][T][4][16];
  * other arguments as for msa_sparse_attn_decode (no workspace). */
