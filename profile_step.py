@@ -1,12 +1,13 @@
 """Collect the rocprofv3 figures that bench.py reports, for one workload.
 
-    python profile_step.py [--workload c3_128k] [--only insert|dcp] [--out gpurun_out/profile]
+    python profile_step.py [--workload c3_128k] [--only insert|dcp|prefix] [--out gpurun_out/profile]
 
 Runs bench.py three times as a child process under rocprofv3 (this process
 never touches the GPU):
 
-  1. --kernel-trace --stats      bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-prefill
-  2. --pmc FETCH_SIZE            bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-prefill --calib-copy-mib 512
+  1. --kernel-trace --stats      bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-prefill --no-sides
+  2. --pmc FETCH_SIZE            bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-prefill --no-sides
+                                 --calib-copy-mib 512
   3. --pmc WRITE_SIZE            (same)
 
 Counter readings are per dispatch, in KiB.  Each is scaled by what the same
@@ -117,9 +118,9 @@ def main():
              "prefix": f"shared-prefix index scan against the unshared scan, workload {w}"}[args.only]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(raw, "trace"), "-o", "run",
                  "-f", "csv", "--", py, bench, "--workload", w, "--steps", "10", "--warmup", "2",
-                 "--no-cpu-baseline", "--no-prefill"] + only
+                 "--no-cpu-baseline", "--no-prefill", "--no-sides"] + only
     pmc_bench = [py, bench, "--workload", w, "--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-prefill",
-                 "--calib-copy-mib", str(CALIB_MIB)] + only
+                 "--no-sides", "--calib-copy-mib", str(CALIB_MIB)] + only
     cmds = {"trace": trace_cmd}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds[c] = ["rocprofv3", "--pmc", c, "-d", os.path.join(raw, c), "-o", "run", "-f", "csv", "--"] + pmc_bench
