@@ -336,9 +336,6 @@ hipError_t launch_indexer_shared(const ProblemArgs& p, const void* idx_q, const 
   int chunk = 2;
   for (int c = 16; c > 2; c /= 2)
     if ((int64_t)gx * ((max_blocks + c - 1) / c) * g.n >= want) { chunk = c; break; }
-#ifdef MSA_SH_CHUNK_FIXED
-  chunk = MSA_SH_CHUNK_FIXED;
-#endif
   const dim3 grid(gx, (unsigned)((max_blocks + chunk - 1) / chunk), (unsigned)g.n);
   const uint8_t* q8 = static_cast<const uint8_t*>(idx_q);
 #define MSA_SH_LAUNCH(KT, FM, C)                                                                      \
