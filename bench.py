@@ -4,13 +4,13 @@ One step = msa_indexer_scores (index scan and block max-pool) ->
 msa_topk_sparse_attn (each attention workgroup selects its row's top-16 blocks,
 then attends over them) for the whole batch (one MSA layer).  --path calls runs
 the selection as its own launch (msa_block_topk, then msa_sparse_attn_decode);
---path fused runs the scan and selection as msa_indexer_topk; --path mono runs
+--path fused runs the scan and selection as msa_indexer_topk; --path step runs
 the step as msa_decode_step.  Inputs are seeded synthetic data drawn and packed
 on the GPU before the timed region (resident in HBM).
 
     python bench.py [--steps K] [--warmup W] [--workload c3_128k]
                     [--dequant exact|fp8] [--no-cpu-baseline] [--no-prefill]
-                    [--path select|calls|fused|mono] [--only insert|dcp|prefix]
+                    [--path select|calls|fused|step] [--only insert|dcp|prefix]
 
 Prints one JSON line.  ``value`` is layer-steps/s over the timed steps (wall
 clock, synchronised on both sides); ``roofline`` describes the dominant kernel
@@ -50,10 +50,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill section")
     ap.add_argument("--no-sides", action="store_true",
                     help="skip the dcp and prefix sections (which launch the scan kernel on other shapes)")
-    ap.add_argument("--path", default="select", choices=["select", "calls", "fused", "mono"],
+    ap.add_argument("--path", default="select", choices=["select", "calls", "fused", "step"],
                     help="select: msa_indexer_scores + msa_topk_sparse_attn (the selection inside the "
                          "attention launch); calls: the three calls msa_indexer_scores, msa_block_topk, "
-                         "msa_sparse_attn_decode; fused: msa_indexer_topk + attention; mono: msa_decode_step")
+                         "msa_sparse_attn_decode; fused: msa_indexer_topk + attention; step: msa_decode_step")
     ap.add_argument("--cpu-sample", type=int, default=4, help="sequences the oracle leg runs")
     ap.add_argument("--only", choices=["insert", "dcp", "prefix"], default=None,
                     help="run one side section alone and print its JSON (for profiling), not the step line")
@@ -135,23 +135,21 @@ class Workload:
         # arrival counters of msa_indexer_topk: zero-filled once, left zero-filled by every call
         self.ws = torch.zeros(max(1, M.msa_workspace_size(self.prob, M.MSA_CALL_INDEXER_TOPK) // 4),
                               dtype=torch.int32, device=dev)
-        # work counters and flags of msa_decode_step: likewise
-        self.ws_step = torch.zeros(max(1, M.msa_workspace_size(self.prob, M.MSA_CALL_DECODE_STEP) // 4),
-                                   dtype=torch.int32, device=dev)
         torch.cuda.synchronize()
 
     def step(self, dequant, ev=None, scan_only=False, path="calls"):
-        """One layer step on torch's current stream.  path "calls": the three separate
-        calls; "fused": msa_indexer_topk (scan + selection) then attention; "mono":
-        msa_decode_step.  `ev` events are recorded before the first call and after each
-        call (after the first only, when scan_only)."""
+        """One layer step on torch's current stream.  path "select": msa_indexer_scores
+        then msa_topk_sparse_attn; "calls": the three separate calls; "fused":
+        msa_indexer_topk (scan + selection) then attention; "step": msa_decode_step.
+        `ev` events are recorded before the first call and after each call (after the
+        first only, when scan_only)."""
         M, w = self.M, self.w
         if ev is not None:
             ev[0].record()
-        if path == "mono":
+        if path == "step":
             M.msa_decode_step(self.prob, self.idx_q, w.q_dtype, 1.0, self.caches["idx_k"][2], self.q, w.q_dtype,
                               1.0, self.caches["k"][2], self.caches["v"][2], dequant, 1.0 / math.sqrt(128.0),
-                              self.bs, self.sel, self.out, None, self.ws_step)
+                              self.bs, self.sel, self.out, None)
             if ev is not None:
                 ev[1].record()
             return
@@ -230,7 +228,7 @@ def algorithmic_flops(wl, sel_host):
 
 
 def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
-    """The first kernel of the step (the index scan, or the whole step for "mono") that
+    """The first kernel of the step (the index scan) that
     libmsa launches for this workload, as rocprofv3 names it.  The pages-per-wave
     template argument follows the launcher's rule: the largest of its three sizes
     whose grid gives every CU two workgroups."""
@@ -247,8 +245,6 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
                 return p_
         return big // 4
     b = lambda x: str(x).lower()
-    if path == "mono" and w.T == 1 and not fp8mode:
-        return f"msa::decode_step_kernel<{kt}>"
     if w.T == 1:
         return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16)}, {b(fp8mode)}>"
     if w.T <= 4:
@@ -585,7 +581,7 @@ def main():
 
     K = args.steps
     fused = path == "fused"
-    ncalls = {"calls": 3, "fused": 2, "mono": 1, "select": 2}[path]
+    ncalls = {"calls": 3, "fused": 2, "step": 1, "select": 2}[path]
     # Timed region: K whole steps; HIP events on the launching stream bracket only the
     # first call (the index scan, with the selection when fused: the roofline kernel),
     # so the step itself runs undisturbed.
@@ -611,7 +607,7 @@ def main():
     total_bytes = b_idx + b_topk + b_attn
     idx_ms = float(np.mean(k_idx))
     # bytes of the first (roofline) call
-    b_first = total_bytes if path == "mono" else b_idx + b_topk if fused else b_idx
+    b_first = total_bytes if path == "step" else b_idx + b_topk if fused else b_idx
     achieved_idx = b_first / (idx_ms * 1e-3) / 1e9
     step_tbps = total_bytes / (ms_step * 1e-3) / 1e12
 
@@ -635,16 +631,16 @@ def main():
         "hbm_TBps_step": round(step_tbps, 3),
         "pct_of_peak_hbm_step": round(100 * step_tbps * 1e3 / HBM_PEAK_GBPS, 1),
         "bytes_per_step": {"indexer": b_idx, "topk": b_topk, "attention": b_attn},
-        "call_ms": ({"decode_step": round(idx_ms, 5)} if path == "mono" else
+        "call_ms": ({"decode_step": round(idx_ms, 5)} if path == "step" else
                     {"indexer_topk": round(idx_ms, 5), "attention": round(float(per_call[1]), 5)} if fused else
                     {"indexer": round(idx_ms, 5), "topk_attention": round(float(per_call[1]), 5)}
                     if path == "select" else
                     {"indexer": round(idx_ms, 5), "topk": round(float(per_call[1]), 5),
                      "attention": round(float(per_call[2]), 5)}),
         "roofline": {"bound": "hbm", "kernel": indexer_kernel_name(w, args.dequant, path, wl.lay.max_blocks) +
-                     {"mono": " (the whole step: scan, pool, top-16, attention)",
-                      "fused": " (index-key scan + block max-pool + top-16)",
+                     {                      "fused": " (index-key scan + block max-pool + top-16)",
                       "calls": " (index-key scan + block max-pool)",
+                      "step": " (index-key scan + block max-pool)",
                       "select": " (index-key scan + block max-pool)"}[path],
                      "achieved": round(achieved_idx, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved_idx / HBM_PEAK_GBPS, 4),

@@ -227,11 +227,9 @@ def msa_sparse_attn_prefill(*args, **kw):
 
 
 def msa_decode_step(prob, idx_q, idx_q_dtype, idx_q_scale, idx_k, q, q_dtype, q_scale, k, v, dequant,
-                    softmax_scale, block_scores, sel, out, lse, workspace, stream=None):
-    """One decode layer step (steps 1-4) in one call; `workspace`: a zero-filled device
-    tensor of at least msa_workspace_size(prob, MSA_CALL_DECODE_STEP) bytes (left
-    zero-filled)."""
-    ws_bytes = workspace.numel() * workspace.element_size()
+                    softmax_scale, block_scores, sel, out, lse=None, workspace=None, stream=None):
+    """One decode layer step (steps 1-4) in one call (two launches); no workspace is needed."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib().msa_decode_step(ctypes.byref(prob), _ptr(idx_q), DTYPES[idx_q_dtype], float(idx_q_scale),
                                   ctypes.byref(idx_k), _ptr(q), DTYPES[q_dtype], float(q_scale), ctypes.byref(k),
                                   ctypes.byref(v), DEQUANT[dequant], float(softmax_scale), _ptr(block_scores),

@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["pack.hip", "insert.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "attn.hip",
-           "decode_step.hip", "dcp.hip", "api.cpp"]
+           "dcp.hip", "api.cpp"]
 
 
 def _compile(src):

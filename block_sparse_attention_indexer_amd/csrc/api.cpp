@@ -272,17 +272,12 @@ msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype
       !aligned(out, 16) || (lse && !aligned(lse, 4)))
     return MSA_ERR_INVALID_ARG;
   if (!good_scale(idx_q_scale) || !good_scale(q_scale) || !good_scale(softmax_scale)) return MSA_ERR_INVALID_ARG;
-  if (workspace == nullptr || !aligned(workspace, 4) ||
-      workspace_bytes < msa_workspace_size(prob, MSA_CALL_DECODE_STEP))
-    return MSA_ERR_WORKSPACE;
+  (void)workspace;
+  (void)workspace_bytes;   // no workspace is needed (msa_workspace_size reports 0)
   const ProblemArgs pa = to_args(prob);
   const CacheArgs ia = to_args(idx_k), ka = to_args(k), va = to_args(v);
   const bool fp8 = dequant == MSA_DQ_FP8;
-  if (msa::decode_step_fits(pa, ia, ka, va, fp8))
-    return hip_status(msa::launch_decode_step(pa, idx_q, idx_q_scale, ia, q, q_scale, ka, va, softmax_scale,
-                                              block_scores, sel, out, lse, static_cast<uint32_t*>(workspace),
-                                              stream));
-  // otherwise: the scan, then one launch that selects each row's blocks and attends
+  // the scan, then one launch that selects each row's blocks and attends
   hipError_t e = msa::launch_indexer(pa, idx_q, (int)idx_q_dtype, idx_q_scale, ia, fp8, block_scores, nullptr, stream);
   if (e == hipSuccess)
     e = msa::launch_attention(pa, q, (int)q_dtype, q_scale, ka, va, fp8, sel, softmax_scale, out, lse, stream,
@@ -304,8 +299,6 @@ size_t msa_workspace_size(const msa_problem* prob, msa_call which) {
   if (prob == nullptr || prob->batch <= 0) return 0;
   if (which == MSA_CALL_INDEXER_TOPK)
     return (size_t)prob->batch * sizeof(uint32_t);   // one arrival counter per sequence
-  if (which == MSA_CALL_DECODE_STEP)
-    return msa::decode_step_workspace_words(prob->batch) * sizeof(uint32_t);
   if (which == MSA_CALL_INDEXER_PREFIX)
     return (size_t)prob->batch * sizeof(int32_t);     // shared block count per sequence
   return 0;

@@ -42,9 +42,14 @@ namespace msa {
 #endif
 // SELECT: each workgroup first selects its row's 16 blocks from the block
 // scores (msa_topk_sparse_attn), so the selection needs no launch of its own.
+#ifndef MSA_ATTN_DECODE_WAVES
+#define MSA_ATTN_DECODE_WAVES 16
+#endif
+constexpr int kDecodeWaves = MSA_ATTN_DECODE_WAVES;   // waves per row below kAttnManyRows rows
 template <int KT, bool FP8MODE, int WAVES, bool SELECT = false>
-__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : MSA_ATTN_MANY_WG) void attn_mfma_kernel(AttnArgs a) {
-  attend_row<KT, FP8MODE, WAVES, false, SELECT>(a, blockIdx.x);
+__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : WAVES == 8 ? 2 : MSA_ATTN_MANY_WG) void attn_mfma_kernel(
+    AttnArgs a) {
+  attend_row<KT, FP8MODE, WAVES, SELECT>(a, blockIdx.x);
 }
 
 // fp32 queries and caches: plain fp32 arithmetic on the vector ALUs.  One
@@ -146,9 +151,11 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   if (many)                                                                                            \
     hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4, false>), dim3(rows), dim3(256), 0, s, aa);          \
   else if (select)                                                                                     \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16, true>), dim3(rows), dim3(1024), 0, s, aa);         \
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, kDecodeWaves, true>), dim3(rows), dim3(kDecodeWaves * 64), 0, \
+                       s, aa);                                                                         \
   else                                                                                                 \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 16, false>), dim3(rows), dim3(1024), 0, s, aa)
+    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, kDecodeWaves, false>), dim3(rows), dim3(kDecodeWaves * 64), 0, \
+                       s, aa)
   if (k.dtype == 1) { MSA_ATTN_LAUNCH(1, false); }
   else if (fp8mode) { MSA_ATTN_LAUNCH(2, true); }
   else { MSA_ATTN_LAUNCH(2, false); }

@@ -1,5 +1,6 @@
-// Step 4 of MSA: exact attention over the selected blocks -- device code
-// shared by the attention kernel and the one-launch decode step.
+// Step 4 of MSA: exact attention over the selected blocks -- the device
+// code of one row, used by the attention kernels (with or without the row's
+// own top-16 selection in front).
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
 // and its Figure 1 caption: attention runs exactly, but only over the top
@@ -217,11 +218,10 @@ struct AttnArgs {
 // of which call it): KT 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  Wave w
 // takes selected blocks w, w + WAVES, ... and keeps a running (max, sum, O)
 // over them (online softmax); the WAVES states merge at the end.
-// COHERENT_SEL: the selection was written by another workgroup of the
-// running kernel (device-coherent loads).  SELECT: the workgroup first
-// selects the row's blocks itself from args.block_scores (select_row, the
-// same rule and keys as msa_block_topk) and writes them to args.sel_out.
-template <int KT, bool FP8MODE, int WAVES, bool COHERENT_SEL, bool SELECT = false>
+// SELECT: the workgroup first selects the row's blocks itself from
+// args.block_scores (select_row, the same rule and keys as msa_block_topk)
+// and writes them to args.sel_out.
+template <int KT, bool FP8MODE, int WAVES, bool SELECT = false>
 __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
   const uint8_t* __restrict__ q = args.q;
   const float c_log2 = args.c_log2;
@@ -273,10 +273,7 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
     if (threadIdx.x < kTopK) args.sel_out[(size_t)row * kTopK + threadIdx.x] = sel_sh[threadIdx.x];
   } else {
 #pragma unroll
-    for (int u = 0; u < kTopK / WAVES; ++u) {
-      const int32_t* sp = sel + (size_t)row * kTopK + w + u * WAVES;
-      blks[u] = COHERENT_SEL ? __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sp;
-    }
+    for (int u = 0; u < kTopK / WAVES; ++u) blks[u] = sel[(size_t)row * kTopK + w + u * WAVES];
   }
   if (threadIdx.x == 0) nan_sh = 0;
   if (FP8MODE) build_fp8_lut(lut);

@@ -97,15 +97,4 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
 // into their slots of cache c (heads = c's heads per page).
 hipError_t launch_insert(const ProblemArgs& p, const float* x, const CacheArgs& c, int heads, hipStream_t s);
 
-// One decode layer step (T = 1) in one launch: block_scores, sel and out as the
-// three calls above leave them.  ws: decode_step_workspace_words(B) zeroed
-// uint32 words, left zeroed.  Only where decode_step_fits.
-bool decode_step_fits(const ProblemArgs& p, const CacheArgs& idx_k, const CacheArgs& k, const CacheArgs& v,
-                      bool fp8mode);
-size_t decode_step_workspace_words(int B);
-hipError_t launch_decode_step(const ProblemArgs& p, const void* idx_q, float idx_q_scale, const CacheArgs& idx_k,
-                              const void* q, float q_scale, const CacheArgs& k, const CacheArgs& v,
-                              float softmax_scale, float* block_scores, int32_t* sel, float* out, float* lse,
-                              uint32_t* ws, hipStream_t s);
-
 }  // namespace msa

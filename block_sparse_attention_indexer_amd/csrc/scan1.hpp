@@ -1,6 +1,5 @@
 // One-token decode scan (steps 1+2 of MSA for T = 1) as device code shared
-// by the scan kernel, the scan with top-16 (msa_indexer_topk) and the
-// one-launch decode step.
+// by the scan kernel and the scan with top-16 (msa_indexer_topk).
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer":
 // one index query per GQA group is dotted with every key of a single shared

@@ -260,25 +260,17 @@ msa_status msa_indexer_topk(const msa_problem* prob, const void* idx_q, msa_dtyp
                             size_t workspace_bytes, hipStream_t stream);
 
 /* Steps 1-4 of one decode layer step in one call ("MSA primer": score,
- * max-pool, select the top 16 blocks with the most recent one forced, attend;
- * the AMD section mentions a single kernel for low-latency decode).  Leaves
- * block_scores and sel as msa_indexer_scores + msa_block_topk do, bit for bit,
- * and out/lse as msa_sparse_attn_decode does (within rounding: the rows are
- * merged from 4 partial states instead of 16).  For one query token
- * (tokens == 1) with FP8 caches, or NVFP4 caches read exactly, and index keys
- * of the same dtype as K/V, one persistent kernel does all of it: as soon as
- * a sequence's blocks are scored and selected, its rows are attended while
- * other sequences are still being scanned.  Otherwise the scan runs, then
- * one launch selects and attends (as msa_topk_sparse_attn).
+ * max-pool, select the top 16 blocks with the most recent one forced,
+ * attend): msa_indexer_scores, then msa_topk_sparse_attn -- two launches,
+ * leaving block_scores, sel, out and lse as msa_indexer_scores +
+ * msa_block_topk + msa_sparse_attn_decode do, bit for bit.
  *   idx_q, idx_q_dtype, idx_q_scale, idx_k  as for msa_indexer_scores;
  *   q, q_dtype, q_scale, k, v, softmax_scale, out, lse  as for
- *                msa_sparse_attn_decode (k, v: same dtype);
+ *                msa_sparse_attn_decode (k, v: same dtype; tokens <= 8);
  *   block_scores, sel  outputs as for the two selection calls;
- *   workspace    device, at least msa_workspace_size(prob, MSA_CALL_DECODE_STEP)
- *                bytes (4 + 20 per sequence), zero-filled before its first use;
- *                every call leaves it zero-filled again.  Calls that share a
- *                workspace must not overlap (they are ordered on one stream).
- * Errors as for the three calls, plus MSA_ERR_WORKSPACE. */
+ *   workspace, workspace_bytes  unused (msa_workspace_size reports 0); may
+ *                be NULL and 0.
+ * Errors as for the three calls. */
 msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype idx_q_dtype,
                            float idx_q_scale, const msa_cache* idx_k, const void* q, msa_dtype q_dtype,
                            float q_scale, const msa_cache* k, const msa_cache* v, msa_dequant dequant,

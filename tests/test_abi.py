@@ -142,13 +142,10 @@ def test_decode_step_validation(lib):
         return lib.msa_decode_step(ctypes.byref(prob), 1024, M.MSA_FP8_E4M3, 1.0, ctypes.byref(idx_k), 3072,
                                    q_dtype, qs, ctypes.byref(k), ctypes.byref(v), M.MSA_DQ_EXACT, sm, 2048, sel,
                                    out, None, ws, ws_bytes, None)
-    # 4 counters + an arrival counter and 4 row flags per sequence
-    assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_DECODE_STEP) == (4 + 5 * 2) * 4
+    assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_DECODE_STEP) == 0   # no workspace needed
     assert call(sel=None) == M.MSA_ERR_INVALID_ARG
     assert call(out=None) == M.MSA_ERR_INVALID_ARG
     assert call(out=8196) == M.MSA_ERR_INVALID_ARG          # misaligned
-    assert call(ws=None) == M.MSA_ERR_WORKSPACE
-    assert call(ws_bytes=40) == M.MSA_ERR_WORKSPACE
     assert call(qs=0.0) == M.MSA_ERR_INVALID_ARG
     assert call(sm=float("nan")) == M.MSA_ERR_INVALID_ARG
     assert call(prob=_prob(tokens=9)) == M.MSA_ERR_UNSUPPORTED

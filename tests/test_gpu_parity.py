@@ -293,7 +293,7 @@ def test_indexer_topk_full_size(M):
     assert int(ws.abs().sum()) == 0
 
 
-def _step(M, case, ws, B=None, dequant="exact"):
+def _step(M, case, B=None, dequant="exact"):
     w, lay = case.w, case.lay
     B = w.B if B is None else B
     prob = M.problem(case.d_seq[:B], case.d_table[:B], w.T)
@@ -303,54 +303,35 @@ def _step(M, case, ws, B=None, dequant="exact"):
     lse = torch.empty((B, w.T, 64), dtype=torch.float32, device="cuda")
     M.msa_decode_step(prob, case.d_idx_q[:B], w.q_dtype, 1.0, case.d_caches["idx_k"][2], case.d_q[:B], w.q_dtype,
                       1.0, case.d_caches["k"][2], case.d_caches["v"][2], dequant, H.SOFTMAX_SCALE, bs, sel, out,
-                      lse, ws)
+                      lse)
     torch.cuda.synchronize()
     return bs.cpu().numpy(), sel.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
-
-
-def _same_attention(out, lse, ref_out, ref_lse):
-    """Equal up to how the row is split into partial softmax states: P enters the PV
-    product as f16 relative to each partial state's running max (at most 2^-12
-    relative per element), so 4 states of 4 blocks and 16 states of one block round
-    differently.  Bound: a quarter of the oracle bar, i.e. about twice the error P's
-    f16 rounding was measured to cost on realistic data; both paths are also held to
-    the oracle bar itself."""
-    assert not np.isnan(out).any()
-    d = np.abs(np.asarray(out, np.float64) - np.asarray(ref_out, np.float64))
-    assert d.max() <= H.OUT_MAX_ABS / 4 and d.mean() <= H.OUT_MEAN_ABS / 4, (d.max(), d.mean())
-    assert np.abs(lse - ref_lse).max() <= 1e-5 * (1.0 + np.abs(ref_lse).max())
 
 
 @pytest.mark.parametrize("wname,mode", [("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"), ("tiny_edge", "exact"),
                                         ("long_rows", "exact"), ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"),
                                         ("c1", "exact")])
 def test_decode_step_equals_the_separate_calls(M, wname, mode):
-    """msa_decode_step gives the block scores and selection of the three calls bit for
-    bit and their attention up to merge order, call after call, and leaves its
-    workspace zeroed -- also when a later call covers fewer sequences.  Its output is
-    also checked against the oracle on the selection it made."""
+    """msa_decode_step gives the block scores, selection, outputs and LSE of the three
+    calls bit for bit, call after call and for a smaller batch; its output also meets
+    the oracle bar on the selection it made."""
     _say("decode_step", wname, mode)
     case = H.HostCase(wname).upload()
     w, lay = case.w, case.lay
     ref = H.to_host(H.run_path(case, mode))
     B = w.B
-    ws = torch.zeros(M.msa_workspace_size(M.problem(case.d_seq, case.d_table, w.T), M.MSA_CALL_DECODE_STEP) // 4,
-                     dtype=torch.int32, device="cuda")
-    for rep in range(3):
-        bs, sel, out, lse = _step(M, case, ws, dequant=mode)
+    for rep in range(2):
+        bs, sel, out, lse = _step(M, case, dequant=mode)
         assert np.array_equal(bs, ref["block_scores"], equal_nan=True), rep
         assert np.array_equal(sel, ref["sel"]), rep
-        _same_attention(out, lse, ref["out"], ref["lse"])
-        assert int(ws.abs().sum()) == 0
+        assert np.array_equal(out, ref["out"]) and np.array_equal(lse, ref["lse"]), rep
     seq_lens, table = lay.seq_lens.numpy(), lay.block_table.numpy()
     for b in range(B):
         o, _ = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, sel[b], mode, w.q_dtype, b)
         H.compare_out(out[b], o)
     if B > 1:
-        bs, sel, out, lse = _step(M, case, ws, B=B - 1, dequant=mode)
-        assert np.array_equal(sel, ref["sel"][:B - 1])
-        _same_attention(out, lse, ref["out"][:B - 1], ref["lse"][:B - 1])
-        assert int(ws.abs().sum()) == 0
+        bs, sel, out, lse = _step(M, case, B=B - 1, dequant=mode)
+        assert np.array_equal(sel, ref["sel"][:B - 1]) and np.array_equal(out, ref["out"][:B - 1])
 
 
 @pytest.mark.parametrize("wname", ["c3_128k", "c2"])
@@ -358,13 +339,9 @@ def test_decode_step_full_size(M, wname):
     _say("decode_step full size", wname)
     case = H.DeviceCase(wname, keep_fp32=False)
     ref = H.to_host(H.run_path(case, "exact"))
-    ws = torch.zeros(M.msa_workspace_size(M.problem(case.d_seq, case.d_table, case.w.T), M.MSA_CALL_DECODE_STEP) // 4,
-                     dtype=torch.int32, device="cuda")
-    for rep in range(2):
-        bs, sel, out, lse = _step(M, case, ws)
-        assert np.array_equal(bs, ref["block_scores"]) and np.array_equal(sel, ref["sel"]), rep
-        _same_attention(out, lse, ref["out"], ref["lse"])
-    assert int(ws.abs().sum()) == 0
+    bs, sel, out, lse = _step(M, case)
+    assert np.array_equal(bs, ref["block_scores"]) and np.array_equal(sel, ref["sel"])
+    assert np.array_equal(out, ref["out"]) and np.array_equal(lse, ref["lse"])
 
 
 @pytest.mark.parametrize("dtype,heads,T,lens", [
