@@ -8,7 +8,7 @@ library is missing every call raises instead of falling back.
 The functions keep the C names: msa_indexer_scores, msa_indexer_topk, msa_block_topk,
 msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_decode_step, msa_cache_insert,
 msa_indexer_scores_shard, msa_shard_topk, msa_topk_merge, msa_indexer_scores_prefix,
-msa_topk_sparse_attn, msa_pack_fp8,
+msa_topk_sparse_attn, msa_cache_insert_many, msa_pack_fp8,
 msa_unpack_fp8, msa_pack_nvfp4, msa_unpack_nvfp4, msa_workspace_size.
 """
 import ctypes
@@ -24,10 +24,11 @@ MSA_MAX_SHARDS = 8
 MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK, MSA_CALL_DECODE_STEP = 0, 1, 2, 3, 4
 MSA_CALL_INDEXER_PREFIX = 5
 MSA_MAX_PREFIX_GROUPS = MSA_MAX_PREFIX_SEQS = 64
+MSA_MAX_INSERTS = 4
 
 EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_sparse_attn_decode",
             "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
-            "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn",
+            "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn", "msa_cache_insert_many",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
@@ -79,6 +80,7 @@ def _lib():
             "msa_decode_step": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), vp, ctypes.c_int, f32,
                                 P(msa_cache), P(msa_cache), ctypes.c_int, f32, vp, vp, vp, vp, vp, sz, vp],
             "msa_cache_insert": [P(msa_problem), vp, P(msa_cache), vp],
+            "msa_cache_insert_many": [P(msa_problem), i32, vp, vp, vp],
             "msa_indexer_scores_shard": [P(msa_problem), i32, i32, vp, ctypes.c_int, f32, P(msa_cache),
                                          ctypes.c_int, vp, vp],
             "msa_shard_topk": [P(msa_problem), i32, i32, vp, vp, vp, vp],
@@ -235,6 +237,15 @@ def msa_decode_step(prob, idx_q, idx_q_dtype, idx_q_scale, idx_k, q, q_dtype, q_
                                   ctypes.byref(v), DEQUANT[dequant], float(softmax_scale), _ptr(block_scores),
                                   _ptr(sel), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)),
            "msa_decode_step")
+
+
+def msa_cache_insert_many(prob, xs, caches, stream=None):
+    """Several quantise-and-inserts in one launch: xs[i] into caches[i] (msa_cache objects)."""
+    n = len(xs)
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(x) for x in xs])
+    arr = (msa_cache * n)(*caches)
+    _check(_lib().msa_cache_insert_many(ctypes.byref(prob), n, ctypes.cast(ptrs, ctypes.c_void_p),
+                                        ctypes.cast(arr, ctypes.c_void_p), _stream(stream)), "msa_cache_insert_many")
 
 
 def msa_cache_insert(prob, x, cache_, stream=None):

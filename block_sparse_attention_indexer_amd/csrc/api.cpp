@@ -295,6 +295,23 @@ msa_status msa_cache_insert(const msa_problem* prob, const float* x, const msa_c
   return hip_status(msa::launch_insert(to_args(prob), x, to_args(cache), cache->heads, stream));
 }
 
+msa_status msa_cache_insert_many(const msa_problem* prob, int32_t n, const float* const* x, const msa_cache* caches,
+                                 hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (n < 1 || n > MSA_MAX_INSERTS || x == nullptr || caches == nullptr) return MSA_ERR_INVALID_ARG;
+  msa::CacheArgs c[MSA_MAX_INSERTS];
+  int heads[MSA_MAX_INSERTS];
+  for (int k = 0; k < n; ++k) {
+    if (caches[k].heads != 1 && caches[k].heads != 4) return MSA_ERR_INVALID_ARG;
+    if ((st = check_cache(&caches[k], caches[k].heads)) != MSA_OK) return st;
+    if (x[k] == nullptr || !aligned(x[k], 16)) return MSA_ERR_INVALID_ARG;
+    c[k] = to_args(&caches[k]);
+    heads[k] = caches[k].heads;
+  }
+  return hip_status(msa::launch_insert_many(to_args(prob), n, x, c, heads, stream));
+}
+
 size_t msa_workspace_size(const msa_problem* prob, msa_call which) {
   if (prob == nullptr || prob->batch <= 0) return 0;
   if (which == MSA_CALL_INDEXER_TOPK)

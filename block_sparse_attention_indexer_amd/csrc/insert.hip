@@ -24,15 +24,16 @@ constexpr int kInsertWaves = 4;
 constexpr int kInsertRowsPerWave = 64 / kNvfp4ScaleBytes;   // 8: a lane per 16-dim group
 constexpr int kInsertRowsPerWG = kInsertWaves * kInsertRowsPerWave;
 
+// Workgroup `wg` of one insert: rows wg*32 .. wg*32+31 of x.
 template <int DT>   // 0 F32, 1 FP8, 2 NVFP4
-__global__ __launch_bounds__(64 * kInsertWaves) void insert_rows_kernel(
+__device__ __forceinline__ void insert_rows(
     const float* __restrict__ x, uint8_t* __restrict__ data, uint8_t* __restrict__ scales, int64_t num_pages,
     int hshift, float tensor_scale, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table,
-    int max_blocks, int T, uint32_t rows) {
+    int max_blocks, int T, uint32_t rows, uint32_t wg) {
   // rows = B*T*heads < 2^31 and heads = 1 << hshift, so 32-bit index arithmetic suffices
   const int heads = 1 << hshift;
   const int g = threadIdx.x & 7;   // group: dims 16g .. 16g+15
-  const uint32_t row = blockIdx.x * kInsertRowsPerWG + (threadIdx.x >> 3);   // (b*T + t)*heads + h
+  const uint32_t row = wg * kInsertRowsPerWG + (threadIdx.x >> 3);   // (b*T + t)*heads + h
   if (row >= rows) return;
   const float4* src = reinterpret_cast<const float4*>(x + (size_t)row * kHeadDim + 16 * g);
   float4 f[4];
@@ -76,6 +77,35 @@ __global__ __launch_bounds__(64 * kInsertWaves) void insert_rows_kernel(
   }
 }
 
+template <int DT>
+__global__ __launch_bounds__(64 * kInsertWaves) void insert_rows_kernel(
+    const float* __restrict__ x, uint8_t* __restrict__ data, uint8_t* __restrict__ scales, int64_t num_pages,
+    int hshift, float tensor_scale, const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ table,
+    int max_blocks, int T, uint32_t rows) {
+  insert_rows<DT>(x, data, scales, num_pages, hshift, tensor_scale, seq_lens, table, max_blocks, T, rows,
+                  blockIdx.x);
+}
+
+// Several inserts in one launch: workgroups [wg_begin[k], wg_begin[k+1]) do insert k.
+__global__ __launch_bounds__(64 * kInsertWaves) void insert_many_kernel(InsertSet set,
+                                                                        const int32_t* __restrict__ seq_lens,
+                                                                        const int32_t* __restrict__ table,
+                                                                        int max_blocks, int T) {
+  int k = 0;
+  while (k + 1 < set.n && blockIdx.x >= set.wg_begin[k + 1]) ++k;
+  const InsertSet::One& e = set.one[k];
+  const uint32_t wg = blockIdx.x - set.wg_begin[k];
+  if (e.dtype == 0)
+    insert_rows<0>(e.x, e.data, e.scales, e.num_pages, e.hshift, e.tensor_scale, seq_lens, table, max_blocks, T,
+                   e.rows, wg);
+  else if (e.dtype == 1)
+    insert_rows<1>(e.x, e.data, e.scales, e.num_pages, e.hshift, e.tensor_scale, seq_lens, table, max_blocks, T,
+                   e.rows, wg);
+  else
+    insert_rows<2>(e.x, e.data, e.scales, e.num_pages, e.hshift, e.tensor_scale, seq_lens, table, max_blocks, T,
+                   e.rows, wg);
+}
+
 hipError_t launch_insert(const ProblemArgs& p, const float* x, const CacheArgs& c, int heads, hipStream_t s) {
   const uint32_t rows = (uint32_t)((int64_t)p.B * p.T * heads);   // < 2^31: B*T*4 is bounded by the caller
   const int hshift = heads == 4 ? 2 : 0;
@@ -89,6 +119,24 @@ hipError_t launch_insert(const ProblemArgs& p, const float* x, const CacheArgs& 
   else if (c.dtype == 1) MSA_INSERT_LAUNCH(1);
   else MSA_INSERT_LAUNCH(2);
 #undef MSA_INSERT_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_insert_many(const ProblemArgs& p, int n, const float* const* x, const CacheArgs* c,
+                              const int* heads, hipStream_t s) {
+  InsertSet set{};
+  set.n = n;
+  uint32_t wgs = 0;
+  for (int k = 0; k < n; ++k) {
+    const uint32_t rows = (uint32_t)((int64_t)p.B * p.T * heads[k]);
+    set.one[k] = InsertSet::One{x[k], const_cast<uint8_t*>(c[k].data), const_cast<uint8_t*>(c[k].scales),
+                                c[k].num_pages, heads[k] == 4 ? 2 : 0, c[k].tensor_scale, c[k].dtype, rows};
+    set.wg_begin[k] = wgs;
+    wgs += (rows + kInsertRowsPerWG - 1) / kInsertRowsPerWG;
+  }
+  set.wg_begin[n] = wgs;
+  hipLaunchKernelGGL(insert_many_kernel, dim3(wgs), dim3(64 * kInsertWaves), 0, s, set, p.seq_lens, p.block_table,
+                     p.max_blocks, p.T);
   return hipGetLastError();
 }
 

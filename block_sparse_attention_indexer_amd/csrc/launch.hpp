@@ -96,5 +96,24 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
 // Quantise the fp32 rows x [B, T, heads, 128] of the T new tokens and write them
 // into their slots of cache c (heads = c's heads per page).
 hipError_t launch_insert(const ProblemArgs& p, const float* x, const CacheArgs& c, int heads, hipStream_t s);
+// Up to kMaxInserts inserts of the same new tokens (K, V, index keys) in one launch.
+constexpr int kMaxInserts = 4;
+struct InsertSet {
+  struct One {
+    const float* x;
+    uint8_t* data;
+    uint8_t* scales;
+    int64_t num_pages;
+    int hshift;
+    float tensor_scale;
+    int dtype;
+    uint32_t rows;
+  };
+  int n;
+  One one[kMaxInserts];
+  uint32_t wg_begin[kMaxInserts + 1];
+};
+hipError_t launch_insert_many(const ProblemArgs& p, int n, const float* const* x, const CacheArgs* c,
+                              const int* heads, hipStream_t s);
 
 }  // namespace msa

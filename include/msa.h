@@ -295,6 +295,20 @@ msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype
  * share pages; rows of one call must not share a slot. */
 msa_status msa_cache_insert(const msa_problem* prob, const float* x, const msa_cache* cache, hipStream_t stream);
 
+/* Several quantise-and-inserts of the same new tokens in one launch (the K,
+ * V and index-key rows a decode step appends): the same writes as n calls
+ * of msa_cache_insert(prob, x[i], &caches[i]), bit for bit.
+ *   n       1 .. MSA_MAX_INSERTS;
+ *   x       HOST array of n device pointers, each as msa_cache_insert's x for
+ *           caches[i] (fp32 [batch, tokens, caches[i].heads, 128], 16-byte
+ *           aligned);
+ *   caches  HOST array of n caches (FP8, NVFP4 or fp32; heads 1 or 4), whose
+ *           data (and scales) are WRITTEN as msa_cache_insert writes them.
+ * The caches must not overlap one another. */
+#define MSA_MAX_INSERTS 4
+msa_status msa_cache_insert_many(const msa_problem* prob, int32_t n, const float* const* x, const msa_cache* caches,
+                                 hipStream_t stream);
+
 typedef enum {
   MSA_CALL_INDEXER = 0,
   MSA_CALL_TOPK = 1,

@@ -246,3 +246,22 @@ def test_topk_sparse_attn_validation(lib):
     assert call(out=16388) == M.MSA_ERR_INVALID_ARG
     assert call(kk=_cache(heads=1)) == M.MSA_ERR_INVALID_ARG
     assert call(vv=_cache(heads=4, dtype=M.MSA_FP8_E4M3, scales=None)) == M.MSA_ERR_UNSUPPORTED
+
+
+def test_cache_insert_many_validation(lib):
+    p = _prob()
+
+    def call(n=2, xs=(1024, 2048), caches=None, prob=p):
+        cs = caches if caches is not None else [_cache(heads=4), _cache(heads=1)]
+        xa = (ctypes.c_void_p * max(len(xs), 1))(*xs) if xs is not None else None
+        ca = (M.msa_cache * max(len(cs), 1))(*cs)
+        return lib.msa_cache_insert_many(ctypes.byref(prob), n, ctypes.cast(xa, ctypes.c_void_p) if xa else None,
+                                         ctypes.cast(ca, ctypes.c_void_p), None)
+
+    assert call(n=0) == M.MSA_ERR_INVALID_ARG
+    assert call(n=5, xs=(1024,) * 5, caches=[_cache(heads=4)] * 5) == M.MSA_ERR_INVALID_ARG
+    assert call(xs=None) == M.MSA_ERR_INVALID_ARG
+    assert call(xs=(1024, 2056)) == M.MSA_ERR_INVALID_ARG                   # misaligned rows
+    assert call(caches=[_cache(heads=4), _cache(heads=2)]) == M.MSA_ERR_INVALID_ARG
+    assert call(caches=[_cache(heads=4), _cache(heads=1, tensor_scale=0.0)]) == M.MSA_ERR_INVALID_ARG
+    assert call(prob=_prob(block_size=64)) == M.MSA_ERR_UNSUPPORTED

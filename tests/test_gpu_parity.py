@@ -385,6 +385,45 @@ def test_cache_insert_bit_exact(M, dtype, heads, T, lens):
         assert np.array_equal(d_sc.cpu().numpy(), want["scales"])
 
 
+@pytest.mark.parametrize("specs,T,lens", [
+    ((("nvfp4", 4), ("nvfp4", 4), ("nvfp4", 1)), 1, [300, 129, 5000, 128]),     # a decode step's K, V, index keys
+    ((("nvfp4", 4), ("nvfp4", 4), ("fp8", 1), ("f32", 1)), 37, [300, 700]),    # mixed dtypes, a chunk
+])
+def test_cache_insert_many_bit_exact(M, specs, T, lens):
+    """msa_cache_insert_many writes what one msa_cache_insert per cache writes -- the
+    oracle's quantised rows in their slots and nothing else."""
+    _say("cache_insert_many", specs, T, lens)
+    from tests.test_oracle_msa import _insert_pool
+    rng = np.random.default_rng(77 + T)
+    B = len(lens)
+    nbs = [(L + 127) // 128 for L in lens]
+    maxb = max(nbs)
+    P = sum(nbs) + 2
+    perm = rng.permutation(P)
+    table = np.full((B, maxb), -1, np.int32)
+    off = 0
+    for b, n in enumerate(nbs):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    prob = M.problem(torch.tensor(lens, dtype=torch.int32, device="cuda"), torch.from_numpy(table).cuda(), T)
+    pools, wants, xs, caches, devs = [], [], [], [], []
+    for dtype, heads in specs:
+        pool = _insert_pool(dtype, P, heads, rng)
+        x = (3.0 * rng.normal(size=(B, T, heads, 128))).astype(np.float32)
+        wants.append(OM.cache_insert(pool, x, lens, table, T))
+        d_data = torch.from_numpy(pool["data"]).cuda()
+        d_sc = torch.from_numpy(pool["scales"]).cuda() if dtype == "nvfp4" else None
+        caches.append(M.cache(dtype, d_data, d_sc, pool["tensor_scale"], heads))
+        devs.append((d_data, d_sc))
+        xs.append(torch.from_numpy(x).cuda())
+    M.msa_cache_insert_many(prob, xs, caches)
+    torch.cuda.synchronize()
+    for (d_data, d_sc), want in zip(devs, wants):
+        assert np.array_equal(d_data.cpu().numpy(), want["data"])
+        if d_sc is not None:
+            assert np.array_equal(d_sc.cpu().numpy(), want["scales"])
+
+
 # ------------------------------------------------------------------ context parallelism (DCP) on one GPU
 
 SENTINEL = 12345.0
