@@ -16,7 +16,7 @@ counter reads for the 512 MiB elementwise copy that bench.py launches with
 bytes are calibrated HBM bytes per launch.  Writes, into --out:
 
 With --only, bench.py runs that side section alone (bench.py --only ...) and the
-files are named insert_rows_c5_chunk_and_c3_decode.*, dcp_<workload>.* or prefix_<workload>.*
+files are named cache_insert_c5_chunk_and_c3_decode.*, dcp_<workload>.* or prefix_<workload>.*
 instead.
 
   layer_step_<workload>.md           per-kernel launches and durations, calibrated HBM
@@ -110,10 +110,11 @@ def main():
     shutil.rmtree(raw, ignore_errors=True)
 
     only = ["--only", args.only] if args.only else []
-    tag = {None: f"layer_step_{w}", "insert": "insert_rows_c5_chunk_and_c3_decode", "dcp": f"dcp_{w}",
+    tag = {None: f"layer_step_{w}", "insert": "cache_insert_c5_chunk_and_c3_decode", "dcp": f"dcp_{w}",
            "prefix": f"prefix_{w}"}[args.only]
     title = {None: f"MSA layer step, workload {w}",
-             "insert": "quantise-and-insert (msa_cache_insert), c5 prefill chunk and c3_128k decode token",
+             "insert": "quantise-and-insert (msa_cache_insert_many, msa_cache_insert), c5 prefill chunk and "
+                       "c3_128k decode token",
              "dcp": f"single-GPU DCP (4 shard scans, local top-16s, merge), workload {w}",
              "prefix": f"shared-prefix index scan against the unshared scan, workload {w}"}[args.only]
     trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(raw, "trace"), "-o", "run",
@@ -128,6 +129,17 @@ def main():
         if run(cmd, os.path.join(args.out, f"{tag}_{k}.log")) != 0:
             sys.exit(f"rocprofv3 pass {k} failed; see {args.out}/{tag}_{k}.log")
 
+    # per-dispatch durations by launch shape (grid size), for kernels launched with several shapes
+    shapes = {}
+    for f in glob.glob(os.path.join(raw, "trace", "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "")
+                if "msa::" not in name:
+                    continue
+                grid = "x".join(row[k] for k in sorted(row) if k.startswith("Grid_Size"))
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                shapes.setdefault((short(name), grid), []).append(dur)
     # kernel trace statistics
     stats = {}
     for f in glob.glob(os.path.join(raw, "trace", "**", "*kernel_stats.csv"), recursive=True):
@@ -182,6 +194,16 @@ def main():
     for name, e in kernels.items():
         lines.append(f"| `{name}` | {e.get('calls', '')} | {e.get('avg_us', 0):.2f} | {e.get('min_us', 0):.2f} | "
                      f"{e.get('max_us', 0):.2f} | {e.get('fetch_bytes', 0):,.0f} | {e.get('write_bytes', 0):,.0f} |")
+    grids_of = {}
+    for name, grid in shapes:
+        grids_of.setdefault(name, set()).add(grid)
+    multi = sorted(name for name, grids in grids_of.items() if len(grids) > 1)
+    if multi:
+        lines += ["", "Kernels launched with several grid sizes, by launch shape (kernel trace):", "",
+                  "| kernel | grid (threads) | launches | avg us | min us |", "|---|---|---|---|---|"]
+        for (name, grid), durs in sorted(shapes.items()):
+            if name in multi:
+                lines.append(f"| `{name}` | {grid} | {len(durs)} | {sum(durs) / len(durs):.2f} | {min(durs):.2f} |")
     with open(os.path.join(args.out, f"{tag}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines), flush=True)
