@@ -74,6 +74,8 @@ msa_status attention(const msa_problem* prob, const void* q, msa_dtype q_dtype, 
     return MSA_ERR_INVALID_ARG;
   if (block_scores != nullptr && !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;
   if (!good_scale(q_scale) || !good_scale(softmax_scale)) return MSA_ERR_INVALID_ARG;
+  // the combined logit scale (in the exp2 domain) must itself be a positive finite float
+  if (!good_scale(softmax_scale * q_scale * k->tensor_scale * 1.4426950408889634f)) return MSA_ERR_INVALID_ARG;
   if (msa_workspace_size(prob, MSA_CALL_ATTN) > workspace_bytes) return MSA_ERR_WORKSPACE;
   (void)workspace;
   return hip_status(msa::launch_attention(to_args(prob), q, (int)q_dtype, q_scale, to_args(k),

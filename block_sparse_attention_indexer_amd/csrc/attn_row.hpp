@@ -351,7 +351,8 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
 #pragma unroll
     for (int kt = 0; kt < kVAhead<KT>; ++kt) vraw[kt] = load_v_tile<KT>(vbase, vsb, kt * 16 + 2 * kpl, dgl);
 
-    // ---------------- S^T = K Q^T, 8 tiles of 16 keys (exp2 domain)
+    // ---------------- S^T = K Q^T, 8 tiles of 16 keys (raw dot products; the
+    // softmax scale c_log2 > 0 enters in the exponent's FMA below)
     const bool full = nkeys == kBlock;   // uniform: no key of the block is past p
     float x[8][4];
 #pragma unroll
@@ -364,7 +365,7 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
       // lane (Q, head j) holds keys kt*16 + 4Q + r
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[kt][r] = acc[r] * c_log2;
+      for (int r = 0; r < 4; ++r) x[kt][r] = acc[r];
       if (!full) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -377,7 +378,8 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kt][r]);
-    mx = max_over_quarters(mx);
+    // rounding is monotone and c_log2 > 0, so this is the max of the scaled logits
+    mx = max_over_quarters(mx) * c_log2;
     const float m_new = fmaxf(m, mx);
     if (m != NEG_INF && m_new != m) {          // rescale what earlier blocks left
       const float alpha = fast_exp2(m - m_new);
@@ -391,7 +393,7 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        x[kt][r] = fast_exp2(x[kt][r] - m);
+        x[kt][r] = fast_exp2(fmaf(x[kt][r], c_log2, -m));
         s += x[kt][r];
       }
     l += sum_over_quarters(s);

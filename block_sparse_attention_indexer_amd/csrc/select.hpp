@@ -84,11 +84,20 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
     if (tid < kTopK) sel_sh[tid] = tid <= own ? tid : -1;
     return;
   }
+  // all of the row's loads in flight before the first use (ne is uniform;
+  // indices past the candidates are clamped and their keys dropped)
+  const int ne = min(E, (own + NT - 1) / NT);
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] = 0.0f;
+    if (e < ne) v[e] = S[min(tid + e * NT, own - 1)];
+  }
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = tid + e * NT;
-    key[e] = i < own ? select_key(S[i], i) : 0ull;
+    key[e] = (e < ne && i < own) ? select_key(v[e], i) : 0ull;
   }
   uint64_t prefix, mask;
   radix_cut<NT, E>(key, kTopK - 1, prefix, mask);   // own >= 16 older blocks

@@ -47,11 +47,21 @@ __global__ __launch_bounds__(NT) void topk_radix_kernel(
   const float* S = block_scores + row * max_blocks;
   const int n = own;   // candidates: blocks 0 .. own-1
 
+  // The row's loads are all issued before the first is used: ne (uniform) is
+  // the number of slots that reach a candidate, and indices past the row are
+  // clamped to its last candidate (their keys are dropped below).
+  const int ne = min(E, (n + NT - 1) / NT);
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] = 0.0f;
+    if (e < ne) v[e] = S[min(tid + e * NT, n - 1)];
+  }
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = tid + e * NT;
-    key[e] = i < n ? ((uint64_t)order_key(S[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
+    key[e] = (e < ne && i < n) ? ((uint64_t)order_key(v[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
   }
   // Index 0xFFFFFFFF is never a block, so a real key is never 0: 0 marks "no key".
   uint64_t prefix = 0, mask = 0;

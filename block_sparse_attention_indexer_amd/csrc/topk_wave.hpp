@@ -121,12 +121,21 @@ __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out,
     return;
   }
   const int n = own;
-  uint32_t k32[E];
+  // ne (uniform): the slots that reach a candidate; their loads are all issued
+  // before the first is used, indices past the row clamped to its last candidate
+  const int ne = min(E, (n + 63) / 64);
+  float v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = lane + 64 * e;
-    k32[e] = i < n ? order_key(COHERENT ? coherent_load(S + i) : S[i]) : 0u;
+    v[e] = 0.0f;
+    if (e < ne) {
+      const float* p = S + min(lane + 64 * e, n - 1);
+      v[e] = COHERENT ? coherent_load(p) : *p;
+    }
   }
+  uint32_t k32[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) k32[e] = (e < ne && lane + 64 * e < n) ? order_key(v[e]) : 0u;
   auto key_of = [&](int e) -> uint64_t {
     return ((uint64_t)k32[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * e));
   };

@@ -136,6 +136,8 @@ msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, in
  *   k, v         caches with heads = 4 (F32 with F32 q; FP8 or NVFP4 with FP8 q).
  *   sel          device [B][T][4][16] as written by msa_block_topk.
  *   softmax_scale  logits are softmax_scale * (q . k) (1/sqrt(128) for MSA).
+ *                softmax_scale * q_scale * k->tensor_scale * log2(e) must be a
+ *                positive finite float, else MSA_ERR_INVALID_ARG.
  *   out          device out [B][T][64][128] fp32.
  *   lse          device out, nullable, [B][T][64] fp32: natural-log
  *                log-sum-exp of the scaled logits.

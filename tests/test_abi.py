@@ -99,6 +99,9 @@ def test_attention_and_topk_validation(lib):
     assert call(lib.msa_sparse_attn_decode, args(sel=None)) == M.MSA_ERR_INVALID_ARG
     assert call(lib.msa_sparse_attn_decode, args(out=None)) == M.MSA_ERR_INVALID_ARG
     assert call(lib.msa_sparse_attn_decode, args(sm=0.0)) == M.MSA_ERR_INVALID_ARG
+    # each scale valid, but their product (the logit scale) underflows or overflows a float
+    assert call(lib.msa_sparse_attn_decode, args(sm=1e-30, qs=1e-30)) == M.MSA_ERR_INVALID_ARG
+    assert call(lib.msa_sparse_attn_decode, args(sm=1e30, qs=1e30)) == M.MSA_ERR_INVALID_ARG
     assert call(lib.msa_sparse_attn_decode, args(v=_cache(heads=4, dtype=M.MSA_FP8_E4M3))) == M.MSA_ERR_UNSUPPORTED
     assert call(lib.msa_sparse_attn_decode, args(k=_cache(heads=1))) == M.MSA_ERR_INVALID_ARG
     assert call(lib.msa_sparse_attn_decode, args(), prob=_prob(tokens=9)) == M.MSA_ERR_UNSUPPORTED
