@@ -544,6 +544,42 @@ def cpu_baseline(wl, dequant, sample):
                       f"{total:.1f} s of CPU time"}
 
 
+def graph_timing(wl, dequant, path, steps):
+    """The same layer step captured once in a HIP graph and replayed: ms per replay
+    over `steps` back-to-back replays between two HIP events.  Before timing, three
+    replays, each followed by an eager step, must leave outputs bit-identical to the
+    eager step's (the path records no memset nodes)."""
+    import torch
+    ref_sel, ref_out = wl.sel.clone(), wl.out.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wl.step(dequant, path=path)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        wl.step(dequant, path=path)
+    identical = True
+    for _ in range(3):
+        wl.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        identical &= bool(torch.equal(wl.sel, ref_sel) and torch.equal(wl.out, ref_out))
+        wl.step(dequant, path=path)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return {"ms_per_step": round(ms, 5), "layer_steps_per_s": round(1e3 / ms, 2),
+            "replays_identical_to_eager": identical}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -604,6 +640,12 @@ def main():
     torch.cuda.synchronize()
     per_call = np.array([[evb[k][i].elapsed_time(evb[k][i + 1]) for i in range(ncalls)] for k in range(Kb)]).mean(axis=0)
 
+    step_ev = np.array([evb[k][0].elapsed_time(evb[k][ncalls]) for k in range(Kb)])
+    timing = {"step_event_ms": {"median": round(float(np.median(step_ev)), 5),
+                                "p10": round(float(np.percentile(step_ev, 10)), 5),
+                                "p90": round(float(np.percentile(step_ev, 90)), 5), "steps": Kb},
+              "graph": graph_timing(wl, args.dequant, path, K)}
+
     sel = wl.sel.cpu().numpy()
     b_idx, b_topk, b_attn = algorithmic_bytes(wl, sel)
     total_bytes = b_idx + b_topk + b_attn
@@ -649,6 +691,7 @@ def main():
                      "traffic": measured_traffic(w.name, indexer_kernel_name(w, args.dequant, path,
                                                                               wl.lay.max_blocks))},
         "cpu_baseline": None,
+        "timing": timing,
     }
     if w.T <= 4 and w.kv_dtype != "f32" and not args.no_sides:
         out["dcp"] = dcp_section(wl, args.dequant)
