@@ -149,7 +149,15 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   // blocks [c0, c_comp) of this chunk have visible keys; [c_comp, c_end) get -inf
   const int c_comp = max(c0, min(c_end, min(nb, own_last + 1)));
   const float NEG_INF = -__builtin_inff();
-  const float QNAN = __builtin_nanf("");
+  // A block whose page id is unreadable is marked NaN through the bit pattern
+  // (an integer select and store): this file is compiled without NaN
+  // semantics (-fno-honor-nans: no MFMA result is NaN, and without the flag
+  // every fmaxf of one is preceded by a canonicalising max), under which a
+  // float select of a NaN constant could be folded away.
+  constexpr uint32_t kQNanBits = 0x7FC00000u;
+  auto mark = [&](float* dst, bool bad_blk, float v) {
+    *reinterpret_cast<uint32_t*>(dst) = bad_blk ? kQNanBits : __builtin_bit_cast(uint32_t, v);
+  };
   const size_t tstride = (size_t)max_blocks * kBlock;
 
   if (FP8MODE) build_fp8_lut(lut);
@@ -280,8 +288,8 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int key = i * kBlock + kh * 64 + kt * 16 + 4 * Q + r;
-                token_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * tstride + key] =
-                    bad ? QNAN : (key <= p_of[rr] ? acc[rr][kt][r] * sigma : NEG_INF);
+                mark(&token_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * tstride + key], bad,
+                     key <= p_of[rr] ? acc[rr][kt][r] * sigma : NEG_INF);
               }
           }
         }
@@ -290,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const float mx = quarter_max4(m, lane);              // query row n of row tile Q
     {
       const int t = t0 + 4 * (4 * wave + Q) + (n >> 2);
-      if (t < Tn) block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i] = bad ? QNAN : mx * sigma;
+      if (t < Tn) mark(&block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i], bad, mx * sigma);
     }
 
     if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves], half_ld);

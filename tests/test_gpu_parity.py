@@ -199,14 +199,24 @@ def test_deterministic_and_page_order_invariant(M):
         assert np.array_equal(r1[k], r3[k]), k
 
 
-def test_out_of_range_page_gives_nan_not_a_fault(M):
-    case = H.HostCase("tiny_fp8").upload()
+@pytest.mark.parametrize("wname", ["tiny_fp8", "tiny_spec", "tiny_prefill"])
+def test_out_of_range_page_gives_nan_not_a_fault(M, wname):
+    # decode scan, speculative scan and the prefill GEMM (built without NaN semantics,
+    # so its NaN mark must survive as a bit pattern)
+    case = H.HostCase(wname).upload()
     tab = case.lay.block_table.numpy().copy()
     tab[0, 2] = case.lay.num_pages + 5            # never dereferenced by the kernels
     case.d_table = torch.from_numpy(tab).cuda()
     res = H.to_host(H.run_path(case, "exact", attention=False))
-    assert np.isnan(res["block_scores"][0, :, :, 2]).all()
-    assert not np.isnan(res["block_scores"][1]).any()
+    bs = res["block_scores"]
+    seq = case.lay.seq_lens.numpy()
+    T = case.w.T
+    visible = (seq[0] - T + np.arange(T)) // 128 >= 2        # tokens whose own block is at or past 2
+    assert visible.any()
+    assert np.isnan(bs[0, visible, :, 2]).all()
+    assert not np.isnan(bs[0, ~visible, :, 2]).any()          # -inf: block 2 is in their future
+    assert not np.isnan(np.delete(bs[0], 2, axis=-1)).any()
+    assert not np.isnan(bs[1]).any()
 
 
 # ------------------------------------------------------------------ full sizes, sampled
