@@ -323,26 +323,31 @@ def insert_section(seed, steps=50):
     """Quantise-and-insert of the new tokens' K, V and index-key rows (NVFP4): c5's
     2 x 4,096-token prefill chunk and one decode token of c3_128k, as one
     msa_cache_insert_many launch and as three msa_cache_insert launches.  Each is
-    launched `steps` times back to back between two HIP events on the stream, and
-    the time per repetition is reported (for the decode token the kernels are a few
+    launched `steps` times back to back in five groups, each between two HIP events
+    on the stream, and the median group's time per repetition is reported (for the decode token the kernels are a few
     microseconds, so there it is bounded by the host's launch rate; the
     rocprofv3 summary has the kernel durations).  Algorithmic bytes: each row read
     once in fp32 (512 B) and written once in NVFP4 (64 B codes + 8 B scales)."""
+    import numpy as np
     import torch
     import block_sparse_attention_indexer_amd as M
     out = {}
 
-    def per_rep_ms(run):
+    def per_rep_ms(run, groups=5):
+        # `steps` launches in `groups` back-to-back groups, each between two events;
+        # the median group's time per launch (one host stall cannot skew it)
         for _ in range(3):
             run()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            run()
-        e1.record()
+        n = max(1, steps // groups)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+        ev[0].record()
+        for gi in range(groups):
+            for _ in range(n):
+                run()
+            ev[gi + 1].record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        return float(np.median([ev[gi].elapsed_time(ev[gi + 1]) / n for gi in range(groups)]))
 
     for name, B, T, L in (("prefill_c5", 2, 4096, 69632), ("decode_c3_128k", 64, 1, 131072)):
         g = torch.Generator(device="cuda").manual_seed(seed)
