@@ -12,7 +12,11 @@
 // key prefix until exactly 15 keys lie at or above it; each pass streams the
 // row from memory (written just before by other workgroups), counts
 // digits in a 256-bin histogram in LDS, and lets one wave scan find the digit.
-// Only one wave takes part, so no workgroup barrier is needed.
+// Only one wave takes part, so no workgroup barrier is needed.  The form that
+// holds the row in registers first tries a threshold pass: the 15th largest of
+// the 64 lane maxima bounds the 15th best key from below, and when at most 64
+// keys reach it they are ranked directly, with no histogram atomics (on rows
+// whose best keys crowd into a few lanes the radix select runs instead).
 #pragma once
 #include "common.hpp"
 
@@ -22,7 +26,28 @@ struct WaveTopkLds {
   uint32_t hist[256];
   int32_t won[kTopK];
   uint32_t n_won;
+  uint64_t cand[64];   // threshold candidates (wave_topk_row_regs)
 };
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int j) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, j);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The 15 winners in sh.won (any order) plus the own block, written ascending to
+// out[0..15] by one wave.
+template <bool COHERENT>
+__device__ __forceinline__ void wave_rank_and_store(const WaveTopkLds& sh, int own, int32_t* out, int lane) {
+  const int32_t mine = lane < kTopK - 1 ? sh.won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
+  int rank = 0;
+#pragma unroll
+  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
+  if (lane < kTopK) {
+    if (COHERENT) __hip_atomic_store(out + rank, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else out[rank] = mine;
+  }
+}
 
 __device__ __forceinline__ uint64_t topk_key(float s, int i) {
   return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
@@ -99,11 +124,7 @@ __device__ inline void wave_topk_row(const float* S, int own, int32_t* out, Wave
     }
   }
   lds_wait();
-  const int32_t mine = lane < kTopK - 1 ? sh.won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
-  int rank = 0;
-#pragma unroll
-  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
-  if (lane < kTopK) __hip_atomic_store(out + rank, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wave_rank_and_store<true>(sh, own, out, lane);
 }
 
 // The same selection with the row held in registers: each lane loads its
@@ -139,6 +160,47 @@ __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out,
   auto key_of = [&](int e) -> uint64_t {
     return ((uint64_t)k32[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * e));
   };
+
+  // Threshold pass.  tau, the 15th largest of the 64 lane maxima, is at most the
+  // row's 15th best key (at least 15 lanes hold a key >= tau), so the 15 winners
+  // are among the keys >= tau.  With n >= 16 candidates lanes 0..15 all hold one,
+  // so exactly one lane has 14 larger lane maxima.  When at most 64 keys reach
+  // tau (the usual case) they are ranked directly; otherwise the radix select
+  // below runs.  No LDS atomics either way on this path.
+  {
+    uint64_t lmax = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lane + 64 * e < n) lmax = key_of(e) > lmax ? key_of(e) : lmax;
+    int greater = 0;
+#pragma unroll 1
+    for (int j = 0; j < 64; ++j) greater += readlane_u64(lmax, j) > lmax ? 1 : 0;
+    const uint64_t at15 = __ballot(lmax != 0ull && greater == kTopK - 2);
+    const uint64_t tau = readlane_u64(lmax, __builtin_ctzll(at15));
+    uint32_t ncand = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ncand += (uint32_t)__popcll(__ballot(lane + 64 * e < n && key_of(e) >= tau));
+    if (ncand <= 64) {
+      uint32_t base = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool c = lane + 64 * e < n && key_of(e) >= tau;
+        const uint64_t bm = __ballot(c);
+        if (c) sh.cand[base + (uint32_t)__popcll(bm & ((1ull << lane) - 1ull))] = key_of(e);
+        base += (uint32_t)__popcll(bm);
+      }
+      lds_wait();
+      const uint64_t mine = (uint32_t)lane < ncand ? sh.cand[lane] : 0ull;
+      int r = 0;
+#pragma unroll 1
+      for (uint32_t j = 0; j < ncand; ++j) r += sh.cand[j] > mine ? 1 : 0;
+      if ((uint32_t)lane < ncand && r < kTopK - 1) sh.won[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)mine);
+      lds_wait();
+      wave_rank_and_store<COHERENT>(sh, own, out, lane);
+      return;
+    }
+  }
+
   uint64_t prefix = 0, mask = 0;
   uint32_t need = kTopK - 1;
 #pragma unroll 1
@@ -193,14 +255,7 @@ __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out,
     }
   }
   lds_wait();
-  const int32_t mine = lane < kTopK - 1 ? sh.won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
-  int rank = 0;
-#pragma unroll
-  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
-  if (lane < kTopK) {
-    if (COHERENT) __hip_atomic_store(out + rank, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else out[rank] = mine;
-  }
+  wave_rank_and_store<COHERENT>(sh, own, out, lane);
 }
 
 }  // namespace msa

@@ -633,3 +633,79 @@ def test_topk_sparse_attn_full_size(M):
     torch.cuda.synchronize()
     assert np.array_equal(sel.cpu().numpy(), ref["sel"])
     assert np.array_equal(out.cpu().numpy(), ref["out"]) and np.array_equal(lse.cpu().numpy(), ref["lse"])
+
+
+# ------------------------------------------------------------------ crafted score rows
+
+def _crafted_scores(rng, B, T, maxb, L, period, width):
+    """Score rows for the four groups: random; a "crowded" row whose best scores fill
+    the first 14 lanes (or waves) of the selection and whose 15th lane (or wave) sits
+    lower, so that more than 64 keys reach the threshold; scores rounded to integers
+    (ties, broken by block index); 10% NaN (below every number).  Blocks at or past a
+    token's own block hold +inf, which the selection must never read."""
+    s = rng.standard_normal((B, T, 4, maxb)).astype(np.float32)
+    slot = (np.arange(maxb) % period) // width     # the lane (or wave) that holds each block
+    s[:, :, 1, :] += np.where(slot < 14, 200.0, np.where(slot == 14, 100.0, 0.0)).astype(np.float32)
+    s[:, :, 2, :] = np.round(s[:, :, 2, :] * 2.0)
+    s[:, :, 3, :][rng.random((B, T, maxb)) < 0.1] = np.nan
+    for b in range(B):
+        for t in range(T):
+            s[b, t, :, (L[b] - T + t) // 128:] = np.inf
+    return s
+
+
+def _oracle_sel(scores, L, T):
+    """The oracle's selection; NaN scores enter as -1e30 (below every finite score,
+    tied among themselves, so block order decides), as the library ranks NaN."""
+    B, _, G, _ = scores.shape
+    sel = np.empty((B, T, G, 16), dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            own = (int(L[b]) - T + t) // 128
+            for g in range(G):
+                row = np.where(np.isnan(scores[b, t, g]), -1e30, scores[b, t, g]).astype(np.float64)
+                sel[b, t, g] = OM.select_blocks(row, own)
+    return sel
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_block_topk_crafted_rows(M, T):
+    """msa_block_topk on crafted rows: 256 rows (a workgroup per row) and 4,096 rows
+    (a wave per row: threshold pass, with the crowded rows taking the radix fallback)."""
+    _say("block_topk crafted", T)
+    rng = np.random.default_rng(4321 + T)
+    B, maxb = (64, 1000) if T == 1 else (16, 1000)
+    L = rng.integers(T, maxb * 128 + 1, size=B).astype(np.int32)
+    L[:5] = [T, 16 * 128 + T - 1, 17 * 128 + T, 64 * 15 * 128 + 5, maxb * 128]
+    scores = _crafted_scores(rng, B, T, maxb, L, 64, 1)
+    seq = torch.from_numpy(L).cuda()
+    table = torch.zeros((B, maxb), dtype=torch.int32, device="cuda")
+    prob = M.problem(seq, table, T)
+    sel = torch.full((B, T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    M.msa_block_topk(prob, torch.from_numpy(scores).cuda(), sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), _oracle_sel(scores, L, T))
+
+
+def test_selecting_attention_crafted_rows(M):
+    """The attention launch that selects its own rows (a 16-wave workgroup per row,
+    radix select) on crafted score rows of 2,344 blocks -- crowded, tied and NaN rows:
+    the selection equals the oracle's and msa_block_topk's."""
+    _say("selecting attention crafted")
+    case = H.HostCase("long_rows").upload()
+    w, lay = case.w, case.lay
+    rng = np.random.default_rng(99)
+    L = lay.seq_lens.numpy()
+    scores = _crafted_scores(rng, w.B, w.T, lay.max_blocks, L, 1024, 64)
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.from_numpy(scores).cuda()
+    sel = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    sel2 = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+    M.msa_topk_sparse_attn(prob, bs, sel, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2], case.d_caches["v"][2],
+                           "exact", H.SOFTMAX_SCALE, out, None)
+    M.msa_block_topk(prob, bs, sel2)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    assert np.array_equal(got, _oracle_sel(scores, L, w.T))
+    assert np.array_equal(got, sel2.cpu().numpy())
