@@ -340,9 +340,15 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   }
   const uint8_t* q8 = (const uint8_t*)idx_q;
   // Pages per wave: the largest of the kernel's three sizes whose grid still gives
-  // every CU two workgroups (a shard, or few long sequences, has few chunks).
-  const int want = 2 * current_cu_count();
-  auto pick_ppw = [&](int big) {
+  // every CU `per_cu` workgroups (a shard, or few long sequences, has few chunks).
+  // The one-token scan asks for one workgroup per CU: long-lived waves beat a
+  // second, shorter workgroup (c2, 32 x 256 blocks: 8 pages per wave in 31 us
+  // against 4 pages in 34.6 us); the others are unchanged by it.
+#ifndef MSA_DEC_WG_PER_CU
+#define MSA_DEC_WG_PER_CU 1
+#endif
+  auto pick_ppw = [&](int big, int per_cu) {
+    const int want = per_cu * current_cu_count();
     for (int ppw = big; ppw > big / 4; ppw /= 2)
       if ((int64_t)p.B * ((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)) >= want) return ppw;
     return big / 4;
@@ -350,7 +356,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   if (p.T == 1 && !(fp8mode && k.dtype == 2 && sel != nullptr)) {
     // one token: 4x4x4 MFMA scan; the FP8-rounded NVFP4 reading decodes through the
     // LDS table instead of scaling partial dots (not fused with the selection)
-    const int ppw = pick_ppw(kDec1PagesPerWave);
+    const int ppw = pick_ppw(kDec1PagesPerWave, MSA_DEC_WG_PER_CU);
     const bool f8 = fp8mode && k.dtype == 2;
     const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
     const bool ts = token_scores != nullptr;
@@ -378,7 +384,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
 #undef MSA_DEC1_PPW
 #undef MSA_DEC1_LAUNCH
   } else if (p.T <= 4) {
-    const int ppw = pick_ppw(kDecPagesPerWave);
+    const int ppw = pick_ppw(kDecPagesPerWave, 2);
     const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
 #define MSA_DEC_LAUNCH(KT, FM, TS, PPW)                                                                      \
   hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2),            \
