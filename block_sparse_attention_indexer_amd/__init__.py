@@ -65,6 +65,10 @@ def _lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
                                "python -m block_sparse_attention_indexer_amd.build")
+        # torch first: its bundled HIP runtime is then the one libmsa binds to.  Loaded
+        # the other way round, the process would hold two HIP runtimes, and torch's
+        # streams and device pointers would be foreign to the library's launches.
+        import torch  # noqa: F401
         lib = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         P = ctypes.POINTER

@@ -268,3 +268,15 @@ def test_cache_insert_many_validation(lib):
     assert call(caches=[_cache(heads=4), _cache(heads=2)]) == M.MSA_ERR_INVALID_ARG
     assert call(caches=[_cache(heads=4), _cache(heads=1, tensor_scale=0.0)]) == M.MSA_ERR_INVALID_ARG
     assert call(prob=_prob(block_size=64)) == M.MSA_ERR_UNSUPPORTED
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    # loading the library first must not pull in a second HIP runtime next to torch's
+    import subprocess
+    import sys
+    code = ("import os, sys; sys.path.insert(0, %r); import block_sparse_attention_indexer_amd as M; M._lib(); "
+            "m = open('/proc/%%d/maps' %% os.getpid()).read(); "
+            "print(len(set(l.split()[-1] for l in m.splitlines() if 'amdhip64' in l)))") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
