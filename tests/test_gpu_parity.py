@@ -709,3 +709,41 @@ def test_selecting_attention_crafted_rows(M):
     got = sel.cpu().numpy()
     assert np.array_equal(got, _oracle_sel(scores, L, w.T))
     assert np.array_equal(got, sel2.cpu().numpy())
+
+
+def test_decode_step_graph_replays(M):
+    """The decode layer step (index scan, then the selecting attention) captured in a HIP
+    graph: three replays, each followed by an eager step, all bit-identical to eager."""
+    _say("graph replays tiny_nvfp4")
+    case = H.HostCase("tiny_nvfp4").upload()
+    w, lay = case.w, case.lay
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.empty((w.B, w.T, 4, lay.max_blocks), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.B, w.T, 4, 16), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+
+    def step():
+        M.msa_indexer_scores(prob, case.d_idx_q, w.q_dtype, 1.0, case.d_caches["idx_k"][2], "exact", bs, None)
+        M.msa_topk_sparse_attn(prob, bs, sel, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2],
+                               case.d_caches["v"][2], "exact", H.SOFTMAX_SCALE, out, None)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (bs.clone(), sel.clone(), out.clone())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        bs.zero_(), sel.zero_(), out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bs, ref[0]) and torch.equal(sel, ref[1]) and torch.equal(out, ref[2]), rep
+        step()
+        torch.cuda.synchronize()
+    del g
