@@ -149,9 +149,10 @@ __device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, ui
     r.s[0] = keep0 ? r.s[0] : 0u;
     r.s[1] = keep1 ? r.s[1] : 0u;
   } else {
-    const uint4 z = {0u, 0u, 0u, 0u};
-    r.c[0] = keep0 ? r.c[0] : z;
-    r.c[1] = keep1 ? r.c[1] : z;
+    // masked per dword: a select of whole uint4 values went through scratch memory
+    const uint32_t m0 = keep0 ? 0xFFFFFFFFu : 0u, m1 = keep1 ? 0xFFFFFFFFu : 0u;
+    r.c[0].x &= m0; r.c[0].y &= m0; r.c[0].z &= m0; r.c[0].w &= m0;
+    r.c[1].x &= m1; r.c[1].y &= m1; r.c[1].z &= m1; r.c[1].w &= m1;
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
