@@ -351,6 +351,47 @@ def ragged_section(dequant, seed, steps=20, warmup=3):
             "pct_of_peak_hbm_step": round(100 * total / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1)}
 
 
+def ceilings_section(reps=7):
+    """Ceilings measured on this GPU with the library's probes: one streaming read of
+    a 2 GiB buffer (msa_probe_stream_read) and the dense 16x16x32 f16 MFMA issue rate
+    with no memory traffic (msa_probe_mfma_f16), each the median of `reps` event-timed
+    launches, beside the published peaks the roofline fractions use."""
+    import torch
+    import block_sparse_attention_indexer_amd as M
+
+    def median_ms(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    nbytes = 2 << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(M.MSA_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    ms_read = median_ms(lambda: M.msa_probe_stream_read(buf, sink))
+    del buf
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 8 * cus, 2000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    ms_mfma = median_ms(lambda: M.msa_probe_mfma_f16(out, wgs, iters))
+    flops = wgs * 4 * iters * 16 * 16 * 16 * 32 * 2
+    gbps = nbytes / (ms_read * 1e-3) / 1e9
+    tflops = flops / (ms_mfma * 1e-3) / 1e12
+    return {"stream_read": {"bytes": nbytes, "ms": round(ms_read, 4), "GBps": round(gbps, 1),
+                            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+            "mfma_f16": {"workgroups": wgs, "ms": round(ms_mfma, 4), "TFLOPs": round(tflops, 1),
+                         "frac_of_f16_peak": round(tflops / F16_MFMA_PEAK_TFLOPS, 4)},
+            "compute_units": cus}
+
+
 def insert_section(seed, steps=50):
     """Quantise-and-insert of the new tokens' K, V and index-key rows (NVFP4): c5's
     2 x 4,096-token prefill chunk and one decode token of c3_128k, as one
@@ -736,6 +777,9 @@ def main():
         out["prefix"] = prefix_section(wl, args.dequant)
     if args.workload == "c3_128k" and not args.no_sides:
         out["ragged_c3"] = ragged_section(args.dequant, args.seed)
+        out["ceilings"] = ceilings_section()
+        out["roofline"]["frac_of_measured_stream_read"] = round(
+            achieved_idx / out["ceilings"]["stream_read"]["GBps"], 4)
     if not args.no_prefill and args.workload != "c5":
         out["prefill"] = prefill_section(args.dequant, args.seed)
         out["insert"] = insert_section(args.seed)

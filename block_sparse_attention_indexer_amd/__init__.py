@@ -30,7 +30,9 @@ EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_spa
             "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
             "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn", "msa_cache_insert_many",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
-            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
+            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version",
+            "msa_probe_stream_read", "msa_probe_mfma_f16")
+MSA_PROBE_SINK_WORDS = 4096
 
 DTYPES = {"f32": MSA_F32, "fp8": MSA_FP8_E4M3, "nvfp4": MSA_NVFP4}
 DEQUANT = {"exact": MSA_DQ_EXACT, "fp8": MSA_DQ_FP8}
@@ -100,6 +102,8 @@ def _lib():
             "msa_unpack_nvfp4": [vp, vp, i64, i32, f32, ctypes.c_int, vp, vp],
             "msa_status_string": [ctypes.c_int],
             "msa_abi_version": [],
+            "msa_probe_stream_read": [vp, sz, vp, vp],
+            "msa_probe_mfma_f16": [vp, i32, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -261,6 +265,21 @@ def msa_cache_insert(prob, x, cache_, stream=None):
 
 def msa_workspace_size(prob, which):
     return int(_lib().msa_workspace_size(ctypes.byref(prob), int(which)))
+
+
+def msa_probe_stream_read(buf, sink, stream=None):
+    """Measurement probe (include/msa_probe.h): one streaming read of `buf`."""
+    if sink.numel() * sink.element_size() < 4 * MSA_PROBE_SINK_WORDS:
+        raise ValueError("sink must hold MSA_PROBE_SINK_WORDS uint32")
+    _check(_lib().msa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "msa_probe_stream_read")
+
+
+def msa_probe_mfma_f16(out, workgroups, iters, stream=None):
+    """Measurement probe (include/msa_probe.h): dense 16x16x32 f16 MFMA issue rate."""
+    if out.numel() < workgroups * 256:
+        raise ValueError("out must hold workgroups * 256 floats")
+    _check(_lib().msa_probe_mfma_f16(_ptr(out), int(workgroups), int(iters), _stream(stream)), "msa_probe_mfma_f16")
 
 
 def msa_pack_fp8(x, scale, out, stream=None):

@@ -13,8 +13,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "msa.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:msa_status|size_t|const char\*|int)\s+(msa_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:msa_status|size_t|const char\*|int)\s+(msa_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -280,3 +284,14 @@ def test_library_binds_to_torchs_hip_runtime():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_probe_validation(lib):
+    assert lib.msa_probe_stream_read(None, 64, 4096, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_stream_read(64, 0, 4096, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_stream_read(64, 100, 4096, None) == M.MSA_ERR_INVALID_ARG     # not a multiple of 16
+    assert lib.msa_probe_stream_read(72, 64, 4096, None) == M.MSA_ERR_INVALID_ARG      # not 16-byte aligned
+    assert lib.msa_probe_stream_read(64, 64, None, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_f16(None, 1, 1, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_f16(64, 0, 1, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_probe_mfma_f16(64, 1, 0, None) == M.MSA_ERR_INVALID_ARG

@@ -747,3 +747,17 @@ def test_decode_step_graph_replays(M):
         step()
         torch.cuda.synchronize()
     del g
+
+
+def test_probes_run(M):
+    """The measurement probes launch and finish: a streaming read leaves its sink
+    untouched for zero-filled data, and the MFMA probe writes finite sums."""
+    _say("probes")
+    buf = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(M.MSA_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    M.msa_probe_stream_read(buf, sink)
+    out = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    M.msa_probe_mfma_f16(out, 4, 10)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    assert bool(torch.isfinite(out).all())
