@@ -342,8 +342,8 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   // Pages per wave: the largest of the kernel's three sizes whose grid still gives
   // every CU `per_cu` workgroups (a shard, or few long sequences, has few chunks).
   // The one-token scan asks for one workgroup per CU: long-lived waves beat a
-  // second, shorter workgroup (c2, 32 x 256 blocks: 8 pages per wave in 31 us
-  // against 4 pages in 34.6 us); the others are unchanged by it.
+  // second, shorter workgroup (32 sequences x 256 blocks: 8 pages per wave in
+  // 31 us against 4 pages in 34.6 us); longer contexts are unchanged by it.
 #ifndef MSA_DEC_WG_PER_CU
 #define MSA_DEC_WG_PER_CU 1
 #endif
