@@ -319,13 +319,15 @@ def prefill_section(dequant, seed, steps=5, warmup=2):
                           "traffic": measured_traffic("c5", role="attention")}}
 
 
-def ragged_section(dequant, seed, steps=20, warmup=3):
-    """The decode workload c3 as specified (64 sequences, ragged contexts uniform in
-    [64K, 160K] tokens, NVFP4, 5% outliers): the default step (scan, then the
-    selecting attention), each call bracketed by HIP events, with its algorithmic
-    bytes and the step's HBM rate.  Reported beside the uniform-128K headline."""
+def decode_section(name, dequant, seed, steps=20, warmup=3):
+    """Another decode workload through the default step (scan, then the selecting
+    attention), each call bracketed by HIP events, with its algorithmic bytes and the
+    step's HBM rate; reported beside the uniform-128K headline.  c3: 64 sequences,
+    ragged contexts uniform in [64K, 160K] tokens, NVFP4 with 5% outliers; c4: 16
+    sequences of 262,144 tokens, 4 query tokens each (speculative decode), NVFP4;
+    c2: 32 sequences of 32,768 tokens, FP8 (its 203 MB fit the Infinity Cache)."""
     import torch
-    wl = Workload("c3", seed)
+    wl = Workload(name, seed)
     w = wl.w
     for _ in range(warmup):
         wl.step(dequant, path="select")
@@ -340,8 +342,9 @@ def ragged_section(dequant, seed, steps=20, warmup=3):
     scan_ms = float(np.median(t[:, 0]))
     total = b_idx + b_topk + b_attn
     lens = [int(x) for x in wl.lay.seq_lens]
-    return {"workload": f"c3: decode, batch {w.B}, ragged contexts {min(lens)}..{max(lens)} tokens "
-                        f"(sum {sum(lens)}), NVFP4 K/V and index keys, FP8 queries, shuffled pages",
+    return {"workload": f"{name}: decode, batch {w.B}, {w.T} query token(s) per sequence, contexts "
+                        f"{min(lens)}..{max(lens)} tokens (sum {sum(lens)}), {w.kv_dtype} K/V and index keys, "
+                        f"{w.q_dtype} queries, shuffled pages",
             "step_ms": round(step_ms, 5), "layer_steps_per_s": round(1e3 / step_ms, 2),
             "sequence_layer_steps_per_s": round(w.B * 1e3 / step_ms, 1),
             "indexer_ms": round(scan_ms, 5), "topk_attention_ms": round(float(np.median(t[:, 1])), 5),
@@ -776,7 +779,9 @@ def main():
         out["dcp"] = dcp_section(wl, args.dequant)
         out["prefix"] = prefix_section(wl, args.dequant)
     if args.workload == "c3_128k" and not args.no_sides:
-        out["ragged_c3"] = ragged_section(args.dequant, args.seed)
+        out["ragged_c3"] = decode_section("c3", args.dequant, args.seed)
+        out["spec_c4"] = decode_section("c4", args.dequant, 4)
+        out["fp8_c2"] = decode_section("c2", args.dequant, 2)
         out["ceilings"] = ceilings_section()
         out["roofline"]["frac_of_measured_stream_read"] = round(
             achieved_idx / out["ceilings"]["stream_read"]["GBps"], 4)
