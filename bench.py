@@ -19,8 +19,11 @@ the timed region, on the stream it runs on, and ``traffic`` from the rocprofv3
 counter summary under profiles/ (null once the kernel sources changed);
 ``dcp``, ``prefix``, ``prefill`` and ``insert`` time the side sections
 (context-parallel shards, shared-prefix scan, the chunked-prefill workload,
-the cache insert); ``cpu_baseline`` is the CPU fp64 oracle timed on a bounded
-sample.
+the cache insert); ``ragged_c3``, ``spec_c4`` and ``fp8_c2`` run the default
+step on the other decode workloads; ``ceilings`` measures a streaming read and
+the f16 MFMA rate with the library's probes; ``timing`` gives the step's
+median / p10 / p90 and its HIP-graph replay; ``cpu_baseline`` is the CPU fp64
+oracle timed on a bounded sample.
 """
 import argparse
 import json
