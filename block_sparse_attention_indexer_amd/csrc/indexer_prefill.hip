@@ -14,9 +14,9 @@
 // their 64 rows of Q as f16 MFMA operands in registers for the whole chunk.
 // Per block the page is read once (raw bytes are prefetched into registers
 // two blocks ahead of the block being multiplied), dequantised into an f16
-// tile in LDS (double-buffered; rows padded to 272 B and the second half of
-// each row rotated by 4 chunks, so neither the stores nor the operand reads
-// meet bank conflicts), and contracted on 16x16x32 f16 MFMAs (exact
+// tile in LDS (double-buffered; rows padded to 288 B, the 16-byte-aligned
+// stride that measured the fewest LDS bank-conflict cycles), and contracted
+// on 16x16x32 f16 MFMAs (exact
 // products, fp32 sums) as S^T = K Q^T: keys are the MFMA rows, so a lane
 // holds 16 keys of one query row per 64-key half.  The epilogue takes the
 // max over the block's keys in-lane, then across the four lane quarters
@@ -36,7 +36,7 @@ constexpr int kPfTokens = 64;                  // query tokens per workgroup (x 
 #define MSA_PF_CHUNK 16
 #endif
 constexpr int kPfChunk = MSA_PF_CHUNK;         // blocks per workgroup
-constexpr int kPfRowHalves = kHeadDim + 8;     // f16 per LDS key row (272 B)
+constexpr int kPfRowHalves = kHeadDim + 16;   // f16 per LDS key row (288 B)
 constexpr int kPfTileHalves = kBlock * kPfRowHalves;
 
 // 8 NVFP4 codes (one dword, one scale) -> 8 FP8-rounded values as f16, in element order.
@@ -68,9 +68,8 @@ __device__ __forceinline__ void pf_load(PfRaw<KT>& r, const uint8_t* __restrict_
   }
 }
 
-// LDS offset (in f16) of the 16-byte chunk c (dims 8c .. 8c+7) of a tile row:
-// chunks of the second half are rotated by 4.
-__device__ __forceinline__ int pf_chunk(int c) { return 8 * ((c & 8) | ((c + ((c >> 3) << 2)) & 7)); }
+// LDS offset (in f16) of the 16-byte chunk c (dims 8c .. 8c+7) of a tile row.
+__device__ __forceinline__ int pf_chunk(int c) { return 8 * c; }
 
 // Dequantise 64 dims (half `half`) of one key into its f16 tile row.
 template <int KT, bool FP8MODE>
