@@ -48,22 +48,6 @@ def num_blocks(L):
     return (L + BLOCK - 1) // BLOCK
 
 
-# ---------------------------------------------------------------- paging
-
-
-def gather_sequence(pool, block_table_row, L):
-    """Logical-order rows [L, ...] of one sequence from a page pool.
-
-    ``pool`` is [num_pages, 128, ...] (one head, already decoded); logical
-    block i of the sequence lives in page ``block_table_row[i]``.
-    """
-    nb = num_blocks(L)
-    pages = np.asarray(block_table_row[:nb], dtype=np.int64)
-    assert np.all((pages >= 0) & (pages < pool.shape[0])), "page id out of range"
-    rows = pool[pages]
-    return rows.reshape((nb * BLOCK,) + pool.shape[2:])[:L]
-
-
 # ---------------------------------------------------------------- steps 2-3
 
 

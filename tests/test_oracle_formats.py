@@ -171,3 +171,45 @@ def test_fp8_quantize_matches_torch_cast():
     S = np.float32(0.37)
     y = (x / S).astype(np.float64)
     assert np.array_equal(F.fp8_quantize(x, S), torch_e4m3_encode(y))
+
+
+def _e4m3_half_step(v):
+    """Half the spacing of the E4M3 grid at magnitude v (subnormal spacing 2^-9 below
+    2^-6; 2^(floor(log2 v) - 3) in the normal range)."""
+    v = np.asarray(v, np.float64)
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -6)))
+    return 0.5 * np.exp2(e - 3)
+
+
+@pytest.mark.parametrize("S", [float(np.float32(0.37)), float(np.float32(32.0 / 448.0)), 5.0,
+                               float(np.float32(0.0123)), 3.0])
+def test_fp8_tensor_scale_round_trip_bound(S):
+    """The quantiser stores RNE(x / S), so a decoded byte is S * e4m3(byte): the round
+    trip lands within half an E4M3 step of x / S, times S, for every S.  A decoder
+    that divided by S (mirroring the quantiser) would be off by a factor S^2."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.normal(0, 1, 4000), rng.normal(0, 20, 2000) * S, rng.normal(0, 1e-3, 500)])
+    x = x[np.abs(x) / S < 440.0].astype(np.float32)
+    back = F.fp8_dequantize(F.fp8_quantize(x, S), S)
+    y = np.abs(x.astype(np.float64)) / S
+    assert np.all(np.abs(back - x) <= _e4m3_half_step(y) * S * (1 + 1e-6) + 1e-300)
+    # worked values from the definition: byte 0x40 is 2.0 and 0x38 is 1.0 (exponent 8
+    # and 7, bias 7), 0xC4 is -3.0; the decoded value is the tensor scale times that
+    assert F.fp8_dequantize(np.uint8(0x40), 3.0) == 6.0
+    assert F.fp8_dequantize(np.uint8(0x38), 0.25) == 0.25
+    assert F.fp8_dequantize(np.uint8(0xC4), 0.5) == -1.5
+
+
+@pytest.mark.parametrize("s", [float(np.float32(0.37)), 4.0, float(np.float32(1.0 / 48.0))])
+def test_decode_query_applies_its_scale(s):
+    """FP8 query bytes quantised with scale s decode to s * e4m3(byte), within half an
+    E4M3 step of the source; fp32 queries are multiplied by s."""
+    from oracle import msa as OM
+    rng = np.random.default_rng(12)
+    x = (rng.normal(0, 1, (3, 4, 128)) * s * 8).astype(np.float32)
+    x = np.clip(x, -440 * s, 440 * s).astype(np.float32)
+    dq = OM.decode_query(F.fp8_quantize(x, s), "fp8", s)
+    y = np.abs(x.astype(np.float64)) / s
+    assert np.all(np.abs(dq - x) <= _e4m3_half_step(y) * s * (1 + 1e-6))
+    assert np.array_equal(OM.decode_query(x, "f32", s), s * x.astype(np.float64))
+    assert OM.decode_query(np.uint8(0x40), "fp8", s) == 2.0 * s

@@ -375,3 +375,54 @@ def test_dcp_select_all_equals_select_all():
     S = rng.integers(0, 8, (T, 4, M.num_blocks(L))).astype(float)
     for P in (2, 4):
         assert np.array_equal(M.dcp_select_all(S, L, T, P), M.select_all(S, L, T))
+
+
+def test_tensor_scales_enter_where_their_tensors_do():
+    """How the four per-tensor scales act on the layer step, from the definition of a
+    decoded value (scale times stored element) and of softmax attention:
+    * the index-query and index-key scales multiply every block score, so a power-of-
+      two scale multiplies the scores exactly and never changes the selection;
+    * the V scale multiplies the attention output and leaves the LSE alone;
+    * the query and K scales multiply the logits together: only their product counts,
+      and the LSE of logits c*l is the LSE of the logits computed with c folded in.
+    FP8 caches, K and V on different scales."""
+    rng = np.random.default_rng(31)
+    lens, T = [2600, 700], 2
+    B = len(lens)
+    nbs = [(L + 127) // 128 for L in lens]
+    P = sum(nbs)
+    table = np.full((B, max(nbs)), -1, np.int32)
+    perm = rng.permutation(P)
+    table[0, :nbs[0]], table[1, :nbs[1]] = perm[:nbs[0]], perm[nbs[0]:]
+    idx_q = F.fp8_quantize(rng.normal(0, 1, (B, T, 4, 128)), 1.0)
+    q = F.fp8_quantize(rng.normal(0, 1, (B, T, 64, 128)), 1.0)
+
+    def cache(heads, S, seed):
+        x = np.random.default_rng(seed).normal(0, 1, (P, heads, 128, 128)).astype(np.float32)
+        return {"dtype": "fp8", "data": F.fp8_quantize(x, 1.0), "tensor_scale": S}
+
+    def run(iqs, ks, qs, kS, vS):
+        return M.batch_layer(idx_q, q, cache(1, ks, 1), cache(4, kS, 2), cache(4, vS, 3), lens, table, T,
+                             1 / np.sqrt(128), idx_q_dtype="fp8", idx_q_scale=iqs, q_dtype="fp8", q_scale=qs)
+
+    base = run(1.0, 1.0, 1.0, 1.0, 1.0)
+    r = run(2.0, 0.5 * 8, 0.75, 0.4, 3.0)        # index scales multiply to 8, a power of two
+    fin = np.isfinite(base["block_scores"])
+    assert np.array_equal(np.isfinite(r["block_scores"]), fin)
+    assert np.array_equal(r["block_scores"][fin], 8.0 * base["block_scores"][fin])
+    assert np.array_equal(r["sel"], base["sel"])
+    # only q_scale * k_scale matters for the logits; V's scale multiplies the output
+    a = run(1.0, 1.0, 0.75, 0.4, 1.0)
+    b = run(1.0, 1.0, 0.3, 1.0, 3.0)
+    assert np.allclose(3.0 * a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(a["lse"], b["lse"], rtol=1e-12, atol=1e-12)
+    assert not np.allclose(a["out"], base["out"], atol=1e-3)      # the logit scale does act
+    # shrinking the logits to zero leaves the mean of V over the attended keys
+    z = run(1.0, 1.0, 1e-30, 1.0, 1.0)
+    for bb, L in enumerate(lens):
+        V = M.sequence_view(cache(4, 1.0, 3), table[bb], L)
+        for t in range(T):
+            p = L - T + t
+            for h in (0, 37):
+                keys = M.attended_keys(z["sel"][bb, t, h // 16], p)
+                assert np.allclose(z["out"][bb, t, h], V[h // 16, keys].mean(axis=0), atol=1e-12)

@@ -78,6 +78,27 @@ def _insert_one_scale_per_row(cache, x, seq_lens, block_table, T):
     return out
 
 
+_orig_decode_query = M.decode_query
+
+
+def _fp8_dequantize_dividing(b, tensor_scale):
+    # mirrors the quantiser's division instead of undoing it
+    return F.e4m3_value(b) / float(tensor_scale)
+
+
+def _decode_query_ignoring_scale(qarr, dtype, scale):
+    return _orig_decode_query(qarr, dtype, 1.0)
+
+
+def _decode_pages_without_fp8_scale(cache, pages, mode="exact"):
+    # FP8 pages read without their tensor scale
+    c = dict(cache)
+    if c["dtype"] == "fp8":
+        c["tensor_scale"] = 1.0
+    return _orig_decode_pages(c, pages, mode)
+
+
+_orig_decode_pages = M.decode_pages
 _orig_shard_candidates = M.shard_candidates
 _orig_merge = M.merge_candidates
 
@@ -119,6 +140,11 @@ def _merge_ties_to_higher_block(cs, cb, own, k=16):
     (M, ("shard_candidates", _shard_sends_top8), TM.test_dcp_merge_equals_single_gpu_selection),
     (M, ("shard_candidates", _shard_includes_own_block), TM.test_dcp_merge_equals_single_gpu_selection),
     (M, ("merge_candidates", _merge_ties_to_higher_block), TM.test_dcp_merge_equals_single_gpu_selection),
+    (F, ("fp8_dequantize", _fp8_dequantize_dividing), lambda: TF.test_fp8_tensor_scale_round_trip_bound(0.37)),
+    (F, ("fp8_dequantize", _fp8_dequantize_dividing), lambda: TF.test_decode_query_applies_its_scale(4.0)),
+    (M, ("decode_query", _decode_query_ignoring_scale), lambda: TF.test_decode_query_applies_its_scale(4.0)),
+    (M, ("decode_query", _decode_query_ignoring_scale), TM.test_tensor_scales_enter_where_their_tensors_do),
+    (M, ("decode_pages", _decode_pages_without_fp8_scale), TM.test_tensor_scales_enter_where_their_tensors_do),
 ])
 def test_planted_mistake_is_caught(monkeypatch, target, mutant, pin):
     name, fn = mutant

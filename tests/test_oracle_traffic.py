@@ -66,3 +66,34 @@ def test_bench_bytes_model_matches_the_oracle_model():
         keys = sum(min(128, lens[b] - 128 * i) for b in range(B) for g in range(4)
                    for i in set(int(x) for x in sel[b, :, g].reshape(-1) if x >= 0))
         assert attn == TR.attention_bytes(keys, kv, qd, B, T, 64)
+
+
+def test_flop_model_counts_the_oracles_products():
+    """indexer_flops and attention_flops, and bench.py's restatement of them, against
+    the products the oracle forms on a small seeded case: 2*128 flops per finite
+    per-key index score (one 128-dim dot product each), and 2*(2*128) per (query
+    head, attended key) -- one QK dot product and one PV accumulation."""
+    import types
+    import numpy as np
+    import bench
+    from oracle import msa as OM
+    rng = np.random.default_rng(5)
+    lens, T = [700, 3000, 2049], 3
+    idx_pairs = attn_pairs = 0
+    sels = []
+    for L in lens:
+        iq = rng.normal(0, 1, (T, 4, 128))
+        ik = rng.normal(0, 1, (L, 128))
+        s = OM.indexer_token_scores(iq, ik, L, T)
+        idx_pairs += int(np.isfinite(s).sum()) // 4           # (token, key) pairs, per group
+        sel = OM.select_all(OM.block_max_pool(s, L), L, T)
+        sels.append(sel)
+        p = OM.positions(L, T)
+        for t in range(T):
+            for g in range(4):
+                attn_pairs += 16 * len(OM.attended_keys(sel[t, g], int(p[t])))
+    w = types.SimpleNamespace(B=len(lens), T=T, kv_dtype="fp8", q_dtype="fp8")
+    lay = types.SimpleNamespace(seq_lens=np.array(lens), max_blocks=24)
+    f_idx, f_attn = bench.algorithmic_flops(types.SimpleNamespace(w=w, lay=lay), np.stack(sels))
+    assert f_idx == TR.indexer_flops(idx_pairs, 4) == 2 * 128 * 4 * idx_pairs
+    assert f_attn == TR.attention_flops(attn_pairs) == 4 * 128 * attn_pairs
