@@ -21,7 +21,7 @@ counter summary under profiles/ (null once the kernel sources changed);
 (context-parallel shards, shared-prefix scan, the chunked-prefill workload,
 the cache insert); ``ragged_c3``, ``spec_c4`` and ``fp8_c2`` run the default
 step on the other decode workloads; ``ceilings`` measures a streaming read and
-the f16 MFMA rate with the library's probes; ``timing`` gives the step's
+the f16 MFMA rate with the benchmark's probe library; ``timing`` gives the step's
 median / p10 / p90 and its HIP-graph replay; ``cpu_baseline`` is the CPU fp64
 oracle timed on a bounded sample.
 """
@@ -358,12 +358,13 @@ def decode_section(name, dequant, seed, steps=20, warmup=3):
 
 
 def ceilings_section(reps=7):
-    """Ceilings measured on this GPU with the library's probes: one streaming read of
-    a 2 GiB buffer (msa_probe_stream_read) and the dense 16x16x32 f16 MFMA issue rate
-    with no memory traffic (msa_probe_mfma_f16), each the median of `reps` event-timed
-    launches, beside the published peaks the roofline fractions use."""
+    """Ceilings measured on this GPU with the benchmark's probe library
+    (bench_probes/libmsa_probe.so, not part of libmsa): one streaming read of a 2 GiB
+    buffer and the dense 16x16x32 f16 MFMA issue rate with no memory traffic, each the
+    median of `reps` event-timed launches, beside the published peaks the roofline
+    fractions use."""
     import torch
-    import block_sparse_attention_indexer_amd as M
+    import bench_probes as BP
 
     def median_ms(fn):
         for _ in range(2):
@@ -381,13 +382,13 @@ def ceilings_section(reps=7):
 
     nbytes = 2 << 30
     buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(M.MSA_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
-    ms_read = median_ms(lambda: M.msa_probe_stream_read(buf, sink))
+    sink = torch.zeros(BP.SINK_WORDS, dtype=torch.int32, device="cuda")
+    ms_read = median_ms(lambda: BP.stream_read(buf, sink))
     del buf
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wgs, iters = 8 * cus, 2000
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
-    ms_mfma = median_ms(lambda: M.msa_probe_mfma_f16(out, wgs, iters))
+    ms_mfma = median_ms(lambda: BP.mfma_f16(out, wgs, iters))
     flops = wgs * 4 * iters * 16 * 16 * 16 * 32 * 2
     gbps = nbytes / (ms_read * 1e-3) / 1e9
     tflops = flops / (ms_mfma * 1e-3) / 1e12

@@ -1,9 +1,10 @@
 /*
- * msa_probe.h -- measurement probes shipped with libmsa.  They are not part
- * of the MSA path: they measure, on the GPU at hand, the two ceilings the
- * path's kernels are read against -- a streaming HBM read and the dense f16
- * MFMA issue rate -- so that a kernel's fraction of the published peak can be
- * set beside what the chip actually sustains.
+ * probe.h -- measurement probes of the benchmark (libmsa_probe.so, built
+ * beside libmsa.so but not part of it).  They are not on the MSA path: they
+ * measure, on the GPU at hand, the two ceilings the path's kernels are read
+ * against -- a streaming HBM read and the dense f16 MFMA issue rate -- so
+ * that a kernel's fraction of the published peak can be set beside what the
+ * chip actually sustains.
  *
  * Conventions as in msa.h: caller-owned device memory, asynchronous on
  * `stream`, argument errors returned before any HIP call, MSA_ERR_HIP when a
@@ -15,7 +16,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "msa.h"
+#include "../include/msa.h"
 
 #ifdef __cplusplus
 extern "C" {

@@ -1,11 +1,15 @@
-// Measurement probes: a streaming read of a device buffer and the dense f16
-// MFMA issue rate.  Not part of the MSA path; they give the ceilings the
-// path's kernels are measured against on the GPU at hand.
-#include "common.hpp"
-#include "launch.hpp"
-#include "msa_probe.h"
+// Measurement probes of the benchmark: a streaming read of a device buffer and
+// the dense f16 MFMA issue rate.  Not part of the MSA path (built into
+// libmsa_probe.so, not libmsa.so); they give the ceilings the path's kernels
+// are measured against on the GPU at hand.
+#include <hip/hip_runtime.h>
 
-namespace msa {
+#include "probe.h"
+
+namespace msa_probe {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kProbeMagic = 0x9E3779B9u;
 
@@ -35,7 +39,7 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* __restrict__ out,
   for (int k = 0; k < 16; ++k) acc[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = mfma_16x16x32(a, b, acc[k]);
+    for (int k = 0; k < 16; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[k], 0, 0, 0);
   }
   float s = 0.0f;
 #pragma unroll
@@ -43,23 +47,23 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* __restrict__ out,
   out[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-}  // namespace msa
+}  // namespace msa_probe
 
 extern "C" msa_status msa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 ||
       reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return MSA_ERR_INVALID_ARG;
   const size_t n = bytes / 16;
-  const size_t per_wg = (size_t)256 * msa::kProbeLoads;
+  const size_t per_wg = (size_t)256 * msa_probe::kProbeLoads;
   if ((n + per_wg - 1) / per_wg > 0x7FFFFFFFu) return MSA_ERR_INVALID_ARG;
   const unsigned grid = (unsigned)((n + per_wg - 1) / per_wg);
-  hipLaunchKernelGGL(msa::stream_read_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4*>(buf), n,
+  hipLaunchKernelGGL(msa_probe::stream_read_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const uint4*>(buf), n,
                      sink);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }
 
 extern "C" msa_status msa_probe_mfma_f16(float* out, int32_t workgroups, int32_t iters, hipStream_t stream) {
   if (out == nullptr || workgroups < 1 || iters < 1) return MSA_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(msa::mfma_peak_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream, out, (int)iters);
+  hipLaunchKernelGGL(msa_probe::mfma_peak_kernel, dim3((unsigned)workgroups), dim3(256), 0, stream, out, (int)iters);
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_HIP;
 }

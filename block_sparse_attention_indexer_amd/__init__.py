@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
 MSA_F32, MSA_FP8_E4M3, MSA_NVFP4 = 0, 1, 2
-MSA_DQ_EXACT, MSA_DQ_FP8 = 0, 1
+MSA_DQ_FP8, MSA_DQ_EXACT = 0, 1
 MSA_MAX_SHARDS = 8
 MSA_CALL_INDEXER, MSA_CALL_TOPK, MSA_CALL_ATTN, MSA_CALL_INDEXER_TOPK, MSA_CALL_DECODE_STEP = 0, 1, 2, 3, 4
 MSA_CALL_INDEXER_PREFIX = 5
@@ -30,9 +30,7 @@ EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_spa
             "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
             "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn", "msa_cache_insert_many",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
-            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version",
-            "msa_probe_stream_read", "msa_probe_mfma_f16")
-MSA_PROBE_SINK_WORDS = 4096
+            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
 
 DTYPES = {"f32": MSA_F32, "fp8": MSA_FP8_E4M3, "nvfp4": MSA_NVFP4}
 DEQUANT = {"exact": MSA_DQ_EXACT, "fp8": MSA_DQ_FP8}
@@ -78,7 +76,7 @@ def _lib():
             "msa_indexer_scores": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp, vp],
             "msa_indexer_topk": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp, vp,
                                  sz, vp],
-            "msa_block_topk": [P(msa_problem), vp, vp, vp],
+            "msa_block_topk": [P(msa_problem), vp, vp, vp, sz, vp],
             "msa_sparse_attn_decode": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
                                        ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
             "msa_sparse_attn_prefill": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
@@ -102,8 +100,6 @@ def _lib():
             "msa_unpack_nvfp4": [vp, vp, i64, i32, f32, ctypes.c_int, vp, vp],
             "msa_status_string": [ctypes.c_int],
             "msa_abi_version": [],
-            "msa_probe_stream_read": [vp, sz, vp, vp],
-            "msa_probe_mfma_f16": [vp, i32, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -214,9 +210,11 @@ def msa_topk_sparse_attn(prob, block_scores, sel, q, q_dtype, q_scale, k, v, deq
            "msa_topk_sparse_attn")
 
 
-def msa_block_topk(prob, block_scores, sel, stream=None):
-    _check(_lib().msa_block_topk(ctypes.byref(prob), _ptr(block_scores), _ptr(sel), _stream(stream)),
-           "msa_block_topk")
+def msa_block_topk(prob, block_scores, sel, workspace=None, stream=None):
+    """Step 3; msa_workspace_size(prob, MSA_CALL_TOPK) is 0, so workspace may be None."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().msa_block_topk(ctypes.byref(prob), _ptr(block_scores), _ptr(sel), _ptr(workspace), ws_bytes,
+                                 _stream(stream)), "msa_block_topk")
 
 
 def _attn(name, prob, q, q_dtype, q_scale, k, v, dequant, sel, softmax_scale, out, lse=None,
@@ -265,21 +263,6 @@ def msa_cache_insert(prob, x, cache_, stream=None):
 
 def msa_workspace_size(prob, which):
     return int(_lib().msa_workspace_size(ctypes.byref(prob), int(which)))
-
-
-def msa_probe_stream_read(buf, sink, stream=None):
-    """Measurement probe (include/msa_probe.h): one streaming read of `buf`."""
-    if sink.numel() * sink.element_size() < 4 * MSA_PROBE_SINK_WORDS:
-        raise ValueError("sink must hold MSA_PROBE_SINK_WORDS uint32")
-    _check(_lib().msa_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
-           "msa_probe_stream_read")
-
-
-def msa_probe_mfma_f16(out, workgroups, iters, stream=None):
-    """Measurement probe (include/msa_probe.h): dense 16x16x32 f16 MFMA issue rate."""
-    if out.numel() < workgroups * 256:
-        raise ValueError("out must hold workgroups * 256 floats")
-    _check(_lib().msa_probe_mfma_f16(_ptr(out), int(workgroups), int(iters), _stream(stream)), "msa_probe_mfma_f16")
 
 
 def msa_pack_fp8(x, scale, out, stream=None):

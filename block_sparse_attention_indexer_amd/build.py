@@ -1,4 +1,5 @@
-"""Build libmsa.so for gfx950 in-tree with hipcc (cross-compiles without a GPU).
+"""Build libmsa.so for gfx950 in-tree with hipcc (cross-compiles without a GPU),
+and the benchmark's probe library bench_probes/libmsa_probe.so beside it.
 
     python -m block_sparse_attention_indexer_amd.build
 """
@@ -12,13 +13,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmsa.so")
 BUILD = os.path.join(ROOT, "_build", "msa")
+PROBE_SRC = os.path.join(ROOT, "bench_probes", "probe.hip")
+PROBE_OUT = os.path.join(ROOT, "bench_probes", "libmsa_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are kept out of the device code on purpose.
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["pack.hip", "insert.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "attn.hip",
-           "dcp.hip", "probe.hip", "api.cpp"]
+           "dcp.hip", "api.cpp"]
 # Per-file flags.  The prefill index GEMM only takes maxima of MFMA results, which
 # hold no NaN (an unreadable page is marked through the NaN bit pattern, stored as
 # an integer); with NaN semantics every fmaxf of an MFMA result is preceded by a
@@ -27,9 +30,10 @@ EXTRA = {"indexer_prefill.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src):
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + (["-x", "hip"] if src.endswith(".hip") else []) + \
-        ["-c", os.path.join(CSRC, src), "-o", obj]
+        ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -37,19 +41,25 @@ def _compile(src):
     return obj, msgs
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for _, msgs in results:
-        if msgs.strip() and verbose:
-            print(msgs)
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
+        results = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
+    for _, msgs in results:
+        if msgs.strip() and verbose:
+            print(msgs)
+    objs = [o for o, _ in results]
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], PROBE_OUT)
     return OUT
 
 

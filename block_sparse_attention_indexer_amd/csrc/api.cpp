@@ -132,11 +132,13 @@ msa_status msa_indexer_topk(const msa_problem* prob, const void* idx_q, msa_dtyp
 }
 
 msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, int32_t* sel,
-                          hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   msa_status st = check_problem(prob);
   if (st != MSA_OK) return st;
   if (block_scores == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
   if (!aligned(block_scores, 4) || !aligned(sel, 4)) return MSA_ERR_INVALID_ARG;
+  if (msa_workspace_size(prob, MSA_CALL_TOPK) > workspace_bytes) return MSA_ERR_WORKSPACE;
+  (void)workspace;   // the selection needs no scratch (its size is 0)
   return hip_status(msa::launch_topk(to_args(prob), block_scores, sel, stream));
 }
 

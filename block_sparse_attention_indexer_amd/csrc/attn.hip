@@ -2,9 +2,9 @@
 // launcher; the MFMA path's device code is in attn_row.hpp).
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
-// and its Figure 1 caption: attention runs exactly, but only over the top
-// blocks; every query head of a GQA group attends over its group's block
-// set, so a query reads full K/V for at most 2,048 keys.
+// and its Figure 1 caption: attention is computed exactly, restricted to
+// the keys of the kept blocks, and all query heads of a GQA group share their
+// group's blocks -- so full K/V is read for 2,048 keys at most per query.
 //
 // One workgroup per (sequence, query token, group) with 16 waves; wave w
 // takes the w-th selected block.  All of a block's K loads and the first V
@@ -37,17 +37,12 @@
 
 namespace msa {
 
-#ifndef MSA_ATTN_MANY_WG
-#define MSA_ATTN_MANY_WG 3
-#endif
 // SELECT: each workgroup first selects its row's 16 blocks from the block
 // scores (msa_topk_sparse_attn), so the selection needs no launch of its own.
-#ifndef MSA_ATTN_DECODE_WAVES
-#define MSA_ATTN_DECODE_WAVES 16
-#endif
-constexpr int kDecodeWaves = MSA_ATTN_DECODE_WAVES;   // waves per row below kAttnManyRows rows
+constexpr int kDecodeWaves = 16;   // waves per row below kAttnManyRows rows
+constexpr int kAttnManyWg = 3;     // resident workgroups per CU of the 4-wave form
 template <int KT, bool FP8MODE, int WAVES, bool SELECT = false>
-__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : WAVES == 8 ? 2 : MSA_ATTN_MANY_WG) void attn_mfma_kernel(
+__global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : WAVES == 8 ? 2 : kAttnManyWg) void attn_mfma_kernel(
     AttnArgs a) {
   attend_row<KT, FP8MODE, WAVES, SELECT>(a, blockIdx.x);
 }

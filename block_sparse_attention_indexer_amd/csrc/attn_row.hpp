@@ -3,9 +3,9 @@
 // own top-16 selection in front).
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
-// and its Figure 1 caption: attention runs exactly, but only over the top
-// blocks; every query head of a GQA group attends over its group's block
-// set, so a query reads full K/V for at most 2,048 keys.
+// and its Figure 1 caption: attention is computed exactly, restricted to
+// the keys of the kept blocks, and all query heads of a GQA group share their
+// group's blocks -- so full K/V is read for 2,048 keys at most per query.
 //
 // One workgroup per (sequence, query token, group) with 16 waves; wave w
 // takes the w-th selected block.  All of a block's K loads and the first V
@@ -37,10 +37,7 @@
 
 namespace msa {
 
-#ifndef MSA_ATTN_MANY_ROWS
-#define MSA_ATTN_MANY_ROWS 8192
-#endif
-constexpr int kAttnManyRows = MSA_ATTN_MANY_ROWS;   // rows from which the 4-wave form is used
+constexpr int kAttnManyRows = 8192;   // rows from which the 4-wave form is used
 
 // One 16-key V tile in LDS: f16 [16 keys][128 dims], 256 B per key.  The
 // 16-byte chunk c of key k sits at chunk c ^ vt_swizzle(k): with it the
@@ -178,14 +175,8 @@ __device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, ui
 }
 
 // V tiles in flight ahead of the one being multiplied.
-#ifndef MSA_ATTN_VAHEAD
-#define MSA_ATTN_VAHEAD 4
-#endif
-#ifndef MSA_ATTN_KRING
-#define MSA_ATTN_KRING 8
-#endif
-template <int KT> constexpr int kVAhead = KT == 2 ? MSA_ATTN_VAHEAD : 2;
-constexpr int kKRing = MSA_ATTN_KRING;   // K tiles of a block in flight (divides 8)
+template <int KT> constexpr int kVAhead = KT == 2 ? 4 : 2;
+constexpr int kKRing = 8;   // K tiles of a block in flight (divides 8)
 constexpr int kMergeStride = kHeadDim + 4;   // fp32 row of one head in the merge buffer (padded)
 
 // KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  WAVES waves per workgroup;

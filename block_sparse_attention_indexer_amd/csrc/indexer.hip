@@ -31,16 +31,10 @@ namespace msa {
 // The MFMA rows are 4 tokens x 4 groups.  sigma > 0 is applied to the pooled
 // maximum only: fl(sigma*x) is monotone in x, so this equals the maximum of
 // the scaled scores.
-#ifndef MSA_DEC_PAGES_PER_WAVE
-#define MSA_DEC_PAGES_PER_WAVE 8
-#endif
-#ifndef MSA_DEC_TPU
-#define MSA_DEC_TPU 4
-#endif
-#ifndef MSA_DEC_PIPE
-#define MSA_DEC_PIPE 1
-#endif
-constexpr int kDecPagesPerWave = MSA_DEC_PAGES_PER_WAVE;
+constexpr int kDecPagesPerWave = 8;
+constexpr int kDecTpu = 4;          // 16-key units per NVFP4 lane load (half for FP8)
+constexpr bool kDecPipe = true;     // next unit loaded while the current one is contracted
+constexpr int kDec1WgPerCu = 1;     // one-token scan: workgroups per CU the chunking aims for
 
 template <int KT, int TPU> struct IdxUnit;
 template <int TPU> struct IdxUnit<2, TPU> { uint4 c[TPU]; uint32_t s[TPU]; };   // NVFP4 codes + 2 scale bytes
@@ -344,9 +338,6 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   // The one-token scan asks for one workgroup per CU: long-lived waves beat a
   // second, shorter workgroup (32 sequences x 256 blocks: 8 pages per wave in
   // 31 us against 4 pages in 34.6 us); longer contexts are unchanged by it.
-#ifndef MSA_DEC_WG_PER_CU
-#define MSA_DEC_WG_PER_CU 1
-#endif
   auto pick_ppw = [&](int big, int per_cu) {
     const int want = per_cu * current_cu_count();
     for (int ppw = big; ppw > big / 4; ppw /= 2)
@@ -356,7 +347,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   if (p.T == 1 && !(fp8mode && k.dtype == 2 && sel != nullptr)) {
     // one token: 4x4x4 MFMA scan; the FP8-rounded NVFP4 reading decodes through the
     // LDS table instead of scaling partial dots (not fused with the selection)
-    const int ppw = pick_ppw(kDec1PagesPerWave, MSA_DEC_WG_PER_CU);
+    const int ppw = pick_ppw(kDec1PagesPerWave, kDec1WgPerCu);
     const bool f8 = fp8mode && k.dtype == 2;
     const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
     const bool ts = token_scores != nullptr;
@@ -387,8 +378,8 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     const int ppw = pick_ppw(kDecPagesPerWave, 2);
     const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
 #define MSA_DEC_LAUNCH(KT, FM, TS, PPW)                                                                      \
-  hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? MSA_DEC_TPU : MSA_DEC_TPU / 2),            \
-                                            MSA_DEC_PIPE != 0, PPW>), grid, dim3(kDecWaves * 64), 0, s, q8,   \
+  hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? kDecTpu : kDecTpu / 2),            \
+                                            kDecPipe, PPW>), grid, dim3(kDecWaves * 64), 0, s, q8,   \
                      k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T,             \
                      sigma, block_scores, token_scores, shard, num_shards, skip)
 #define MSA_DEC_PPW(KT, FM, TS)                                                                   \

@@ -3,8 +3,8 @@
 // its epilogue.
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer"
-// (one index query per GQA group dotted with every key of a single shared
-// index-key head, then max-pooled per block) and section "Performance
+// (each group's index query scores every key against the one index-key head
+// all groups use; a block keeps its best key's score) and section "Performance
 // optimizations" (separate indexer prefill and decode kernels).
 //
 // For one sequence the scores are Q K^T with Q = [T tokens x 4 groups, 128]
@@ -29,13 +29,7 @@
 namespace msa {
 
 constexpr int kPfTokens = 64;                  // query tokens per workgroup (x 4 groups = 256 rows)
-#ifndef MSA_PF_SCHED
-#define MSA_PF_SCHED 0
-#endif
-#ifndef MSA_PF_CHUNK
-#define MSA_PF_CHUNK 16
-#endif
-constexpr int kPfChunk = MSA_PF_CHUNK;         // blocks per workgroup
+constexpr int kPfChunk = 16;         // blocks per workgroup
 constexpr int kPfRowHalves = kHeadDim + 16;   // f16 per LDS key row (288 B)
 constexpr int kPfTileHalves = kBlock * kPfRowHalves;
 
@@ -253,10 +247,6 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) acc[rr][kt] = mfma_16x16x32(Kf[kt], A[rr][ks], acc[rr][kt]);
-#if MSA_PF_SCHED
-        // keep the next k-step's operand reads from being hoisted (register pressure)
-        __builtin_amdgcn_sched_barrier(0);
-#endif
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {

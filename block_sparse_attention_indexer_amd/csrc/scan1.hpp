@@ -60,10 +60,7 @@ __device__ __forceinline__ float e4m3_byte_to_f(uint32_t w, int k) {
   }
 }
 
-#ifndef MSA_DEC1_CHAINS
-#define MSA_DEC1_CHAINS 2
-#endif
-constexpr int kDec1Chains = MSA_DEC1_CHAINS;   // independent MFMA accumulation chains (divides 8)
+constexpr int kDec1Chains = 2;   // independent MFMA accumulation chains (divides 8)
 
 // The 4 group scores of this lane's key (before the tensor scales).
 // A[c] gives dims 4c .. 4c+3 of this lane's group (lane % 4) -- for the
@@ -136,18 +133,12 @@ struct AInRegs {
   __device__ __forceinline__ h4 operator[](int c) const { return v[c]; }
 };
 
-#ifndef MSA_DEC1_PAGES_PER_WAVE
-#define MSA_DEC1_PAGES_PER_WAVE 16
-#endif
-constexpr int kDec1PagesPerWave = MSA_DEC1_PAGES_PER_WAVE;
+constexpr int kDec1PagesPerWave = 16;
 
 // Each wave keeps a ring of kDec1Ring key sets in registers, kDec1Ring - 1 of
 // them in flight while one is contracted; at ~170 VGPRs that is two
 // workgroups per CU, so about 24 sets (110 KB) are in flight per CU.
-#ifndef MSA_DEC1_RING
-#define MSA_DEC1_RING 4
-#endif
-constexpr int kDec1Ring = MSA_DEC1_RING;
+constexpr int kDec1Ring = 4;
 
 // FUSE: the last workgroup of a sequence to finish (a per-sequence arrival
 // counter in `counters`, zero before the call and reset to zero by that

@@ -2,7 +2,7 @@
 // attention kernel that selects its own row's blocks.
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer":
-// the top 16 blocks by score, the most recent block always kept.  A (score,
+// 16 blocks per group, chosen by score, the newest one always included.  A (score,
 // block) pair becomes one 64-bit key: order-preserving score bits (NaN
 // lowest, -0 == +0) over the complemented block id, so keys are distinct and
 // (score descending, block ascending) is plain integer order.

@@ -2,8 +2,8 @@
 // row, the query's own (most recent) block always kept.
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer":
-// attention runs over the top 16 blocks and the most recent block is always
-// kept, capping a query at 2,048 keys.  Rows with 16 or fewer visible blocks
+// per group 16 blocks are kept, the newest block always among them, which
+// bounds a query at 2,048 keys.  Rows with 16 or fewer visible blocks
 // select them all.  Otherwise the own block is joined by the 15 best older
 // blocks under the strict order (score descending, block index ascending).
 //
@@ -128,10 +128,7 @@ __global__ __launch_bounds__(NT) void topk_radix_kernel(
 // Rows of up to 64*E blocks: one wave per row, the row held in registers and
 // the digit search done with wave operations only (no workgroup barrier).
 constexpr int kTopkWaveRows = 4;   // rows (waves) per workgroup
-#ifndef MSA_TOPK_MANY_ROWS
-#define MSA_TOPK_MANY_ROWS 4096
-#endif
-constexpr int kTopkManyRows = MSA_TOPK_MANY_ROWS;
+constexpr int kTopkManyRows = 4096;
 
 template <int E>
 __global__ __launch_bounds__(64 * kTopkWaveRows) void topk_wave_kernel(

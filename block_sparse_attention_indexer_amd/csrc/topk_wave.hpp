@@ -1,8 +1,7 @@
 // Top-16 selection for one row by a single wavefront (step 3 of MSA).
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "MSA primer":
-// attention runs over the top 16 blocks and the most recent block is always
-// kept.  With own+1 <= 16 visible blocks all are selected; otherwise the own
+// per group 16 blocks are kept, the newest block always among them.  With own+1 <= 16 visible blocks all are selected; otherwise the own
 // block joins the 15 best older blocks under (score descending, block index
 // ascending).  NaN ranks below every number.
 //

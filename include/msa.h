@@ -3,14 +3,14 @@
  * Attention (MSA).
  *
  * The method (source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", English
- * post, section "MSA primer" and its Figure 1 caption): the KV cache is cut
- * into 128-token blocks; a lightweight indexer scores every key of the
- * context with one index query per GQA group against one shared 128-dim
- * index-key head; the scores are max-pooled into one score per block; exact
- * attention then runs over the top 16 blocks only, the most recent block
- * always kept, so a query attends at most 2,048 keys; every query head of a
- * group uses its group's block set.  K/V and index keys are stored in FP8 or
- * NVFP4 and the query is FP8 (sections "What is new in the MiniMax-M3.1
+ * post, section "MSA primer" and its Figure 1 caption): keys are grouped in
+ * blocks of 128 tokens.  A small indexer gives every key a score per GQA
+ * group (the group's 128-dim index query dotted with the key's entry in one
+ * index-key head common to all groups) and reduces each block to the maximum
+ * of its keys' scores.  Per group 16 blocks are kept -- always including the
+ * newest -- and exact attention runs over those keys only (2,048 at most),
+ * shared by the group's query heads.  K/V and index keys are held as FP8 or
+ * NVFP4, queries as FP8 (sections "What is new in the MiniMax-M3.1
  * architecture" and "NVIDIA Blackwell optimized MSA kernels").
  *
  * Conventions shared by every call
@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 typedef enum {
   MSA_OK = 0,
@@ -71,12 +71,15 @@ typedef enum {
 typedef enum { MSA_F32 = 0, MSA_FP8_E4M3 = 1, MSA_NVFP4 = 2 } msa_dtype;
 
 /* How NVFP4 elements are decoded before a dot product (ignored for F32/FP8).
- *  MSA_DQ_EXACT: e2m1 * e4m3 scale, exactly -- the reading under which
- *    "the scores become exact" ("NVIDIA Rubin optimized MSA").
- *  MSA_DQ_FP8:   that product re-rounded to E4M3 (nearest-even, saturating
- *    at 448), as the Blackwell and CDNA4 kernels that feed an FP8 MMA do
- *    ("NVIDIA Blackwell optimized MSA kernels", "NVFP4 MSA kernel"). */
-typedef enum { MSA_DQ_EXACT = 0, MSA_DQ_FP8 = 1 } msa_dequant;
+ *  MSA_DQ_FP8:   e2m1 * e4m3 scale re-rounded to E4M3 (nearest-even,
+ *    saturating at 448) -- what the kernels that dequantise NVFP4 to FP8 for
+ *    an FP8 matrix product compute ("NVIDIA Blackwell optimized MSA kernels";
+ *    the CDNA4 kernel's table of pre-rounded products, "NVFP4 MSA kernel").
+ *  MSA_DQ_EXACT: the product e2m1 * e4m3 scale itself, as a 16-bit
+ *    dequantisation keeps it ("NVIDIA Rubin optimized MSA", where the scores
+ *    are exact).
+ * Every call takes the reading explicitly; neither is implied. */
+typedef enum { MSA_DQ_FP8 = 0, MSA_DQ_EXACT = 1 } msa_dequant;
 
 typedef struct {
   msa_dtype dtype;
@@ -101,9 +104,10 @@ typedef struct {
   int32_t max_blocks;        /* >= 1; <= 8192                                */
 } msa_problem;
 
-/* Steps 1+2: index scores max-pooled per block ("MSA primer": a lightweight
- * indexer scores every key with one index query per GQA group against a
- * single shared index-key head, then max-pools the scores per block).
+/* Steps 1+2: index scores max-pooled per block ("MSA primer": each GQA group
+ * has one index query, dotted with the single index-key head that all groups
+ * share, for every key of the context; a block's score is the largest of its
+ * keys' scores).
  *   idx_q        device [B][T][4][128]: F32 floats or FP8 bytes (q_dtype),
  *                each decoded value times q_scale.
  *   idx_k        the index-key cache (heads = 1): F32 with F32 queries;
@@ -118,19 +122,22 @@ msa_status msa_indexer_scores(const msa_problem* prob, const void* idx_q, msa_dt
                               float q_scale, const msa_cache* idx_k, msa_dequant dequant,
                               float* block_scores, float* token_scores, hipStream_t stream);
 
-/* Step 3: top-16 blocks per (sequence, token, group) ("MSA primer": the top
- * 16 blocks, the most recent block always kept).  With own+1 <= 16 visible
- * blocks all of them are selected; otherwise the own block plus the 15 best
- * older blocks by (score descending, block index ascending).  NaN ranks
- * below every number.
+/* Step 3: top-16 blocks per (sequence, token, group) ("MSA primer": 16
+ * blocks are kept per group, one of them always the newest).  With own+1 <=
+ * 16 visible blocks all of them are selected; otherwise the own block plus
+ * the 15 best older blocks by (score descending, block index ascending).
+ * NaN ranks below every number.
  *   block_scores device [B][T][4][max_blocks] (as written above).
  *   sel          device out [B][T][4][16] int32 logical block ids,
- *                ascending, padded with -1. */
+ *                ascending, padded with -1.
+ *   workspace    device scratch of at least msa_workspace_size(prob,
+ *                MSA_CALL_TOPK) bytes; that size is 0, so NULL and 0 are
+ *                accepted. */
 msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, int32_t* sel,
-                          hipStream_t stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Step 4: exact attention over the selected blocks ("MSA primer" and Figure
- * 1: attention runs exactly, but only over the selected blocks; every query
+ * 1: exact attention, restricted to the keys of the kept blocks; every query
  * head of a group uses its group's selection).  Head h uses group h / 16.
  *   q            device [B][T][64][128]: F32 floats or FP8 bytes, times q_scale.
  *   k, v         caches with heads = 4 (F32 with F32 q; FP8 or NVFP4 with FP8 q).
@@ -197,8 +204,8 @@ msa_status msa_topk_merge(const msa_problem* prob, int32_t num_shards, const flo
                           const int32_t* cand_blocks, int32_t* sel, hipStream_t stream);
 
 /* Shared-prefix decode for the index scan (section "NVFP4 MSA kernel": a
- * shared-prefix page is dequantised only once for up to 64 requests that
- * share it).  Sequences [group_start[k], group_start[k+1]) of the batch form
+ * prefix page common to as many as 64 requests is decoded a single time for
+ * all of them).  Sequences [group_start[k], group_start[k+1]) of the batch form
  * prefix group k; their block-table rows hold the same page ids in their
  * first prefix_blocks[k] logical blocks (the caller's promise: the pages are
  * read through the group's first row).  Writes the same block_scores as

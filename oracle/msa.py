@@ -3,14 +3,14 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援" (English post),
-section "MSA primer" and its Figure 1 caption:
-  1. the KV cache is cut into blocks of 128 tokens;
-  2. a lightweight indexer scores every key of the context, with one index
-     query per GQA group against one shared index-key head;
-  3. the scores are max-pooled into one score per block;
-  4. attention runs exactly, but only over the top 16 blocks, and the most
-     recent block is always kept, capping each query at 2,048 keys;
-  5. every query head of a group attends over its group's block set.
+section "MSA primer" and its Figure 1 caption, in this module's words:
+  1. keys are grouped in blocks of 128 tokens (one cache page each);
+  2. every visible key gets a score per GQA group: the group's index query
+     dotted with the key's row in the single index-key head all groups share;
+  3. a block's score is the largest score among its keys;
+  4. per group, 16 blocks are kept -- the newest always among them -- so a
+     query sees at most 2,048 keys, and attention over those keys is exact;
+  5. all query heads of a group use that group's kept blocks.
 
 Readings where the pages are silent (each is also a test):
   * the index score is the plain dot product of the decoded index query and

@@ -3,11 +3,11 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援" (English post),
-section "MSA primer": decode scans the index keys of the whole context at 128
-bytes per token per layer (FP8), an eighth of the 1,024 bytes of K/V per token
-(FP8, 4 KV heads x 128 dims) that dense attention reads, and then reads full
-K/V for only the 2,048 selected keys, so per-step traffic at long context
-falls to about 12.5% of dense.  Section "What is new in the MiniMax-M3.1
+section "MSA primer": every decode step reads the index key of each context
+token (128 B per token per layer in FP8) -- one eighth of what dense attention
+reads for that token's K/V (1,024 B: 4 KV heads x 128 dims in FP8) -- plus the
+K/V rows of just the 2,048 chosen keys; at long context that is about 12.5%
+of the dense traffic.  Section "What is new in the MiniMax-M3.1
 architecture": NVFP4 needs 34,560 bytes per token where FP8 needs 61,440,
 i.e. 4.5 bits per element instead of 8.
 

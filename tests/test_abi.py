@@ -32,10 +32,64 @@ def test_header_declares_the_binding_surface():
     assert declared_functions() == sorted(M.EXPORTED)
 
 
+# The calls the boundary must carry, with their parameter types in order: the four
+# steps of the method and the FP8 / NVFP4 pack and unpack helpers, plus the workspace
+# query, the status string and the version.
+REQUIRED = {
+    "msa_indexer_scores": ("const msa_problem*", "const void*", "msa_dtype", "float", "const msa_cache*",
+                           "msa_dequant", "float*", "float*", "hipStream_t"),
+    "msa_block_topk": ("const msa_problem*", "const float*", "int32_t*", "void*", "size_t", "hipStream_t"),
+    "msa_sparse_attn_decode": ("const msa_problem*", "const void*", "msa_dtype", "float", "const msa_cache*",
+                               "const msa_cache*", "msa_dequant", "const int32_t*", "float", "float*", "float*",
+                               "void*", "size_t", "hipStream_t"),
+    "msa_workspace_size": ("const msa_problem*", "msa_call"),
+    "msa_pack_fp8": ("const float*", "int64_t", "float", "uint8_t*", "hipStream_t"),
+    "msa_unpack_fp8": ("const uint8_t*", "int64_t", "float", "float*", "hipStream_t"),
+    "msa_pack_nvfp4": ("const float*", "int64_t", "int32_t", "float", "uint8_t*", "uint8_t*", "hipStream_t"),
+    "msa_unpack_nvfp4": ("const uint8_t*", "const uint8_t*", "int64_t", "int32_t", "float", "msa_dequant",
+                         "float*", "hipStream_t"),
+    "msa_status_string": ("msa_status",),
+    "msa_abi_version": ("void",),
+}
+REQUIRED["msa_sparse_attn_prefill"] = REQUIRED["msa_sparse_attn_decode"]
+
+
+def header_signatures():
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    sigs = {}
+    for name, params in re.findall(r"(?:msa_status|size_t|const char\*|int)\s+(msa_\w+)\s*\(([^)]*)\)\s*;", text):
+        types = []
+        for prm in params.split(","):
+            prm = " ".join(prm.split())
+            prm = re.sub(r"\s*\*\s*", "* ", prm).strip()
+            toks = prm.split()
+            if len(toks) > 1 and re.fullmatch(r"\w+", toks[-1]) and toks[-1] not in ("void",):
+                toks = toks[:-1]                      # drop the parameter name
+            types.append(" ".join(toks).replace("* ", "*").replace(" *", "*"))
+        sigs[name] = tuple(types)
+    return sigs
+
+
+def test_header_carries_the_boundary_calls():
+    sigs = header_signatures()
+    for name, types in REQUIRED.items():
+        assert name in sigs, name
+        assert sigs[name] == types, (name, sigs[name])
+    text = open(os.path.join(ROOT, "include", "msa.h")).read()
+    assert re.search(r"MSA_DQ_FP8\s*=\s*0\s*,\s*MSA_DQ_EXACT\s*=\s*1", text)
+    assert re.search(r"MSA_F32\s*=\s*0\s*,\s*MSA_FP8_E4M3\s*=\s*1\s*,\s*MSA_NVFP4\s*=\s*2", text)
+    assert (M.MSA_DQ_FP8, M.MSA_DQ_EXACT) == (0, 1)
+    # include/ declares the method's library only
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["msa.h"]
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.msa_abi_version() == 1
+    assert lib.msa_abi_version() == 2
+    # the benchmark's probes live in their own library, outside the product ABI
+    assert not hasattr(lib, "msa_probe_stream_read") and not hasattr(lib, "msa_probe_mfma_f16")
     for s in range(5):
         assert lib.msa_status_string(s)
 
@@ -109,8 +163,9 @@ def test_attention_and_topk_validation(lib):
     assert call(lib.msa_sparse_attn_decode, args(v=_cache(heads=4, dtype=M.MSA_FP8_E4M3))) == M.MSA_ERR_UNSUPPORTED
     assert call(lib.msa_sparse_attn_decode, args(k=_cache(heads=1))) == M.MSA_ERR_INVALID_ARG
     assert call(lib.msa_sparse_attn_decode, args(), prob=_prob(tokens=9)) == M.MSA_ERR_UNSUPPORTED
-    assert lib.msa_block_topk(ctypes.byref(p), None, 4096, None) == M.MSA_ERR_INVALID_ARG
-    assert lib.msa_block_topk(ctypes.byref(p), 4096, None, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_block_topk(ctypes.byref(p), None, 4096, None, 0, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_block_topk(ctypes.byref(p), 4096, None, None, 0, None) == M.MSA_ERR_INVALID_ARG
+    assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_TOPK) == 0
     assert lib.msa_workspace_size(ctypes.byref(p), M.MSA_CALL_ATTN) == 0
 
 
@@ -286,7 +341,11 @@ def test_library_binds_to_torchs_hip_runtime():
     assert out.stdout.strip().splitlines()[-1] == "1"
 
 
-def test_probe_validation(lib):
+def test_bench_probe_library_validation():
+    import bench_probes as BP
+    if not os.path.exists(BP.LIB_PATH):
+        pytest.skip("libmsa_probe.so not built")
+    lib = BP._lib()
     assert lib.msa_probe_stream_read(None, 64, 4096, None) == M.MSA_ERR_INVALID_ARG
     assert lib.msa_probe_stream_read(64, 0, 4096, None) == M.MSA_ERR_INVALID_ARG
     assert lib.msa_probe_stream_read(64, 100, 4096, None) == M.MSA_ERR_INVALID_ARG     # not a multiple of 16
