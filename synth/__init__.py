@@ -86,6 +86,9 @@ WORKLOADS = {
     # more than 2,048 blocks
     "tiny_t2": Workload("tiny_t2", 2, 2, (130, 3000), "nvfp4", "fp8", 4, [], 0.05),
     "tiny_t3": Workload("tiny_t3", 3, 3, (2200, 4000), "fp8", "fp8", 4),
+    # speculative decode with 7 speculative tokens (T = 8) and a T = 6 case
+    "tiny_spec8": Workload("tiny_spec8", 2, 8, (2100, 6000), "nvfp4", "fp8", 4, [], 0.05),
+    "tiny_t6": Workload("tiny_t6", 3, 6, (130, 4000), "fp8", "fp8", 4),
     "tiny_edge": Workload("tiny_edge", 5, 1, [1, 128, 129, 2048, 2049], "nvfp4", "fp8", 2, [], 0.0),
     "tiny_prefill_nocache": Workload("tiny_prefill_nocache", 2, 129, [129, 700], "nvfp4", "fp8", 2, [], 0.0,
                                      True, True),

@@ -30,39 +30,59 @@ def msa_lib():
 # ------------------------------------------------------------------ oracle-side packing
 
 def oracle_pack(x, dtype, S):
-    """fp32 numpy [..., 128] -> oracle cache dict (same layout as the library)."""
+    """fp32 numpy [..., 128] -> oracle cache dict (same layout as the library).  An
+    fp32 cache keeps x as stored elements, so its decoded values are S * x."""
     if dtype == "f32":
-        return {"dtype": "f32", "data": np.asarray(x, np.float32), "tensor_scale": 1.0}
+        return {"dtype": "f32", "data": np.asarray(x, np.float32), "tensor_scale": S}
     if dtype == "fp8":
         return {"dtype": "fp8", "data": OF.fp8_quantize(x, S), "tensor_scale": S}
     codes, sc = OF.nvfp4_quantize(x, S)
     return {"dtype": "nvfp4", "data": codes, "scales": sc, "tensor_scale": S}
 
 
-def oracle_query(x, dtype):
-    return np.asarray(x, np.float32) if dtype == "f32" else OF.fp8_quantize(x, 1.0)
+def oracle_query(x, dtype, scale=1.0):
+    """Query bytes: FP8 of x / scale (so they decode to about x), or fp32 x itself."""
+    return np.asarray(x, np.float32) if dtype == "f32" else OF.fp8_quantize(x, scale)
+
+
+# Per-tensor scales other than 1, with the index keys, K and V all on different
+# scales: large enough that no NVFP4 block scale of the workloads' data (|x| up to
+# about 26) saturates, and not powers of two, so a scale applied twice, dropped or
+# taken from the wrong tensor shows in the results.
+SCALED = {"idx_q": float(np.float32(0.37)), "q": float(np.float32(1.9)), "idx_k": float(np.float32(0.093)),
+          "k": float(np.float32(0.061)), "v": float(np.float32(0.113))}
+
+
+def case_scales(w, scaled):
+    """Query and cache scales of a case: the workload's defaults, or SCALED."""
+    if scaled:
+        return dict(SCALED)
+    S = w.tensor_scale()
+    return {"idx_q": 1.0, "q": 1.0, "idx_k": S, "k": S, "v": S}
 
 
 # ------------------------------------------------------------------ small cases
 
 class HostCase:
-    """All inputs drawn on the CPU and packed by the oracle."""
+    """All inputs drawn on the CPU and packed by the oracle.  scaled=True packs the
+    queries and the three caches with the per-tensor scales of SCALED."""
 
-    def __init__(self, wname, seed=0):
+    def __init__(self, wname, seed=0, scaled=False):
         w = synth.WORKLOADS[wname]
         self.w, self.seed = w, seed
         self.lay = lay = synth.make_layout(w, seed)
         idx_q, q, qhat = synth.queries(w, seed)
         hot = synth.hot_blocks(w, lay, seed)
         P = lay.num_pages
-        S = w.tensor_scale()
-        self.S = S
+        self.scales = sc = case_scales(w, scaled)
+        self.S = sc["k"]
+        self.idx_q_scale, self.q_scale = sc["idx_q"], sc["q"]
         self.caches = {}
         for name in ("idx_k", "k", "v"):
             x = synth.cache_pages(w, lay, seed, name, 0, P, qhat, hot).numpy()
-            self.caches[name] = oracle_pack(x, w.kv_dtype, S)
-        self.idx_q = oracle_query(idx_q.numpy(), w.q_dtype)
-        self.q = oracle_query(q.numpy(), w.q_dtype)
+            self.caches[name] = oracle_pack(x, w.kv_dtype, sc[name])
+        self.idx_q = oracle_query(idx_q.numpy(), w.q_dtype, sc["idx_q"])
+        self.q = oracle_query(q.numpy(), w.q_dtype, sc["q"])
 
     # device copies of the same bytes
     def upload(self):
@@ -85,9 +105,10 @@ class HostCase:
 # ------------------------------------------------------------------ full-size cases
 
 class DeviceCase:
-    """Inputs drawn on the GPU and packed by the library's pack kernels."""
+    """Inputs drawn on the GPU and packed by the library's pack kernels (scaled: as
+    for HostCase)."""
 
-    def __init__(self, wname, seed=0, keep_fp32=True):
+    def __init__(self, wname, seed=0, keep_fp32=True, scaled=False):
         M = msa_lib()
         w = synth.WORKLOADS[wname]
         self.w, self.seed = w, seed
@@ -97,14 +118,16 @@ class DeviceCase:
         self.idx_q32, self.q32 = idx_q, q
         hot = synth.hot_blocks(w, lay, seed)
         P = lay.num_pages
-        S = w.tensor_scale()
-        self.S = S
+        self.scales = sc = case_scales(w, scaled)
+        self.S = sc["k"]
+        self.idx_q_scale, self.q_scale = sc["idx_q"], sc["q"]
         self.d_seq = lay.seq_lens.to(dev)
         self.d_table = lay.block_table.to(dev)
         self.fp32 = {}
         self.d_caches = {}
         for name in ("idx_k", "k", "v"):
             heads = 1 if name == "idx_k" else 4
+            S = sc[name]
             x = synth.cache_pages(w, lay, seed, name, 0, P, qhat, hot, device=dev)
             if keep_fp32:
                 self.fp32[name] = x
@@ -118,14 +141,14 @@ class DeviceCase:
                 M.msa_pack_fp8(x, S, data)
                 self.d_caches[name] = (data, None, M.cache("fp8", data, None, S, heads))
             else:
-                self.d_caches[name] = (x, None, M.cache("f32", x, None, 1.0, heads))
+                self.d_caches[name] = (x, None, M.cache("f32", x, None, S, heads))
             if not keep_fp32:
                 del x
         if w.q_dtype == "fp8":
             self.d_idx_q = torch.empty(idx_q.shape, dtype=torch.uint8, device=dev)
             self.d_q = torch.empty(q.shape, dtype=torch.uint8, device=dev)
-            M.msa_pack_fp8(idx_q, 1.0, self.d_idx_q)
-            M.msa_pack_fp8(q, 1.0, self.d_q)
+            M.msa_pack_fp8(idx_q, sc["idx_q"], self.d_idx_q)
+            M.msa_pack_fp8(q, sc["q"], self.d_q)
         else:
             self.d_idx_q, self.d_q = idx_q, q
         torch.cuda.synchronize()
@@ -140,7 +163,7 @@ class DeviceCase:
         nb = (L + 127) // 128
         pages = lay.block_table[b, :nb].long()
         ik = self.fp32["idx_k"][pages.to(self.fp32["idx_k"].device)].cpu().numpy()
-        caches = {"idx_k": oracle_pack(ik, w.kv_dtype, self.S)}
+        caches = {"idx_k": oracle_pack(ik, w.kv_dtype, self.scales["idx_k"])}
         blocks = list(range(nb)) if kv_blocks is None else sorted(set(int(i) for i in kv_blocks if 0 <= i < nb))
         kv_table = np.zeros((1, lay.max_blocks), np.int32)        # default: zero page 0
         for slot, i in enumerate(blocks):
@@ -149,11 +172,11 @@ class DeviceCase:
         for n in ("k", "v"):
             src = self.fp32[n][sel_pages.to(self.fp32[n].device)].cpu().numpy()
             src = np.concatenate([np.zeros((1,) + src.shape[1:], np.float32), src])
-            caches[n] = oracle_pack(src, w.kv_dtype, self.S)
+            caches[n] = oracle_pack(src, w.kv_dtype, self.scales[n])
         idx_table = np.full((1, lay.max_blocks), -1, np.int32)
         idx_table[0, :nb] = np.arange(nb)
-        idx_q = oracle_query(self.idx_q32[b:b + 1].cpu().numpy(), w.q_dtype)
-        q = oracle_query(self.q32[b:b + 1].cpu().numpy(), w.q_dtype)
+        idx_q = oracle_query(self.idx_q32[b:b + 1].cpu().numpy(), w.q_dtype, self.idx_q_scale)
+        q = oracle_query(self.q32[b:b + 1].cpu().numpy(), w.q_dtype, self.q_scale)
         return {"caches": caches, "idx_q": idx_q, "q": q, "seq_lens": np.array([L]),
                 "idx_table": idx_table, "kv_table": kv_table}
 
@@ -168,8 +191,8 @@ def run_path(case, dequant="exact", token_scores=False, attention=True, stream=N
     dev = "cuda"
     bs = torch.empty((B, T, 4, maxb), dtype=torch.float32, device=dev)
     ts = torch.empty((B, T, 4, maxb * 128), dtype=torch.float32, device=dev) if token_scores else None
-    M.msa_indexer_scores(prob, case.d_idx_q, w.q_dtype, 1.0, case.d_caches["idx_k"][2], dequant, bs, ts,
-                         stream=stream)
+    M.msa_indexer_scores(prob, case.d_idx_q, w.q_dtype, case.idx_q_scale, case.d_caches["idx_k"][2], dequant, bs,
+                         ts, stream=stream)
     sel = torch.empty((B, T, 4, 16), dtype=torch.int32, device=dev)
     M.msa_block_topk(prob, bs, sel, stream=stream)
     res = {"block_scores": bs, "sel": sel, "token_scores": ts}
@@ -177,7 +200,7 @@ def run_path(case, dequant="exact", token_scores=False, attention=True, stream=N
         out = torch.empty((B, T, 64, 128), dtype=torch.float32, device=dev)
         lse = torch.empty((B, T, 64), dtype=torch.float32, device=dev)
         fn = M.msa_sparse_attn_decode if T <= 8 else M.msa_sparse_attn_prefill
-        fn(prob, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2], case.d_caches["v"][2], dequant, sel,
+        fn(prob, case.d_q, w.q_dtype, case.q_scale, case.d_caches["k"][2], case.d_caches["v"][2], dequant, sel,
            SOFTMAX_SCALE, out, lse, stream=stream)
         res.update(out=out, lse=lse)
     torch.cuda.synchronize()
@@ -190,17 +213,17 @@ def to_host(res):
 
 # ------------------------------------------------------------------ oracle side
 
-def oracle_scores(caches, idx_q, seq_lens, table, T, mode, q_dtype, sequences=None):
+def oracle_scores(caches, idx_q, seq_lens, table, T, mode, q_dtype, sequences=None, idx_q_scale=1.0):
     """Oracle block scores, selection and near-tie flags (no attention)."""
     dummy_q = np.zeros((len(seq_lens), T, 64, 128), np.float32)
     return OM.batch_layer(idx_q, dummy_q, caches["idx_k"], caches["k"], caches["v"], seq_lens, table, T,
-                          SOFTMAX_SCALE, mode=mode, idx_q_dtype=q_dtype, q_dtype=q_dtype,
+                          SOFTMAX_SCALE, mode=mode, idx_q_dtype=q_dtype, idx_q_scale=idx_q_scale, q_dtype=q_dtype,
                           sequences=sequences, with_attention=False)
 
 
-def oracle_attention(caches, q, seq_lens, table, T, sel, mode, q_dtype, b):
+def oracle_attention(caches, q, seq_lens, table, T, sel, mode, q_dtype, b, q_scale=1.0):
     L = int(seq_lens[b])
-    qq = OM.decode_query(q[b], q_dtype, 1.0)
+    qq = OM.decode_query(q[b], q_dtype, q_scale)
     K = OM.sequence_view(caches["k"], table[b], L, mode)
     V = OM.sequence_view(caches["v"], table[b], L, mode)
     return OM.sparse_attention(qq, K, V, sel, L, T, SOFTMAX_SCALE)
@@ -224,6 +247,33 @@ def compare_scores(gpu_bs, ora_bs, rows_mask=None):
     return float(err.max(initial=0.0))
 
 
+NEAR_TIE_BAND = 2e-5      # relative half-width of the band a near-tie choice may fall in
+
+
+def check_valid_top16(row_sel, scores, own):
+    """A selection row that differs from the oracle's on a near-tie must still be a
+    top-16 of the oracle's scores up to the tie band: distinct ids, ascending, the own
+    block in, 16 of them (or every block up to own); every older block it keeps scores
+    at least thr - eps, and every older block scoring above thr + eps is kept, where
+    thr is the oracle's 15th-best older score and eps = NEAR_TIE_BAND * |thr| + 1e-6."""
+    ids = [int(i) for i in row_sel]
+    row = [i for i in ids if i >= 0]
+    assert all(i == -1 for i in ids[len(row):]), f"padding not at the end: {ids}"
+    assert len(set(row)) == len(row), f"repeated block id: {row}"
+    assert row == sorted(row) and own in row and len(row) == min(16, own + 1), (row, own)
+    assert all(0 <= i <= own for i in row), (row, own)
+    if own + 1 <= 16:
+        return                                   # every visible block, nothing to rank
+    older = np.asarray(scores[:own], np.float64)
+    thr = np.sort(older)[::-1][14]
+    eps = NEAR_TIE_BAND * abs(thr) + 1e-6
+    kept = set(row)
+    for i in kept - {own}:
+        assert older[i] >= thr - eps, f"block {i} ({older[i]}) is below the 15th-best older score {thr}"
+    missing = [int(i) for i in np.flatnonzero(older > thr + eps) if int(i) not in kept]
+    assert not missing, f"blocks {missing} clearly above the 15th-best older score {thr} are not selected"
+
+
 def compare_selection(gpu_sel, ora_sel, ora_bs, near_tie, seq_lens, T):
     """Bit-exact except near-tie rows; near-tie rows must still be a valid top-16."""
     gs, os_ = np.asarray(gpu_sel), np.asarray(ora_sel)
@@ -234,13 +284,7 @@ def compare_selection(gpu_sel, ora_sel, ora_bs, near_tie, seq_lens, T):
         b, t, g = idx
         L = int(seq_lens[b])
         own = (L - T + t) // 128
-        row = [int(i) for i in gs[b, t, g] if i >= 0]
-        assert own in row and row == sorted(row) and len(row) == min(16, own + 1)
-        cand = np.sort(ora_bs[b, t, g, :own])[::-1]
-        thr = cand[14]
-        for i in row:
-            if i != own:
-                assert ora_bs[b, t, g, i] >= thr * (1 - 2e-5) - 1e-6
+        check_valid_top16(gs[b, t, g], ora_bs[b, t, g], own)
     return int(mism.sum())
 
 

@@ -147,22 +147,32 @@ SMALL = [("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_n
          ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"), ("tiny_spec", "fp8"),
          ("tiny_prefill", "exact"), ("tiny_prefill", "fp8"), ("tiny_prefill_fp8", "exact"),
          ("tiny_prefill_many", "exact"), ("tiny_t2", "exact"), ("tiny_t2", "fp8"), ("tiny_t3", "exact"),
-         ("tiny_edge", "exact"), ("tiny_prefill_nocache", "exact"), ("long_rows", "exact")]
+         ("tiny_edge", "exact"), ("tiny_prefill_nocache", "exact"), ("long_rows", "exact"),
+         # 7 speculative tokens (T = 8) and T = 6: the prefill index GEMM and the decode attention
+         ("tiny_spec8", "exact"), ("tiny_spec8", "fp8"), ("tiny_t6", "exact")]
+SMALL = [(w, m, False) for w, m in SMALL]
+# per-tensor scales other than 1 (index query, query, index keys, K and V all different)
+SMALL += [(w, m, True) for w, m in [
+    ("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"), ("tiny_nvfp4", "fp8"),
+    ("tiny_spec", "exact"), ("tiny_spec", "fp8"), ("tiny_spec8", "fp8"), ("tiny_t3", "exact"),
+    ("tiny_prefill", "exact"), ("tiny_prefill", "fp8"), ("tiny_prefill_fp8", "exact"),
+    ("tiny_prefill_many", "fp8")]]
 
 
-@pytest.mark.parametrize("wname,mode", SMALL)
-def test_layer_parity_small(M, wname, mode):
-    _say("small case", wname, mode)
-    case = H.HostCase(wname).upload()
+@pytest.mark.parametrize("wname,mode,scaled", SMALL)
+def test_layer_parity_small(M, wname, mode, scaled):
+    _say("small case", wname, mode, "scaled" if scaled else "unit scales")
+    case = H.HostCase(wname, scaled=scaled).upload()
     w, lay = case.w, case.lay
     res = H.to_host(H.run_path(case, mode, token_scores=True))
     seq_lens, table = lay.seq_lens.numpy(), lay.block_table.numpy()
-    ora = H.oracle_scores(case.caches, case.idx_q, seq_lens, table, w.T, mode, w.q_dtype)
+    ora = H.oracle_scores(case.caches, case.idx_q, seq_lens, table, w.T, mode, w.q_dtype,
+                          idx_q_scale=case.idx_q_scale)
     H.compare_scores(res["block_scores"], ora["block_scores"])
     # per-key scores
     for b in range(w.B):
         L = int(seq_lens[b])
-        iq = OM.decode_query(case.idx_q[b], w.q_dtype, 1.0)
+        iq = OM.decode_query(case.idx_q[b], w.q_dtype, case.idx_q_scale)
         ik = OM.sequence_view(case.caches["idx_k"], table[b], L, mode)[0]
         s = OM.indexer_token_scores(iq, ik, L, w.T)
         full = np.full((w.T, 4, lay.max_blocks * 128), -np.inf)
@@ -170,7 +180,8 @@ def test_layer_parity_small(M, wname, mode):
         H.compare_scores(res["token_scores"][b], full)
     nties = H.compare_selection(res["sel"], ora["sel"], ora["block_scores"], ora["near_tie"], seq_lens, w.T)
     for b in range(w.B):
-        o, lse = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, res["sel"][b], mode, w.q_dtype, b)
+        o, lse = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, res["sel"][b], mode, w.q_dtype, b,
+                                    q_scale=case.q_scale)
         H.compare_out(res["out"][b], o)
         assert np.abs(res["lse"][b] - lse).max() <= 1e-4
     _say(wname, mode, "ok; near-tie rows that differ:", nties)
@@ -221,14 +232,19 @@ def test_out_of_range_page_gives_nan_not_a_fault(M, wname):
 
 # ------------------------------------------------------------------ full sizes, sampled
 
-FULL = [("c2", [0, 17, 31], "exact"), ("c3", [0, 21, 63], "exact"), ("c3_128k", [5, 40], "exact"),
-        ("c3_128k", [7], "fp8"), ("c4", [3, 11], "exact"), ("c5", [1], "exact")]
+FULL = [("c2", [0, 17, 31], "exact", False), ("c3", [0, 21, 63], "exact", False),
+        ("c3_128k", [5, 40], "exact", False), ("c3_128k", [7], "fp8", False), ("c4", [3, 11], "exact", False),
+        ("c5", [1], "exact", False),
+        # the FP8-rounded reading on the speculative and prefill workloads
+        ("c4", [5], "fp8", False), ("c5", [0], "fp8", False),
+        # per-tensor scales other than 1 (K and V on different scales) at full size
+        ("c2", [9], "exact", True), ("c3_128k", [33], "exact", True), ("c4", [14], "fp8", True)]
 
 
-@pytest.mark.parametrize("wname,samples,mode", FULL)
-def test_full_size_sampled(M, wname, samples, mode):
-    _say("full-size case", wname, "samples", samples, mode)
-    case = H.DeviceCase(wname)
+@pytest.mark.parametrize("wname,samples,mode,scaled", FULL)
+def test_full_size_sampled(M, wname, samples, mode, scaled):
+    _say("full-size case", wname, "samples", samples, mode, "scaled" if scaled else "unit scales")
+    case = H.DeviceCase(wname, scaled=scaled)
     w, lay = case.w, case.lay
     res = H.to_host(H.run_path(case, mode))
     T = w.T
@@ -236,14 +252,15 @@ def test_full_size_sampled(M, wname, samples, mode):
         gsel = res["sel"][b]
         # oracle scores over the whole sequence, K/V packed for the oracle's and GPU's blocks
         inp = case.oracle_inputs(b, kv_blocks=None if w.kv_dtype == "f32" else [])
-        ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], T, mode, w.q_dtype)
+        ora = H.oracle_scores(inp["caches"], inp["idx_q"], inp["seq_lens"], inp["idx_table"], T, mode, w.q_dtype,
+                              idx_q_scale=case.idx_q_scale)
         H.compare_scores(res["block_scores"][b:b + 1], ora["block_scores"])
         H.compare_selection(gsel[None], ora["sel"], ora["block_scores"], ora["near_tie"], inp["seq_lens"], T)
         blocks = np.union1d(gsel[gsel >= 0], ora["sel"][ora["sel"] >= 0])
         inp = case.oracle_inputs(b, kv_blocks=blocks)
         rows = range(T) if T <= 8 else np.random.default_rng(b).choice(T, 64, replace=False)
         for t in rows:
-            qq = OM.decode_query(inp["q"][0, t:t + 1], w.q_dtype, 1.0)
+            qq = OM.decode_query(inp["q"][0, t:t + 1], w.q_dtype, case.q_scale)
             L = int(inp["seq_lens"][0])
             K = OM.sequence_view(inp["caches"]["k"], inp["kv_table"][0], L, mode)
             V = OM.sequence_view(inp["caches"]["v"], inp["kv_table"][0], L, mode)
@@ -263,7 +280,8 @@ def _fused(M, case, ws, B=None, dequant="exact"):
     prob = M.problem(case.d_seq[:B], case.d_table[:B], w.T)
     bs = torch.empty((B, w.T, 4, lay.max_blocks), dtype=torch.float32, device="cuda")
     sel = torch.empty((B, w.T, 4, 16), dtype=torch.int32, device="cuda")
-    M.msa_indexer_topk(prob, case.d_idx_q[:B], w.q_dtype, 1.0, case.d_caches["idx_k"][2], dequant, bs, sel, ws)
+    M.msa_indexer_topk(prob, case.d_idx_q[:B], w.q_dtype, case.idx_q_scale, case.d_caches["idx_k"][2], dequant, bs,
+                       sel, ws)
     torch.cuda.synchronize()
     return bs.cpu().numpy(), sel.cpu().numpy()
 
@@ -311,22 +329,24 @@ def _step(M, case, B=None, dequant="exact"):
     sel = torch.empty((B, w.T, 4, 16), dtype=torch.int32, device="cuda")
     out = torch.empty((B, w.T, 64, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, w.T, 64), dtype=torch.float32, device="cuda")
-    M.msa_decode_step(prob, case.d_idx_q[:B], w.q_dtype, 1.0, case.d_caches["idx_k"][2], case.d_q[:B], w.q_dtype,
-                      1.0, case.d_caches["k"][2], case.d_caches["v"][2], dequant, H.SOFTMAX_SCALE, bs, sel, out,
-                      lse)
+    M.msa_decode_step(prob, case.d_idx_q[:B], w.q_dtype, case.idx_q_scale, case.d_caches["idx_k"][2], case.d_q[:B],
+                      w.q_dtype, case.q_scale, case.d_caches["k"][2], case.d_caches["v"][2], dequant, H.SOFTMAX_SCALE,
+                      bs, sel, out, lse)
     torch.cuda.synchronize()
     return bs.cpu().numpy(), sel.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("wname,mode", [("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"), ("tiny_edge", "exact"),
-                                        ("long_rows", "exact"), ("tiny_nvfp4", "fp8"), ("tiny_spec", "exact"),
-                                        ("c1", "exact")])
-def test_decode_step_equals_the_separate_calls(M, wname, mode):
+@pytest.mark.parametrize("wname,mode,scaled", [
+    ("tiny_fp8", "exact", False), ("tiny_nvfp4", "exact", False), ("tiny_edge", "exact", False),
+    ("long_rows", "exact", False), ("tiny_nvfp4", "fp8", False), ("tiny_spec", "exact", False), ("c1", "exact", False),
+    ("tiny_spec8", "fp8", False), ("tiny_fp8", "exact", True), ("tiny_nvfp4", "fp8", True),
+    ("tiny_spec8", "exact", True)])
+def test_decode_step_equals_the_separate_calls(M, wname, mode, scaled):
     """msa_decode_step gives the block scores, selection, outputs and LSE of the three
     calls bit for bit, call after call and for a smaller batch; its output also meets
     the oracle bar on the selection it made."""
-    _say("decode_step", wname, mode)
-    case = H.HostCase(wname).upload()
+    _say("decode_step", wname, mode, "scaled" if scaled else "unit scales")
+    case = H.HostCase(wname, scaled=scaled).upload()
     w, lay = case.w, case.lay
     ref = H.to_host(H.run_path(case, mode))
     B = w.B
@@ -337,7 +357,8 @@ def test_decode_step_equals_the_separate_calls(M, wname, mode):
         assert np.array_equal(out, ref["out"]) and np.array_equal(lse, ref["lse"]), rep
     seq_lens, table = lay.seq_lens.numpy(), lay.block_table.numpy()
     for b in range(B):
-        o, _ = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, sel[b], mode, w.q_dtype, b)
+        o, _ = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, sel[b], mode, w.q_dtype, b,
+                                  q_scale=case.q_scale)
         H.compare_out(out[b], o)
     if B > 1:
         bs, sel, out, lse = _step(M, case, B=B - 1, dequant=mode)
