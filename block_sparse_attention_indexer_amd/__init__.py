@@ -30,7 +30,8 @@ EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_spa
             "msa_decode_step", "msa_cache_insert", "msa_indexer_scores_shard", "msa_shard_topk",
             "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn", "msa_cache_insert_many",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
-            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version")
+            "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version",
+            "msa_sparse_attn_decode_prefix", "msa_sparse_attn_prefix_workspace_size")
 
 DTYPES = {"f32": MSA_F32, "fp8": MSA_FP8_E4M3, "nvfp4": MSA_NVFP4}
 DEQUANT = {"exact": MSA_DQ_EXACT, "fp8": MSA_DQ_FP8}
@@ -91,6 +92,9 @@ def _lib():
             "msa_topk_merge": [P(msa_problem), i32, vp, vp, vp, vp],
             "msa_indexer_scores_prefix": [P(msa_problem), i32, vp, vp, vp, ctypes.c_int, f32, P(msa_cache),
                                           ctypes.c_int, vp, vp, sz, vp],
+            "msa_sparse_attn_decode_prefix": [P(msa_problem), i32, vp, vp, vp, ctypes.c_int, f32, P(msa_cache),
+                                              P(msa_cache), ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
+            "msa_sparse_attn_prefix_workspace_size": [P(msa_problem), i32, vp, vp],
             "msa_topk_sparse_attn": [P(msa_problem), vp, vp, vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
                                      ctypes.c_int, f32, vp, vp, vp],
             "msa_workspace_size": [P(msa_problem), ctypes.c_int],
@@ -106,6 +110,7 @@ def _lib():
             fn.argtypes = args
             fn.restype = ctypes.c_int
         lib.msa_workspace_size.restype = sz
+        lib.msa_sparse_attn_prefix_workspace_size.restype = sz
         lib.msa_status_string.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -200,6 +205,33 @@ def msa_indexer_scores_prefix(prob, group_start, prefix_blocks, idx_q, q_dtype, 
                                             float(q_scale), ctypes.byref(idx_k), DEQUANT[dequant],
                                             _ptr(block_scores), _ptr(workspace), ws_bytes, _stream(stream)),
            "msa_indexer_scores_prefix")
+
+
+def _groups(group_start, prefix_blocks):
+    n = len(prefix_blocks)
+    gs = (ctypes.c_int32 * (n + 1))(*[int(x) for x in group_start])
+    pb = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in prefix_blocks])
+    return n, gs, pb
+
+
+def msa_sparse_attn_prefix_workspace_size(prob, group_start, prefix_blocks):
+    n, gs, pb = _groups(group_start, prefix_blocks)
+    return int(_lib().msa_sparse_attn_prefix_workspace_size(ctypes.byref(prob), n, ctypes.cast(gs, ctypes.c_void_p),
+                                                             ctypes.cast(pb, ctypes.c_void_p)))
+
+
+def msa_sparse_attn_decode_prefix(prob, group_start, prefix_blocks, q, q_dtype, q_scale, k, v, dequant, sel,
+                                  softmax_scale, out, lse=None, workspace=None, stream=None):
+    """Decode attention with shared-prefix blocks dequantised once per group (see
+    include/msa.h); workspace: a 256-byte aligned device tensor of at least
+    msa_sparse_attn_prefix_workspace_size(prob, group_start, prefix_blocks) bytes."""
+    n, gs, pb = _groups(group_start, prefix_blocks)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib().msa_sparse_attn_decode_prefix(ctypes.byref(prob), n, ctypes.cast(gs, ctypes.c_void_p),
+                                                ctypes.cast(pb, ctypes.c_void_p), _ptr(q), DTYPES[q_dtype],
+                                                float(q_scale), ctypes.byref(k), ctypes.byref(v), DEQUANT[dequant],
+                                                _ptr(sel), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                                ws_bytes, _stream(stream)), "msa_sparse_attn_decode_prefix")
 
 
 def msa_topk_sparse_attn(prob, block_scores, sel, q, q_dtype, q_scale, k, v, dequant, softmax_scale, out,

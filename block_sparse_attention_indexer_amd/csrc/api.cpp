@@ -56,6 +56,29 @@ ProblemArgs to_args(const msa_problem* p) {
 }
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
 
+// Prefix groups from the host arrays of a shared-prefix call: 0..64 groups of
+// 1..64 consecutive sequences, group_start strictly increasing within [0, batch],
+// prefix_blocks within [0, max_blocks].
+msa_status read_prefix_groups(const msa_problem* prob, int32_t num_groups, const int32_t* group_start,
+                              const int32_t* prefix_blocks, msa::PrefixGroups& g) {
+  if (num_groups < 0 || num_groups > MSA_MAX_PREFIX_GROUPS) return MSA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (group_start == nullptr || prefix_blocks == nullptr)) return MSA_ERR_INVALID_ARG;
+  g.n = num_groups;
+  for (int k = 0; num_groups > 0 && k <= num_groups; ++k) {
+    g.start[k] = group_start[k];
+    if (g.start[k] < 0 || g.start[k] > prob->batch) return MSA_ERR_INVALID_ARG;
+    if (k > 0) {
+      const int n = g.start[k] - g.start[k - 1];
+      if (n < 1 || n > MSA_MAX_PREFIX_SEQS) return MSA_ERR_INVALID_ARG;
+    }
+  }
+  for (int k = 0; k < num_groups; ++k) {
+    g.blocks[k] = prefix_blocks[k];
+    if (g.blocks[k] < 0 || g.blocks[k] > prob->max_blocks) return MSA_ERR_INVALID_ARG;
+  }
+  return MSA_OK;
+}
+
 msa_status attention(const msa_problem* prob, const void* q, msa_dtype q_dtype, float q_scale,
                      const msa_cache* k, const msa_cache* v, msa_dequant dequant,
                      const int32_t* sel, float softmax_scale, float* out, float* lse,
@@ -184,22 +207,8 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
   if (idx_q == nullptr || block_scores == nullptr) return MSA_ERR_INVALID_ARG;
   if (!aligned(idx_q, 16) || !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;
   if (!good_scale(q_scale)) return MSA_ERR_INVALID_ARG;
-  if (num_groups < 0 || num_groups > MSA_MAX_PREFIX_GROUPS) return MSA_ERR_INVALID_ARG;
-  if (num_groups > 0 && (group_start == nullptr || prefix_blocks == nullptr)) return MSA_ERR_INVALID_ARG;
   msa::PrefixGroups g{};
-  g.n = num_groups;
-  for (int k = 0; num_groups > 0 && k <= num_groups; ++k) {
-    g.start[k] = group_start[k];
-    if (g.start[k] < 0 || g.start[k] > prob->batch) return MSA_ERR_INVALID_ARG;
-    if (k > 0) {
-      const int n = g.start[k] - g.start[k - 1];
-      if (n < 1 || n > MSA_MAX_PREFIX_SEQS) return MSA_ERR_INVALID_ARG;
-    }
-  }
-  for (int k = 0; k < num_groups; ++k) {
-    g.blocks[k] = prefix_blocks[k];
-    if (g.blocks[k] < 0 || g.blocks[k] > prob->max_blocks) return MSA_ERR_INVALID_ARG;
-  }
+  if ((st = read_prefix_groups(prob, num_groups, group_start, prefix_blocks, g)) != MSA_OK) return st;
   if (workspace == nullptr || !aligned(workspace, 4) ||
       workspace_bytes < msa_workspace_size(prob, MSA_CALL_INDEXER_PREFIX))
     return MSA_ERR_WORKSPACE;
@@ -253,6 +262,41 @@ msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_d
                                    hipStream_t stream) {
   return attention(prob, q, q_dtype, q_scale, k, v, dequant, sel, softmax_scale, out, lse,
                    workspace, workspace_bytes, stream, 262144);
+}
+
+msa_status msa_sparse_attn_decode_prefix(const msa_problem* prob, int32_t num_groups, const int32_t* group_start,
+                                         const int32_t* prefix_blocks, const void* q, msa_dtype q_dtype,
+                                         float q_scale, const msa_cache* k, const msa_cache* v, msa_dequant dequant,
+                                         const int32_t* sel, float softmax_scale, float* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (prob->tokens > 8) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_cache(k, 4)) != MSA_OK) return st;
+  if ((st = check_cache(v, 4)) != MSA_OK) return st;
+  if (k->dtype != v->dtype || k->dtype == MSA_F32) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_pair(q_dtype, k->dtype)) != MSA_OK) return st;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (q == nullptr || sel == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(sel, 4) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return MSA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale) || !good_scale(softmax_scale)) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(softmax_scale * q_scale * k->tensor_scale * 1.4426950408889634f)) return MSA_ERR_INVALID_ARG;
+  msa::PrefixGroups g{};
+  if ((st = read_prefix_groups(prob, num_groups, group_start, prefix_blocks, g)) != MSA_OK) return st;
+  const size_t need = msa::prefix_workspace_layout(g, prob->tokens).bytes;
+  if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need) return MSA_ERR_WORKSPACE;
+  return hip_status(msa::launch_attention_prefix(to_args(prob), q, q_scale, to_args(k), to_args(v),
+                                                 dequant == MSA_DQ_FP8, sel, softmax_scale, out, lse, g, workspace,
+                                                 stream));
+}
+
+size_t msa_sparse_attn_prefix_workspace_size(const msa_problem* prob, int32_t num_groups,
+                                             const int32_t* group_start, const int32_t* prefix_blocks) {
+  msa::PrefixGroups g{};
+  if (check_problem(prob) != MSA_OK || read_prefix_groups(prob, num_groups, group_start, prefix_blocks, g) != MSA_OK)
+    return 0;
+  return msa::prefix_workspace_layout(g, prob->tokens).bytes;
 }
 
 msa_status msa_decode_step(const msa_problem* prob, const void* idx_q, msa_dtype idx_q_dtype,

@@ -47,6 +47,13 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : WAVES == 8 ? 2 : kAtt
   attend_row<KT, FP8MODE, WAVES, SELECT>(a, blockIdx.x);
 }
 
+// Shared-prefix form: staged prefix blocks come from their operand images.
+// Always the 16-wave form (decode row counts), whatever the number of rows.
+template <int KT, bool FP8MODE, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void attn_prefix_kernel(AttnArgs a, PrefixAttnArgs pa) {
+  attend_row<KT, FP8MODE, WAVES, false, true>(a, blockIdx.x, &pa);
+}
+
 // fp32 queries and caches: plain fp32 arithmetic on the vector ALUs.  One
 // workgroup per (sequence, token, group); thread (head h = tid/16, part =
 // tid%16) owns dims part*8 .. part*8+7 of head h's output.
@@ -113,7 +120,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
 hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, float q_scale,
                             const CacheArgs& k, const CacheArgs& v, bool fp8mode,
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
-                            hipStream_t s, const float* block_scores, int32_t* sel_out) {
+                            hipStream_t s, const float* block_scores, int32_t* sel_out,
+                            const PrefixAttnArgs* pa) {
   const unsigned rows = (unsigned)((int64_t)p.B * p.T * kGroups);
   const bool many = rows >= kAttnManyRows;
   // The selection inside the attention launch pays off for decode (few rows: it
@@ -144,7 +152,10 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   const AttnArgs aa{q8, c_log2, k.data, k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale,
                     sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse, block_scores, sel_out};
 #define MSA_ATTN_LAUNCH(KT, FM)                                                                        \
-  if (many)                                                                                            \
+  if (pa != nullptr)                                                                                   \
+    hipLaunchKernelGGL((attn_prefix_kernel<KT, FM, kDecodeWaves>), dim3(rows), dim3(kDecodeWaves * 64), 0, s, \
+                       aa, *pa);                                                                       \
+  else if (many)                                                                                       \
     hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4, false>), dim3(rows), dim3(256), 0, s, aa);          \
   else if (select)                                                                                     \
     hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, kDecodeWaves, true>), dim3(rows), dim3(kDecodeWaves * 64), 0, \

@@ -72,34 +72,73 @@ template <int KT> struct VRaw;
 template <> struct VRaw<1> { uint4 c[2]; };
 template <> struct VRaw<2> { uint2 c[2]; uint32_t s[2]; };
 
-// Loads take the base of one (page, KV head) slice -- uniform across the wave
-// -- and a 32-bit row offset within it, so addresses are a scalar base plus a
-// per-lane offset.
+// Loads go through buffer resources built once per block for its (page, KV
+// head) slice -- a scalar base and the slice's byte size, uniform across the
+// wave -- with offsets fixed per lane (computed once per row) and the tile's
+// offset as a scalar, so a load costs no vector address arithmetic.  Reads past
+// the slice's size return zero instead of touching memory.
+struct KvRsrc {
+  __amdgpu_buffer_rsrc_t codes, scales;
+};
 template <int KT>
-__device__ __forceinline__ KRaw<KT> load_k_tile(const uint8_t* kbase, const uint8_t* sbase, uint32_t r, int Q) {
+__device__ __forceinline__ KvRsrc kv_rsrc(const uint8_t* codes, const uint8_t* scales, size_t rowbase) {
+  constexpr int kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
+  KvRsrc r;
+  r.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + rowbase * kRowBytes), (short)0,
+                                              kBlock * kRowBytes, kBufferFlags);
+  r.scales = KT == 2 ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(scales + rowbase * kNvfp4ScaleBytes),
+                                                         (short)0, kBlock * kNvfp4ScaleBytes, kBufferFlags)
+                     : r.codes;
+  return r;
+}
+// Per-lane byte offsets within a block's slice.
+//   K tile kt, lane (quarter Q, key j): row kt*16 + j, dims [32Q, 32Q+32).
+//   V tile kt, lane (key pair kp, 16-dim group dg): rows kt*16 + 2kp + u, dims [16dg, 16dg+16).
+struct KvLaneOffsets {
+  uint32_t k, ks, v[2], vs[2];
+};
+template <int KT>
+__device__ __forceinline__ KvLaneOffsets kv_lane_offsets(int j, int Q, int kp, int dg) {
+  constexpr int kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
+  KvLaneOffsets o;
+  o.k = j * kRowBytes + (KT == 2 ? 16 : 32) * Q;
+  o.ks = j * kNvfp4ScaleBytes + 2 * Q;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    o.v[u] = (2 * kp + u) * kRowBytes + (KT == 2 ? 8 : 16) * dg;
+    o.vs[u] = (2 * kp + u) * kNvfp4ScaleBytes + dg;
+  }
+  return o;
+}
+
+template <int KT>
+__device__ __forceinline__ KRaw<KT> load_k_tile(const KvRsrc& rs, const KvLaneOffsets& o, int kt) {
+  constexpr int kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
   KRaw<KT> t;
   if constexpr (KT == 2) {
-    t.c = *reinterpret_cast<const uint4*>(kbase + r * kNvfp4RowBytes + 16 * Q);
-    t.s = *reinterpret_cast<const uint16_t*>(sbase + r * kNvfp4ScaleBytes + 2 * Q);
+    t.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.codes, o.k, kt * 16 * kRowBytes, 0));
+    t.s = __builtin_amdgcn_raw_buffer_load_b16(rs.scales, o.ks, kt * 16 * kNvfp4ScaleBytes, 0);
   } else {
-    const uint4* src = reinterpret_cast<const uint4*>(kbase + r * kHeadDim + 32 * Q);
-    t.c0 = src[0];
-    t.c1 = src[1];
+    t.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.codes, o.k, kt * 16 * kRowBytes, 0));
+    t.c1 = __builtin_bit_cast(uint4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs.codes, o.k + 16, kt * 16 * kRowBytes, 0));
   }
   return t;
 }
 
 template <int KT>
-__device__ __forceinline__ VRaw<KT> load_v_tile(const uint8_t* vbase, const uint8_t* sbase, uint32_t r0, int dg) {
+__device__ __forceinline__ VRaw<KT> load_v_tile(const KvRsrc& rs, const KvLaneOffsets& o, int kt) {
+  constexpr int kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
   VRaw<KT> t;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const uint32_t r = r0 + u;
     if constexpr (KT == 2) {
-      t.c[u] = *reinterpret_cast<const uint2*>(vbase + r * kNvfp4RowBytes + 8 * dg);
-      t.s[u] = sbase[r * kNvfp4ScaleBytes + dg];
+      t.c[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.codes, o.v[u],
+                                                                              kt * 16 * kRowBytes, 0));
+      t.s[u] = __builtin_amdgcn_raw_buffer_load_b8(rs.scales, o.vs[u], kt * 16 * kNvfp4ScaleBytes, 0);
     } else {
-      t.c[u] = *reinterpret_cast<const uint4*>(vbase + r * kHeadDim + 16 * dg);
+      t.c[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.codes, o.v[u],
+                                                                               kt * 16 * kRowBytes, 0));
     }
   }
   return t;
@@ -139,10 +178,11 @@ __device__ __forceinline__ void decode_k_tile(const KRaw<KT>& r, const uint32_t*
 // an NVFP4 key through its scale bytes (E2M1 codes are always finite), an
 // FP8 key through its bytes, so unwritten rows of a partly filled page never
 // reach the product (0 * NaN would).
-template <int KT, bool FP8MODE>
+template <int KT, bool FP8MODE, bool MASK>
 __device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, uint8_t* vt,
                                              const int (&woff)[2][2], bool keep0, bool keep1) {
-  if constexpr (KT == 2) {
+  if constexpr (!MASK) {
+  } else if constexpr (KT == 2) {
     r.s[0] = keep0 ? r.s[0] : 0u;
     r.s[1] = keep1 ? r.s[1] : 0u;
   } else {
@@ -178,6 +218,26 @@ __device__ __forceinline__ void stage_v_tile(VRaw<KT> r, const uint32_t* lut, ui
 template <int KT> constexpr int kVAhead = KT == 2 ? 4 : 2;
 constexpr int kKRing = 8;   // K tiles of a block in flight (divides 8)
 constexpr int kMergeStride = kHeadDim + 4;   // fp32 row of one head in the merge buffer (padded)
+constexpr float kRescaleSlack = 8.0f;        // log2 headroom of the softmax weights before O is rescaled
+
+// Shared-prefix staging (msa_sparse_attn_decode_prefix).  A staged block is
+// one (page, KV head) slice dequantised once into the operand images the
+// attention's MFMAs take, 64 KiB per slot:
+//   K image: [tile kt 0..7][k-chunk c 0..3][lane 0..63] h8 -- lane's Ak[c] of tile kt;
+//   V image: [tile pair 0..3][dim tile dt 0..7][lane 0..63] h8 -- lane's V^T operand.
+// Lane mappings are those of attend_row, so a staged block gives the same
+// operands, and the same results, as decoding the page in the attention.
+constexpr int kStageKBytes = 8 * 4 * 64 * 16;
+constexpr int kStageBytes = 2 * kStageKBytes;
+constexpr int kMaxPrefixGroupsDev = 64;
+struct PrefixAttnArgs {
+  const uint8_t* staged;      // slot images
+  const int32_t* slot_of;     // per group k: [4 heads][blocks[k]] slot ids, -1 = not staged
+  int n;                      // prefix groups
+  int start[kMaxPrefixGroupsDev + 1];   // sequences [start[k], start[k+1]) form group k
+  int blocks[kMaxPrefixGroupsDev];      // shared leading blocks of group k
+  int slot_of_base[kMaxPrefixGroupsDev];   // offset of group k's slot_of entries
+};
 
 // KT: 1 = FP8 K/V, 2 = NVFP4 K/V (queries FP8).  WAVES waves per workgroup;
 // wave w takes selected blocks w, w + WAVES, ... and keeps a running (max,
@@ -213,8 +273,11 @@ struct AttnArgs {
 // SELECT: the workgroup first selects the row's blocks itself from
 // args.block_scores (select_row, the same rule and keys as msa_block_topk)
 // and writes them to args.sel_out.
-template <int KT, bool FP8MODE, int WAVES, bool SELECT = false>
-__device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
+// PREFIX (with pa): blocks older than the row's own block that lie in its
+// sequence's shared prefix and were staged are read from their images instead
+// of being decoded from the pages.
+template <int KT, bool FP8MODE, int WAVES, bool SELECT = false, bool PREFIX = false>
+__device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const PrefixAttnArgs* pa = nullptr) {
   const uint8_t* __restrict__ q = args.q;
   const float c_log2 = args.c_log2;
   const uint8_t* __restrict__ kdata = args.kdata;
@@ -257,8 +320,14 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
   if constexpr (SELECT) {
     __shared__ int32_t sel_sh[kTopK];
     const int own = max(0, min((L - T + t) / kBlock, max_blocks - 1));
-    select_row<WAVES * 64, kMaxBlocksSelect / (WAVES * 64)>(args.block_scores + (size_t)row * max_blocks, own,
-                                                            sel_sh);
+    // keys per thread sized to the row (uniform): a row of at most WAVES*64 older
+    // blocks needs one slot per thread, not the 8,192-block maximum
+    constexpr int NT = WAVES * 64, EMAX = kMaxBlocksSelect / NT;
+    const float* srow = args.block_scores + (size_t)row * max_blocks;
+    const int ne = (own + NT - 1) / NT;
+    if (ne <= 1) select_row<NT, 1>(srow, own, sel_sh);
+    else if (ne <= 2 && EMAX >= 2) select_row<NT, (EMAX >= 2 ? 2 : EMAX)>(srow, own, sel_sh);
+    else select_row<NT, EMAX>(srow, own, sel_sh);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kTopK / WAVES; ++u) blks[u] = sel_sh[w + u * WAVES];
@@ -296,10 +365,22 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) woff[u][hh] = vt_offset(2 * kp + u, 2 * dg + hh);
   const int roff = vt_offset(lane >> 2, (lane & 3) >> 1) + 8 * (lane & 1);
+  const KvLaneOffsets lo = kv_lane_offsets<KT>(j, Q, kp, dg);
   float m = NEG_INF, l = 0.0f;
   f4 O[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) O[dt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  // shared prefix of this row's sequence (PREFIX): blocks below pfx_blocks are
+  // candidates for their staged images
+  int pfx_blocks = 0, pfx_base = 0;
+  if constexpr (PREFIX) {
+    for (int k = 0; k < pa->n; ++k)
+      if (b >= pa->start[k] && b < pa->start[k + 1]) {
+        pfx_blocks = pa->blocks[k];
+        pfx_base = pa->slot_of_base[k] + g * pa->blocks[k];
+      }
+  }
+  const int own_blk = p / kBlock;
 
 #pragma unroll 1
   for (int u = 0; u < kTopK / WAVES; ++u) {
@@ -321,37 +402,62 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
     }
     if (nkeys <= 0) continue;   // uniform per wave
 
+    // PREFIX: a block of the shared prefix older than the row's own block may
+    // have been staged; its operands are then read from the slot's images
+    bool staged = false;
+    const uint8_t* img_base = nullptr;
+    if constexpr (PREFIX) {
+      if (blk < pfx_blocks && blk < own_blk) {
+        const int slot = __builtin_amdgcn_readfirstlane(pa->slot_of[pfx_base + blk]);
+        if (slot >= 0) {
+          staged = true;
+          img_base = pa->staged + (size_t)slot * kStageBytes;
+        }
+      }
+    }
+    const bool full = nkeys == kBlock;   // uniform: no key of the block is past p
+    float x[8][4];
+    const KvRsrc vr = kv_rsrc<KT>(vdata, vscales, rowbase);
+    VRaw<KT> vraw[8];
+    if (PREFIX && staged) {
+      const __amdgpu_buffer_rsrc_t img =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(img_base), (short)0, kStageBytes, kBufferFlags);
+      // ---------------- S^T = K Q^T from the K image (a full block: no mask)
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        // one tile's loads at a time (hoisting all 32 would cost 128 registers)
+        __builtin_amdgcn_sched_barrier(0);
+        h8 Ak[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          Ak[c] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(img, lane * 16, (kt * 4 + c) * 1024, 0));
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[kt][r] = acc[r];
+      }
+    } else {
     // Every K load and the first V tiles are issued before the first product.
     // All 128 rows of the page are read (they exist even when the block is
     // only partly visible), which keeps control flow uniform so that each
     // wait covers exactly the tile it needs.
-    // lane indices made opaque here so that the per-lane load offsets are
-    // recomputed per block instead of hoisted out of the loop (and spilled)
-    int jl = j, kpl = kp, dgl = dg, Ql = Q;
-    asm volatile("" : "+v"(jl), "+v"(kpl), "+v"(dgl), "+v"(Ql));
-    constexpr size_t kRowBytes = KT == 2 ? kNvfp4RowBytes : kHeadDim;
-    const uint8_t* kbase = kdata + rowbase * kRowBytes;
-    const uint8_t* vbase = vdata + rowbase * kRowBytes;
-    const uint8_t* ksb = KT == 2 ? kscales + rowbase * kNvfp4ScaleBytes : nullptr;
-    const uint8_t* vsb = KT == 2 ? vscales + rowbase * kNvfp4ScaleBytes : nullptr;
+    const KvRsrc kr = kv_rsrc<KT>(kdata, kscales, rowbase);
     // K tiles in a ring of kKRing slots: tile kt + kKRing is loaded into the
     // slot tile kt leaves once decoded
     KRaw<KT> kraw[kKRing];
 #pragma unroll
-    for (int kt = 0; kt < kKRing; ++kt) kraw[kt] = load_k_tile<KT>(kbase, ksb, kt * 16 + jl, Ql);
-    VRaw<KT> vraw[8];
+    for (int kt = 0; kt < kKRing; ++kt) kraw[kt] = load_k_tile<KT>(kr, lo, kt);
 #pragma unroll
-    for (int kt = 0; kt < kVAhead<KT>; ++kt) vraw[kt] = load_v_tile<KT>(vbase, vsb, kt * 16 + 2 * kpl, dgl);
+    for (int kt = 0; kt < kVAhead<KT>; ++kt) vraw[kt] = load_v_tile<KT>(vr, lo, kt);
 
     // ---------------- S^T = K Q^T, 8 tiles of 16 keys (raw dot products; the
     // softmax scale c_log2 > 0 enters in the exponent's FMA below)
-    const bool full = nkeys == kBlock;   // uniform: no key of the block is past p
-    float x[8][4];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       h8 Ak[4];
       decode_k_tile<KT, FP8MODE>(kraw[kt % kKRing], lut, Ak);
-      if (kt + kKRing < 8) kraw[kt % kKRing] = load_k_tile<KT>(kbase, ksb, (kt + kKRing) * 16 + jl, Ql);
+      if (kt + kKRing < 8) kraw[kt % kKRing] = load_k_tile<KT>(kr, lo, kt + kKRing);
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Ak[c], Bq[c], acc);
@@ -364,6 +470,7 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
           if (kt * 16 + 4 * Q + r >= nkeys) x[kt][r] = NEG_INF;
       }
     }
+    }
     // ---------------- online softmax over this wave's blocks
     float mx = NEG_INF;
 #pragma unroll
@@ -372,14 +479,32 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kt][r]);
     // rounding is monotone and c_log2 > 0, so this is the max of the scaled logits
     mx = max_over_quarters(mx) * c_log2;
-    const float m_new = fmaxf(m, mx);
-    if (m != NEG_INF && m_new != m) {          // rescale what earlier blocks left
-      const float alpha = fast_exp2(m - m_new);
-      l *= alpha;
+    // NVFP4: the running maximum m moves only when a block's maximum exceeds it
+    // by more than kRescaleSlack (log2 units): the weights exp2(s*c - m) then
+    // stay below 2^kRescaleSlack, well inside f16, and most blocks skip
+    // rescaling O -- the same softmax, written in a shifted frame.  FP8 K/V
+    // rescale at every new maximum (the extra live value of the lazy form
+    // would push the 4-wave FP8 kernel past its register budget).
+    if constexpr (KT == 2) {
+      if (mx > m + kRescaleSlack) {
+        if (m != NEG_INF) {                      // rescale what earlier blocks left
+          const float alpha = fast_exp2(m - mx);
+          l *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+          for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+        }
+        m = mx;
+      }
+    } else {
+      const float m_new = fmaxf(m, mx);
+      if (m != NEG_INF && m_new != m) {
+        const float alpha = fast_exp2(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) O[dt] *= alpha;
+      }
+      m = m_new;
     }
-    m = m_new;
     float s = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
@@ -394,6 +519,24 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
     // One 16x16x32 MFMA covers two tiles: lane (Q, j) takes keys 4Q..4Q+3 of
     // each tile of the pair, in P^T (from S^T's layout) and in V^T (two
     // transposing reads) alike.
+    if (PREFIX && staged) {
+      const __amdgpu_buffer_rsrc_t img =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(img_base), (short)0, kStageBytes, kBufferFlags);
+#pragma unroll
+      for (int kt2 = 0; kt2 < 8; kt2 += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        h8 ph;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ph[e] = (_Float16)x[kt2 + (e >> 2)][e & 3];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const h8 a = __builtin_bit_cast(
+              h8, __builtin_amdgcn_raw_buffer_load_b128(img, lane * 16, kStageKBytes + ((kt2 / 2) * 8 + dt) * 1024, 0));
+          O[dt] = mfma_16x16x32(a, ph, O[dt]);
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int kt2 = 0; kt2 < 8; kt2 += 2) {
 #pragma unroll
@@ -402,13 +545,13 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row) {
         // keeps the V window at kVAhead tiles (hoisting further costs registers)
         __builtin_amdgcn_sched_barrier(0);
         if (kt + kVAhead<KT> < 8)
-          vraw[kt + kVAhead<KT>] = load_v_tile<KT>(vbase, vsb, (kt + kVAhead<KT>) * 16 + 2 * kpl, dgl);
+          vraw[kt + kVAhead<KT>] = load_v_tile<KT>(vr, lo, kt + kVAhead<KT>);
         const int key0 = kt * 16 + 2 * kp;
-        stage_v_tile<KT, FP8MODE>(vraw[kt], lut, vt + t2 * kVtBytes, woff, full || key0 < nkeys,
-                                  full || key0 + 1 < nkeys);
+        stage_v_tile<KT, FP8MODE, true>(vraw[kt], lut, vt + t2 * kVtBytes, woff, full || key0 < nkeys,
+                                        full || key0 + 1 < nkeys);
       }
       lds_wait();
-      // P^T operand in f16 (P in (0, 1], rounded to nearest)
+      // P^T operand in f16 (P in (0, 2^kRescaleSlack], rounded to nearest)
       h8 ph;
 #pragma unroll
       for (int e = 0; e < 8; ++e) ph[e] = (_Float16)x[kt2 + (e >> 2)][e & 3];

@@ -30,6 +30,9 @@ constexpr int kHeads = kGroups * kHeadsPerGroup;
 constexpr int kTopK = 16;
 constexpr int kNvfp4RowBytes = kHeadDim / 2;     // codes per 128-dim row
 constexpr int kNvfp4ScaleBytes = kHeadDim / 16;  // E4M3 scales per row
+// Word 3 of a raw buffer resource on gfx950: 32-bit data format, no swizzle,
+// no index stride (byte offsets only).
+constexpr int kBufferFlags = 0x00020000;
 
 // ------------------------------------------------------------------ MFMA
 __device__ __forceinline__ f4 mfma_16x16x32(h8 a, h8 b, f4 c) {

@@ -88,10 +88,26 @@ hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t*
 
 // With block_scores non-null the selection is made inside the attention launch
 // (each workgroup selects its own row; written to sel_out) and sel is not read.
+// With pa non-null (FP8 / NVFP4 caches, no block_scores) staged shared-prefix
+// blocks are read from their images (launch_attention_prefix).
+struct PrefixAttnArgs;
 hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, float q_scale,
                             const CacheArgs& k, const CacheArgs& v, bool fp8mode,
                             const int32_t* sel, float softmax_scale, float* out, float* lse,
-                            hipStream_t s, const float* block_scores = nullptr, int32_t* sel_out = nullptr);
+                            hipStream_t s, const float* block_scores = nullptr, int32_t* sel_out = nullptr,
+                            const PrefixAttnArgs* pa = nullptr);
+
+// Shared-prefix decode attention: byte offsets of its workspace parts for a call
+// with prefix groups gr and T query tokens (staged slot images, slot map, slot
+// block ids, slot counts), and the attention through the staged blocks.
+struct PrefixWorkspace {
+  int slots;
+  size_t staged, slot_of, slot_blk, count, bytes;
+};
+PrefixWorkspace prefix_workspace_layout(const PrefixGroups& gr, int T);
+hipError_t launch_attention_prefix(const ProblemArgs& p, const void* q, float q_scale, const CacheArgs& k,
+                                   const CacheArgs& v, bool fp8mode, const int32_t* sel, float softmax_scale,
+                                   float* out, float* lse, const PrefixGroups& gr, void* workspace, hipStream_t s);
 
 // Quantise the fp32 rows x [B, T, heads, 128] of the T new tokens and write them
 // into their slots of cache c (heads = c's heads per page).

@@ -234,6 +234,37 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
                                      float* block_scores, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
 
+/* Shared-prefix decode attention (section "NVFP4 MSA kernel": a prefix page
+ * common to as many as 64 requests is decoded a single time for all of them).
+ * The same out and lse as msa_sparse_attn_decode with the same arguments, bit
+ * for bit.  Prefix groups as for msa_indexer_scores_prefix: sequences
+ * [group_start[k], group_start[k+1]) hold the same page ids in their first
+ * prefix_blocks[k] logical blocks.  Every block below prefix_blocks[k] that some
+ * row of group k selected as an older block (not its own block) is
+ * dequantised once per KV head into the workspace, as the operands the
+ * attention's matrix products take; the group's rows read it from there
+ * instead of decoding the page again.  Other blocks are decoded as usual.
+ *   num_groups, group_start, prefix_blocks  HOST arrays, as for
+ *                msa_indexer_scores_prefix (0..64 groups of 1..64 sequences);
+ *   workspace    device, 256-byte aligned, at least
+ *                msa_sparse_attn_prefix_workspace_size(prob, num_groups,
+ *                group_start, prefix_blocks) bytes (64 KiB per block slot,
+ *                min(prefix_blocks[k], 16 * rows of group k) slots per group
+ *                and KV head, plus a slot map); scratch, overwritten by every
+ *                call, so calls sharing it must not overlap.
+ * FP8 or NVFP4 K/V and tokens <= 8, else MSA_ERR_UNSUPPORTED; other arguments
+ * and errors as for msa_sparse_attn_decode. */
+msa_status msa_sparse_attn_decode_prefix(const msa_problem* prob, int32_t num_groups, const int32_t* group_start,
+                                         const int32_t* prefix_blocks, const void* q, msa_dtype q_dtype,
+                                         float q_scale, const msa_cache* k, const msa_cache* v, msa_dequant dequant,
+                                         const int32_t* sel, float softmax_scale, float* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Workspace bytes msa_sparse_attn_decode_prefix needs for these prefix groups
+ * (reads only host memory and host-visible fields of prob); 0 for invalid
+ * arguments. */
+size_t msa_sparse_attn_prefix_workspace_size(const msa_problem* prob, int32_t num_groups,
+                                             const int32_t* group_start, const int32_t* prefix_blocks);
+
 /* Steps 3+4 in one launch ("MSA primer": keep the top 16 blocks with the most
  * recent one forced, then attend exactly over them): what msa_block_topk
  * followed by msa_sparse_attn_decode / _prefill computes, with sel written

@@ -2,18 +2,25 @@
 
     python profile_step.py [--workload c3_128k] [--only insert|dcp|prefix] [--out gpurun_out/profile]
 
-Runs bench.py three times as a child process under rocprofv3 (this process
+Runs bench.py five times as a child process under rocprofv3 (this process
 never touches the GPU):
 
   1. --kernel-trace --stats      bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-prefill --no-sides
   2. --pmc FETCH_SIZE            bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-prefill --no-sides
                                  --calib-copy-mib 512
   3. --pmc WRITE_SIZE            (same)
+  4. --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU
+           SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE   (same bench.py)
+  5. --pmc SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_LDS SQ_INST_LEVEL_VMEM
+           SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE                                  (same bench.py)
 
-Counter readings are per dispatch, in KiB.  Each is scaled by what the same
-counter reads for the 512 MiB elementwise copy that bench.py launches with
---calib-copy-mib (which reads and writes exactly 512 MiB), so the reported
-bytes are calibrated HBM bytes per launch.  Writes, into --out:
+FETCH_SIZE / WRITE_SIZE readings are per dispatch, in KiB.  Each is scaled by
+what the same counter reads for the 512 MiB elementwise copy that bench.py
+launches with --calib-copy-mib (which reads and writes exactly 512 MiB), so the
+reported bytes are calibrated HBM bytes per launch.  The SQ counters give, per
+kernel: VALU and MFMA instructions per wave, the VALU and MFMA pipes' busy
+fractions, the share of wave time spent waiting, and LDS bank-conflict cycles
+per LDS instruction (formulas in the summary).  Writes, into --out:
 
 With --only, bench.py runs that side section alone (bench.py --only ...) and the
 files are named cache_insert_c5_chunk_and_c3_decode.*, dcp_<workload>.* or prefix_<workload>.*
@@ -39,6 +46,15 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_attention_indexer_amd", "csrc")
 CALIB_MIB = 512
+# SQ counter passes (at most 8 SQ and 2 GRBM counters each, which one rocprofv3 pass can hold)
+SQ_PASSES = {
+    "SQ1": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+            "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    "SQ2": ["SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_LDS", "SQ_INST_LEVEL_VMEM",
+            "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE"],
+}
+XCDS = 8          # MI355X: GRBM_GUI_ACTIVE sums the active cycles of its 8 XCDs
+CUS = 256         # MI355X compute units (4 SIMDs each)
 
 
 def sources_hash():
@@ -73,6 +89,34 @@ def short(name):
     return n
 
 
+def derive(c):
+    """Per-kernel figures from the SQ counters of one dispatch (whole-GPU sums).
+    SIMD-cycles = 4 SIMDs x CUs x (GRBM_GUI_ACTIVE / XCDS) -- the kernel's active
+    cycles on every SIMD; a wave64 VALU instruction occupies its SIMD 4 cycles and
+    SQ_VALU_MFMA_BUSY_CYCLES counts MFMA pipe cycles directly."""
+    out = {}
+    waves = c.get("SQ_WAVES", 0)
+    gui = c.get("GRBM_GUI_ACTIVE", 0) / XCDS
+    simd_cycles = 4 * CUS * gui
+    if waves:
+        if "SQ_INSTS_VALU" in c:
+            out["valu_per_wave"] = c["SQ_INSTS_VALU"] / waves
+        if "SQ_INSTS_MFMA" in c:
+            out["mfma_per_wave"] = c["SQ_INSTS_MFMA"] / waves
+        if "SQ_INSTS_LDS" in c:
+            out["lds_per_wave"] = c["SQ_INSTS_LDS"] / waves
+    if simd_cycles:
+        if "SQ_ACTIVE_INST_VALU" in c:
+            out["valu_busy"] = 4 * c["SQ_ACTIVE_INST_VALU"] / simd_cycles
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            out["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
+    if c.get("SQ_WAVE_CYCLES"):
+        out["wait_share"] = c.get("SQ_WAIT_INST_ANY", 0) / c["SQ_WAVE_CYCLES"]
+    if c.get("SQ_INSTS_LDS"):
+        out["lds_conflict_cycles_per_lds_inst"] = c.get("SQ_LDS_BANK_CONFLICT", 0) / c["SQ_INSTS_LDS"]
+    return out
+
+
 def run(cmd, log):
     env = dict(os.environ, TMPDIR="/tmp")
     print("[profile] " + " ".join(cmd), flush=True)
@@ -102,6 +146,7 @@ def main():
     ap.add_argument("--only", choices=["insert", "dcp", "prefix"], default=None)
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
     args = ap.parse_args()
+    args.out = os.path.abspath(args.out)   # rocprofv3 runs from /tmp
     os.makedirs(args.out, exist_ok=True)
     py = sys.executable
     bench = os.path.join(ROOT, "bench.py")
@@ -125,6 +170,9 @@ def main():
     cmds = {"trace": trace_cmd}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         cmds[c] = ["rocprofv3", "--pmc", c, "-d", os.path.join(raw, c), "-o", "run", "-f", "csv", "--"] + pmc_bench
+    for tagp, cs in SQ_PASSES.items():
+        cmds[tagp] = ["rocprofv3", "--pmc"] + cs + ["-d", os.path.join(raw, tagp), "-o", "run", "-f", "csv",
+                                                   "--"] + pmc_bench
     for k, cmd in cmds.items():
         if run(cmd, os.path.join(args.out, f"{tag}_{k}.log")) != 0:
             sys.exit(f"rocprofv3 pass {k} failed; see {args.out}/{tag}_{k}.log")
@@ -160,6 +208,12 @@ def main():
         for (name, cn), lst in vals.items():
             if "msa::" in name and cn == c:
                 kib.setdefault(short(name), {})[c] = sum(v for _, v in lst) / len(lst)
+    sq = {}
+    for tagp, cs in SQ_PASSES.items():
+        vals = read_counters(os.path.join(raw, tagp))
+        for (name, cn), lst in vals.items():
+            if "msa::" in name:
+                sq.setdefault(short(name), {})[cn] = sum(v for _, v in lst) / len(lst)
     shutil.rmtree(raw, ignore_errors=True)
 
     kernels = {}
@@ -173,6 +227,10 @@ def main():
         if "WRITE_SIZE" in k:
             e["write_bytes"] = k["WRITE_SIZE"] * 1024.0 * calib["WRITE_SIZE"]
         e["role"] = role_of(name)
+        c = sq.get(name)
+        if c:
+            e["sq"] = c
+            e["derived"] = derive(c)
         kernels[name] = e
     out = {"workload": w, "sources_sha256": sources_hash(), "calibration": calib,
            "commands": {k: " ".join(v) for k, v in cmds.items()}, "kernels": kernels}
@@ -194,6 +252,25 @@ def main():
     for name, e in kernels.items():
         lines.append(f"| `{name}` | {e.get('calls', '')} | {e.get('avg_us', 0):.2f} | {e.get('min_us', 0):.2f} | "
                      f"{e.get('max_us', 0):.2f} | {e.get('fetch_bytes', 0):,.0f} | {e.get('write_bytes', 0):,.0f} |")
+    with_sq = [(n, e) for n, e in kernels.items() if "derived" in e]
+    if with_sq:
+        lines += ["", "SQ counters (passes SQ1 and SQ2, whole-GPU sums per dispatch).  VALU busy = 4 x "
+                  "SQ_ACTIVE_INST_VALU / SIMD-cycles and MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles, "
+                  f"with SIMD-cycles = 4 x {CUS} x GRBM_GUI_ACTIVE / {XCDS}; wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; "
+                  "LDS conflict = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS.", "",
+                  "| kernel | waves | VALU / wave | MFMA / wave | LDS / wave | VALU busy | MFMA busy | wait | "
+                  "LDS conflict cycles / LDS inst |", "|---|---|---|---|---|---|---|---|---|"]
+        for name, e in with_sq:
+            d, c = e["derived"], e["sq"]
+            f = lambda k, fmt: format(d[k], fmt) if k in d else ""
+            lines.append(f"| `{name}` | {c.get('SQ_WAVES', 0):,.0f} | {f('valu_per_wave', ',.0f')} | "
+                         f"{f('mfma_per_wave', ',.1f')} | {f('lds_per_wave', ',.1f')} | {f('valu_busy', '.3f')} | "
+                         f"{f('mfma_busy', '.3f')} | {f('wait_share', '.3f')} | "
+                         f"{f('lds_conflict_cycles_per_lds_inst', '.3f')} |")
+        lines += ["", "Raw SQ counters:", "", "| kernel | counter | value |", "|---|---|---|"]
+        for name, e in with_sq:
+            for cn, v in sorted(e["sq"].items()):
+                lines.append(f"| `{name}` | {cn} | {v:,.0f} |")
     grids_of = {}
     for name, grid in shapes:
         grids_of.setdefault(name, set()).add(grid)

@@ -118,16 +118,16 @@ class DeviceCase:
         self.idx_q32, self.q32 = idx_q, q
         hot = synth.hot_blocks(w, lay, seed)
         P = lay.num_pages
-        self.scales = sc = case_scales(w, scaled)
-        self.S = sc["k"]
-        self.idx_q_scale, self.q_scale = sc["idx_q"], sc["q"]
+        self.scales = scl = case_scales(w, scaled)
+        self.S = scl["k"]
+        self.idx_q_scale, self.q_scale = scl["idx_q"], scl["q"]
         self.d_seq = lay.seq_lens.to(dev)
         self.d_table = lay.block_table.to(dev)
         self.fp32 = {}
         self.d_caches = {}
         for name in ("idx_k", "k", "v"):
             heads = 1 if name == "idx_k" else 4
-            S = sc[name]
+            S = scl[name]
             x = synth.cache_pages(w, lay, seed, name, 0, P, qhat, hot, device=dev)
             if keep_fp32:
                 self.fp32[name] = x
@@ -147,8 +147,8 @@ class DeviceCase:
         if w.q_dtype == "fp8":
             self.d_idx_q = torch.empty(idx_q.shape, dtype=torch.uint8, device=dev)
             self.d_q = torch.empty(q.shape, dtype=torch.uint8, device=dev)
-            M.msa_pack_fp8(idx_q, sc["idx_q"], self.d_idx_q)
-            M.msa_pack_fp8(q, sc["q"], self.d_q)
+            M.msa_pack_fp8(idx_q, scl["idx_q"], self.d_idx_q)
+            M.msa_pack_fp8(q, scl["q"], self.d_q)
         else:
             self.d_idx_q, self.d_q = idx_q, q
         torch.cuda.synchronize()

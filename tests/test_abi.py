@@ -292,6 +292,37 @@ def test_indexer_prefix_validation(lib):
     assert call(prob=big, gs=gs, pb=(1,), wsb=4 * 70) == M.MSA_ERR_INVALID_ARG   # more than 64 sequences
 
 
+def test_sparse_attn_decode_prefix_validation(lib):
+    p = _prob(batch=4)
+    k = _cache(heads=4)
+    gs = (ctypes.c_int32 * 3)(0, 2, 4)
+    pb = (ctypes.c_int32 * 2)(3, 1)
+    need = lib.msa_sparse_attn_prefix_workspace_size(ctypes.byref(p), 2, ctypes.cast(gs, ctypes.c_void_p),
+                                                     ctypes.cast(pb, ctypes.c_void_p))
+    # 4 heads x (3 + 1) slots of 64 KiB, plus the slot map, ids and counts
+    assert need >= 4 * 4 * 65536
+
+    def call(prob=p, n=2, g=gs, b=pb, kk=None, ws=1 << 20, wsb=None, sel=4096, qs=1.0):
+        kk = k if kk is None else kk
+        wsb = need if wsb is None else wsb
+        return lib.msa_sparse_attn_decode_prefix(ctypes.byref(prob), n, ctypes.cast(g, ctypes.c_void_p) if g else None,
+                                                 ctypes.cast(b, ctypes.c_void_p) if b else None, 8192,
+                                                 M.MSA_FP8_E4M3, qs, ctypes.byref(kk), ctypes.byref(kk),
+                                                 M.MSA_DQ_EXACT, sel, 0.088, 16384, None, ws, wsb, None)
+    assert call(wsb=need - 1) == M.MSA_ERR_WORKSPACE
+    assert call(ws=None) == M.MSA_ERR_WORKSPACE
+    assert call(ws=(1 << 20) + 16) == M.MSA_ERR_WORKSPACE                 # not 256-byte aligned
+    assert call(g=(ctypes.c_int32 * 3)(0, 2, 2)) == M.MSA_ERR_INVALID_ARG  # empty group
+    assert call(b=(ctypes.c_int32 * 2)(3, 99)) == M.MSA_ERR_INVALID_ARG    # past max_blocks
+    assert call(g=None) == M.MSA_ERR_INVALID_ARG
+    assert call(n=65) == M.MSA_ERR_INVALID_ARG
+    assert call(sel=None) == M.MSA_ERR_INVALID_ARG
+    assert call(qs=0.0) == M.MSA_ERR_INVALID_ARG
+    assert call(prob=_prob(batch=4, tokens=9)) == M.MSA_ERR_UNSUPPORTED
+    assert call(kk=_cache(heads=4, dtype=M.MSA_F32, scales=None)) == M.MSA_ERR_UNSUPPORTED
+    assert lib.msa_sparse_attn_prefix_workspace_size(ctypes.byref(p), 65, None, None) == 0
+
+
 def test_topk_sparse_attn_validation(lib):
     p = _prob()
     k = _cache(heads=4)

@@ -256,14 +256,16 @@ def test_full_size_sampled(M, wname, samples, mode, scaled):
                               idx_q_scale=case.idx_q_scale)
         H.compare_scores(res["block_scores"][b:b + 1], ora["block_scores"])
         H.compare_selection(gsel[None], ora["sel"], ora["block_scores"], ora["near_tie"], inp["seq_lens"], T)
-        blocks = np.union1d(gsel[gsel >= 0], ora["sel"][ora["sel"] >= 0])
+        rows = np.arange(T) if T <= 8 else np.random.default_rng(b).choice(T, 64, replace=False)
+        # K/V packed (by the oracle, from the fp32 sources) for the blocks the sampled rows attend
+        blocks = np.unique(gsel[rows][gsel[rows] >= 0])
         inp = case.oracle_inputs(b, kv_blocks=blocks)
-        rows = range(T) if T <= 8 else np.random.default_rng(b).choice(T, 64, replace=False)
+        L = int(inp["seq_lens"][0])
+        K = OM.sequence_view(inp["caches"]["k"], inp["kv_table"][0], L, mode)       # decoded once per sample
+        V = OM.sequence_view(inp["caches"]["v"], inp["kv_table"][0], L, mode)
+        _say(wname, "sample", b, "scores and selection ok; attention rows", len(rows))
         for t in rows:
             qq = OM.decode_query(inp["q"][0, t:t + 1], w.q_dtype, case.q_scale)
-            L = int(inp["seq_lens"][0])
-            K = OM.sequence_view(inp["caches"]["k"], inp["kv_table"][0], L, mode)
-            V = OM.sequence_view(inp["caches"]["v"], inp["kv_table"][0], L, mode)
             # a single query token at position L - T + t: view the sequence as ending there
             Lt = L - T + t + 1
             o, lse = OM.sparse_attention(qq, K[:, :Lt], V[:, :Lt], gsel[t:t + 1], Lt, 1, H.SOFTMAX_SCALE)
@@ -613,6 +615,98 @@ def test_indexer_prefix_full_size(M, wname, groups, samples):
         H.compare_scores(got[b:b + 1], ora["block_scores"])
 
 
+# ------------------------------------------------------------------ shared-prefix decode attention
+
+def _force_prefix_blocks(sel, seq_lens, T, groups, per_row=8, seed=0):
+    """A selection in which every row of a group also picks the same `per_row`
+    shared-prefix blocks older than its own block: the own block is kept, the row's
+    other entries are trimmed to make room; rows stay distinct, ascending and -1
+    padded.  (The attention takes any such selection.)"""
+    rng = np.random.default_rng(seed)
+    out = sel.copy()
+    for s0, e0, pb in groups:
+        common = [int(x) for x in rng.permutation(pb)[:per_row]]
+        for b in range(s0, e0):
+            for t in range(T):
+                own = (int(seq_lens[b]) - T + t) // 128
+                for g in range(4):
+                    add = [i for i in common if i < own]
+                    others = [int(i) for i in out[b, t, g] if 0 <= i != own and int(i) not in add]
+                    others = others[:max(0, 15 - len(add))]
+                    row = sorted(set(others + add + [own]))
+                    out[b, t, g] = np.array(row + [-1] * (16 - len(row)), np.int32)
+    return out
+
+
+def _attn_prefix(M, case, groups, mode, sel):
+    w = case.w
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    starts = [g[0] for g in groups] + [groups[-1][1]]
+    blocks = [g[2] for g in groups]
+    nws = M.msa_sparse_attn_prefix_workspace_size(prob, starts, blocks)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda")
+    d_sel = torch.from_numpy(np.ascontiguousarray(sel)).cuda()
+    ref_out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+    ref_lse = torch.empty((w.B, w.T, 64), dtype=torch.float32, device="cuda")
+    M.msa_sparse_attn_decode(prob, case.d_q, w.q_dtype, case.q_scale, case.d_caches["k"][2], case.d_caches["v"][2],
+                             mode, d_sel, H.SOFTMAX_SCALE, ref_out, ref_lse)
+    out = torch.full_like(ref_out, float("nan"))
+    lse = torch.full_like(ref_lse, float("nan"))
+    M.msa_sparse_attn_decode_prefix(prob, starts, blocks, case.d_q, w.q_dtype, case.q_scale, case.d_caches["k"][2],
+                                    case.d_caches["v"][2], mode, d_sel, H.SOFTMAX_SCALE, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), ref_out.cpu().numpy(), ref_lse.cpu().numpy()
+
+
+ATTN_PREFIX = [("tiny_nvfp4", "exact", [(0, 3, 8)], False), ("tiny_nvfp4", "fp8", [(0, 2, 12)], False),
+               ("tiny_fp8", "exact", [(0, 2, 5)], False), ("tiny_spec", "exact", [(0, 2, 10)], False),
+               ("tiny_spec8", "fp8", [(0, 2, 14)], False), ("tiny_t3", "exact", [(0, 1, 4), (1, 3, 12)], False),
+               ("tiny_edge", "exact", [(0, 5, 1)], False), ("long_rows", "exact", [(0, 1, 2000)], False),
+               ("tiny_nvfp4", "exact", [(0, 3, 8)], True), ("tiny_fp8", "exact", [(1, 3, 7)], True)]
+
+
+@pytest.mark.parametrize("wname,mode,groups,scaled", ATTN_PREFIX)
+def test_sparse_attn_decode_prefix(M, wname, mode, groups, scaled):
+    """msa_sparse_attn_decode_prefix equals msa_sparse_attn_decode bit for bit on the
+    same selection -- one where the rows of a group share prefix blocks, so the
+    staged images are read -- and then on the plain selection through the same
+    workspace (nothing of the first call is reused); the output meets the oracle bar
+    on the sharing block table."""
+    _say("attn prefix", wname, mode, groups, "scaled" if scaled else "unit scales")
+    case = H.HostCase(wname, scaled=scaled).upload()
+    _share_prefixes(case, groups)
+    w, lay = case.w, case.lay
+    seq_lens, table = lay.seq_lens.numpy(), lay.block_table.numpy()
+    base = H.to_host(H.run_path(case, mode, attention=False))["sel"]
+    forced = _force_prefix_blocks(base, seq_lens, w.T, groups)
+    shared = sum(int(((forced[s0:e0] >= 0) & (forced[s0:e0] < pb)).sum()) for s0, e0, pb in groups)
+    assert shared > 0
+    results = []
+    for sel in (forced, base):
+        out, lse, ref_out, ref_lse = _attn_prefix(M, case, groups, mode, sel)
+        assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
+        results.append((out, lse))
+    out, lse = results[0]
+    for b in range(w.B):
+        o, l_ = H.oracle_attention(case.caches, case.q, seq_lens, table, w.T, forced[b], mode, w.q_dtype, b,
+                                   q_scale=case.q_scale)
+        H.compare_out(out[b], o)
+        assert np.abs(lse[b] - l_).max() <= 1e-4
+
+
+def test_sparse_attn_decode_prefix_full_size(M):
+    """c3_128k with all 64 sequences sharing their first 512 blocks and every row
+    also selecting 8 common prefix blocks: bit for bit equal to msa_sparse_attn_decode."""
+    _say("attn prefix full size c3_128k")
+    case = H.DeviceCase("c3_128k", keep_fp32=False)
+    groups = [(0, 64, 512)]
+    _share_prefixes(case, groups)
+    base = H.to_host(H.run_path(case, "exact", attention=False))["sel"]
+    forced = _force_prefix_blocks(base, case.lay.seq_lens.numpy(), case.w.T, groups)
+    out, lse, ref_out, ref_lse = _attn_prefix(M, case, groups, "exact", forced)
+    assert np.array_equal(out, ref_out) and np.array_equal(lse, ref_lse)
+
+
 # ------------------------------------------------------------------ selection inside the attention launch
 
 @pytest.mark.parametrize("wname,mode", [("tiny_nvfp4", "exact"), ("tiny_nvfp4", "fp8"), ("tiny_fp8", "exact"),
@@ -771,14 +865,16 @@ def test_decode_step_graph_replays(M):
 
 
 def test_probes_run(M):
-    """The measurement probes launch and finish: a streaming read leaves its sink
-    untouched for zero-filled data, and the MFMA probe writes finite sums."""
+    """The benchmark's measurement probes (bench_probes, not part of libmsa) launch and
+    finish: a streaming read leaves its sink untouched for zero-filled data, and the
+    MFMA probe writes finite sums."""
+    import bench_probes as BP
     _say("probes")
     buf = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(M.MSA_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
-    M.msa_probe_stream_read(buf, sink)
+    sink = torch.zeros(BP.SINK_WORDS, dtype=torch.int32, device="cuda")
+    BP.stream_read(buf, sink)
     out = torch.full((4 * 256,), float("nan"), dtype=torch.float32, device="cuda")
-    M.msa_probe_mfma_f16(out, 4, 10)
+    BP.mfma_f16(out, 4, 10)
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0
     assert bool(torch.isfinite(out).all())
