@@ -31,7 +31,8 @@ EXPORTED = ("msa_indexer_scores", "msa_indexer_topk", "msa_block_topk", "msa_spa
             "msa_topk_merge", "msa_indexer_scores_prefix", "msa_topk_sparse_attn", "msa_cache_insert_many",
             "msa_sparse_attn_prefill", "msa_workspace_size", "msa_pack_fp8", "msa_unpack_fp8",
             "msa_pack_nvfp4", "msa_unpack_nvfp4", "msa_status_string", "msa_abi_version",
-            "msa_sparse_attn_decode_prefix", "msa_sparse_attn_prefix_workspace_size")
+            "msa_indexer_topk_noalloc", "msa_sparse_attn_decode_prefix", "msa_sparse_attn_prefix_workspace_size")
+MSA_NOALLOC_MAX_BATCH = 4096
 
 DTYPES = {"f32": MSA_F32, "fp8": MSA_FP8_E4M3, "nvfp4": MSA_NVFP4}
 DEQUANT = {"exact": MSA_DQ_EXACT, "fp8": MSA_DQ_FP8}
@@ -78,6 +79,8 @@ def _lib():
             "msa_indexer_topk": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp, vp,
                                  sz, vp],
             "msa_block_topk": [P(msa_problem), vp, vp, vp, sz, vp],
+            "msa_indexer_topk_noalloc": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), ctypes.c_int, vp, vp,
+                                         vp],
             "msa_sparse_attn_decode": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
                                        ctypes.c_int, vp, f32, vp, vp, vp, sz, vp],
             "msa_sparse_attn_prefill": [P(msa_problem), vp, ctypes.c_int, f32, P(msa_cache), P(msa_cache),
@@ -171,6 +174,15 @@ def msa_indexer_topk(prob, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores
     _check(_lib().msa_indexer_topk(ctypes.byref(prob), _ptr(idx_q), DTYPES[q_dtype], float(q_scale),
                                    ctypes.byref(idx_k), DEQUANT[dequant], _ptr(block_scores), _ptr(sel),
                                    _ptr(workspace), ws_bytes, _stream(stream)), "msa_indexer_topk")
+
+
+def msa_indexer_topk_noalloc(prob, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores, sel, stream=None):
+    """msa_indexer_topk without a workspace: the library's own per-GPU scratch array
+    holds the arrival counters (at most MSA_NOALLOC_MAX_BATCH sequences; calls that
+    overlap on one GPU race on it)."""
+    _check(_lib().msa_indexer_topk_noalloc(ctypes.byref(prob), _ptr(idx_q), DTYPES[q_dtype], float(q_scale),
+                                           ctypes.byref(idx_k), DEQUANT[dequant], _ptr(block_scores), _ptr(sel),
+                                           _stream(stream)), "msa_indexer_topk_noalloc")
 
 
 def msa_indexer_scores_shard(prob, shard, num_shards, idx_q, q_dtype, q_scale, idx_k, dequant, block_scores,

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = ["pack.hip", "insert.hip", "indexer.hip", "indexer_prefill.hip", "topk.hip", "attn.hip",
-           "dcp.hip", "prefix_attn.hip", "api.cpp"]
+           "dcp.hip", "prefix_attn.hip", "noalloc.hip", "api.cpp"]
 # Per-file flags.  The prefill index GEMM only takes maxima of MFMA results, which
 # hold no NaN (an unreadable page is marked through the NaN bit pattern, stored as
 # an integer); with NaN semantics every fmaxf of an MFMA result is preceded by a

@@ -154,6 +154,37 @@ msa_status msa_indexer_topk(const msa_problem* prob, const void* idx_q, msa_dtyp
   return hip_status(msa::launch_topk(pa, block_scores, sel, stream));
 }
 
+msa_status msa_indexer_topk_noalloc(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
+                                    float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                                    float* block_scores, int32_t* sel, hipStream_t stream) {
+  msa_status st = check_problem(prob);
+  if (st != MSA_OK) return st;
+  if (prob->batch > MSA_NOALLOC_MAX_BATCH) return MSA_ERR_UNSUPPORTED;
+  if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
+  if ((st = check_pair(q_dtype, idx_k->dtype)) != MSA_OK) return st;
+  if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
+  if (idx_q == nullptr || block_scores == nullptr || sel == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned(idx_q, 16) || !aligned(block_scores, 4) || !aligned(sel, 4)) return MSA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale)) return MSA_ERR_INVALID_ARG;
+  static_assert(MSA_NOALLOC_MAX_BATCH <= msa::kStaticMaxBatch, "the static scratch holds every counter");
+  const ProblemArgs pa = to_args(prob);
+  const CacheArgs ka = to_args(idx_k);
+  const bool fp8 = dequant == MSA_DQ_FP8;
+  if (!msa::indexer_can_fuse_topk(pa, ka, fp8)) {
+    // the two kernels, which need no scratch
+    hipError_t e = msa::launch_indexer(pa, idx_q, (int)q_dtype, q_scale, ka, fp8, block_scores, nullptr, stream);
+    if (e != hipSuccess) return MSA_ERR_HIP;
+    return hip_status(msa::launch_topk(pa, block_scores, sel, stream));
+  }
+  uint32_t* counters = nullptr;
+  if (msa::static_scratch(&counters) != hipSuccess) return MSA_ERR_HIP;
+  // the counters of the previous call were left at zero; cleared again all the same
+  hipError_t e = msa::launch_zero_u32(counters, prob->batch, stream);
+  if (e != hipSuccess) return MSA_ERR_HIP;
+  return hip_status(msa::launch_indexer(pa, idx_q, (int)q_dtype, q_scale, ka, fp8, block_scores, nullptr, stream,
+                                        sel, counters));
+}
+
 msa_status msa_block_topk(const msa_problem* prob, const float* block_scores, int32_t* sel,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   msa_status st = check_problem(prob);

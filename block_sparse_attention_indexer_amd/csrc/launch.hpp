@@ -86,6 +86,14 @@ hipError_t launch_fill_skip(const PrefixGroups& g, int B, int32_t* skip, hipStre
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s);
 
+// The allocation-free entry point's scratch: arrival counters for at most
+// kStaticMaxBatch sequences in a file-scope device array.  static_scratch gives
+// its address on the current device (looked up once per device); launch_zero_u32
+// clears n counters with a kernel.
+constexpr int kStaticMaxBatch = 4096;
+hipError_t static_scratch(uint32_t** out);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+
 // With block_scores non-null the selection is made inside the attention launch
 // (each workgroup selects its own row; written to sel_out) and sel is not read.
 // With pa non-null (FP8 / NVFP4 caches, no block_scores) staged shared-prefix

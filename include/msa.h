@@ -299,6 +299,23 @@ msa_status msa_indexer_topk(const msa_problem* prob, const void* idx_q, msa_dtyp
                             float* block_scores, int32_t* sel, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* msa_indexer_topk for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same block_scores and sel, bit for bit, with no workspace argument.  The
+ * per-sequence arrival counters live in a file-scope device array inside the
+ * library (one per GPU, MSA_NOALLOC_MAX_BATCH counters = 16 KiB, held until the
+ * process ends); each call clears the counters it uses with a small kernel on
+ * `stream` before scanning.  No allocation is made.  Calls on one GPU share
+ * that array, so calls that overlap on one GPU (different streams without
+ * ordering) race; calls ordered on one stream do not.
+ *   batch > MSA_NOALLOC_MAX_BATCH returns MSA_ERR_UNSUPPORTED (before any HIP
+ *   call); a failed lookup of the array's address returns MSA_ERR_HIP.
+ * Other arguments and errors as for msa_indexer_topk. */
+#define MSA_NOALLOC_MAX_BATCH 4096
+msa_status msa_indexer_topk_noalloc(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
+                                    float q_scale, const msa_cache* idx_k, msa_dequant dequant,
+                                    float* block_scores, int32_t* sel, hipStream_t stream);
+
 /* Steps 1-4 of one decode layer step in one call ("MSA primer": score,
  * max-pool, select the top 16 blocks with the most recent one forced,
  * attend): msa_indexer_scores, then msa_topk_sparse_attn -- two launches,

@@ -195,6 +195,18 @@ def test_indexer_topk_validation(lib):
     assert call(prob=_prob(topk=8)) == M.MSA_ERR_UNSUPPORTED
 
 
+def test_indexer_topk_noalloc_validation(lib):
+    """The allocation-free call rejects a batch beyond its scratch before any HIP call."""
+    c = _cache()
+
+    def call(prob, sel=4096):
+        return lib.msa_indexer_topk_noalloc(ctypes.byref(prob), 1024, M.MSA_FP8_E4M3, 1.0, ctypes.byref(c), 0, 2048,
+                                            sel, None)
+    assert call(_prob(batch=M.MSA_NOALLOC_MAX_BATCH + 1)) == M.MSA_ERR_UNSUPPORTED
+    assert call(_prob(), sel=None) == M.MSA_ERR_INVALID_ARG
+    assert call(_prob(topk=8)) == M.MSA_ERR_UNSUPPORTED
+
+
 def test_decode_step_validation(lib):
     p = _prob()
     ik = _cache()
