@@ -47,6 +47,23 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 16 ? 1 : WAVES == 8 ? 2 : kAtt
   attend_row<KT, FP8MODE, WAVES, SELECT>(a, blockIdx.x);
 }
 
+// Many rows (prefill): workgroups go to the 8 XCDs round-robin, so workgroup
+// w runs on XCD w % 8.  Rows are renumbered (sequence, group)-major -- r' =
+// (b*4 + g)*T + t -- and XCD x takes the contiguous run of r' starting at
+// x * per: each XCD's L2 then serves consecutive tokens of as few (sequence,
+// KV head) pairs as possible, which share their own block, planted blocks and
+// many others (c5: one pair per XCD instead of two sequences' alternate
+// tokens).  The grid is 8 * per; workgroups past the rows return at once.
+constexpr int kXcds = 8;
+template <int KT, bool FP8MODE>
+__global__ __launch_bounds__(256, kAttnManyWg) void attn_many_kernel(AttnArgs a, int nrows, int per) {
+  const int rr = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (rr >= nrows) return;
+  const int bg = rr / a.T, t = rr - bg * a.T;
+  const int b = bg >> 2, g = bg & 3;
+  attend_row<KT, FP8MODE, 4, false>(a, (b * a.T + t) * kGroups + g);
+}
+
 // Shared-prefix form: staged prefix blocks come from their operand images.
 // Always the 16-wave form (decode row counts), whatever the number of rows.
 template <int KT, bool FP8MODE, int WAVES>
@@ -149,6 +166,7 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   // block of the step is in flight at once.  Many rows (prefill): 4 waves per
   // row with 4 blocks each and a 4-way merge -- a small LDS footprint and many
   // resident rows per CU.  The choice depends only on the row count.
+  const int per = (int)((rows + kXcds - 1) / kXcds);   // rows per XCD in the many-rows form
   const AttnArgs aa{q8, c_log2, k.data, k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale,
                     sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse, block_scores, sel_out};
 #define MSA_ATTN_LAUNCH(KT, FM)                                                                        \
@@ -156,7 +174,7 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
     hipLaunchKernelGGL((attn_prefix_kernel<KT, FM, kDecodeWaves>), dim3(rows), dim3(kDecodeWaves * 64), 0, s, \
                        aa, *pa);                                                                       \
   else if (many)                                                                                       \
-    hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, 4, false>), dim3(rows), dim3(256), 0, s, aa);          \
+    hipLaunchKernelGGL((attn_many_kernel<KT, FM>), dim3(kXcds * per), dim3(256), 0, s, aa, (int)rows, per); \
   else if (select)                                                                                     \
     hipLaunchKernelGGL((attn_mfma_kernel<KT, FM, kDecodeWaves, true>), dim3(rows), dim3(kDecodeWaves * 64), 0, \
                        s, aa);                                                                         \

@@ -29,6 +29,7 @@
 namespace msa {
 
 constexpr int kPfTokens = 64;                  // query tokens per workgroup (x 4 groups = 256 rows)
+constexpr int kPfXcds = 8;                     // XCDs the workgroups are spread over, round-robin
 constexpr int kPfChunk = 16;         // blocks per workgroup
 constexpr int kPfRowHalves = kHeadDim + 16;   // f16 per LDS key row (288 B)
 constexpr int kPfTileHalves = kBlock * kPfRowHalves;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ table, int max_blocks, int T, float sigma,
-    float* __restrict__ block_scores, float* __restrict__ token_scores, PrefixGroups groups) {
+    float* __restrict__ block_scores, float* __restrict__ token_scores, PrefixGroups groups, int nitems = 0) {
   static_assert(!(SHARED && TOKSC), "per-key scores are not written for shared prefixes");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
   __shared__ __attribute__((aligned(16))) _Float16 tile[2][kPfTileHalves];
@@ -114,11 +115,30 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Q = lane >> 4, n = lane & 15;
   // b: the sequence of row token 0 (whose block-table row gives the pages); Tn: row tokens
-  const int b = SHARED ? groups.start[blockIdx.z] : (int)blockIdx.z;
-  const int Tn = SHARED ? (groups.start[blockIdx.z + 1] - b) * T : T;
-  const int blim = SHARED ? min(groups.blocks[blockIdx.z], max_blocks) : max_blocks;
-  const int t0 = blockIdx.x * kPfTokens;
-  const int c0 = blockIdx.y * CHUNK;
+  // Work item (token tile tx, chunk cy, sequence or group bz).  Without SHARED the
+  // grid is 1-D: workgroups go to the 8 XCDs round-robin (workgroup w on XCD
+  // w % 8), and XCD x takes the x-th eighth of the items in (sequence, chunk,
+  // token tile) order, so one key chunk's token tiles share one L2 instead of
+  // every XCD reading every chunk.  SHARED keeps its 3-D grid.
+  int tx, cy, bz;
+  if constexpr (SHARED) {
+    tx = blockIdx.x;
+    cy = blockIdx.y;
+    bz = blockIdx.z;
+  } else {
+    const int ntx = (T + kPfTokens - 1) / kPfTokens, ncy = (max_blocks + CHUNK - 1) / CHUNK;
+    const int per = (int)(gridDim.x / kPfXcds);   // the grid is kPfXcds * per
+    const int item = (int)(blockIdx.x % kPfXcds) * per + (int)(blockIdx.x / kPfXcds);
+    if (item >= nitems) return;
+    tx = item % ntx;
+    cy = (item / ntx) % ncy;
+    bz = item / (ntx * ncy);
+  }
+  const int b = SHARED ? groups.start[bz] : bz;
+  const int Tn = SHARED ? (groups.start[bz + 1] - b) * T : T;
+  const int blim = SHARED ? min(groups.blocks[bz], max_blocks) : max_blocks;
+  const int t0 = tx * kPfTokens;
+  const int c0 = cy * CHUNK;
   if (SHARED && (t0 >= Tn || c0 >= blim)) return;   // the grid covers the largest group
   const int L = seq_lens[b];
   // position of row token t (t < Tn)
@@ -299,15 +319,18 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
 hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const CacheArgs& k,
                                   bool fp8mode, float sigma, float* block_scores, float* token_scores,
                                   hipStream_t s) {
-  const dim3 grid((unsigned)((p.T + kPfTokens - 1) / kPfTokens),
-                  (unsigned)((p.max_blocks + kPfChunk - 1) / kPfChunk), (unsigned)p.B);
+  // 1-D grid over the XCDs (see the kernel): 8 * ceil(items / 8) workgroups,
+  // those past the items return at once
+  const int64_t items = (int64_t)((p.T + kPfTokens - 1) / kPfTokens) * ((p.max_blocks + kPfChunk - 1) / kPfChunk) * p.B;
+  if (items > 0x7FFFFFFF - kPfXcds) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(kPfXcds * ((items + kPfXcds - 1) / kPfXcds)), 1, 1);
   const uint8_t* q8 = static_cast<const uint8_t*>(idx_q);
   const bool ts = token_scores != nullptr;
   const PrefixGroups none{};
 #define MSA_PF_LAUNCH(KT, FM, TS)                                                                \
   hipLaunchKernelGGL((indexer_prefill_kernel<KT, FM, TS>), grid, dim3(256), 0, s, q8, k.data,     \
                      k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T, sigma,  \
-                     block_scores, token_scores, none)
+                     block_scores, token_scores, none, (int)items)
   if (k.dtype == 1) {
     if (ts) MSA_PF_LAUNCH(1, false, true); else MSA_PF_LAUNCH(1, false, false);
   } else if (fp8mode) {

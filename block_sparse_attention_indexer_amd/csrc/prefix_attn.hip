@@ -1,15 +1,15 @@
 // Shared-prefix decode attention (msa_sparse_attn_decode_prefix): every
-// shared-prefix block that some request of a prefix group selected is
-// dequantised once, and all of the group's requests read it from there.
+// shared-prefix block that two or more requests of a prefix group selected is
+// dequantised once, and all of those requests read it from there.
 //
 // Source: "vLLM 為 MiniMax-M3.1-Flash 提供 Day-0 支援", section "NVFP4 MSA
 // kernel" (AMD): the sparse decode attention decodes a prefix page common to
 // as many as 64 requests a single time for all of them.
 //
 // Three launches, no workgroup waits for another:
-//  1. plan: one workgroup per (prefix group, KV head) marks, in an LDS bitmap,
-//     the prefix blocks any of the group's rows selected as an older block,
-//     and numbers them in block order: slot_of[k][g][i] (-1 when not selected)
+//  1. plan: one workgroup per (prefix group, KV head) marks, in LDS bitmaps,
+//     the prefix blocks two or more of the group's rows selected as an older
+//     block, and numbers them in block order: slot_of[k][g][i] (-1 otherwise)
 //     and slot_blk[slot] = i, count[k][g] = the number of slots used.  Slots of
 //     (k, g) lie in a fixed region of the workspace whose size the host derives
 //     from the call's arguments (min(prefix blocks, 16 x the group's rows)).
@@ -39,11 +39,13 @@ struct PrefixPlanArgs {
 };
 
 __global__ __launch_bounds__(256) void prefix_plan_kernel(PrefixPlanArgs a) {
-  __shared__ uint32_t bits[kMaxBlocksSelect / 32];
+  __shared__ uint32_t bits[kMaxBlocksSelect / 32];    // selected by at least one row
+  __shared__ uint32_t multi[kMaxBlocksSelect / 32];   // selected by at least two rows
   __shared__ uint32_t scan[256];
   const int k = blockIdx.x >> 2, g = blockIdx.x & 3, tid = threadIdx.x;
   const int pb = a.map.blocks[k], s0 = a.map.start[k], s1 = a.map.start[k + 1], T = a.T;
   bits[tid] = 0u;
+  multi[tid] = 0u;
   __syncthreads();
   const int entries = (s1 - s0) * T * kTopK;
   for (int e = tid; e < entries; e += 256) {
@@ -51,11 +53,17 @@ __global__ __launch_bounds__(256) void prefix_plan_kernel(PrefixPlanArgs a) {
     const int s = s0 + r / T, t = r % T;
     const int id = a.sel[((size_t)(s * T + t) * kGroups + g) * kTopK + e % kTopK];
     const int own = (a.seq_lens[s] - T + t) / kBlock;
-    if (id >= 0 && id < pb && id < own) atomicOr(&bits[id >> 5], 1u << (id & 31));
+    if (id >= 0 && id < pb && id < own) {
+      const uint32_t m = 1u << (id & 31);
+      // a row's ids are distinct, so a bit already set means a second row
+      if (atomicOr(&bits[id >> 5], m) & m) atomicOr(&multi[id >> 5], m);
+    }
   }
   __syncthreads();
-  // exclusive prefix sum of the 256 words' bit counts (Hillis-Steele over LDS)
-  const uint32_t mine = bits[tid];
+  // Only blocks that two or more rows selected are staged: for a block one row
+  // reads, decoding it in place costs no more than decoding it for the image.
+  // Exclusive prefix sum of the 256 words' bit counts (Hillis-Steele over LDS).
+  const uint32_t mine = multi[tid];
   uint32_t v = __builtin_popcount(mine);
   scan[tid] = v;
   __syncthreads();

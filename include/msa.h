@@ -239,11 +239,11 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
  * The same out and lse as msa_sparse_attn_decode with the same arguments, bit
  * for bit.  Prefix groups as for msa_indexer_scores_prefix: sequences
  * [group_start[k], group_start[k+1]) hold the same page ids in their first
- * prefix_blocks[k] logical blocks.  Every block below prefix_blocks[k] that some
- * row of group k selected as an older block (not its own block) is
- * dequantised once per KV head into the workspace, as the operands the
- * attention's matrix products take; the group's rows read it from there
- * instead of decoding the page again.  Other blocks are decoded as usual.
+ * prefix_blocks[k] logical blocks.  Every block below prefix_blocks[k] that two
+ * or more rows of group k selected as an older block (not their own block)
+ * is dequantised once per KV head into the workspace, as the operands the
+ * attention's matrix products take; those rows read it from there instead of
+ * decoding the page again.  Other blocks are decoded as usual.
  *   num_groups, group_start, prefix_blocks  HOST arrays, as for
  *                msa_indexer_scores_prefix (0..64 groups of 1..64 sequences);
  *   workspace    device, 256-byte aligned, at least
