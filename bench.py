@@ -19,7 +19,7 @@ the timed region, on the stream it runs on, and ``traffic`` from the rocprofv3
 counter summary under profiles/ (null once the kernel sources changed);
 ``dcp``, ``prefix``, ``prefill`` and ``insert`` time the side sections
 (context-parallel shards, shared-prefix scan, the chunked-prefill workload,
-the cache insert); ``ragged_c3``, ``spec_c4`` and ``fp8_c2`` run the default
+the cache insert); ``ragged_c3``, ``spec_c4``, ``fp8_c2`` and ``spec8_c3_128k`` run the default
 step on the other decode workloads; ``ceilings`` measures a streaming read and
 the f16 MFMA rate with the benchmark's probe library; ``timing`` gives the step's
 median / p10 / p90 and its HIP-graph replay; ``cpu_baseline`` is the CPU fp64
@@ -256,7 +256,8 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
     """The first kernel of the step (the index scan) that
     libmsa launches for this workload, as rocprofv3 names it.  The pages-per-wave
     template argument follows the launcher's rule: the largest of its three sizes
-    whose grid gives every CU two workgroups."""
+    whose grid gives every CU one workgroup (one token) or two (speculative
+    decode)."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
@@ -264,16 +265,17 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
     fused = path == "fused" and not fp8mode
     nb = max_blocks if max_blocks is not None else -(-max(np.atleast_1d(w.lens)) // 128)
 
-    def ppw(big):
+    def ppw(big, per_cu):
         for p_ in (big, big // 2):
-            if w.B * -(-nb // (4 * p_)) >= 2 * cus:
+            if w.B * -(-nb // (4 * p_)) >= per_cu * cus:
                 return p_
         return big // 4
     b = lambda x: str(x).lower()
     if w.T == 1:
-        return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16)}, {b(fp8mode)}>"
-    if w.T <= 4:
-        return f"msa::indexer_decode_kernel<{kt}, {b(fp8mode)}, false, {4 if kt == 2 else 2}, true, {ppw(8)}>"
+        return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16, 1)}, {b(fp8mode)}>"
+    if w.T <= 8:
+        return (f"msa::indexer_decode_kernel<{kt}, {b(fp8mode)}, false, {4 if kt == 2 else 2}, true, {ppw(8, 2)}, "
+                f"{1 if w.T <= 4 else 2}>")
     return f"msa::indexer_prefill_kernel<{kt}, {b(fp8mode)}, false>"
 
 
@@ -351,6 +353,7 @@ def decode_section(name, dequant, seed, steps=20, warmup=3):
     step's HBM rate; reported beside the uniform-128K headline.  c3: 64 sequences,
     ragged contexts uniform in [64K, 160K] tokens, NVFP4 with 5% outliers; c4: 16
     sequences of 262,144 tokens, 4 query tokens each (speculative decode), NVFP4;
+    c3_t8: the 128K batch with 8 query tokens each (1 verified + 7 speculative);
     c2: 32 sequences of 32,768 tokens, FP8.  A step whose bytes fit the 256 MB
     Infinity Cache (c2: 203 MB) is reported cold (caches rotated, cold_timing) as its
     headline figures, with the back-to-back (cache-resident) figures beside them."""
@@ -951,6 +954,7 @@ def main():
         out["ragged_c3"] = decode_section("c3", args.dequant, args.seed)
         out["spec_c4"] = decode_section("c4", args.dequant, 4)
         out["fp8_c2"] = decode_section("c2", args.dequant, 2)
+        out["spec8_c3_128k"] = decode_section("c3_t8", args.dequant, 5)
         out["ceilings"] = ceilings_section()
         out["roofline"]["frac_of_measured_stream_read"] = round(
             achieved_idx / out["ceilings"]["stream_read"]["GBps"], 4)

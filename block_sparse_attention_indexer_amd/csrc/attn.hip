@@ -142,10 +142,10 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   const unsigned rows = (unsigned)((int64_t)p.B * p.T * kGroups);
   const bool many = rows >= kAttnManyRows;
   // The selection inside the attention launch pays off for decode (few rows: it
-  // saves a launch); with many rows (prefill) each workgroup's selection latency
-  // adds up (2 x 4,096 prefill tokens on 69,632-token contexts: 1.94 ms against
-  // 0.10 + 1.68 ms), and the fp32 kernel takes a
-  // selection -- there the top-16 kernel runs first.
+  // saves a launch); with many rows (prefill, many speculative tokens) each
+  // workgroup's selection latency adds up (2 x 4,096 prefill tokens on
+  // 69,632-token contexts: 1.94 ms against 0.10 + 1.68 ms), and the fp32 kernel
+  // takes a selection -- there the top-16 kernel runs first.
   bool select = block_scores != nullptr;
   if (select && (k.dtype == 0 || many)) {
     const hipError_t e = launch_topk(p, block_scores, sel_out, s);
@@ -163,9 +163,11 @@ hipError_t launch_attention(const ProblemArgs& p, const void* q, int q_dtype, fl
   const float c_log2 = softmax_scale * q_scale * k.tensor_scale * 1.4426950408889634f;
   const uint8_t* q8 = (const uint8_t*)q;
   // Few rows (decode): 16 waves per row, one selected block each, so every
-  // block of the step is in flight at once.  Many rows (prefill): 4 waves per
-  // row with 4 blocks each and a 4-way merge -- a small LDS footprint and many
-  // resident rows per CU.  The choice depends only on the row count.
+  // block of the step is in flight at once, but one row per CU at a time.
+  // Many rows (>= 1,024: prefill, or 8 speculative tokens on 64 sequences): 4
+  // waves per row with 4 blocks each and a 4-way merge -- a small LDS
+  // footprint and three resident rows per CU (2,048 rows: 165 us against
+  // 215 us).  The choice depends only on the row count.
   const int per = (int)((rows + kXcds - 1) / kXcds);   // rows per XCD in the many-rows form
   const AttnArgs aa{q8, c_log2, k.data, k.scales, k.num_pages, v.data, v.scales, v.num_pages, v.tensor_scale,
                     sel, p.seq_lens, p.block_table, p.max_blocks, p.T, out, lse, block_scores, sel_out};

@@ -37,7 +37,7 @@
 
 namespace msa {
 
-constexpr int kAttnManyRows = 8192;   // rows from which the 4-wave form is used
+constexpr int kAttnManyRows = 1024;   // rows from which the 4-wave form is used
 
 // One 16-key V tile in LDS: f16 [16 keys][128 dims], 256 B per key.  The
 // 16-byte chunk c of key k sits at chunk c ^ vt_swizzle(k): with it the

@@ -1,4 +1,4 @@
-// Steps 1+2 of MSA for decode and speculative decode (T <= 4 query tokens):
+// Steps 1+2 of MSA for decode and speculative decode (T <= 8 query tokens):
 // index scores over the paged index-key cache, max-pooled per 128-token block
 // in the same pass.  (Many query tokens: indexer_prefill.hip.)
 //
@@ -18,7 +18,7 @@
 namespace msa {
 
 // ---------------------------------------------------------------------------
-// Decode and speculative decode (T <= 4): a streaming scan.
+// Decode and speculative decode (T <= 8): a streaming scan.
 //
 // Grid (page range, sequence); each of the 4 waves of a workgroup owns PPW
 // consecutive blocks (kDecPagesPerWave, or a half or a quarter of it when the
@@ -28,7 +28,9 @@ namespace msa {
 // current unit is contracted, so memory and math overlap inside the wave;
 // those loads are unconditional (past the last unit a wave re-reads its last
 // unit, which hits in cache) so that every wait covers exactly one unit.
-// The MFMA rows are 4 tokens x 4 groups.  sigma > 0 is applied to the pooled
+// The MFMA rows are 4 tokens x 4 groups per row tile; NT = 2 tiles (T = 5..8)
+// contract each decoded key tile twice, so the dequantisation is shared by all
+// T tokens and the scan stays bound by the page reads.  sigma > 0 is applied to the pooled
 // maximum only: fl(sigma*x) is monotone in x, so this equals the maximum of
 // the scaled scores.
 constexpr int kDecPagesPerWave = 8;
@@ -88,34 +90,38 @@ __device__ __forceinline__ void decode_idx_tile(const IdxUnit<KT, TPU>& u, int k
   }
 }
 
-// Contract one unit: per tile four 16x16x32 MFMAs and the masked running max.
-// Lane (Q, j) gets token Q, groups 0..3 of key `key0 + 16*kt` (key0 includes j).
-template <int KT, bool FP8MODE, bool TOKSC, int TPU>
-__device__ __forceinline__ void contract_idx_unit(const IdxUnit<KT, TPU>& u, const h8 (&A)[4],
-                                                  const uint32_t* lut, int key0, int p_tok, bool tok_ok,
-                                                  float sigma, float (&bmax)[4], float* tsc_row,
-                                                  size_t tsc_stride) {
+// Contract one unit: per tile and row tile four 16x16x32 MFMAs and the masked
+// running max.  Lane (Q, j) gets token 4n + Q, groups 0..3 of key `key0 + 16*kt`
+// (key0 includes j) from row tile n.
+template <int KT, bool FP8MODE, bool TOKSC, int TPU, int NT>
+__device__ __forceinline__ void contract_idx_unit(const IdxUnit<KT, TPU>& u, const h8 (&A)[NT][4],
+                                                  const uint32_t* lut, int key0, const int (&p_tok)[NT],
+                                                  const bool (&tok_ok)[NT], float sigma, float (&bmax)[NT][4],
+                                                  float* const (&tsc_row)[NT], size_t tsc_stride) {
   const float NEG_INF = -__builtin_inff();
 #pragma unroll
   for (int kt = 0; kt < TPU; ++kt) {
     h8 Bc[4];
     decode_idx_tile<KT, FP8MODE, TPU>(u, kt, lut, Bc);
-    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(A[c], Bc[c], acc);
     const int key = key0 + 16 * kt;
-    const bool vis = tok_ok && key <= p_tok;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      bmax[r] = fmaxf(bmax[r], vis ? acc[r] : NEG_INF);
-      if constexpr (TOKSC) {
-        if (tok_ok) tsc_row[r * tsc_stride + key] = vis ? acc[r] * sigma : NEG_INF;
+    for (int n = 0; n < NT; ++n) {
+      f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(A[n][c], Bc[c], acc);
+      const bool vis = tok_ok[n] && key <= p_tok[n];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bmax[n][r] = fmaxf(bmax[n][r], vis ? acc[r] : NEG_INF);
+        if constexpr (TOKSC) {
+          if (tok_ok[n]) tsc_row[n][r * tsc_stride + key] = vis ? acc[r] * sigma : NEG_INF;
+        }
       }
     }
   }
 }
 
-template <int KT, bool FP8MODE, bool TOKSC, int TPU, bool PIPE, int PPW>
+template <int KT, bool FP8MODE, bool TOKSC, int TPU, bool PIPE, int PPW, int NT>
 __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     const uint8_t* __restrict__ idx_q, const uint8_t* __restrict__ kdata,
     const uint8_t* __restrict__ kscales, int64_t num_pages, const int32_t* __restrict__ seq_lens,
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   static_assert(PPW >= 1 && PPW <= 64, "page ids are held one per lane");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
   // pooled scores of each wave's blocks, [block][token*4 + group], written out at the end
-  __shared__ float pooled[kDecWaves][PPW][16];
+  __shared__ float pooled[kDecWaves][PPW][16 * NT];
   if (FP8MODE) {
     build_fp8_lut(lut);
     __syncthreads();
@@ -155,10 +161,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   const int pid_bad = (pid < 0 || (int64_t)pid >= num_pages) ? 1 : 0;
   const int pid_safe = pid_bad ? 0 : pid;
 
-  // A operand: row j = token j/4, group j%4; k-chunk c = dims 32Q+8c .. +7
-  h8 A[4];
-  {
-    const int t = j >> 2, g = j & 3;
+  // A operands: row j of tile n = token 4n + j/4, group j%4; k-chunk c = dims 32Q+8c .. +7
+  h8 A[NT][4];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int t = 4 * n + (j >> 2), g = j & 3;
     if (t < T) {
       const uint4* src =
           reinterpret_cast<const uint4*>(idx_q + (((size_t)b * T + t) * kGroups + g) * kHeadDim + 32 * Q);
@@ -167,33 +174,47 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const h8 a = fp8x8_to_h8(wq[2 * c], wq[2 * c + 1]);
-        A[c] = (KT == 2 && FP8MODE) ? h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]} : a;
+        A[n][c] = (KT == 2 && FP8MODE) ? h8{a[0], a[2], a[4], a[6], a[1], a[3], a[5], a[7]} : a;
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) A[c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int c = 0; c < 4; ++c) A[n][c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  const bool tok_ok = Q < T;
-  const int p_tok = L - T + Q;
+  bool tok_ok[NT];
+  int p_tok[NT];
   const size_t tstride = (size_t)max_blocks * kBlock;
-  float* tsc_row = TOKSC ? token_scores + (((size_t)b * T + (tok_ok ? Q : 0)) * kGroups) * tstride : nullptr;
+  float* tsc_row[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    tok_ok[n] = 4 * n + Q < T;
+    p_tok[n] = L - T + 4 * n + Q;
+    tsc_row[n] = TOKSC ? token_scores + (((size_t)b * T + (tok_ok[n] ? 4 * n + Q : 0)) * kGroups) * tstride : nullptr;
+  }
 
   // blocks of this wave past the sequence: -inf
-  if (TOKSC && tok_ok) {
-    for (int i = w0 + nreal; i < wend; ++i)
+  if (TOKSC) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)gblk(i) * kBlock + kk] = NEG_INF;
+    for (int n = 0; n < NT; ++n) {
+      if (!tok_ok[n]) continue;
+      for (int i = w0 + nreal; i < wend; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          for (int kk = j; kk < kBlock; kk += 16) tsc_row[n][r * tstride + (size_t)gblk(i) * kBlock + kk] = NEG_INF;
+    }
   }
-  for (int e = lane; e < 16 * (wend - w0 - nreal); e += 64) {
+  for (int e = lane; e < 16 * NT * (wend - w0 - nreal); e += 64) {
     const int n = wend - w0 - nreal;
     const int rowi = e / n, i = gblk(w0 + nreal + e % n);
     if ((rowi >> 2) < T) block_scores[(((size_t)b * T + (rowi >> 2)) * kGroups + (rowi & 3)) * max_blocks + i] = NEG_INF;
   }
 
   const int nunits = nreal * UPP;
-  float bmax[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+  float bmax[NT][4];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bmax[n][r] = NEG_INF;
   IdxUnit<KT, TPU> buf0, buf1;
   if (PIPE && nunits > 0)
     load_idx_unit<KT, TPU>(buf0, kdata, kscales, (size_t)__builtin_amdgcn_readlane(pid_safe, 0) * kBlock + j, Q);
@@ -207,28 +228,31 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
       const size_t row0 = (size_t)__builtin_amdgcn_readlane(pid_safe, blk) * kBlock + part * (16 * TPU) + j;
       load_idx_unit<KT, TPU>(buf0, kdata, kscales, row0, Q);
     }
-    contract_idx_unit<KT, FP8MODE, TOKSC, TPU>(buf0, A, lut, gblk(w0 + blk) * kBlock + part * (16 * TPU) + j,
-                                               p_tok, tok_ok, sigma, bmax, tsc_row, tstride);
+    contract_idx_unit<KT, FP8MODE, TOKSC, TPU, NT>(buf0, A, lut, gblk(w0 + blk) * kBlock + part * (16 * TPU) + j,
+                                                   p_tok, tok_ok, sigma, bmax, tsc_row, tstride);
     if (PIPE) buf0 = buf1;
     if (part == UPP - 1) {
       const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float m = max16(bmax[r]);
-        if (j == 0) pooled[wave][blk][4 * Q + r] = bad ? QNAN : m * sigma;
-        bmax[r] = NEG_INF;
-      }
-      if (TOKSC && bad && tok_ok) {
-        const int i = gblk(w0 + blk);
+      for (int n = 0; n < NT; ++n) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          for (int kk = j; kk < kBlock; kk += 16) tsc_row[r * tstride + (size_t)i * kBlock + kk] = QNAN;
+        for (int r = 0; r < 4; ++r) {
+          const float m = max16(bmax[n][r]);
+          if (j == 0) pooled[wave][blk][16 * n + 4 * Q + r] = bad ? QNAN : m * sigma;
+          bmax[n][r] = NEG_INF;
+        }
+        if (TOKSC && bad && tok_ok[n]) {
+          const int i = gblk(w0 + blk);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            for (int kk = j; kk < kBlock; kk += 16) tsc_row[n][r * tstride + (size_t)i * kBlock + kk] = QNAN;
+        }
       }
     }
   }
   lds_wait();
   // write the pooled scores: entry e -> row (token, group) e / nreal, block w0 + e % nreal
-  for (int e = lane; e < 16 * nreal; e += 64) {
+  for (int e = lane; e < 16 * NT * nreal; e += 64) {
     const int rowi = e / nreal, i = e % nreal;
     const int tt = rowi >> 2, g = rowi & 3;
     if (tt < T) block_scores[(((size_t)b * T + tt) * kGroups + g) * max_blocks + gblk(w0 + i)] = pooled[wave][i][rowi];
@@ -374,28 +398,35 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
     }
 #undef MSA_DEC1_PPW
 #undef MSA_DEC1_LAUNCH
-  } else if (p.T <= 4) {
+  } else if (p.T <= 8) {
+    // speculative decode: one row tile of 4 tokens x 4 groups for T <= 4, two for T <= 8
     const int ppw = pick_ppw(kDecPagesPerWave, 2);
     const dim3 grid((unsigned)((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)), (unsigned)p.B);
-#define MSA_DEC_LAUNCH(KT, FM, TS, PPW)                                                                      \
+#define MSA_DEC_LAUNCH(KT, FM, TS, PPW, NT)                                                                  \
   hipLaunchKernelGGL((indexer_decode_kernel<KT, FM, TS, (KT == 2 ? kDecTpu : kDecTpu / 2),            \
-                                            kDecPipe, PPW>), grid, dim3(kDecWaves * 64), 0, s, q8,   \
+                                            kDecPipe, PPW, NT>), grid, dim3(kDecWaves * 64), 0, s, q8, \
                      k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, p.T,             \
                      sigma, block_scores, token_scores, shard, num_shards, skip)
-#define MSA_DEC_PPW(KT, FM, TS)                                                                   \
-  do {                                                                                            \
-    if (ppw == kDecPagesPerWave) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave);                    \
-    else if (ppw == kDecPagesPerWave / 2) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave / 2);       \
-    else MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave / 4);                                        \
+#define MSA_DEC_PPW(KT, FM, TS, NT)                                                                   \
+  do {                                                                                                \
+    if (ppw == kDecPagesPerWave) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave, NT);                    \
+    else if (ppw == kDecPagesPerWave / 2) MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave / 2, NT);       \
+    else MSA_DEC_LAUNCH(KT, FM, TS, kDecPagesPerWave / 4, NT);                                        \
+  } while (0)
+#define MSA_DEC_NT(KT, FM, TS)                      \
+  do {                                              \
+    if (p.T <= 4) MSA_DEC_PPW(KT, FM, TS, 1);       \
+    else MSA_DEC_PPW(KT, FM, TS, 2);                \
   } while (0)
     const bool ts = token_scores != nullptr;
     if (k.dtype == 1) {
-      if (ts) MSA_DEC_PPW(1, false, true); else MSA_DEC_PPW(1, false, false);
+      if (ts) MSA_DEC_NT(1, false, true); else MSA_DEC_NT(1, false, false);
     } else if (fp8mode) {
-      if (ts) MSA_DEC_PPW(2, true, true); else MSA_DEC_PPW(2, true, false);
+      if (ts) MSA_DEC_NT(2, true, true); else MSA_DEC_NT(2, true, false);
     } else {
-      if (ts) MSA_DEC_PPW(2, false, true); else MSA_DEC_PPW(2, false, false);
+      if (ts) MSA_DEC_NT(2, false, true); else MSA_DEC_NT(2, false, false);
     }
+#undef MSA_DEC_NT
 #undef MSA_DEC_PPW
 #undef MSA_DEC_LAUNCH
   } else {

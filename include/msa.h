@@ -117,7 +117,7 @@ typedef struct {
  *                wholly after p and for i >= ceil(L_b/128).
  *   token_scores device out, nullable, [B][T][4][max_blocks*128] fp32:
  *                the per-key scores (-inf past p), for inspection only.
- * Any T >= 1: T <= 4 runs the decode scan, larger T the prefill kernel. */
+ * Any T >= 1: T <= 8 runs the decode scans, larger T the prefill kernel. */
 msa_status msa_indexer_scores(const msa_problem* prob, const void* idx_q, msa_dtype q_dtype,
                               float q_scale, const msa_cache* idx_k, msa_dequant dequant,
                               float* block_scores, float* token_scores, hipStream_t stream);
@@ -270,10 +270,11 @@ size_t msa_sparse_attn_prefix_workspace_size(const msa_problem* prob, int32_t nu
  * followed by msa_sparse_attn_decode / _prefill computes, with sel written
  * as msa_block_topk writes it (bit for bit) and out / lse as the attention
  * call writes them given that selection (bit for bit).  With fewer than
- * 8,192 (sequence, token, group) rows (decode) each attention workgroup first
+ * 1,024 (sequence, token, group) rows (decode) each attention workgroup first
  * selects its own row's blocks from block_scores, so the selection needs no
- * launch of its own; with more rows (prefill), and for fp32 caches, the
- * top-16 kernel runs first (there it is the faster way).  Any T >= 1.
+ * launch of its own; with more rows (speculative decode of many tokens,
+ * prefill), and for fp32 caches, the top-16 kernel runs first (there it is
+ * the faster way).  Any T >= 1.
  *   block_scores  device [B][T][4][max_blocks], as msa_indexer_scores writes;
  *   sel           device out [B][T][4][16];
  * other arguments as for msa_sparse_attn_decode (no workspace). */

@@ -73,6 +73,8 @@ WORKLOADS = {
     "c3": Workload("c3", 64, 1, (65536, 163840), "nvfp4", "fp8", 0, [], 0.05),
     "c3_128k": Workload("c3_128k", 64, 1, 131072, "nvfp4", "fp8", 0, [], 0.05),
     "c4": Workload("c4", 16, 4, 262144, "nvfp4", "fp8"),
+    # the 128K decode batch verifying 1 + 7 speculative tokens per sequence
+    "c3_t8": Workload("c3_t8", 64, 8, 131072, "nvfp4", "fp8", 0, [], 0.05),
     "c5": Workload("c5", 2, 4096, 69632, "nvfp4", "fp8", 8, [], 0.0, True, True),
     # small cases with the same structure (several tiles, ragged tails)
     "tiny_f32": Workload("tiny_f32", 2, 1, (300, 2600), "f32", "f32", 3, [0, 1, 2], 0.0, True),

@@ -148,7 +148,7 @@ SMALL = [("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_n
          ("tiny_prefill", "exact"), ("tiny_prefill", "fp8"), ("tiny_prefill_fp8", "exact"),
          ("tiny_prefill_many", "exact"), ("tiny_t2", "exact"), ("tiny_t2", "fp8"), ("tiny_t3", "exact"),
          ("tiny_edge", "exact"), ("tiny_prefill_nocache", "exact"), ("long_rows", "exact"),
-         # 7 speculative tokens (T = 8) and T = 6: the prefill index GEMM and the decode attention
+         # 7 speculative tokens (T = 8) and T = 6: the two-row-tile speculative scan and the decode attention
          ("tiny_spec8", "exact"), ("tiny_spec8", "fp8"), ("tiny_t6", "exact")]
 SMALL = [(w, m, False) for w, m in SMALL]
 # per-tensor scales other than 1 (index query, query, index keys, K and V all different)
@@ -238,7 +238,9 @@ FULL = [("c2", [0, 17, 31], "exact", False), ("c3", [0, 21, 63], "exact", False)
         # the FP8-rounded reading on the speculative and prefill workloads
         ("c4", [5], "fp8", False), ("c5", [0], "fp8", False),
         # per-tensor scales other than 1 (K and V on different scales) at full size
-        ("c2", [9], "exact", True), ("c3_128k", [33], "exact", True), ("c4", [14], "fp8", True)]
+        ("c2", [9], "exact", True), ("c3_128k", [33], "exact", True), ("c4", [14], "fp8", True),
+        # 1 + 7 speculative tokens on the 128K batch (two row tiles in the scan)
+        ("c3_t8", [2], "exact", False), ("c3_t8", [50], "fp8", True)]
 
 
 @pytest.mark.parametrize("wname,samples,mode,scaled", FULL)
