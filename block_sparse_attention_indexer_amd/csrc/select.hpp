@@ -75,11 +75,23 @@ __device__ void radix_cut(const uint64_t (&key)[E], uint32_t need, uint64_t& pre
 // best older blocks (keys as above).  Leaves sel_sh[0..15] (LDS) ascending,
 // padded with -1; the caller synchronises before reading it.  S: the row's
 // block scores; E*NT >= own.
+//
+// First a bound, then an exact rank.  Each wave finds, with 16 ballots over
+// the top 16 bits of its keys, the largest prefix x_w such that at least C of
+// its keys are >= x_w << 48; with tau the R-th largest x_w over the NW waves
+// (C * R >= 15), at least 15 keys are >= tau << 48, so tau is at most the
+// row's 15th-best key and every winner is >= it.  The keys >= tau (a few dozen
+// on block-max score rows: a 16-bit prefix resolves a score to 2^-7 relative)
+// go to an LDS list, and one wave ranks them exactly (keys are distinct).  Two
+// barriers instead of three per radix digit.  When more than 64 keys pass
+// (many equal scores), the radix cut over all keys decides instead.
 template <int NT, int E>
 __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
   __shared__ int32_t won[kTopK - 1];
   __shared__ uint32_t n_won;
-  const int tid = threadIdx.x;
+  __shared__ uint32_t tau_sh[NT / 64];
+  __shared__ uint64_t cand[64];
+  const int tid = threadIdx.x, lane = tid & 63;
   if (own + 1 <= kTopK) {
     if (tid < kTopK) sel_sh[tid] = tid <= own ? tid : -1;
     return;
@@ -99,6 +111,72 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
     const int i = tid + e * NT;
     key[e] = (e < ne && i < own) ? select_key(v[e], i) : 0ull;
   }
+
+  // the wave's bound x (wave-uniform): at least C of its keys have a prefix >= x
+  constexpr int NW = NT / 64;
+  static_assert(NW >= 1 && (NW & (NW - 1)) == 0 && NW <= 64, "a power-of-two number of waves");
+  constexpr int C = (kTopK - 1 + NW - 1) / NW > 2 ? (kTopK - 1 + NW - 1) / NW : 2;
+  constexpr int R = (kTopK - 1 + C - 1) / C;
+  static_assert(R <= NW && C * R >= kTopK - 1, "R waves of C keys cover the 15 winners");
+  uint32_t x = 0;
+#pragma unroll 1
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t c = x | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += (uint32_t)__popcll(__ballot(key[e] != 0ull && (uint32_t)(key[e] >> 48) >= c));
+    if (cnt >= (uint32_t)C) x = c;
+  }
+  if (lane == 0) tau_sh[tid >> 6] = x;
+  if (tid == 0) n_won = 0;
+  __syncthreads();
+  // tau: the R-th largest wave bound, found in every wave (lane i < NW holds
+  // bound i; ranks break ties by wave index, so exactly one lane has rank R-1)
+  const uint32_t bnd = tau_sh[lane & (NW - 1)];
+  int rk = 0;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane(bnd, j);
+    rk += (o > bnd || (o == bnd && j < lane)) ? 1 : 0;
+  }
+  const uint64_t at_r = __ballot(lane < NW && rk == R - 1);
+  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane(bnd, __builtin_ctzll(at_r));
+  const uint64_t tau64 = (uint64_t)tau << 48;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (key[e] != 0ull && key[e] >= tau64) {
+      const uint32_t slot = atomicAdd(&n_won, 1u);
+      if (slot < 64u) cand[slot] = key[e];
+    }
+  }
+  __syncthreads();
+  const uint32_t M = n_won;   // >= 15; the same for every thread
+  if (M <= 64u) {
+    if (tid < 64) {
+      // lane l holds candidate l (lanes past M hold 0, below every key); each
+      // lane counts the candidates above its own, read lane by lane
+      const uint64_t mine = (uint32_t)tid < M ? cand[tid] : 0ull;
+      const uint32_t mhi = (uint32_t)(mine >> 32), mlo = (uint32_t)mine;
+      int rank = 0;
+#pragma unroll
+      for (int jj = 0; jj < 64; ++jj) {
+        // readlane yields a signed int: widen each half through uint32_t
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(mhi, jj) << 32) |
+                           (uint64_t)(uint32_t)__builtin_amdgcn_readlane(mlo, jj);
+        rank += o > mine ? 1 : 0;
+      }
+      if ((uint32_t)tid < M && rank < kTopK - 1) won[rank] = select_key_block(mine);
+      // the wave's own LDS writes are seen by its later reads
+      const int32_t id = tid < kTopK - 1 ? won[tid] : (tid == kTopK - 1 ? own : 0x7FFFFFFF);
+      int r2 = 0;
+#pragma unroll
+      for (int k = 0; k < kTopK; ++k) r2 += (__shfl(id, k) < id) ? 1 : 0;
+      if (tid < kTopK) sel_sh[r2] = id;
+    }
+    return;
+  }
+
+  // many keys at the bound (ties): the radix cut over every key
   uint64_t prefix, mask;
   radix_cut<NT, E>(key, kTopK - 1, prefix, mask);   // own >= 16 older blocks
   if (tid == 0) n_won = 0;

@@ -828,6 +828,45 @@ def test_selecting_attention_crafted_rows(M):
     assert np.array_equal(got, sel2.cpu().numpy())
 
 
+def test_selecting_attention_bound_edges(M):
+    """The selecting attention's bound-then-rank selection at its edges (2,344-block
+    rows, three keys per thread): exactly 64 keys at the bound (all tied, the ranked
+    list is full), 65 (the radix fallback), 15 winners alone in their 16-bit prefix
+    above a crowd one prefix lower, and a row of equal scores (every key at the
+    bound).  Ties are broken by block order; the selection equals the oracle's and
+    msa_block_topk's."""
+    _say("selecting attention bound edges")
+    case = H.HostCase("long_rows").upload()
+    w, lay = case.w, case.lay
+    rng = np.random.default_rng(5)
+    L = lay.seq_lens.numpy()
+    maxb = lay.max_blocks
+    s = (-100.0 + 0.01 * rng.standard_normal((w.B, w.T, 4, maxb))).astype(np.float32)
+    s[:, :, 0, 0:64] = 5.0          # 64 ties, all held by wave 0
+    s[:, :, 1, 0:65] = 5.0          # 65 ties: wave 0 and one key of wave 1
+    s[:, :, 2, 100:115] = 7.0       # 15 winners in wave 1
+    s[:, :, 2, 200:300] = 6.99      # a crowd in the next-lower prefix (waves 3 and 4)
+    s[:, :, 3, :] = 1.0             # every key tied
+    for b in range(w.B):
+        for t in range(w.T):
+            s[b, t, :, (L[b] - w.T + t) // 128:] = np.inf
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.from_numpy(s).cuda()
+    sel = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    sel2 = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+    M.msa_topk_sparse_attn(prob, bs, sel, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2], case.d_caches["v"][2],
+                           "exact", H.SOFTMAX_SCALE, out, None)
+    M.msa_block_topk(prob, bs, sel2)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    want = _oracle_sel(s, L, w.T)
+    own = (int(L[0]) - w.T) // 128
+    assert list(want[0, 0, 0]) == list(range(15)) + [own] and list(want[0, 0, 2]) == list(range(100, 115)) + [own]
+    assert np.array_equal(got, want)
+    assert np.array_equal(got, sel2.cpu().numpy())
+
+
 def test_decode_step_graph_replays(M):
     """The decode layer step (index scan, then the selecting attention) captured in a HIP
     graph: three replays, each followed by an eager step, all bit-identical to eager."""
