@@ -254,10 +254,11 @@ def algorithmic_flops(wl, sel_host):
 
 def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
     """The first kernel of the step (the index scan) that
-    libmsa launches for this workload, as rocprofv3 names it.  The pages-per-wave
-    template argument follows the launcher's rule: the largest of its three sizes
-    whose grid gives every CU one workgroup (one token) or two (speculative
-    decode)."""
+    libmsa launches for this workload, as rocprofv3 names it: for one token the
+    evenly spread scan unless the selection is fused into it (then, as for
+    speculative decode, the pages-per-wave template argument follows the
+    launcher's rule: the largest of its three sizes whose grid gives every CU
+    one workgroup (one token) or two (speculative decode))."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
@@ -271,6 +272,8 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
                 return p_
         return big // 4
     b = lambda x: str(x).lower()
+    if w.T == 1 and not fused and w.B <= 1024:
+        return f"msa::indexer_decode1_flat_kernel<{kt}, {b(fp8mode)}>"
     if w.T == 1:
         return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16, 1)}, {b(fp8mode)}>"
     if w.T <= 8:

@@ -37,6 +37,7 @@ constexpr int kDecPagesPerWave = 8;
 constexpr int kDecTpu = 4;          // 16-key units per NVFP4 lane load (half for FP8)
 constexpr bool kDecPipe = true;     // next unit loaded while the current one is contracted
 constexpr int kDec1WgPerCu = 1;     // one-token scan: workgroups per CU the chunking aims for
+constexpr int kDec1FlatWgPerCu = 2; // flat one-token scan: workgroups per CU for large batches (all resident)
 
 template <int KT, int TPU> struct IdxUnit;
 template <int TPU> struct IdxUnit<2, TPU> { uint4 c[TPU]; uint32_t s[TPU]; };   // NVFP4 codes + 2 scale bytes
@@ -277,6 +278,16 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_kernel(Scan
   if constexpr (FUSE) scan1_select_if_last(a, blockIdx.y, gridDim.x, sel, counters);
 }
 
+// The one-token scan spread evenly over a fixed grid (scan1_flat): for
+// ragged contexts, with no selection, shard or skip and no per-key scores.
+template <int KT, bool FP8MODE>
+__global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_flat_kernel(Scan1Args a, int B) {
+  __shared__ __align__(8) uint32_t lut[FP8MODE ? 512 : 2];
+  __shared__ int pre[kFlatMaxSeqs + 1];
+  if constexpr (FP8MODE) build_fp8_lut(lut);   // the prefix pass below synchronises
+  scan1_flat<KT, FP8MODE>(a, B, lut, pre);
+}
+
 // fp32 index keys and queries: one workgroup per (block, sequence), one
 // thread per key, fp32 FMAs in dimension order.
 __global__ __launch_bounds__(128) void indexer_f32_kernel(
@@ -368,7 +379,23 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
       if ((int64_t)p.B * ((nloc + kDecWaves * ppw - 1) / (kDecWaves * ppw)) >= want) return ppw;
     return big / 4;
   };
-  if (p.T == 1 && !(fp8mode && k.dtype == 2 && sel != nullptr)) {
+  const bool flat = p.T == 1 && sel == nullptr && token_scores == nullptr && num_shards == 1 && skip == nullptr &&
+                    p.B <= kFlatMaxSeqs;
+  if (flat) {
+    // one-token scan over a fixed grid, each wave a contiguous share of all
+    // sequences' blocks: two workgroups per CU (the scan's residency), or one
+    // when even B x max_blocks would give a wave fewer than 16 blocks --
+    // long-lived waves win there (32 x 256 blocks: 35.0 us against 39.5 us)
+    const Scan1Args sa{q8, k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,
+                       block_scores, nullptr};
+    const int cus = current_cu_count();
+    const int64_t bound = (int64_t)p.B * p.max_blocks;
+    const int per_cu = bound >= (int64_t)kDec1FlatWgPerCu * cus * kDecWaves * 16 ? kDec1FlatWgPerCu : 1;
+    const dim3 grid((unsigned)(per_cu * cus));
+    if (k.dtype == 1) hipLaunchKernelGGL((indexer_decode1_flat_kernel<1, false>), grid, dim3(kDecWaves * 64), 0, s, sa, p.B);
+    else if (fp8mode) hipLaunchKernelGGL((indexer_decode1_flat_kernel<2, true>), grid, dim3(kDecWaves * 64), 0, s, sa, p.B);
+    else hipLaunchKernelGGL((indexer_decode1_flat_kernel<2, false>), grid, dim3(kDecWaves * 64), 0, s, sa, p.B);
+  } else if (p.T == 1 && !(fp8mode && k.dtype == 2 && sel != nullptr)) {
     // one token: 4x4x4 MFMA scan; the FP8-rounded NVFP4 reading decodes through the
     // LDS table instead of scaling partial dots (not fused with the selection)
     const int ppw = pick_ppw(kDec1PagesPerWave, kDec1WgPerCu);

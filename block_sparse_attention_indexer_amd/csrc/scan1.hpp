@@ -171,29 +171,24 @@ __host__ __device__ __forceinline__ int shard_count(int n, int off, int step) {
 }
 constexpr int kScan1Blocks = kDecWaves * kDec1PagesPerWave;   // blocks per workgroup chunk
 
-// One workgroup's chunk of the scan: shard blocks [4*PPW*chunk, +4*PPW) of
-// sequence b, PPW per wave (blocks past the sequence get -inf).  Smaller PPW
-// gives more, shorter chunks: used when the grid would not fill the chip.
+// Blocks [w0, wend) (local shard indices, wend - w0 <= PPW) of sequence b,
+// scored by one wave: blocks at or past the sequence's end get -inf, the others
+// their pooled score (NaN for an unreadable page).  pooled: this wave's
+// [PPW][4] LDS slice.  b, w0 and wend are wave-uniform.
 // COHERENT: the pooled scores are stored device-coherently, for another
 // workgroup of the same kernel to read.
-template <int KT, bool TOKSC, bool COHERENT, int PPW = kDec1PagesPerWave, bool FP8MODE = false>
-__device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk, const uint32_t* lut = nullptr) {
+template <int KT, bool TOKSC, bool COHERENT, int PPW, bool FP8MODE>
+__device__ __forceinline__ void scan1_blocks(const Scan1Args& a, int b, int w0, int wend, const uint32_t* lut,
+                                             float (*pooled)[kGroups]) {
   static_assert(PPW >= 1 && PPW <= 64, "page ids are held one per lane");
-  __shared__ float pooled[kDecWaves][PPW][kGroups];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const float NEG_INF = -__builtin_inff();
   const float QNAN = __builtin_nanf("");
   const int L = a.seq_lens[b];
   const int nb = min((L + kBlock - 1) / kBlock, a.max_blocks);
-  // local index j of the shard is logical block gblk(j); w0, wend, nreal count local blocks
+  // local index j of the shard is logical block gblk(j)
   auto gblk = [&](int j) { return a.blk_off + a.blk_step * j; };
-  const int nloc = shard_count(a.max_blocks, a.blk_off, a.blk_step);
   const int nb_loc = shard_count(nb, a.blk_off, a.blk_step);
-  const int wbase = (chunk * kDecWaves + wave) * PPW;
-  const int wend = min(wbase + PPW, nloc);
-  // local blocks below skip[b] belong to the shared-prefix kernel
-  const int w0 = a.skip == nullptr ? wbase : max(wbase, shard_count(a.skip[b], a.blk_off, a.blk_step));
-  if (w0 < wend) {
   const int nreal = max(0, min(wend, nb_loc) - w0);
 
   int pid = 0;
@@ -225,7 +220,7 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
   const size_t tstride = (size_t)a.max_blocks * kBlock;
   float* tsc = TOKSC ? a.token_scores + (size_t)b * kGroups * tstride : nullptr;
 
-  // blocks of this wave past the sequence: -inf
+  // blocks of this range past the sequence: -inf
   for (int e = lane; e < kGroups * (wend - w0 - nreal); e += 64) {
     const int n = wend - w0 - nreal;
     a.block_scores[((size_t)b * kGroups + e / n) * a.max_blocks + gblk(w0 + nreal + e % n)] = NEG_INF;
@@ -258,7 +253,7 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
     if (half == 1) {
       const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
       const float m = wave_max4(bmax, lane);
-      if ((lane & 15) == 0) pooled[wave][blk][2 * (lane >> 5) + ((lane >> 4) & 1)] = bad ? QNAN : m * a.sigma;
+      if ((lane & 15) == 0) pooled[blk][2 * (lane >> 5) + ((lane >> 4) & 1)] = bad ? QNAN : m * a.sigma;
       if (TOKSC && bad) {
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
@@ -293,12 +288,102 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
     const int g = e / nreal, i = e % nreal;
     float* dst = a.block_scores + ((size_t)b * kGroups + g) * a.max_blocks + gblk(w0 + i);
     if (COHERENT)   // device-coherent store: read back by another workgroup in this kernel
-      __hip_atomic_store(dst, pooled[wave][i][g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst, pooled[i][g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
-      *dst = pooled[wave][i][g];
+      *dst = pooled[i][g];
   }
-  }   // w0 < wend
+  lds_wait();   // the slice is reused by the wave's next range
+}
 
+// One workgroup's chunk of the scan: shard blocks [4*PPW*chunk, +4*PPW) of
+// sequence b, PPW per wave (blocks past the sequence get -inf).  Smaller PPW
+// gives more, shorter chunks: used when the grid would not fill the chip.
+template <int KT, bool TOKSC, bool COHERENT, int PPW = kDec1PagesPerWave, bool FP8MODE = false>
+__device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk, const uint32_t* lut = nullptr) {
+  __shared__ float pooled[kDecWaves][PPW][kGroups];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nloc = shard_count(a.max_blocks, a.blk_off, a.blk_step);
+  const int wbase = (chunk * kDecWaves + wave) * PPW;
+  const int wend = min(wbase + PPW, nloc);
+  // local blocks below skip[b] belong to the shared-prefix kernel
+  const int w0 = a.skip == nullptr ? wbase : max(wbase, shard_count(a.skip[b], a.blk_off, a.blk_step));
+  if (w0 < wend) scan1_blocks<KT, TOKSC, COHERENT, PPW, FP8MODE>(a, b, w0, wend, lut, pooled[wave]);
+}
+
+// The whole one-token scan spread evenly: the blocks of all sequences, taken
+// in (sequence, block) order, are cut into one contiguous share per wave of
+// the grid (sizes differ by at most one), and each share into ranges that end
+// at sequence boundaries or after 64 blocks.  With ragged contexts every CU
+// then reads the same number of pages, where per-sequence chunks leave some
+// CUs a chunk more than others.  The blocks past each sequence (up to
+// max_blocks) are spread the same way and get -inf.  pre: LDS, B + 1 ints,
+// filled here with the exclusive prefix sums of the sequences' block counts.
+constexpr int kFlatMaxSeqs = 1024;   // sequences the prefix sums in LDS cover
+template <int KT, bool FP8MODE>
+__device__ __forceinline__ void scan1_flat(const Scan1Args& a, int B, const uint32_t* lut, int* pre) {
+  __shared__ float pooled[kDecWaves][64][kGroups];
+  __shared__ int wsum[kDecWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int carry = 0;
+  for (int base = 0; base < B; base += kDecWaves * 64) {
+    const int i = base + tid;
+    int v = 0;
+    if (i < B) v = min((a.seq_lens[i] + kBlock - 1) / kBlock, a.max_blocks);
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) {
+      before += w2 < wave ? wsum[w2] : 0;
+      total += wsum[w2];
+    }
+    if (i < B) pre[i] = carry + before + x - v;
+    carry += total;
+    __syncthreads();   // wsum is rewritten by the next pass
+  }
+  if (tid == 0) pre[B] = carry;
+  __syncthreads();
+  const int64_t N = carry;                                   // blocks with keys, all sequences
+  const int64_t W = (int64_t)gridDim.x * kDecWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kDecWaves + wave;
+  int s = (int)(N * gw / W);
+  const int s1 = (int)(N * (gw + 1) / W);
+  // the sequence holding flat block s: the last b with pre[b] <= s
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= s) lo = mid; else hi = mid;
+  }
+  int b = lo;
+  while (s < s1) {
+    while (pre[b + 1] <= s) ++b;                             // sequences with no block
+    const int j = s - pre[b];
+    const int n = min(min(s1, pre[b + 1]) - s, 64);
+    scan1_blocks<KT, false, false, 64, FP8MODE>(a, b, j, j + n, lut, pooled[wave]);
+    s += n;
+  }
+  // -inf past each sequence: pad entry p of sequence b is block nb_b + (p - padpre[b]),
+  // padpre[b] = b * max_blocks - pre[b]
+  const int64_t P = (int64_t)B * a.max_blocks - N;
+  const int64_t p0 = P * gw / W, p1 = P * (gw + 1) / W;
+  const float NEG_INF = -__builtin_inff();
+  for (int64_t pp = p0 + lane; pp < p1; pp += 64) {
+    int l2 = 0, h2 = B;   // the last b with padpre[b] <= pp
+    while (h2 - l2 > 1) {
+      const int mid = (l2 + h2) >> 1;
+      if ((int64_t)mid * a.max_blocks - pre[mid] <= pp) l2 = mid; else h2 = mid;
+    }
+    const int nbb = pre[l2 + 1] - pre[l2];
+    const int blk = nbb + (int)(pp - ((int64_t)l2 * a.max_blocks - pre[l2]));
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) a.block_scores[((size_t)l2 * kGroups + g) * a.max_blocks + blk] = NEG_INF;
+  }
 }
 
 // After scan1_chunk: counts this workgroup's chunk of sequence b in

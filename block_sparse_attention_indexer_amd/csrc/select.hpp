@@ -78,9 +78,10 @@ __device__ void radix_cut(const uint64_t (&key)[E], uint32_t need, uint64_t& pre
 //
 // First a bound, then an exact rank.  Each wave finds, with 16 ballots over
 // the top 16 bits of its keys, the largest prefix x_w such that at least C of
-// its keys are >= x_w << 48; with tau the R-th largest x_w over the NW waves
-// (C * R >= 15), at least 15 keys are >= tau << 48, so tau is at most the
-// row's 15th-best key and every winner is >= it.  The keys >= tau (a few dozen
+// its keys are >= x_w << 48; with tau the R-th largest x_w over the waves
+// (C * R >= 15; C = max(2, ceil(15 / the number of waves full of candidates))),
+// at least 15 keys are >= tau << 48, so tau is at most the row's 15th-best key
+// and every winner is >= it.  The keys >= tau (a few dozen
 // on block-max score rows: a 16-bit prefix resolves a score to 2^-7 relative)
 // go to an LDS list, and one wave ranks them exactly (keys are distinct).  Two
 // barriers instead of three per radix digit.  When more than 64 keys pass
@@ -112,12 +113,14 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
     key[e] = (e < ne && i < own) ? select_key(v[e], i) : 0ull;
   }
 
-  // the wave's bound x (wave-uniform): at least C of its keys have a prefix >= x
+  // the wave's bound x (wave-uniform): at least C of its keys have a prefix >= x.
+  // C and R follow the number of waves whose 64 keys are all candidates (nwa):
+  // R <= nwa of them reach the R-th largest bound, with C * R >= 15.
   constexpr int NW = NT / 64;
   static_assert(NW >= 1 && (NW & (NW - 1)) == 0 && NW <= 64, "a power-of-two number of waves");
-  constexpr int C = (kTopK - 1 + NW - 1) / NW > 2 ? (kTopK - 1 + NW - 1) / NW : 2;
-  constexpr int R = (kTopK - 1 + C - 1) / C;
-  static_assert(R <= NW && C * R >= kTopK - 1, "R waves of C keys cover the 15 winners");
+  const int nwa = max(1, min(NW, min(own, NT) / 64));
+  const int C = max(2, (kTopK - 1 + nwa - 1) / nwa);
+  const int R = (kTopK - 1 + C - 1) / C;
   uint32_t x = 0;
 #pragma unroll 1
   for (int bit = 15; bit >= 0; --bit) {

@@ -230,6 +230,35 @@ def test_out_of_range_page_gives_nan_not_a_fault(M, wname):
     assert not np.isnan(bs[1]).any()
 
 
+@pytest.mark.parametrize("wname,mode", [("tiny_fp8", "exact"), ("tiny_nvfp4", "exact"), ("tiny_nvfp4", "fp8"),
+                                        ("tiny_edge", "exact"), ("long_rows", "exact"), ("c3", "exact")])
+def test_flat_scan_equals_per_sequence_chunks(M, wname, mode):
+    """The one-token scan spread evenly over all sequences' blocks (used when no
+    per-key scores are asked for) writes every block score -- -inf past each
+    sequence, NaN for an unreadable page -- bit for bit as the per-sequence
+    chunked scan (the form that also writes per-key scores), on ragged batches up
+    to c3's 64 contexts of 64K-160K tokens."""
+    _say("flat scan", wname, mode)
+    case = H.DeviceCase(wname) if wname == "c3" else H.HostCase(wname).upload()
+    w, lay = case.w, case.lay
+    tab = lay.block_table.numpy().copy()
+    bb = int(np.argmax(lay.seq_lens.numpy()))      # a sequence with at least 4 blocks
+    tab[bb, 3] = lay.num_pages + 9                 # one unreadable page
+    d_tab = torch.from_numpy(tab).cuda()
+    prob = M.problem(case.d_seq, d_tab, w.T)
+    shape = (w.B, w.T, 4, lay.max_blocks)
+    flat = torch.full(shape, 7.25, dtype=torch.float32, device="cuda")
+    chunked = torch.full(shape, -7.25, dtype=torch.float32, device="cuda")
+    ts = torch.empty((w.B, w.T, 4, lay.max_blocks * 128), dtype=torch.float32, device="cuda")
+    ik = case.d_caches["idx_k"][2]
+    M.msa_indexer_scores(prob, case.d_idx_q, w.q_dtype, case.idx_q_scale, ik, mode, flat, None)
+    M.msa_indexer_scores(prob, case.d_idx_q, w.q_dtype, case.idx_q_scale, ik, mode, chunked, ts)
+    torch.cuda.synchronize()
+    a, b = flat.cpu().numpy(), chunked.cpu().numpy()
+    assert np.isnan(a[bb, :, :, 3]).all()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 # ------------------------------------------------------------------ full sizes, sampled
 
 FULL = [("c2", [0, 17, 31], "exact", False), ("c3", [0, 21, 63], "exact", False),
