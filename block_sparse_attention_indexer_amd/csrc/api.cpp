@@ -214,7 +214,7 @@ msa_status msa_indexer_scores_shard(const msa_problem* prob, int32_t shard, int3
   if (num_shards < 1 || num_shards > MSA_MAX_SHARDS || shard < 0 || shard >= num_shards) return MSA_ERR_INVALID_ARG;
   if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
   if ((st = check_pair(q_dtype, idx_k->dtype)) != MSA_OK) return st;
-  if (idx_k->dtype == MSA_F32 || prob->tokens > 4) return MSA_ERR_UNSUPPORTED;
+  if (idx_k->dtype == MSA_F32 || prob->tokens > 8) return MSA_ERR_UNSUPPORTED;
   if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
   if (idx_q == nullptr || block_scores == nullptr) return MSA_ERR_INVALID_ARG;
   if (!aligned(idx_q, 16) || !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;
@@ -233,7 +233,7 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
   if (st != MSA_OK) return st;
   if ((st = check_cache(idx_k, 1)) != MSA_OK) return st;
   if ((st = check_pair(q_dtype, idx_k->dtype)) != MSA_OK) return st;
-  if (idx_k->dtype == MSA_F32 || prob->tokens > 4) return MSA_ERR_UNSUPPORTED;
+  if (idx_k->dtype == MSA_F32 || prob->tokens > 8) return MSA_ERR_UNSUPPORTED;
   if (dequant != MSA_DQ_EXACT && dequant != MSA_DQ_FP8) return MSA_ERR_INVALID_ARG;
   if (idx_q == nullptr || block_scores == nullptr) return MSA_ERR_INVALID_ARG;
   if (!aligned(idx_q, 16) || !aligned(block_scores, 4)) return MSA_ERR_INVALID_ARG;

@@ -359,7 +359,7 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
                           int shard, int num_shards, const int32_t* skip) {
   const float sigma = q_scale * k.tensor_scale;
   const int nloc = shard_count(p.max_blocks, shard, num_shards);   // blocks of the shard
-  if ((num_shards != 1 || skip != nullptr) && (k.dtype == 0 || p.T > 4 || sel != nullptr)) return hipErrorInvalidValue;
+  if ((num_shards != 1 || skip != nullptr) && (k.dtype == 0 || p.T > 8 || sel != nullptr)) return hipErrorInvalidValue;
   if (nloc == 0) return hipSuccess;   // a shard past the last block has nothing to score
   if (k.dtype == 0) {
     hipLaunchKernelGGL(indexer_f32_kernel, dim3(p.max_blocks, p.B), dim3(128), 0, s,

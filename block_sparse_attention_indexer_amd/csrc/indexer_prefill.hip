@@ -31,6 +31,7 @@ namespace msa {
 constexpr int kPfTokens = 64;                  // query tokens per workgroup (x 4 groups = 256 rows)
 constexpr int kPfXcds = 8;                     // XCDs the workgroups are spread over, round-robin
 constexpr int kPfChunk = 16;         // blocks per workgroup
+constexpr int kPfWriteWindow = 8;    // blocks whose scores a lane writes back to back
 constexpr int kPfRowHalves = kHeadDim + 16;   // f16 per LDS key row (288 B)
 constexpr int kPfTileHalves = kBlock * kPfRowHalves;
 
@@ -240,6 +241,11 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
   raw = raw2;
   __syncthreads();
 
+  // (with per-key scores, which write every key anyway, one block at a time)
+  constexpr int WW = TOKSC ? 1 : kPfWriteWindow;
+  uint32_t win[WW];   // this lane's row: scores of the current window's blocks
+#pragma unroll
+  for (int u = 0; u < WW; ++u) win[u] = 0u;
   for (int k = 0; k < nblocks; ++k) {
     const int i = c0 + k;
     const _Float16* B = tile[k & 1];
@@ -306,8 +312,24 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
     }
     const float mx = quarter_max4(m, lane);              // query row n of row tile Q
     {
-      const int t = t0 + 4 * (4 * wave + Q) + (n >> 2);
-      if (t < Tn) mark(&block_scores[(((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + i], bad, mx * sigma);
+      // this lane's row keeps the scores of kPfWriteWindow consecutive blocks and
+      // writes them back to back: one score per block would touch each 128-byte
+      // line of the row many times, and lines evicted partly written between
+      // touches multiply the HBM writes
+      const uint32_t bits = bad ? kQNanBits : __builtin_bit_cast(uint32_t, mx * sigma);
+      const int slot = k % WW;
+#pragma unroll
+      for (int u = 0; u < WW; ++u) win[u] = slot == u ? bits : win[u];
+      if (slot == WW - 1 || k == nblocks - 1) {
+        const int t = t0 + 4 * (4 * wave + Q) + (n >> 2);
+        if (t < Tn) {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(block_scores) +
+                          (((size_t)b * T + t) * kGroups + (n & 3)) * max_blocks + (i - slot);
+#pragma unroll
+          for (int u = 0; u < WW; ++u)
+            if (u <= slot) dst[u] = win[u];
+        }
+      }
     }
 
     if (k + 1 < nblocks) pf_store<KT, FP8MODE>(raw, lut, &tile[(k + 1) & 1][key_ld * kPfRowHalves], half_ld);

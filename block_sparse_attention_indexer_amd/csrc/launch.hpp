@@ -55,7 +55,7 @@ hipError_t launch_unpack_nvfp4(const uint8_t* codes, const uint8_t* scales, int6
 // With sel and counters non-null (only where indexer_can_fuse_topk), the scan also
 // writes the top-16 selection; counters: one zeroed uint32 per sequence, left zeroed.
 // num_shards > 1: only the logical blocks i with i % num_shards == shard are scored
-// (FP8 / NVFP4 keys, T <= 4, no fused selection).  skip (device [B], nullable): the
+// (FP8 / NVFP4 keys, T <= 8, no fused selection).  skip (device [B], nullable): the
 // first skip[b] blocks of sequence b are left to another kernel (same restrictions).
 hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
                           const CacheArgs& k, bool fp8mode, float* block_scores,
@@ -77,7 +77,7 @@ hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const
                                   hipStream_t s);
 
 // Shared-prefix decode: the shared blocks of every prefix group scored once for all
-// of the group's query rows (T <= 4); skip: device [B] int32 filled with the shared
+// of the group's query rows (T <= 8); skip: device [B] int32 filled with the shared
 // block count of each sequence (0 outside the groups), for the per-sequence scans.
 hipError_t launch_indexer_shared(const ProblemArgs& p, const void* idx_q, const CacheArgs& k, bool fp8mode,
                                  float sigma, const PrefixGroups& g, float* block_scores, hipStream_t s);

@@ -177,7 +177,7 @@ msa_status msa_sparse_attn_prefill(const msa_problem* prob, const void* q, msa_d
  *   (the same bits as one msa_indexer_scores call writes there, -inf past the
  *   sequence); every other entry is left untouched, so running every shard
  *   once fills block_scores exactly as msa_indexer_scores does.  FP8 or NVFP4
- *   index keys and tokens <= 4 (decode and speculative decode), else
+ *   index keys and tokens <= 8 (decode and speculative decode), else
  *   MSA_ERR_UNSUPPORTED; no per-key scores.
  * msa_shard_topk: the shard's local top-16 per (sequence, token, group) row
  *   of block_scores: among the shard's blocks older than the row's own block
@@ -224,7 +224,7 @@ msa_status msa_topk_merge(const msa_problem* prob, int32_t num_shards, const flo
  *                  MSA_CALL_INDEXER_PREFIX) bytes (4 per sequence), scratch:
  *                  overwritten by every call, so calls that share it must not
  *                  overlap.
- * FP8 or NVFP4 index keys and tokens <= 4, else MSA_ERR_UNSUPPORTED; other
+ * FP8 or NVFP4 index keys and tokens <= 8, else MSA_ERR_UNSUPPORTED; other
  * arguments as for msa_indexer_scores (no per-key scores). */
 #define MSA_MAX_PREFIX_GROUPS 64
 #define MSA_MAX_PREFIX_SEQS 64

@@ -253,7 +253,7 @@ def test_dcp_validation(lib):
     assert shard_scan(n=M.MSA_MAX_SHARDS + 1) == M.MSA_ERR_INVALID_ARG
     assert shard_scan(shard=4) == M.MSA_ERR_INVALID_ARG
     assert shard_scan(shard=-1) == M.MSA_ERR_INVALID_ARG
-    assert shard_scan(prob=_prob(tokens=5)) == M.MSA_ERR_UNSUPPORTED          # decode and speculative only
+    assert shard_scan(prob=_prob(tokens=9)) == M.MSA_ERR_UNSUPPORTED          # decode and speculative only
     assert shard_scan(cache=_cache(dtype=M.MSA_F32, scales=None), qd=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED
     assert shard_scan(bs=None) == M.MSA_ERR_INVALID_ARG
     assert shard_scan(q=1032) == M.MSA_ERR_INVALID_ARG
@@ -297,7 +297,7 @@ def test_indexer_prefix_validation(lib):
     assert call(gs=None) == M.MSA_ERR_INVALID_ARG
     assert call(wsb=12) == M.MSA_ERR_WORKSPACE
     assert call(ws=None) == M.MSA_ERR_WORKSPACE
-    assert call(prob=_prob(batch=4, tokens=5)) == M.MSA_ERR_UNSUPPORTED
+    assert call(prob=_prob(batch=4, tokens=9)) == M.MSA_ERR_UNSUPPORTED
     assert call(cache=_cache(dtype=M.MSA_F32, scales=None), qd=M.MSA_F32) == M.MSA_ERR_UNSUPPORTED
     big = _prob(batch=70)
     gs = (0, 65)

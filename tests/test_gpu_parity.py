@@ -547,7 +547,8 @@ def _check_dcp(case, ref, bs, cs, cb, sel, P, rows=None):
                                           ("tiny_nvfp4", "fp8", 3), ("tiny_fp8", "exact", 2),
                                           ("tiny_spec", "exact", 4), ("tiny_spec", "fp8", 8),
                                           ("tiny_t3", "exact", 5), ("tiny_edge", "exact", 4),
-                                          ("long_rows", "exact", 4), ("long_rows", "exact", 2)])
+                                          ("long_rows", "exact", 4), ("long_rows", "exact", 2),
+                                          ("tiny_spec8", "exact", 4), ("tiny_spec8", "fp8", 3), ("tiny_t6", "exact", 2)])
 def test_dcp_shards_and_merge(M, wname, mode, P):
     """Shard scans write only their own blocks and, together, the unsharded scores bit
     for bit; local top-16s and the merge match the oracle; the merged selection
@@ -609,7 +610,8 @@ def _check_prefix(got, ref, groups, B):
 PREFIX = [("tiny_nvfp4", "exact", [(0, 3, 8)]), ("tiny_nvfp4", "fp8", [(0, 2, 12)]),
           ("tiny_fp8", "exact", [(0, 2, 5)]), ("tiny_spec", "exact", [(0, 2, 10)]),
           ("tiny_spec", "fp8", [(0, 2, 17)]), ("tiny_t3", "exact", [(0, 1, 4), (1, 3, 12)]),
-          ("tiny_edge", "exact", [(0, 5, 16)]), ("long_rows", "exact", [(0, 1, 2000)])]
+          ("tiny_edge", "exact", [(0, 5, 16)]), ("long_rows", "exact", [(0, 1, 2000)]),
+          ("tiny_spec8", "exact", [(0, 2, 12)]), ("tiny_t6", "exact", [(0, 3, 1)])]
 
 
 @pytest.mark.parametrize("wname,mode,groups", PREFIX)
