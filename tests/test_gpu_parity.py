@@ -259,6 +259,41 @@ def test_flat_scan_equals_per_sequence_chunks(M, wname, mode):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("B", [1024, 1025])
+def test_flat_scan_at_its_batch_limit(M, B):
+    """The even-split scan covers batches of up to 1,024 sequences (its prefix sums
+    live in LDS); at 1,024 short ragged contexts (1..700 tokens, a third of them a
+    single block or less, pages shared at random) its block scores equal the
+    chunked scan's bit for bit, and at 1,025 the call takes the chunked scan."""
+    _say("flat scan batch limit", B)
+    g = torch.Generator(device="cpu").manual_seed(77 + B)
+    maxb = 6
+    L = torch.randint(1, 701, (B,), generator=g, dtype=torch.int32)
+    L[: B // 3] = torch.randint(1, 129, (B // 3,), generator=g, dtype=torch.int32)
+    pages = 300
+    table = torch.randint(0, pages, (B, maxb), generator=g, dtype=torch.int32)
+    x = torch.randn((pages * 128, 128), generator=g).cuda()
+    codes = torch.empty((pages * 128, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((pages * 128, 8), dtype=torch.uint8, device="cuda")
+    S = 32.0 / 448.0
+    M.msa_pack_nvfp4(x, S, codes, scales)
+    ik = M.cache("nvfp4", codes, scales, S, heads=1)
+    q = torch.empty((B, 1, 4, 128), dtype=torch.uint8, device="cuda")
+    M.msa_pack_fp8(torch.randn((B, 1, 4, 128), generator=g).cuda(), 1.0, q)
+    prob = M.problem(L.cuda(), table.cuda(), 1)
+    flat = torch.full((B, 1, 4, maxb), 7.25, dtype=torch.float32, device="cuda")
+    chunked = torch.full((B, 1, 4, maxb), -7.25, dtype=torch.float32, device="cuda")
+    ts = torch.empty((B, 1, 4, maxb * 128), dtype=torch.float32, device="cuda")
+    M.msa_indexer_scores(prob, q, "fp8", 1.0, ik, "exact", flat, None)
+    M.msa_indexer_scores(prob, q, "fp8", 1.0, ik, "exact", chunked, ts)
+    torch.cuda.synchronize()
+    a, b = flat.cpu().numpy(), chunked.cpu().numpy()
+    nb = (L.numpy() + 127) // 128
+    assert np.isneginf(a[np.arange(B), 0, 0, np.minimum(nb, maxb - 1)][nb < maxb]).all()   # past each sequence
+    assert np.isfinite(a[:, 0, :, 0]).all()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 # ------------------------------------------------------------------ full sizes, sampled
 
 FULL = [("c2", [0, 17, 31], "exact", False), ("c3", [0, 21, 63], "exact", False),
