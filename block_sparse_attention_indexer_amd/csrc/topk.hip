@@ -130,16 +130,16 @@ __global__ __launch_bounds__(NT) void topk_radix_kernel(
 constexpr int kTopkWaveRows = 4;   // rows (waves) per workgroup
 constexpr int kTopkManyRows = 4096;
 
+// Grid: (token, sequence); wave w of the workgroup takes group w.
 template <int E>
 __global__ __launch_bounds__(64 * kTopkWaveRows) void topk_wave_kernel(
     const float* __restrict__ block_scores, int32_t* __restrict__ sel,
-    const int32_t* __restrict__ seq_lens, int T, int max_blocks, int64_t rows) {
+    const int32_t* __restrict__ seq_lens, int T, int max_blocks) {
+  static_assert(kTopkWaveRows == kGroups, "one wave per group of a (sequence, token)");
   __shared__ WaveTopkLds sh[kTopkWaveRows];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kTopkWaveRows + w;
-  if (row >= rows) return;   // whole wave
-  const int b = (int)(row / ((int64_t)T * kGroups));
-  const int t = (int)((row / kGroups) % T);
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int64_t row = ((int64_t)b * T + t) * kGroups + w;
   const int own = max(0, min((seq_lens[b] - T + t) / kBlock, max_blocks - 1));
   wave_topk_row_regs<E, false>(block_scores + row * max_blocks, own, sel + row * kTopK, sh[w], lane);
 }
@@ -148,16 +148,16 @@ hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t*
                        hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.T * kGroups;
   const dim3 grid((unsigned)rows), block(kTopkThreads);
-  const dim3 wgrid((unsigned)((rows + kTopkWaveRows - 1) / kTopkWaveRows)), wblock(64 * kTopkWaveRows);
+  const dim3 wgrid((unsigned)p.T, (unsigned)p.B), wblock(64 * kTopkWaveRows);   // B <= 65535
   // Many rows: a wave per row keeps every CU busy.  Few rows (decode): a
   // workgroup per row shortens each row's critical path.
   const bool many = rows >= kTopkManyRows;
   if (many && p.max_blocks <= 64 * 16)
     hipLaunchKernelGGL(topk_wave_kernel<16>, wgrid, wblock, 0, s, block_scores, sel, p.seq_lens, p.T,
-                       p.max_blocks, rows);
+                       p.max_blocks);
   else if (many && p.max_blocks <= 64 * 32)
     hipLaunchKernelGGL(topk_wave_kernel<32>, wgrid, wblock, 0, s, block_scores, sel, p.seq_lens, p.T,
-                       p.max_blocks, rows);
+                       p.max_blocks);
   else if (p.max_blocks <= 8 * kTopkThreads)
     hipLaunchKernelGGL(topk_radix_kernel<8>, grid, block, 0, s, block_scores, sel, p.seq_lens, p.T,
                        p.max_blocks);

@@ -12,10 +12,10 @@
 // row from memory (written just before by other workgroups), counts
 // digits in a 256-bin histogram in LDS, and lets one wave scan find the digit.
 // Only one wave takes part, so no workgroup barrier is needed.  The form that
-// holds the row in registers first tries a threshold pass: the 15th largest of
-// the 64 lane maxima bounds the 15th best key from below, and when at most 64
-// keys reach it they are ranked directly, with no histogram atomics (on rows
-// whose best keys crowd into a few lanes the radix select runs instead).
+// holds the row in registers first bounds the 15th best key from below with
+// the lanes' largest keys, and when at most 64 keys reach the bound they are
+// ranked directly, with no histogram atomics (on rows whose best keys crowd
+// into a few lanes the radix select runs instead).
 #pragma once
 #include "common.hpp"
 
@@ -27,6 +27,13 @@ struct WaveTopkLds {
   uint32_t n_won;
   uint64_t cand[64];   // threshold candidates (wave_topk_row_regs)
 };
+
+// The number of lanes for which c holds, counted in 32-bit halves (a 64-bit
+// count would be compared on the vector unit).
+__device__ __forceinline__ uint32_t ballot_count(bool c) {
+  const uint64_t b = __ballot(c);
+  return (uint32_t)__builtin_popcount((uint32_t)b) + (uint32_t)__builtin_popcount((uint32_t)(b >> 32));
+}
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int j) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, j);
@@ -41,7 +48,7 @@ __device__ __forceinline__ void wave_rank_and_store(const WaveTopkLds& sh, int o
   const int32_t mine = lane < kTopK - 1 ? sh.won[lane] : (lane == kTopK - 1 ? own : 0x7FFFFFFF);
   int rank = 0;
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
+  for (int k = 0; k < kTopK; ++k) rank += (__builtin_amdgcn_readlane(mine, k) < mine) ? 1 : 0;
   if (lane < kTopK) {
     if (COHERENT) __hip_atomic_store(out + rank, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else out[rank] = mine;
@@ -126,11 +133,35 @@ __device__ inline void wave_topk_row(const float* S, int own, int32_t* out, Wave
   wave_rank_and_store<true>(sh, own, out, lane);
 }
 
+
+// A 32-bit key of a score for the selection by one wave, in the score order
+// of the selection: -0 and +0 equal, NaN 0 (below every number), other
+// distinct scores distinct.  Non-negative scores keep their bits with the top
+// bit set; negative ones take the two's-complement negation of their bits.
+__device__ __forceinline__ uint32_t wave_score_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t s = (uint32_t)((int32_t)u >> 31);
+  const uint32_t k = (u ^ (s | 0x80000000u)) - s;
+  return x != x ? 0u : k;
+}
+
 // The same selection with the row held in registers: each lane loads its
-// E scores once (lane + 64e), all loads in flight together, and the radix
-// passes run on registers.  For rows of up to 64*E older blocks.  COHERENT:
-// the scores were written, and the selection is read, by other workgroups of
-// the running kernel (device-coherent loads and stores).
+// scores once (blocks lane + 64e, all loads in flight together) and the
+// selection runs on registers.  For rows of up to 64*E older blocks.
+// COHERENT: the scores were written, and the selection is read, by other
+// workgroups of the running kernel (device-coherent loads and stores).
+//
+// First a bound, then an exact rank.  With 16 ballots the wave finds the
+// largest 16-bit prefix x such that at least 15 lanes hold a key whose top 16
+// bits reach x (each lane compares its largest key).  Those lanes hold at
+// least 15 keys >= x << 16, so every winner is >= it.  The keys that reach
+// the bound (the 15 winners and a few more on ordinary rows) go to an LDS
+// list as (key, complemented block) pairs and are ranked exactly.  When more
+// than 64 reach it (scores that agree in their top 16 bits, as when a row's
+// spread is small beside its magnitude), 16 more ballots set the bound's low
+// bits; when that still leaves more than 64 (many equal or crowded scores),
+// or fewer than 15 lanes hold a number at all, a most-significant-digit radix
+// select over all keys decides instead.
 template <int E, bool COHERENT = true>
 __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out, WaveTopkLds& sh, int lane) {
   if (own + 1 <= kTopK) {
@@ -141,63 +172,74 @@ __device__ inline void wave_topk_row_regs(const float* S, int own, int32_t* out,
     return;
   }
   const int n = own;
-  // ne (uniform): the slots that reach a candidate; their loads are all issued
-  // before the first is used, indices past the row clamped to its last candidate
+  // ne (uniform): the slots that hold a candidate; later slots are skipped
   const int ne = min(E, (n + 63) / 64);
   float v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     v[e] = 0.0f;
-    if (e < ne) {
-      const float* p = S + min(lane + 64 * e, n - 1);
-      v[e] = COHERENT ? coherent_load(p) : *p;
-    }
+    if (lane + 64 * e < n) v[e] = COHERENT ? coherent_load(S + lane + 64 * e) : S[lane + 64 * e];
   }
   uint32_t k32[E];
+  uint32_t lmax = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) k32[e] = (e < ne && lane + 64 * e < n) ? order_key(v[e]) : 0u;
+  for (int e = 0; e < E; ++e) {
+    k32[e] = 0;
+    if (e < ne) {
+      k32[e] = lane + 64 * e < n ? wave_score_key(v[e]) : 0u;
+      lmax = max(lmax, k32[e]);
+    }
+  }
   auto key_of = [&](int e) -> uint64_t {
     return ((uint64_t)k32[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * e));
   };
 
-  // Threshold pass.  tau, the 15th largest of the 64 lane maxima, is at most the
-  // row's 15th best key (at least 15 lanes hold a key >= tau), so the 15 winners
-  // are among the keys >= tau.  With n >= 16 candidates lanes 0..15 all hold one,
-  // so exactly one lane has 14 larger lane maxima.  When at most 64 keys reach
-  // tau (the usual case) they are ranked directly; otherwise the radix select
-  // below runs.  No LDS atomics either way on this path.
-  {
-    uint64_t lmax = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (lane + 64 * e < n) lmax = key_of(e) > lmax ? key_of(e) : lmax;
-    int greater = 0;
+  // pass 0 sets the top 16 bits of x; when more than 64 keys reach that bound,
+  // pass 1 sets the low 16 (x is then the 15th largest lane maximum itself)
+  uint32_t x = 0;
 #pragma unroll 1
-    for (int j = 0; j < 64; ++j) greater += readlane_u64(lmax, j) > lmax ? 1 : 0;
-    const uint64_t at15 = __ballot(lmax != 0ull && greater == kTopK - 2);
-    const uint64_t tau = readlane_u64(lmax, __builtin_ctzll(at15));
-    uint32_t ncand = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint32_t top = pass == 0 ? 0x80000000u : 0x8000u;
 #pragma unroll
-    for (int e = 0; e < E; ++e) ncand += (uint32_t)__popcll(__ballot(lane + 64 * e < n && key_of(e) >= tau));
-    if (ncand <= 64) {
-      uint32_t base = 0;
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = x | (top >> i);
+      if (ballot_count(lmax >= c) >= (uint32_t)(kTopK - 1)) x = c;
+    }
+    if (x == 0) break;   // fewer than 15 lanes hold a number
+    // the keys >= x (x > 0 leaves out the empty slots), listed in slot order
+    uint32_t M = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool c = lane + 64 * e < n && key_of(e) >= tau;
+    for (int e = 0; e < E; ++e) {
+      if (e < ne) {
+        const bool c = k32[e] >= x;
         const uint64_t bm = __ballot(c);
-        if (c) sh.cand[base + (uint32_t)__popcll(bm & ((1ull << lane) - 1ull))] = key_of(e);
-        base += (uint32_t)__popcll(bm);
+        if (bm != 0ull) {
+          // position M + (the lanes below this one that hold a key >= x); past 64
+          // entries the list is not used, so positions wrap instead of being tested
+          const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, M));
+          if (c) sh.cand[pos & 63u] = key_of(e);
+          M += ballot_count(c);
+        }
       }
+    }
+    if (M <= 64u) {
+      // zero entries (below every key) up to a multiple of four, read four at a time
+      if ((uint32_t)lane >= M && (uint32_t)lane < ((M + 3u) & ~3u)) sh.cand[lane] = 0ull;
       lds_wait();
-      const uint64_t mine = (uint32_t)lane < ncand ? sh.cand[lane] : 0ull;
+      const uint64_t mine = (uint32_t)lane < M ? sh.cand[lane] : 0ull;
       int r = 0;
 #pragma unroll 1
-      for (uint32_t j = 0; j < ncand; ++j) r += sh.cand[j] > mine ? 1 : 0;
-      if ((uint32_t)lane < ncand && r < kTopK - 1) sh.won[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)mine);
+      for (uint32_t j = 0; j < M; j += 4) {
+        const uint64_t a0 = sh.cand[j], a1 = sh.cand[j + 1], a2 = sh.cand[j + 2], a3 = sh.cand[j + 3];
+        r += (a0 > mine ? 1 : 0) + (a1 > mine ? 1 : 0) + (a2 > mine ? 1 : 0) + (a3 > mine ? 1 : 0);
+      }
+      if ((uint32_t)lane < M && r < kTopK - 1) sh.won[r] = (int32_t)(0xFFFFFFFFu - (uint32_t)mine);
       lds_wait();
       wave_rank_and_store<COHERENT>(sh, own, out, lane);
       return;
     }
+    // the list's writes are complete before the next pass writes it again
+    lds_wait();
   }
 
   uint64_t prefix = 0, mask = 0;

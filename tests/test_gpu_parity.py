@@ -870,6 +870,49 @@ def test_block_topk_crafted_rows(M, T):
     assert np.array_equal(sel.cpu().numpy(), _oracle_sel(scores, L, T))
 
 
+def test_block_topk_wave_bound_edges(M):
+    """msa_block_topk's one-wave form (4,096 rows of up to 1,000 blocks; block i sits in
+    lane i mod 64) at the edges of its bound-then-rank selection: exactly 64 keys at the
+    bound (the ranked list full); 65 (the radix fallback); 15 winners alone in their
+    16-bit prefix above a crowd one prefix lower; every score equal; scores 1,000 apart
+    from zero with a spread of 0.01 or 1 (the top 16 bits agree, so the bound's low bits
+    are set in a second pass), negative and positive; 97% NaN (fewer than 15 lanes hold a
+    number); -3e38 everywhere but 20 blocks.  Equal to the oracle."""
+    _say("block_topk wave bound edges")
+    rng = np.random.default_rng(808)
+    B, T, maxb = 16, 64, 1000
+    L = rng.integers(T + 40 * 128, maxb * 128 + 1, size=B).astype(np.int32)
+    L[0] = maxb * 128
+    s = (-100.0 + 0.01 * rng.standard_normal((B, T, 4, maxb))).astype(np.float32)
+    ev, od = s[:, 0::2], s[:, 1::2]              # views: even and odd tokens
+    ev[:, :, 0, 0:64] = 5.0                       # 64 ties, one per lane
+    ev[:, :, 1, 0:65] = 5.0                       # 65 ties
+    ev[:, :, 2, :] = -1000.0 - np.abs(rng.standard_normal((B, T // 2, maxb)))
+    ev[:, :, 3, :] = rng.standard_normal((B, T // 2, maxb))
+    ev[:, :, 3, :][rng.random((B, T // 2, maxb)) < 0.97] = np.nan
+    od[:, :, 0, 100:115] = 7.0                    # 15 winners in 15 lanes
+    od[:, :, 0, 200:400] = 6.99                   # a crowd one 16-bit prefix lower
+    od[:, :, 1, :] = 1.0                          # every key tied
+    od[:, :, 2, :] = 1000.0 + 0.01 * rng.standard_normal((B, T // 2, maxb))
+    od[:, :, 3, :] = -3.0e38                      # the oracle takes finite scores only
+    for b in range(B):
+        for t in range(1, T, 2):
+            od[b, t // 2, 3, rng.permutation(40)[:20]] = rng.standard_normal(20)   # 20 lanes
+    for b in range(B):
+        for t in range(T):
+            s[b, t, :, (L[b] - T + t) // 128:] = np.inf
+    seq = torch.from_numpy(L).cuda()
+    table = torch.zeros((B, maxb), dtype=torch.int32, device="cuda")
+    prob = M.problem(seq, table, T)
+    sel = torch.full((B, T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    M.msa_block_topk(prob, torch.from_numpy(s).cuda(), sel)
+    torch.cuda.synchronize()
+    want = _oracle_sel(s, L, T)
+    assert list(want[0, 0, 0]) == list(range(15)) + [(int(L[0]) - T) // 128]
+    assert list(want[0, 1, 0]) == list(range(100, 115)) + [(int(L[0]) - T + 1) // 128]
+    assert np.array_equal(sel.cpu().numpy(), want)
+
+
 def test_selecting_attention_crafted_rows(M):
     """The attention launch that selects its own rows (a 16-wave workgroup per row,
     radix select) on crafted score rows of 2,344 blocks -- crowded, tied and NaN rows:
