@@ -188,6 +188,13 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------------ waves
+// The number of lanes for which c holds, counted in 32-bit halves (a 64-bit
+// count would be compared on the vector unit).
+__device__ __forceinline__ uint32_t ballot_count(bool c) {
+  const uint64_t b = __ballot(c);
+  return (uint32_t)__builtin_popcount((uint32_t)b) + (uint32_t)__builtin_popcount((uint32_t)(b >> 32));
+}
+
 __device__ __forceinline__ float max16(float v) {   // max over the 16 lanes of a row
   v = fmaxf(v, __shfl_xor(v, 1));
   v = fmaxf(v, __shfl_xor(v, 2));

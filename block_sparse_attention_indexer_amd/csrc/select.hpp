@@ -84,8 +84,11 @@ __device__ void radix_cut(const uint64_t (&key)[E], uint32_t need, uint64_t& pre
 // and every winner is >= it.  The keys >= tau (a few dozen
 // on block-max score rows: a 16-bit prefix resolves a score to 2^-7 relative)
 // go to an LDS list, and one wave ranks them exactly (keys are distinct).  Two
-// barriers instead of three per radix digit.  When more than 64 keys pass
-// (many equal scores), the radix cut over all keys decides instead.
+// barriers instead of three per radix digit.  When more than 64 keys pass --
+// scores that agree in their top 16 bits, as when a row's spread is small
+// beside a common offset -- 16 more ballots set the low 16 bits of each
+// wave's bound (the same argument over the keys' upper 32 bits); when still
+// more than 64 pass (many equal scores), the radix cut over all keys decides.
 template <int NT, int E>
 __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
   __shared__ int32_t won[kTopK - 1];
@@ -121,39 +124,48 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
   const int nwa = max(1, min(NW, min(own, NT) / 64));
   const int C = max(2, (kTopK - 1 + nwa - 1) / nwa);
   const int R = (kTopK - 1 + C - 1) / C;
-  uint32_t x = 0;
+  // pass 0 sets the top 16 bits of each wave's bound x (over the keys' upper
+  // 32 bits); when more than 64 keys reach the resulting tau, pass 1 sets the
+  // low 16 bits (x is then the wave's C-th largest score key itself)
+  uint32_t x = 0, M = 0;
 #pragma unroll 1
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t c = x | (1u << bit);
-    uint32_t cnt = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint32_t top = pass == 0 ? 0x80000000u : 0x8000u;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = x | (top >> i);   // c >= 1, so only real keys count
+      uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) cnt += (uint32_t)__popcll(__ballot(key[e] != 0ull && (uint32_t)(key[e] >> 48) >= c));
-    if (cnt >= (uint32_t)C) x = c;
-  }
-  if (lane == 0) tau_sh[tid >> 6] = x;
-  if (tid == 0) n_won = 0;
-  __syncthreads();
-  // tau: the R-th largest wave bound, found in every wave (lane i < NW holds
-  // bound i; ranks break ties by wave index, so exactly one lane has rank R-1)
-  const uint32_t bnd = tau_sh[lane & (NW - 1)];
-  int rk = 0;
-#pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane(bnd, j);
-    rk += (o > bnd || (o == bnd && j < lane)) ? 1 : 0;
-  }
-  const uint64_t at_r = __ballot(lane < NW && rk == R - 1);
-  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane(bnd, __builtin_ctzll(at_r));
-  const uint64_t tau64 = (uint64_t)tau << 48;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (key[e] != 0ull && key[e] >= tau64) {
-      const uint32_t slot = atomicAdd(&n_won, 1u);
-      if (slot < 64u) cand[slot] = key[e];
+      for (int e = 0; e < E; ++e) cnt += ballot_count((uint32_t)(key[e] >> 32) >= c);
+      if (cnt >= (uint32_t)C) x = c;
     }
+    if (pass == 1) __syncthreads();   // the first pass's tau_sh and n_won have been read
+    if (lane == 0) tau_sh[tid >> 6] = x;
+    if (tid == 0) n_won = 0;
+    __syncthreads();
+    // tau: the R-th largest wave bound, found in every wave (lane i < NW holds
+    // bound i; ranks break ties by wave index, so exactly one lane has rank R-1)
+    const uint32_t bnd = tau_sh[lane & (NW - 1)];
+    int rk = 0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane(bnd, j);
+      rk += (o > bnd || (o == bnd && j < lane)) ? 1 : 0;
+    }
+    const uint64_t at_r = __ballot(lane < NW && rk == R - 1);
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane(bnd, __builtin_ctzll(at_r));
+    const uint64_t tau64 = (uint64_t)tau << 32;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (key[e] != 0ull && key[e] >= tau64) {
+        const uint32_t slot = atomicAdd(&n_won, 1u);
+        if (slot < 64u) cand[slot] = key[e];
+      }
+    }
+    __syncthreads();
+    M = n_won;   // >= 15; the same for every thread
+    if (M <= 64u) break;
   }
-  __syncthreads();
-  const uint32_t M = n_won;   // >= 15; the same for every thread
   if (M <= 64u) {
     if (tid < 64) {
       // lane l holds candidate l (lanes past M hold 0, below every key); each

@@ -28,13 +28,6 @@ struct WaveTopkLds {
   uint64_t cand[64];   // threshold candidates (wave_topk_row_regs)
 };
 
-// The number of lanes for which c holds, counted in 32-bit halves (a 64-bit
-// count would be compared on the vector unit).
-__device__ __forceinline__ uint32_t ballot_count(bool c) {
-  const uint64_t b = __ballot(c);
-  return (uint32_t)__builtin_popcount((uint32_t)b) + (uint32_t)__builtin_popcount((uint32_t)(b >> 32));
-}
-
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int j) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, j);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), j);

@@ -976,6 +976,41 @@ def test_selecting_attention_bound_edges(M):
     assert np.array_equal(got, sel2.cpu().numpy())
 
 
+def test_selecting_attention_offset_rows(M):
+    """The selecting attention's selection on rows whose scores share a common offset
+    far larger than their spread (the top 16 bits of every score agree, so the bound's
+    low bits are set in a second pass): 1,000 + 0.01 N(0,1), -1,000 - |N(0,1)|, 3 + 0.001
+    N(0,1), and 1,000 + 0.01 N(0,1) rounded to 0.05 (ties: the radix cut decides).  The
+    selection equals the oracle's and msa_block_topk's."""
+    _say("selecting attention offset rows")
+    case = H.HostCase("long_rows").upload()
+    w, lay = case.w, case.lay
+    rng = np.random.default_rng(17)
+    L = lay.seq_lens.numpy()
+    maxb = lay.max_blocks
+    z = rng.standard_normal((w.B, w.T, 4, maxb))
+    s = np.empty((w.B, w.T, 4, maxb), np.float32)
+    s[:, :, 0] = 1000.0 + 0.01 * z[:, :, 0]
+    s[:, :, 1] = -1000.0 - np.abs(z[:, :, 1])
+    s[:, :, 2] = 3.0 + 0.001 * z[:, :, 2]
+    s[:, :, 3] = 1000.0 + np.round(0.2 * z[:, :, 3]) * 0.05
+    for b in range(w.B):
+        for t in range(w.T):
+            s[b, t, :, (L[b] - w.T + t) // 128:] = np.inf
+    prob = M.problem(case.d_seq, case.d_table, w.T)
+    bs = torch.from_numpy(s).cuda()
+    sel = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    sel2 = torch.full((w.B, w.T, 4, 16), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.T, 64, 128), dtype=torch.float32, device="cuda")
+    M.msa_topk_sparse_attn(prob, bs, sel, case.d_q, w.q_dtype, 1.0, case.d_caches["k"][2], case.d_caches["v"][2],
+                           "exact", H.SOFTMAX_SCALE, out, None)
+    M.msa_block_topk(prob, bs, sel2)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    assert np.array_equal(got, _oracle_sel(s, L, w.T))
+    assert np.array_equal(got, sel2.cpu().numpy())
+
+
 def test_decode_step_graph_replays(M):
     """The decode layer step (index scan, then the selecting attention) captured in a HIP
     graph: three replays, each followed by an eager step, all bit-identical to eager."""

@@ -6,7 +6,9 @@ Each wave of NT/64 finds the largest 16-bit key prefix x that at least C of its
 keys reach; the R-th largest such x over the waves (C * R >= 15, C = max(2,
 ceil(15 / full waves))) is reached by at least 15 keys, so it never exceeds the
 row's 15th-best key: every winner survives the filter, and ranking the
-survivors exactly gives the brute-force selection.  Keys are the library's:
+survivors exactly gives the brute-force selection.  When more than 64 keys
+survive, a second pass sets the low 16 bits of each wave's bound over the keys'
+upper 32 bits (the same argument).  Keys are the library's:
 order-preserving score bits over the complemented block id (NaN lowest, -0 ==
 +0), so they are distinct.  This checks the rule, not the kernel; the GPU tests
 check the kernel against msa_block_topk and the oracle.
@@ -41,24 +43,22 @@ def bound_rank(scores, own, NT):
     nwa = max(1, min(NW, min(own, NT) // 64))
     C = max(2, -(-15 // nwa))
     R = -(-15 // C)
-    hi = (slot_keys >> np.uint64(48)).astype(np.int64)
-    valid = slot_keys != 0
-    xs = []
-    for w in range(NW):
-        h, v = hi[:, 64 * w:64 * w + 64], valid[:, 64 * w:64 * w + 64]
-        x = 0
-        for bit in range(15, -1, -1):
-            c = x | (1 << bit)
-            if int(((h >= c) & v).sum()) >= C:
-                x = c
-        xs.append(x)
-    tau = np.uint64(sorted(xs, reverse=True)[R - 1]) << np.uint64(48)
-    cand = keys[keys >= tau]
-    if len(cand) > 64:
-        return None, tau
-    winners = np.sort(cand)[::-1][:15]
-    ids = sorted([int(np.uint64(0xFFFFFFFF) - (k & np.uint64(0xFFFFFFFF))) for k in winners] + [own])
-    return ids, tau
+    hi = (slot_keys >> np.uint64(32)).astype(np.int64)
+    xs = [0] * NW
+    for bits in (range(31, 15, -1), range(15, -1, -1)):   # the second pass only when needed
+        for w in range(NW):
+            h = hi[:, 64 * w:64 * w + 64]
+            for bit in bits:
+                c = xs[w] | (1 << bit)
+                if int((h >= c).sum()) >= C:
+                    xs[w] = c
+        tau = np.uint64(sorted(xs, reverse=True)[R - 1]) << np.uint64(32)
+        cand = keys[keys >= tau]
+        if len(cand) <= 64:
+            winners = np.sort(cand)[::-1][:15]
+            ids = sorted([int(np.uint64(0xFFFFFFFF) - (k & np.uint64(0xFFFFFFFF))) for k in winners] + [own])
+            return ids, tau
+    return None, tau
 
 
 def brute(scores, own):
@@ -66,7 +66,7 @@ def brute(scores, own):
     return sorted([int(np.uint64(0xFFFFFFFF) - (k & np.uint64(0xFFFFFFFF))) for k in keys[:15]] + [own]), keys[14]
 
 
-@pytest.mark.parametrize("kind", ["normal", "block_max", "rounded", "nan", "flat", "hot"])
+@pytest.mark.parametrize("kind", ["normal", "block_max", "rounded", "nan", "flat", "hot", "offset", "negative"])
 @pytest.mark.parametrize("NT", [1024, 256])
 def test_bound_never_drops_a_winner(kind, NT):
     rng = np.random.default_rng([NT] + [ord(ch) for ch in kind])
@@ -86,6 +86,10 @@ def test_bound_never_drops_a_winner(kind, NT):
             s[:] = 1.0
         if kind == "hot":
             s[rng.permutation(own)[:8]] += 40.0
+        if kind == "offset":
+            s = 1000.0 + 0.01 * s                   # the top 16 bits of every score agree
+        if kind == "negative":
+            s = -np.abs(s) - 1000.0
         s = s.astype(np.float32)
         ids, tau = bound_rank(s, own, NT)
         want, kth = brute(s, own)
@@ -93,7 +97,7 @@ def test_bound_never_drops_a_winner(kind, NT):
         if ids is not None:
             fast += 1
             assert ids == want
-    if kind in ("normal", "block_max", "hot"):
+    if kind in ("normal", "block_max", "hot", "offset", "negative"):
         assert fast >= 9                       # the ranked list covers typical rows
 
 
