@@ -195,45 +195,68 @@ __device__ __forceinline__ uint32_t ballot_count(bool c) {
   return (uint32_t)__builtin_popcount((uint32_t)b) + (uint32_t)__builtin_popcount((uint32_t)(b >> 32));
 }
 
+// Cross-lane exchanges on the vector unit, with no LDS round trip.
+// swap32(a, b): gfx950's 32-lane swap trades lanes 32..63 of a for lanes
+// 0..31 of b, so it returns {a.lo | b.lo, a.hi | b.hi} (halves of 32 lanes).
+// swap16(a, b): the row swap trades rows 1 and 3 of a for rows 0 and 2 of b,
+// returning {a.r0 b.r0 a.r2 b.r2, a.r1 b.r1 a.r3 b.r3} (rows of 16 lanes).
+// dpp(v, ctrl): lane l reads the lane of its 16-lane row that ctrl names.
+// (Lane mappings fixed by an in-bounds probe.)
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+constexpr int kDppQuad1032 = 0xB1;       // lanes 4k + {1, 0, 3, 2}
+constexpr int kDppQuad2301 = 0x4E;       // lanes 4k + {2, 3, 0, 1}
+constexpr int kDppRowHalfMirror = 0x141; // lane 7 - i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane 15 - i within each row
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float max16(float v) {   // max over the 16 lanes of a row
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
+  v = fmaxf(v, dpp<kDppQuad1032>(v));
+  v = fmaxf(v, dpp<kDppQuad2301>(v));
+  v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+  return fmaxf(v, dpp<kDppRowMirror>(v));
 }
 __device__ __forceinline__ float max_over_quarters(float v) {   // lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a = v, b = v;
+  swap32(a, b);             // a = v.lo | v.lo, b = v.hi | v.hi
+  float c = fmaxf(a, b), d = c;
+  swap16(c, d);             // rows 0 and 1 of the pair maxima, in every row
+  return fmaxf(c, d);
 }
-__device__ __forceinline__ float sum_over_quarters(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float sum_over_quarters(float v) {   // the same sum in every lane
+  float a = v, b = v;
+  swap32(a, b);
+  float c = a + b, d = c;
+  swap16(c, d);
+  return c + d;
 }
 // Lane l = 16Q + n returns the maximum of value Q over lanes n, n+16, n+32,
-// n+48: 3 exchanges (each lane keeps the half of its values that its side
-// of the exchange owns).
+// n+48: two half swaps pair value 0 (lanes below 32) and value 2 (above)
+// across halves, and values 1 and 3 likewise; one row swap then pairs rows.
 __device__ __forceinline__ float quarter_max4(f4 v, int lane) {
-  const bool up = lane & 32;
-  float a = up ? v[2] : v[0], b = up ? v[3] : v[1];          // keep these two
-  const float sa = up ? v[0] : v[2], sb = up ? v[1] : v[3];  // partner keeps these
-  a = fmaxf(a, __shfl_xor(sa, 32));
-  b = fmaxf(b, __shfl_xor(sb, 32));
-  const bool up16 = lane & 16;
-  const float m = up16 ? b : a;
-  return fmaxf(m, __shfl_xor(up16 ? a : b, 16));
+  (void)lane;
+  float a = v[0], b = v[2], c = v[1], d = v[3];
+  swap32(a, b);             // a = v0.lo | v2.lo, b = v0.hi | v2.hi
+  swap32(c, d);             // c = v1.lo | v3.lo, d = v1.hi | v3.hi
+  float e = fmaxf(a, b), f = fmaxf(c, d);   // halves: value 0 | value 2, value 1 | value 3
+  swap16(e, f);             // e = e.r0 f.r0 e.r2 f.r2, f = e.r1 f.r1 e.r3 f.r3
+  return fmaxf(e, f);
 }
-// Max over the 64 lanes of 4 values: 7 exchanges.  Lane l returns the
-// maximum of value g = 2*(l/32) + (l/16)%2.
+// Max over the 64 lanes of 4 values.  Lane l returns the maximum of value
+// g = 2*(l/32) + (l/16)%2.
 __device__ __forceinline__ float wave_max4(f4 v, int lane) {
-  float m = quarter_max4(v, lane);
-  m = fmaxf(m, __shfl_xor(m, 8));
-  m = fmaxf(m, __shfl_xor(m, 4));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 1));
-  return m;
+  return max16(quarter_max4(v, lane));
 }
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)

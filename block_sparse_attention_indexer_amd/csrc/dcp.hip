@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(
   const int32_t mine = lane < (int)need ? won[lane] : lane == (int)need ? own : 0x7FFFFFFF;
   int rank = 0;
 #pragma unroll
-  for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
+  for (int k = 0; k < kTopK; ++k) rank += (__builtin_amdgcn_readlane(mine, k) < mine) ? 1 : 0;
   if (lane <= (int)need) out[rank] = mine;
   else if (lane < kTopK) out[lane] = -1;
 }

@@ -185,7 +185,7 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
       const int32_t id = tid < kTopK - 1 ? won[tid] : (tid == kTopK - 1 ? own : 0x7FFFFFFF);
       int r2 = 0;
 #pragma unroll
-      for (int k = 0; k < kTopK; ++k) r2 += (__shfl(id, k) < id) ? 1 : 0;
+      for (int k = 0; k < kTopK; ++k) r2 += (__builtin_amdgcn_readlane(id, k) < id) ? 1 : 0;
       if (tid < kTopK) sel_sh[r2] = id;
     }
     return;
@@ -208,7 +208,7 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
     const int32_t mine = tid < kTopK - 1 ? won[tid] : (tid == kTopK - 1 ? own : 0x7FFFFFFF);
     int rank = 0;
 #pragma unroll
-    for (int k = 0; k < kTopK; ++k) rank += (__shfl(mine, k) < mine) ? 1 : 0;
+    for (int k = 0; k < kTopK; ++k) rank += (__builtin_amdgcn_readlane(mine, k) < mine) ? 1 : 0;
     if (tid < kTopK) sel_sh[rank] = mine;
   }
 }
