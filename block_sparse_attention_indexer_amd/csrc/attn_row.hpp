@@ -317,6 +317,12 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const 
       reinterpret_cast<const uint4*>(q + (((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + j) * kHeadDim + 32 * Q);
   const uint4 qu0 = qsrc[0], qu1 = qsrc[1];
   int blks[kTopK / WAVES];
+  // SELECT with 16 waves: the sequence's block-table row (up to 2,048 blocks)
+  // is copied into LDS while the selection runs, so a wave's page id is an LDS
+  // read instead of a memory round trip after the selection
+  constexpr int kTblPerThread = (SELECT && WAVES == 16) ? 2 : 0;
+  __shared__ int32_t tbl_sh[kTblPerThread > 0 ? kTblPerThread * WAVES * 64 : 1];
+  const bool tbl_lds = kTblPerThread > 0 && max_blocks <= kTblPerThread * WAVES * 64;
   if constexpr (SELECT) {
     __shared__ int32_t sel_sh[kTopK];
     const int own = max(0, min((L - T + t) / kBlock, max_blocks - 1));
@@ -325,9 +331,11 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const 
     constexpr int NT = WAVES * 64, EMAX = kMaxBlocksSelect / NT;
     const float* srow = args.block_scores + (size_t)row * max_blocks;
     const int ne = (own + NT - 1) / NT;
-    if (ne <= 1) select_row<NT, 1>(srow, own, sel_sh);
-    else if (ne <= 2 && EMAX >= 2) select_row<NT, (EMAX >= 2 ? 2 : EMAX)>(srow, own, sel_sh);
-    else select_row<NT, EMAX>(srow, own, sel_sh);
+    TablePrefetch tp;
+    if (tbl_lds) tp = TablePrefetch{table + (size_t)b * max_blocks, max_blocks, tbl_sh};
+    if (ne <= 1) select_row<NT, 1, kTblPerThread>(srow, own, sel_sh, tp);
+    else if (ne <= 2 && EMAX >= 2) select_row<NT, (EMAX >= 2 ? 2 : EMAX), kTblPerThread>(srow, own, sel_sh, tp);
+    else select_row<NT, EMAX, kTblPerThread>(srow, own, sel_sh, tp);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kTopK / WAVES; ++u) blks[u] = sel_sh[w + u * WAVES];
@@ -391,7 +399,7 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const 
       if (blk >= max_blocks) {
         nan_sh = 1;
       } else {
-        const int pg = __builtin_amdgcn_readfirstlane(table[(size_t)b * max_blocks + blk]);
+        const int pg = __builtin_amdgcn_readfirstlane(tbl_lds ? tbl_sh[blk] : table[(size_t)b * max_blocks + blk]);
         if (pg < 0 || (int64_t)pg >= kpages || (int64_t)pg >= vpages) {
           nan_sh = 1;
         } else {
@@ -573,10 +581,22 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const 
     l_sh[w][j] = l;
   }
   __syncthreads();   // also: every wave is done with its V^T slice
+  __shared__ float inv_sh[16], lse_sh[16];
   {
     float M = NEG_INF;
 #pragma unroll
     for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][j]);
+    if (w == 0 && Q == 0) {
+      // head j's softmax normaliser and log-sum-exp, once for the whole row
+      float Lt = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < WAVES; ++ww) {
+        const float mw = m_sh[ww][j];
+        if (mw != NEG_INF) Lt += l_sh[ww][j] * exp2f(mw - M);
+      }
+      inv_sh[j] = v_scale / Lt;
+      lse_sh[j] = (M + log2f(Lt)) * 0.69314718055994530942f;
+    }
     const float f = (m == NEG_INF) ? 0.0f : exp2f(m - M);
     float* red = reinterpret_cast<float*>(smem) + ((size_t)w * 16 + j) * kMergeStride;
     if constexpr (KT == 2 && FP8MODE) {
@@ -596,15 +616,6 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const 
   for (int e = threadIdx.x; e < 16 * 64; e += WAVES * 64) {
     // e -> head hh, dims 2*dl, 2*dl+1
     const int hh = e >> 6, dl = e & 63;
-    float M = NEG_INF;
-#pragma unroll
-    for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, m_sh[ww][hh]);
-    float Lt = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < WAVES; ++ww) {
-      const float mw = m_sh[ww][hh];
-      if (mw != NEG_INF) Lt += l_sh[ww][hh] * exp2f(mw - M);
-    }
     const float* red = reinterpret_cast<const float*>(smem) + (size_t)hh * kMergeStride + 2 * dl;
     float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
@@ -613,15 +624,12 @@ __device__ __forceinline__ void attend_row(const AttnArgs& args, int row, const 
       acc.x += v.x;
       acc.y += v.y;
     }
-    const float inv = v_scale / Lt;
+    const float inv = inv_sh[hh];
     float2 o = make_float2(acc.x * inv, acc.y * inv);
     if (bad) o = make_float2(__builtin_nanf(""), __builtin_nanf(""));
     const size_t orow = ((size_t)b * T + t) * kHeads + g * kHeadsPerGroup + hh;
     *reinterpret_cast<float2*>(out + orow * kHeadDim + 2 * dl) = o;
-    if (lse != nullptr && dl == 0) {
-      const float v = (M + log2f(Lt)) * 0.69314718055994530942f;
-      lse[orow] = bad ? __builtin_nanf("") : v;
-    }
+    if (lse != nullptr && dl == 0) lse[orow] = bad ? __builtin_nanf("") : lse_sh[hh];
   }
 }
 

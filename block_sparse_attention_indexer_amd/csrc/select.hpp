@@ -89,15 +89,44 @@ __device__ void radix_cut(const uint64_t (&key)[E], uint32_t need, uint64_t& pre
 // beside a common offset -- 16 more ballots set the low 16 bits of each
 // wave's bound (the same argument over the keys' upper 32 bits); when still
 // more than 64 pass (many equal scores), the radix cut over all keys decides.
-template <int NT, int E>
-__device__ void select_row(const float* S, int own, int32_t* sel_sh) {
+// Optionally a row of the block table is copied into LDS while the selection
+// runs (its loads go out with the score loads; up to TE * NT entries), so the
+// caller reads the selected blocks' pages from LDS after its next barrier.
+struct TablePrefetch {
+  const int32_t* row = nullptr;   // nullptr: no copy
+  int n = 0;
+  int32_t* lds = nullptr;
+};
+
+template <int NT, int E, int TE = 0>
+__device__ void select_row(const float* S, int own, int32_t* sel_sh, TablePrefetch tp = {}) {
   __shared__ int32_t won[kTopK - 1];
   __shared__ uint32_t n_won;
   __shared__ uint32_t tau_sh[NT / 64];
   __shared__ uint64_t cand[64];
   const int tid = threadIdx.x, lane = tid & 63;
+  int32_t tv[TE > 0 ? TE : 1];
+  auto table_loads = [&]() {
+    if constexpr (TE > 0) {
+      if (tp.row != nullptr) {
+#pragma unroll
+        for (int u = 0; u < TE; ++u) tv[u] = tid + u * NT < tp.n ? tp.row[tid + u * NT] : 0;
+      }
+    }
+  };
+  auto table_stores = [&]() {
+    if constexpr (TE > 0) {
+      if (tp.row != nullptr) {
+#pragma unroll
+        for (int u = 0; u < TE; ++u)
+          if (tid + u * NT < tp.n) tp.lds[tid + u * NT] = tv[u];
+      }
+    }
+  };
   if (own + 1 <= kTopK) {
     if (tid < kTopK) sel_sh[tid] = tid <= own ? tid : -1;
+    table_loads();
+    table_stores();
     return;
   }
   // all of the row's loads in flight before the first use (ne is uniform;
@@ -109,6 +138,7 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
     v[e] = 0.0f;
     if (e < ne) v[e] = S[min(tid + e * NT, own - 1)];
   }
+  table_loads();
   uint64_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -188,6 +218,7 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
       for (int k = 0; k < kTopK; ++k) r2 += (__builtin_amdgcn_readlane(id, k) < id) ? 1 : 0;
       if (tid < kTopK) sel_sh[r2] = id;
     }
+    table_stores();
     return;
   }
 
@@ -211,6 +242,7 @@ __device__ void select_row(const float* S, int own, int32_t* sel_sh) {
     for (int k = 0; k < kTopK; ++k) rank += (__builtin_amdgcn_readlane(mine, k) < mine) ? 1 : 0;
     if (tid < kTopK) sel_sh[rank] = mine;
   }
+  table_stores();
 }
 
 }  // namespace msa
