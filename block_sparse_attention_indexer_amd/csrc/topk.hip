@@ -9,14 +9,14 @@
 //
 // Each older block becomes a 64-bit key: order-preserving score bits above
 // the complemented block index, so the keys are distinct and the order above
-// is plain integer order.  The row is read once into registers.  Few rows
-// (decode, below 4,096): one 1,024-thread workgroup per row runs the
-// bound-then-rank selection of the selecting attention (a per-wave bound from
-// ballots over 16-bit key prefixes, then an exact rank of the few keys above
-// it; a radix cut when many keys tie at the bound).  Many rows of up to 2,048
-// blocks: one wave per row (topk_wave_kernel; a bound from the lanes' largest
-// keys, no workgroup barrier).  The 15 winners plus the own block are written
-// ascending.
+// is plain integer order.  The row is read once into registers.  Rows of up
+// to 2,048 blocks take one wave each (topk_wave_kernel; a bound from the
+// lanes' largest keys, no workgroup barrier); longer rows one 1,024-thread
+// workgroup each (topk_row_kernel), running the selecting attention's
+// bound-then-rank selection (a per-wave bound from ballots over 16-bit key
+// prefixes, then an exact rank of the few keys above it; a radix cut when
+// many keys tie at the bound).  The 15 winners plus the own block are
+// written ascending.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
@@ -42,9 +42,8 @@ __global__ __launch_bounds__(NT) void topk_row_kernel(
 }
 
 // Rows of up to 64*E blocks: one wave per row, the row held in registers and
-// the digit search done with wave operations only (no workgroup barrier).
+// its selection done with wave operations only (no workgroup barrier).
 constexpr int kTopkWaveRows = 4;   // rows (waves) per workgroup
-constexpr int kTopkManyRows = 4096;
 
 // Grid: (token, sequence); wave w of the workgroup takes group w.
 template <int E>
@@ -65,13 +64,13 @@ hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t*
   const int64_t rows = (int64_t)p.B * p.T * kGroups;
   const dim3 grid((unsigned)rows), block(kTopkThreads);
   const dim3 wgrid((unsigned)p.T, (unsigned)p.B), wblock(64 * kTopkWaveRows);   // B <= 65535
-  // Many rows: a wave per row keeps every CU busy.  Few rows (decode): a
-  // workgroup per row shortens each row's critical path.
-  const bool many = rows >= kTopkManyRows;
-  if (many && p.max_blocks <= 64 * 16)
+  // Rows of up to 2,048 blocks: a wave per row, at any row count (c3_128k's
+  // 256 rows take as long as in the workgroup form, 2,048 rows of 1,023 blocks
+  // 6.9 against 23 us).  Longer rows: a 1,024-thread workgroup per row.
+  if (p.max_blocks <= 64 * 16)
     hipLaunchKernelGGL(topk_wave_kernel<16>, wgrid, wblock, 0, s, block_scores, sel, p.seq_lens, p.T,
                        p.max_blocks);
-  else if (many && p.max_blocks <= 64 * 32)
+  else if (p.max_blocks <= 64 * 32)
     hipLaunchKernelGGL(topk_wave_kernel<32>, wgrid, wblock, 0, s, block_scores, sel, p.seq_lens, p.T,
                        p.max_blocks);
   else if (p.max_blocks <= kTopkThreads)

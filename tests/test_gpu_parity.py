@@ -853,8 +853,8 @@ def _oracle_sel(scores, L, T):
 
 @pytest.mark.parametrize("T", [1, 64])
 def test_block_topk_crafted_rows(M, T):
-    """msa_block_topk on crafted rows: 256 rows (a workgroup per row) and 4,096 rows
-    (a wave per row: threshold pass, with the crowded rows taking the radix fallback)."""
+    """msa_block_topk on crafted rows of up to 1,000 blocks, 256 and 4,096 rows (a wave
+    per row: the lane-maximum bound, with the crowded rows taking the radix fallback)."""
     _say("block_topk crafted", T)
     rng = np.random.default_rng(4321 + T)
     B, maxb = (64, 1000) if T == 1 else (16, 1000)
