@@ -244,8 +244,7 @@ __device__ __forceinline__ float sum_over_quarters(float v) {   // the same sum 
 // Lane l = 16Q + n returns the maximum of value Q over lanes n, n+16, n+32,
 // n+48: two half swaps pair value 0 (lanes below 32) and value 2 (above)
 // across halves, and values 1 and 3 likewise; one row swap then pairs rows.
-__device__ __forceinline__ float quarter_max4(f4 v, int lane) {
-  (void)lane;
+__device__ __forceinline__ float quarter_max4(f4 v) {
   float a = v[0], b = v[2], c = v[1], d = v[3];
   swap32(a, b);             // a = v0.lo | v2.lo, b = v0.hi | v2.hi
   swap32(c, d);             // c = v1.lo | v3.lo, d = v1.hi | v3.hi
@@ -255,8 +254,8 @@ __device__ __forceinline__ float quarter_max4(f4 v, int lane) {
 }
 // Max over the 64 lanes of 4 values.  Lane l returns the maximum of value
 // g = 2*(l/32) + (l/16)%2.
-__device__ __forceinline__ float wave_max4(f4 v, int lane) {
-  return max16(quarter_max4(v, lane));
+__device__ __forceinline__ float wave_max4(f4 v) {
+  return max16(quarter_max4(v));
 }
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(
         }
       }
     }
-    const float mx = quarter_max4(m, lane);              // query row n of row tile Q
+    const float mx = quarter_max4(m);              // query row n of row tile Q
     {
       // this lane's row keeps the scores of kPfWriteWindow consecutive blocks and
       // writes them back to back: one score per block would touch each 128-byte

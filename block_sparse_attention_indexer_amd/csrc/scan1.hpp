@@ -252,7 +252,7 @@ __device__ __forceinline__ void scan1_blocks(const Scan1Args& a, int b, int w0, 
     }
     if (half == 1) {
       const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
-      const float m = wave_max4(bmax, lane);
+      const float m = wave_max4(bmax);
       if ((lane & 15) == 0) pooled[blk][2 * (lane >> 5) + ((lane >> 4) & 1)] = bad ? QNAN : m * a.sigma;
       if (TOKSC && bad) {
 #pragma unroll
