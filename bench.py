@@ -352,10 +352,11 @@ def prefill_section(wl, dequant, steps=5, warmup=2):
                           "traffic": measured_traffic("c5", role="attention")}}
 
 
-def decode_section(name, dequant, seed, steps=20, warmup=3):
+def decode_section(name, dequant, seed, steps=100, warmup=100, ev_steps=20):
     """Another decode workload through the default step (scan, then the selecting
-    attention): the step from `steps` steps back to back (one event pair around
-    them), the calls from a pass with each call bracketed by HIP events (medians),
+    attention): after `warmup` steps (the clocks settle over the first milliseconds
+    of work), the step from `steps` steps back to back (one event pair around
+    them), the calls from `ev_steps` steps with each call bracketed by HIP events (medians),
     with the step's algorithmic bytes and HBM rate; reported beside the
     uniform-128K headline.  c3: 64 sequences,
     ragged contexts uniform in [64K, 160K] tokens, NVFP4 with 5% outliers; c4: 16
@@ -370,11 +371,11 @@ def decode_section(name, dequant, seed, steps=20, warmup=3):
     for _ in range(warmup):
         wl.step(dequant, path="select")
     step_ms = unbracketed_ms(lambda k: wl.step(dequant, path="select"), steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(steps):
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_steps)]
+    for k in range(ev_steps):
         wl.step(dequant, evs[k], path="select")
     torch.cuda.synchronize()
-    t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(2)] for k in range(steps)])
+    t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(2)] for k in range(ev_steps)])
     b_idx, b_topk, b_attn = algorithmic_bytes(wl, wl.sel.cpu().numpy())
     scan_ms = float(np.median(t[:, 0]))
     total = b_idx + b_topk + b_attn
@@ -384,7 +385,7 @@ def decode_section(name, dequant, seed, steps=20, warmup=3):
         hot = {"step_ms": round(step_ms, 5), "indexer_ms": round(scan_ms, 5),
                "layer_steps_per_s": round(1e3 / step_ms, 2),
                "note": "back to back: the step's bytes stay resident in the Infinity Cache"}
-        cold = cold_timing(wl, dequant, total, steps=steps)
+        cold = cold_timing(wl, dequant, total, steps=ev_steps)
         step_ms, scan_ms = cold["step_ms"], cold["indexer_ms"]
         t = np.array([[cold["indexer_ms"], cold["topk_attention_ms"]]])
     res = {"workload": f"{name}: decode, batch {w.B}, {w.T} query token(s) per sequence, contexts "
@@ -404,20 +405,21 @@ def decode_section(name, dequant, seed, steps=20, warmup=3):
     return res
 
 
-def reading_section(wl, dequant, steps=20, warmup=3):
+def reading_section(wl, dequant, steps=100, warmup=100, ev_steps=20):
     """The default decode step of `wl` in another NVFP4 reading (the FP8-rounded one
-    beside the exact headline): the step back to back (one event pair around the
-    steps), the calls bracketed by HIP events in a second pass (medians)."""
+    beside the exact headline): after `warmup` steps, the step back to back (one
+    event pair around `steps` steps), the calls bracketed by HIP events in a second
+    pass of `ev_steps` steps (medians)."""
     import torch
     for _ in range(warmup):
         wl.step(dequant, path="select")
     step_ms = unbracketed_ms(lambda k: wl.step(dequant, path="select"), steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ev_steps)]
     torch.cuda.synchronize()
-    for k in range(steps):
+    for k in range(ev_steps):
         wl.step(dequant, evs[k], path="select")
     torch.cuda.synchronize()
-    t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(2)] for k in range(steps)])
+    t = np.array([[evs[k][i].elapsed_time(evs[k][i + 1]) for i in range(2)] for k in range(ev_steps)])
     b_idx, b_topk, b_attn = algorithmic_bytes(wl, wl.sel.cpu().numpy())
     scan_ms = float(np.median(t[:, 0]))
     return {"dequant": dequant, "kernels": {"scan": indexer_kernel_name(wl.w, dequant, "select", wl.lay.max_blocks)},
