@@ -854,8 +854,8 @@ def graph_timing(wl, dequant, path, steps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build has no "
-              "multi-GPU path).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library runs on one "
+              "GPU (how the path would shard is a design note, not code).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

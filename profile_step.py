@@ -1,6 +1,6 @@
 """Collect the rocprofv3 figures that bench.py reports, for one workload.
 
-    python profile_step.py [--workload c3_128k] [--only insert|dcp|prefix] [--out gpurun_out/profile]
+    python profile_step.py [--workload c3_128k] [--only insert|dcp|prefix] [--out DIR]
 
 Runs bench.py five times as a child process under rocprofv3 (this process
 never touches the GPU):
@@ -144,7 +144,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="c3_128k")
     ap.add_argument("--only", choices=["insert", "dcp", "prefix"], default=None)
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "profile"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "profile_out"))
     args = ap.parse_args()
     args.out = os.path.abspath(args.out)   # rocprofv3 runs from /tmp
     os.makedirs(args.out, exist_ok=True)
