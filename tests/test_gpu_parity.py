@@ -780,7 +780,7 @@ def test_sparse_attn_decode_prefix_full_size(M):
 @pytest.mark.parametrize("wname,mode", [("tiny_nvfp4", "exact"), ("tiny_nvfp4", "fp8"), ("tiny_fp8", "exact"),
                                         ("tiny_spec", "exact"), ("tiny_edge", "exact"), ("tiny_prefill", "exact"),
                                         ("tiny_prefill_many", "exact"), ("long_rows", "exact"), ("c1", "exact"),
-                                        ("tiny_t3", "exact")])
+                                        ("tiny_t3", "exact"), ("rows_2048", "exact")])
 def test_topk_sparse_attn_equals_the_two_calls(M, wname, mode):
     """msa_topk_sparse_attn writes msa_block_topk's selection and the attention call's
     out / lse for it, bit for bit (decode and prefill forms, fp32 fallback)."""
