@@ -254,13 +254,13 @@ def algorithmic_flops(wl, sel_host):
     return idx, attn
 
 
-def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
+def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256, skip=False):
     """The first kernel of the step (the index scan) that
     libmsa launches for this workload, as rocprofv3 names it: for one token the
-    evenly spread scan unless the selection is fused into it (then, as for
-    speculative decode, the pages-per-wave template argument follows the
-    launcher's rule: the largest of its three sizes whose grid gives every CU
-    one workgroup (one token) or two (speculative decode))."""
+    evenly spread scan unless the selection is fused into it or a shared prefix is
+    skipped (then, as for speculative decode, the pages-per-wave template argument
+    follows the launcher's rule: the largest of its three sizes whose grid gives
+    every CU one workgroup (one token) or two (speculative decode))."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
@@ -274,7 +274,7 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256):
                 return p_
         return big // 4
     b = lambda x: str(x).lower()
-    if w.T == 1 and not fused and w.B <= 1024:
+    if w.T == 1 and not fused and not skip and w.B <= 1024:
         return f"msa::indexer_decode1_flat_kernel<{kt}, {b(fp8mode)}>"
     if w.T == 1:
         return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16, 1)}, {b(fp8mode)}>"
@@ -699,7 +699,7 @@ def prefix_section(wl, dequant, shared_blocks=512, steps=20):
     return {"workload": w.name, "shared_blocks": sb, "groups": len(groups), "attention": attn,
             "kernels": {"shared": f"msa::indexer_prefill_kernel<{2 if w.kv_dtype == 'nvfp4' else 1}, "
                                   f"{str(dequant == 'fp8' and w.kv_dtype == 'nvfp4').lower()}, false, true, C>",
-                        "rest": indexer_kernel_name(w, dequant, max_blocks=maxb)},
+                        "rest": indexer_kernel_name(w, dequant, max_blocks=maxb, skip=True)},
             "unshared_scan_ms": round(t_u, 5), "prefix_scan_ms": round(t_p, 5),
             "speedup": round(t_u / t_p, 3),
             "prefix_algorithmic_bytes": int(b_prefix), "unshared_algorithmic_bytes": int(b_plain),
