@@ -303,6 +303,7 @@ FULL = [("c2", [0, 17, 31], "exact", False), ("c3", [0, 21, 63], "exact", False)
         ("c4", [5], "fp8", False), ("c5", [0], "fp8", False),
         # per-tensor scales other than 1 (K and V on different scales) at full size
         ("c2", [9], "exact", True), ("c3_128k", [33], "exact", True), ("c4", [14], "fp8", True),
+        ("c5", [1], "exact", True),
         # 1 + 7 speculative tokens on the 128K batch (two row tiles in the scan)
         ("c3_t8", [2], "exact", False), ("c3_t8", [50], "fp8", True)]
 
