@@ -239,7 +239,7 @@ def main():
 
     lines = [f"# rocprofv3 summary: {title}", "",
              "Produced by `python profile_step.py --workload " + w + " ".join([""] + only) +
-             "` on one MI355X, which runs:", ""]
+             " --out " + os.path.relpath(args.out, ROOT) + "` on one MI355X, which runs:", ""]
     lines += ["    " + " ".join(c if not c.startswith(ROOT) else os.path.relpath(c, ROOT) for c in v)
               .replace(py, "python3") for v in cmds.values()]
     lines += ["", "(rocprofv3 runs from /tmp with TMPDIR=/tmp; raw output is summarised and deleted.)", "",
