@@ -26,7 +26,11 @@ SOURCES = ["pack.hip", "insert.hip", "indexer.hip", "indexer_prefill.hip", "topk
 # hold no NaN (an unreadable page is marked through the NaN bit pattern, stored as
 # an integer); with NaN semantics every fmaxf of an MFMA result is preceded by a
 # canonicalising max, ~6% of that kernel's time.
-EXTRA = {"indexer_prefill.hip": ["-fno-honor-nans"]}
+# The decode scans read their MFMA results straight from ordinary vector
+# registers: left to itself the compiler puts the speculative scan's
+# accumulators in AGPRs and copies every result out (32 extra VALU per unit).
+EXTRA = {"indexer_prefill.hip": ["-fno-honor-nans"],
+         "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src):

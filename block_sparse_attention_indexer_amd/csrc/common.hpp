@@ -252,6 +252,20 @@ __device__ __forceinline__ float quarter_max4(f4 v) {
   swap16(e, f);             // e = e.r0 f.r0 e.r2 f.r2, f = e.r1 f.r1 e.r3 f.r3
   return fmaxf(e, f);
 }
+// IEEE 754-2019 maximum (a NaN operand gives NaN).  gfx950 folds chains of
+// it into v_maximum3_f32 and needs no quieting of the operands, which fmaxf
+// (maxNum) costs on values the compiler cannot prove canonical, such as MFMA
+// results and cross-lane moves.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// Two values: lane l = 32h + 16q + n returns the maximum of value h over
+// lanes n, n+16, n+32, n+48 (one half swap, then one row swap).
+__device__ __forceinline__ float quarter_max2(float v0, float v1) {
+  float a = v0, b = v1;
+  swap32(a, b);             // a = v0.lo | v1.lo, b = v0.hi | v1.hi
+  float e = vmax(a, b), f = e;
+  swap16(e, f);             // e = rows 0, 0, 2, 2 and f = rows 1, 1, 3, 3 of the half maxima
+  return vmax(e, f);
+}
 // Max over the 64 lanes of 4 values.  Lane l returns the maximum of value
 // g = 2*(l/32) + (l/16)%2.
 __device__ __forceinline__ float wave_max4(f4 v) {

@@ -91,31 +91,41 @@ __device__ __forceinline__ void decode_idx_tile(const IdxUnit<KT, TPU>& u, int k
   }
 }
 
-// Contract one unit: per tile and row tile four 16x16x32 MFMAs and the masked
-// running max.  Lane (Q, j) gets token 4n + Q, groups 0..3 of key `key0 + 16*kt`
-// (key0 includes j) from row tile n.
-template <int KT, bool FP8MODE, bool TOKSC, int TPU, int NT>
+// Contract one unit: per tile and row tile four 16x16x32 MFMAs with the keys
+// as the first operand, so lane (Q, j) gets keys 4Q .. 4Q+3 of the tile
+// (`kq` = this lane's first key of the unit) for query row j of row tile n,
+// and folds them into its running maximum bmax[n].  MASK: keys past a row's
+// token position count as -inf (only the units that reach the last T keys
+// of the sequence need it; the caller picks the instance per unit).
+template <int KT, bool FP8MODE, bool TOKSC, int TPU, int NT, bool MASK>
 __device__ __forceinline__ void contract_idx_unit(const IdxUnit<KT, TPU>& u, const h8 (&A)[NT][4],
-                                                  const uint32_t* lut, int key0, const int (&p_tok)[NT],
-                                                  const bool (&tok_ok)[NT], float sigma, float (&bmax)[NT][4],
-                                                  float* const (&tsc_row)[NT], size_t tsc_stride) {
+                                                  const uint32_t* lut, int kq, const int (&p_tok)[NT],
+                                                  const bool (&tok_ok)[NT], float sigma, float (&bmax)[NT],
+                                                  float* const (&tsc_row)[NT]) {
   const float NEG_INF = -__builtin_inff();
 #pragma unroll
   for (int kt = 0; kt < TPU; ++kt) {
     h8 Bc[4];
     decode_idx_tile<KT, FP8MODE, TPU>(u, kt, lut, Bc);
-    const int key = key0 + 16 * kt;
+    const int key = kq + 16 * kt;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(A[n][c], Bc[c], acc);
-      const bool vis = tok_ok[n] && key <= p_tok[n];
+      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(Bc[c], A[n][c], acc);
+      bool vis[4] = {true, true, true, true};
+      if constexpr (MASK) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bmax[n][r] = fmaxf(bmax[n][r], vis ? acc[r] : NEG_INF);
-        if constexpr (TOKSC) {
-          if (tok_ok[n]) tsc_row[n][r * tsc_stride + key] = vis ? acc[r] * sigma : NEG_INF;
+        for (int r = 0; r < 4; ++r) {
+          vis[r] = key + r <= p_tok[n];
+          acc[r] = vis[r] ? acc[r] : NEG_INF;
+        }
+      }
+      bmax[n] = vmax(vmax(vmax(vmax(bmax[n], acc[0]), acc[1]), acc[2]), acc[3]);
+      if constexpr (TOKSC) {
+        if (tok_ok[n]) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tsc_row[n][key + r] = vis[r] ? acc[r] * sigma : NEG_INF;
         }
       }
     }
@@ -131,6 +141,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     const int32_t* __restrict__ skip) {
   constexpr int UPP = 8 / TPU;             // units per page
   static_assert(PPW >= 1 && PPW <= 64, "page ids are held one per lane");
+  static_assert(NT == 1 || NT == 2, "one or two row tiles");
   __shared__ uint32_t lut[FP8MODE ? 512 : 2];
   // pooled scores of each wave's blocks, [block][token*4 + group], written out at the end
   __shared__ float pooled[kDecWaves][PPW][16 * NT];
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
     __syncthreads();
   }
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, held in a scalar register
   const int Q = lane >> 4, j = lane & 15;
   const float NEG_INF = -__builtin_inff();
   const float QNAN = __builtin_nanf("");
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   const int pid_bad = (pid < 0 || (int64_t)pid >= num_pages) ? 1 : 0;
   const int pid_safe = pid_bad ? 0 : pid;
 
-  // A operands: row j of tile n = token 4n + j/4, group j%4; k-chunk c = dims 32Q+8c .. +7
+  // query operand: row j of tile n = token 4n + j/4, group j%4; k-chunk c = dims 32Q+8c .. +7
   h8 A[NT][4];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -182,27 +194,33 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
       for (int c = 0; c < 4; ++c) A[n][c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+  // this lane's query row of each tile: its token's position and token-score row
   bool tok_ok[NT];
   int p_tok[NT];
   const size_t tstride = (size_t)max_blocks * kBlock;
   float* tsc_row[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    tok_ok[n] = 4 * n + Q < T;
-    p_tok[n] = L - T + 4 * n + Q;
-    tsc_row[n] = TOKSC ? token_scores + (((size_t)b * T + (tok_ok[n] ? 4 * n + Q : 0)) * kGroups) * tstride : nullptr;
+    const int t = 4 * n + (j >> 2);
+    tok_ok[n] = t < T;
+    p_tok[n] = L - T + t;
+    tsc_row[n] = TOKSC ? token_scores + (((size_t)b * T + (tok_ok[n] ? t : 0)) * kGroups + (j & 3)) * tstride
+                       : nullptr;
   }
-
-  // blocks of this wave past the sequence: -inf
-  if (TOKSC) {
+  // fill the token scores of block i with v: lane (Q, j) writes keys 4Q + 16m .. +3 of its rows
+  auto fill_token_scores = [&](int i, float v) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if (!tok_ok[n]) continue;
-      for (int i = w0 + nreal; i < wend; ++i)
+      for (int kk = 4 * Q; kk < kBlock; kk += 16)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          for (int kk = j; kk < kBlock; kk += 16) tsc_row[n][r * tstride + (size_t)gblk(i) * kBlock + kk] = NEG_INF;
+        for (int r = 0; r < 4; ++r) tsc_row[n][(size_t)i * kBlock + kk + r] = v;
     }
+  };
+
+  // blocks of this wave past the sequence: -inf
+  if (TOKSC) {
+    for (int i = w0 + nreal; i < wend; ++i) fill_token_scores(gblk(i), NEG_INF);
   }
   for (int e = lane; e < 16 * NT * (wend - w0 - nreal); e += 64) {
     const int n = wend - w0 - nreal;
@@ -211,45 +229,44 @@ __global__ __launch_bounds__(kDecWaves * 64) void indexer_decode_kernel(
   }
 
   const int nunits = nreal * UPP;
-  float bmax[NT][4];
+  float bmax[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int n = 0; n < NT; ++n) bmax[n] = NEG_INF;
+  // units alternate between two register buffers (UPP is even, so a unit's
+  // buffer is fixed by its part); with PIPE the next unit's loads are in
+  // flight while the current one is contracted
+  static_assert(UPP % 2 == 0, "units of a page alternate between two buffers");
+  IdxUnit<KT, TPU> buf[2];
+  auto load_unit = [&](IdxUnit<KT, TPU>& dst, int un) {
+    const size_t row = (size_t)__builtin_amdgcn_readlane(pid_safe, un / UPP) * kBlock + (un % UPP) * (16 * TPU) + j;
+    load_idx_unit<KT, TPU>(dst, kdata, kscales, row, Q);
+  };
+  if (PIPE && nunits > 0) load_unit(buf[0], 0);
+  // units wholly at or below the first token's position need no mask
+  const int vis_end = L - T;
+  for (int blk = 0; blk < nreal; ++blk) {
+    const int kblk = gblk(w0 + blk) * kBlock;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bmax[n][r] = NEG_INF;
-  IdxUnit<KT, TPU> buf0, buf1;
-  if (PIPE && nunits > 0)
-    load_idx_unit<KT, TPU>(buf0, kdata, kscales, (size_t)__builtin_amdgcn_readlane(pid_safe, 0) * kBlock + j, Q);
-  for (int uu = 0; uu < nunits; ++uu) {
-    const int blk = uu / UPP, part = uu % UPP;
-    if (PIPE) {
-      const int un = min(uu + 1, nunits - 1);
-      const size_t row_n = (size_t)__builtin_amdgcn_readlane(pid_safe, un / UPP) * kBlock + (un % UPP) * (16 * TPU) + j;
-      load_idx_unit<KT, TPU>(buf1, kdata, kscales, row_n, Q);
-    } else {
-      const size_t row0 = (size_t)__builtin_amdgcn_readlane(pid_safe, blk) * kBlock + part * (16 * TPU) + j;
-      load_idx_unit<KT, TPU>(buf0, kdata, kscales, row0, Q);
+    for (int part = 0; part < UPP; ++part) {
+      const int uu = blk * UPP + part;
+      IdxUnit<KT, TPU>& cur = buf[part & 1];
+      if (PIPE) load_unit(buf[(part + 1) & 1], min(uu + 1, nunits - 1));
+      else load_unit(cur, uu);
+      const int ku = kblk + part * (16 * TPU);
+      if (ku + 16 * TPU - 1 <= vis_end)
+        contract_idx_unit<KT, FP8MODE, TOKSC, TPU, NT, false>(cur, A, lut, ku + 4 * Q, p_tok, tok_ok, sigma, bmax,
+                                                              tsc_row);
+      else
+        contract_idx_unit<KT, FP8MODE, TOKSC, TPU, NT, true>(cur, A, lut, ku + 4 * Q, p_tok, tok_ok, sigma, bmax,
+                                                             tsc_row);
     }
-    contract_idx_unit<KT, FP8MODE, TOKSC, TPU, NT>(buf0, A, lut, gblk(w0 + blk) * kBlock + part * (16 * TPU) + j,
-                                                   p_tok, tok_ok, sigma, bmax, tsc_row, tstride);
-    if (PIPE) buf0 = buf1;
-    if (part == UPP - 1) {
-      const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
+    // block maxima: lane 32h + 16q + j holds tile h's row j (NT = 2) or tile 0's row j (NT = 1)
+    const bool bad = __builtin_amdgcn_readlane(pid_bad, blk) != 0;
+    const float m = quarter_max2(bmax[0], bmax[NT - 1]);
+    if ((Q & 1) == 0 && (NT == 2 || Q == 0)) pooled[wave][blk][16 * (Q >> 1) + j] = bad ? QNAN : m * sigma;
+    if (TOKSC && bad) fill_token_scores(gblk(w0 + blk), QNAN);
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float m = max16(bmax[n][r]);
-          if (j == 0) pooled[wave][blk][16 * n + 4 * Q + r] = bad ? QNAN : m * sigma;
-          bmax[n][r] = NEG_INF;
-        }
-        if (TOKSC && bad && tok_ok[n]) {
-          const int i = gblk(w0 + blk);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            for (int kk = j; kk < kBlock; kk += 16) tsc_row[n][r * tstride + (size_t)i * kBlock + kk] = QNAN;
-        }
-      }
-    }
+    for (int n = 0; n < NT; ++n) bmax[n] = NEG_INF;
   }
   lds_wait();
   // write the pooled scores: entry e -> row (token, group) e / nreal, block w0 + e % nreal
