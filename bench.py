@@ -257,10 +257,10 @@ def algorithmic_flops(wl, sel_host):
 def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256, skip=False):
     """The first kernel of the step (the index scan) that
     libmsa launches for this workload, as rocprofv3 names it: for one token the
-    evenly spread scan unless the selection is fused into it or a shared prefix is
-    skipped (then, as for speculative decode, the pages-per-wave template argument
-    follows the launcher's rule: the largest of its three sizes whose grid gives
-    every CU one workgroup (one token) or two (speculative decode))."""
+    evenly spread scan (its SKIP form when a shared prefix is skipped) unless the
+    selection is fused into it (then, as for speculative decode, the pages-per-wave
+    template argument follows the launcher's rule: the largest of its three sizes
+    whose grid gives every CU one workgroup (one token) or two (speculative decode))."""
     kt = {"fp8": 1, "nvfp4": 2}.get(w.kv_dtype)
     if kt is None:
         return "msa::indexer_f32_kernel"
@@ -274,8 +274,8 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256, skip
                 return p_
         return big // 4
     b = lambda x: str(x).lower()
-    if w.T == 1 and not fused and not skip and w.B <= 1024:
-        return f"msa::indexer_decode1_flat_kernel<{kt}, {b(fp8mode)}>"
+    if w.T == 1 and not fused and w.B <= 1024:
+        return f"msa::indexer_decode1_flat_kernel<{kt}, {b(fp8mode)}{', true' if skip else ''}>"
     if w.T == 1:
         return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16, 1)}, {b(fp8mode)}>"
     if w.T <= 8:

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "../../include/msa.h"
 #include "launch.hpp"
 
@@ -55,6 +56,7 @@ ProblemArgs to_args(const msa_problem* p) {
   return ProblemArgs{p->batch, p->tokens, p->max_blocks, p->seq_lens, p->block_table};
 }
 msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
 
 // Prefix groups from the host arrays of a shared-prefix call: 0..64 groups of
 // 1..64 consecutive sequences, group_start strictly increasing within [0, batch],
@@ -247,12 +249,10 @@ msa_status msa_indexer_scores_prefix(const msa_problem* prob, int32_t num_groups
   const msa::CacheArgs ka = to_args(idx_k);
   const bool fp8 = dequant == MSA_DQ_FP8;
   int32_t* skip = static_cast<int32_t*>(workspace);
-  hipError_t e = msa::launch_fill_skip(g, prob->batch, skip, stream);
+  hipError_t e =
+      msa::launch_indexer_shared(pa, idx_q, ka, fp8, q_scale * idx_k->tensor_scale, g, block_scores, stream);
   if (e == hipSuccess)
-    e = msa::launch_indexer_shared(pa, idx_q, ka, fp8, q_scale * idx_k->tensor_scale, g, block_scores, stream);
-  if (e == hipSuccess)
-    e = msa::launch_indexer(pa, idx_q, (int)q_dtype, q_scale, ka, fp8, block_scores, nullptr, stream, nullptr,
-                            nullptr, 0, 1, skip);
+    e = msa::launch_indexer_skipping(pa, idx_q, (int)q_dtype, q_scale, ka, fp8, block_scores, g, skip, stream);
   return hip_status(e);
 }
 

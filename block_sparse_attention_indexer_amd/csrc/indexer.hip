@@ -296,13 +296,17 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_kernel(Scan
 }
 
 // The one-token scan spread evenly over a fixed grid (scan1_flat): for
-// ragged contexts, with no selection, shard or skip and no per-key scores.
-template <int KT, bool FP8MODE>
-__global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_flat_kernel(Scan1Args a, int B) {
+// ragged contexts, with no selection or shard and no per-key scores.  SKIP:
+// each sequence of a prefix group g starts after the group's shared blocks
+// (the rest of the shared-prefix call).
+template <int KT, bool FP8MODE, bool SKIP = false>
+__global__ __launch_bounds__(kDecWaves * 64, 2) void indexer_decode1_flat_kernel(Scan1Args a, int B,
+                                                                                 PrefixGroups g) {
   __shared__ __align__(8) uint32_t lut[FP8MODE ? 512 : 2];
   __shared__ int pre[kFlatMaxSeqs + 1];
+  __shared__ int padpre[SKIP ? kFlatMaxSeqs + 1 : 1];
   if constexpr (FP8MODE) build_fp8_lut(lut);   // the prefix pass below synchronises
-  scan1_flat<KT, FP8MODE>(a, B, lut, pre);
+  scan1_flat<KT, FP8MODE, SKIP>(a, B, lut, pre, padpre, g);
 }
 
 // fp32 index keys and queries: one workgroup per (block, sequence), one
@@ -366,6 +370,46 @@ hipError_t launch_fill_skip(const PrefixGroups& g, int B, int32_t* skip, hipStre
   return hipGetLastError();
 }
 
+// The one-token scan over a fixed grid, each wave a contiguous share of all
+// sequences' blocks: two workgroups per CU (the scan's residency), or one when
+// even B x max_blocks would give a wave fewer than 16 blocks -- long-lived
+// waves win there (32 x 256 blocks: 35.0 us against 39.5 us).  groups
+// non-null: the SKIP form, each group's shared blocks left out.
+static void launch_flat(const Scan1Args& sa, int B, int kdtype, bool fp8mode, const PrefixGroups* groups,
+                        hipStream_t s) {
+  const int cus = current_cu_count();
+  const int64_t bound = (int64_t)B * sa.max_blocks;
+  const int per_cu = bound >= (int64_t)kDec1FlatWgPerCu * cus * kDecWaves * 16 ? kDec1FlatWgPerCu : 1;
+  const dim3 grid((unsigned)(per_cu * cus)), block(kDecWaves * 64);
+  const PrefixGroups g = groups != nullptr ? *groups : PrefixGroups{};
+#define MSA_FLAT(KT, FM)                                                                      \
+  do {                                                                                        \
+    if (groups != nullptr)                                                                    \
+      hipLaunchKernelGGL((indexer_decode1_flat_kernel<KT, FM, true>), grid, block, 0, s, sa, B, g); \
+    else hipLaunchKernelGGL((indexer_decode1_flat_kernel<KT, FM>), grid, block, 0, s, sa, B, g);  \
+  } while (0)
+  if (kdtype == 1) MSA_FLAT(1, false);
+  else if (fp8mode) MSA_FLAT(2, true);
+  else MSA_FLAT(2, false);
+#undef MSA_FLAT
+}
+
+hipError_t launch_indexer_skipping(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
+                                   const CacheArgs& k, bool fp8mode, float* block_scores, const PrefixGroups& g,
+                                   int32_t* skip_ws, hipStream_t s) {
+  if (k.dtype == 0) return hipErrorInvalidValue;
+  if (p.T == 1 && p.B <= kFlatMaxSeqs) {
+    const Scan1Args sa{(const uint8_t*)idx_q, k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks,
+                       q_scale * k.tensor_scale, block_scores, nullptr};
+    launch_flat(sa, p.B, k.dtype, fp8mode, &g, s);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_fill_skip(g, p.B, skip_ws, s);
+  if (e != hipSuccess) return e;
+  return launch_indexer(p, idx_q, q_dtype, q_scale, k, fp8mode, block_scores, nullptr, s, nullptr, nullptr, 0, 1,
+                        skip_ws);
+}
+
 bool indexer_can_fuse_topk(const ProblemArgs& p, const CacheArgs& k, bool fp8mode) {
   return p.T == 1 && k.dtype != 0 && !(k.dtype == 2 && fp8mode);
 }
@@ -399,19 +443,9 @@ hipError_t launch_indexer(const ProblemArgs& p, const void* idx_q, int q_dtype, 
   const bool flat = p.T == 1 && sel == nullptr && token_scores == nullptr && num_shards == 1 && skip == nullptr &&
                     p.B <= kFlatMaxSeqs;
   if (flat) {
-    // one-token scan over a fixed grid, each wave a contiguous share of all
-    // sequences' blocks: two workgroups per CU (the scan's residency), or one
-    // when even B x max_blocks would give a wave fewer than 16 blocks --
-    // long-lived waves win there (32 x 256 blocks: 35.0 us against 39.5 us)
     const Scan1Args sa{q8, k.data, k.scales, k.num_pages, p.seq_lens, p.block_table, p.max_blocks, sigma,
                        block_scores, nullptr};
-    const int cus = current_cu_count();
-    const int64_t bound = (int64_t)p.B * p.max_blocks;
-    const int per_cu = bound >= (int64_t)kDec1FlatWgPerCu * cus * kDecWaves * 16 ? kDec1FlatWgPerCu : 1;
-    const dim3 grid((unsigned)(per_cu * cus));
-    if (k.dtype == 1) hipLaunchKernelGGL((indexer_decode1_flat_kernel<1, false>), grid, dim3(kDecWaves * 64), 0, s, sa, p.B);
-    else if (fp8mode) hipLaunchKernelGGL((indexer_decode1_flat_kernel<2, true>), grid, dim3(kDecWaves * 64), 0, s, sa, p.B);
-    else hipLaunchKernelGGL((indexer_decode1_flat_kernel<2, false>), grid, dim3(kDecWaves * 64), 0, s, sa, p.B);
+    launch_flat(sa, p.B, k.dtype, fp8mode, nullptr, s);
   } else if (p.T == 1 && !(fp8mode && k.dtype == 2 && sel != nullptr)) {
     // one token: 4x4x4 MFMA scan; the FP8-rounded NVFP4 reading decodes through the
     // LDS table instead of scaling partial dots (not fused with the selection)

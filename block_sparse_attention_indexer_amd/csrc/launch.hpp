@@ -82,6 +82,13 @@ hipError_t launch_indexer_prefill(const ProblemArgs& p, const void* idx_q, const
 hipError_t launch_indexer_shared(const ProblemArgs& p, const void* idx_q, const CacheArgs& k, bool fp8mode,
                                  float sigma, const PrefixGroups& g, float* block_scores, hipStream_t s);
 hipError_t launch_fill_skip(const PrefixGroups& g, int B, int32_t* skip, hipStream_t s);
+// The decode scan of every block that no prefix group shares (the rest of the
+// shared-prefix call): the evenly spread one-token scan reads the groups itself;
+// the other scans take per-sequence skip counts, written into skip_ws (device
+// [B] int32) first.
+hipError_t launch_indexer_skipping(const ProblemArgs& p, const void* idx_q, int q_dtype, float q_scale,
+                                   const CacheArgs& k, bool fp8mode, float* block_scores, const PrefixGroups& g,
+                                   int32_t* skip_ws, hipStream_t s);
 
 hipError_t launch_topk(const ProblemArgs& p, const float* block_scores, int32_t* sel,
                        hipStream_t s);

@@ -6,6 +6,7 @@
 // index-key head, and the scores are max-pooled into one score per block.
 #pragma once
 #include "common.hpp"
+#include "launch.hpp"
 #include "topk_wave.hpp"
 
 namespace msa {
@@ -316,19 +317,22 @@ __device__ __forceinline__ void scan1_chunk(const Scan1Args& a, int b, int chunk
 // at sequence boundaries or after 64 blocks.  With ragged contexts every CU
 // then reads the same number of pages, where per-sequence chunks leave some
 // CUs a chunk more than others.  The blocks past each sequence (up to
-// max_blocks) are spread the same way and get -inf.  pre: LDS, B + 1 ints,
-// filled here with the exclusive prefix sums of the sequences' block counts.
+// max_blocks) are spread the same way and get -inf.  SKIP: the blocks of a
+// sequence of prefix group q start at groups.blocks[q] (those below belong to
+// another kernel), and its -inf run at the larger of that and its block count.  pre, padpre: LDS, B + 1 ints
+// each, filled here with the exclusive prefix sums of the sequences' scanned
+// and -inf block counts (padpre only with SKIP; without it the -inf counts
+// follow from pre).
 constexpr int kFlatMaxSeqs = 1024;   // sequences the prefix sums in LDS cover
-template <int KT, bool FP8MODE>
-__device__ __forceinline__ void scan1_flat(const Scan1Args& a, int B, const uint32_t* lut, int* pre) {
+template <int KT, bool FP8MODE, bool SKIP>
+__device__ __forceinline__ void scan1_flat(const Scan1Args& a, int B, const uint32_t* lut, int* pre, int* padpre,
+                                           const PrefixGroups& groups) {
   __shared__ float pooled[kDecWaves][64][kGroups];
   __shared__ int wsum[kDecWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int carry = 0;
-  for (int base = 0; base < B; base += kDecWaves * 64) {
-    const int i = base + tid;
-    int v = 0;
-    if (i < B) v = min((a.seq_lens[i] + kBlock - 1) / kBlock, a.max_blocks);
+  // exclusive prefix sums of v over the threads of the workgroup: returns
+  // (sum over the threads before this one, sum over all of them)
+  auto block_scan = [&](int v, int& total) {
     int x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -337,19 +341,51 @@ __device__ __forceinline__ void scan1_flat(const Scan1Args& a, int B, const uint
     }
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
-    int before = 0, total = 0;
+    int before = 0;
+    total = 0;
 #pragma unroll
     for (int w2 = 0; w2 < kDecWaves; ++w2) {
       before += w2 < wave ? wsum[w2] : 0;
       total += wsum[w2];
     }
-    if (i < B) pre[i] = carry + before + x - v;
+    __syncthreads();   // wsum is rewritten by the next scan
+    return before + x - v;
+  };
+  int carry = 0, pcarry = 0;
+  for (int base = 0; base < B; base += kDecWaves * 64) {
+    const int i = base + tid;
+    int v = 0, pv = 0;
+    if (i < B) {
+      const int nbi = min((a.seq_lens[i] + kBlock - 1) / kBlock, a.max_blocks);
+      int sk = 0;   // the shared blocks of i's prefix group (a uniform loop over the groups)
+      if constexpr (SKIP) {
+        for (int q = 0; q < groups.n; ++q)
+          if (i >= groups.start[q] && i < groups.start[q + 1]) sk = groups.blocks[q];
+      }
+      v = max(0, nbi - sk);
+      pv = a.max_blocks - max(nbi, sk);
+    }
+    int total;
+    const int ex = block_scan(v, total);
+    if (i < B) pre[i] = carry + ex;
     carry += total;
-    __syncthreads();   // wsum is rewritten by the next pass
+    if constexpr (SKIP) {
+      const int pex = block_scan(pv, total);
+      if (i < B) padpre[i] = pcarry + pex;
+      pcarry += total;
+    }
   }
-  if (tid == 0) pre[B] = carry;
+  if (tid == 0) {
+    pre[B] = carry;
+    if constexpr (SKIP) padpre[B] = pcarry;
+  }
   __syncthreads();
-  const int64_t N = carry;                                   // blocks with keys, all sequences
+  // padpre[b]: -inf blocks of the sequences before b (b * max_blocks - pre[b] without SKIP)
+  auto pad_before = [&](int bb) -> int64_t {
+    if constexpr (SKIP) return padpre[bb];
+    else return (int64_t)bb * a.max_blocks - pre[bb];
+  };
+  const int64_t N = carry;                                   // blocks to scan, all sequences
   const int64_t W = (int64_t)gridDim.x * kDecWaves;
   const int64_t gw = (int64_t)blockIdx.x * kDecWaves + wave;
   int s = (int)(N * gw / W);
@@ -363,24 +399,27 @@ __device__ __forceinline__ void scan1_flat(const Scan1Args& a, int B, const uint
   int b = lo;
   while (s < s1) {
     while (pre[b + 1] <= s) ++b;                             // sequences with no block
-    const int j = s - pre[b];
+    // first block of b's range: its skip count, which is max_blocks less its
+    // -inf and scanned block counts
+    const int j = s - pre[b] +
+                  (SKIP ? a.max_blocks - (padpre[b + 1] - padpre[b]) - (pre[b + 1] - pre[b]) : 0);
     const int n = min(min(s1, pre[b + 1]) - s, 64);
     scan1_blocks<KT, false, false, 64, FP8MODE>(a, b, j, j + n, lut, pooled[wave]);
     s += n;
   }
-  // -inf past each sequence: pad entry p of sequence b is block nb_b + (p - padpre[b]),
-  // padpre[b] = b * max_blocks - pre[b]
-  const int64_t P = (int64_t)B * a.max_blocks - N;
+  // -inf past each sequence: pad entry p of sequence b is block
+  // max_blocks - (its -inf count) + (p - pad_before(b))
+  const int64_t P = pad_before(B);
   const int64_t p0 = P * gw / W, p1 = P * (gw + 1) / W;
   const float NEG_INF = -__builtin_inff();
   for (int64_t pp = p0 + lane; pp < p1; pp += 64) {
-    int l2 = 0, h2 = B;   // the last b with padpre[b] <= pp
+    int l2 = 0, h2 = B;   // the last b with pad_before(b) <= pp
     while (h2 - l2 > 1) {
       const int mid = (l2 + h2) >> 1;
-      if ((int64_t)mid * a.max_blocks - pre[mid] <= pp) l2 = mid; else h2 = mid;
+      if (pad_before(mid) <= pp) l2 = mid; else h2 = mid;
     }
-    const int nbb = pre[l2 + 1] - pre[l2];
-    const int blk = nbb + (int)(pp - ((int64_t)l2 * a.max_blocks - pre[l2]));
+    const int64_t pb = pad_before(l2);
+    const int blk = a.max_blocks - (int)(pad_before(l2 + 1) - pb) + (int)(pp - pb);
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) a.block_scores[((size_t)l2 * kGroups + g) * a.max_blocks + blk] = NEG_INF;
   }
