@@ -98,6 +98,8 @@ WORKLOADS = {
     # a row of exactly 2,048 blocks: the largest whose block-table row the selecting
     # attention copies into LDS during its selection
     "rows_2048": Workload("rows_2048", 1, 1, 262144, "nvfp4", "fp8", 4, [], 0.05),
+    # more sequences (1,100) than the evenly spread one-token scan takes, short ragged contexts
+    "wide_batch": Workload("wide_batch", 1030, 1, (1, 300), "nvfp4", "fp8", 2, [], 0.05),
     # enough query rows (2 x 1,100 x 4) for the many-row attention form
     "tiny_prefill_many": Workload("tiny_prefill_many", 2, 1100, (2300, 3600), "nvfp4", "fp8", 8, [], 0.0, True, True),
 }

@@ -65,9 +65,10 @@ def case_scales(w, scaled):
 
 class HostCase:
     """All inputs drawn on the CPU and packed by the oracle.  scaled=True packs the
-    queries and the three caches with the per-tensor scales of SCALED."""
+    queries and the three caches with the per-tensor scales of SCALED; names: the
+    caches to draw (the index keys alone for a scan-only case)."""
 
-    def __init__(self, wname, seed=0, scaled=False):
+    def __init__(self, wname, seed=0, scaled=False, names=("idx_k", "k", "v")):
         w = synth.WORKLOADS[wname]
         self.w, self.seed = w, seed
         self.lay = lay = synth.make_layout(w, seed)
@@ -78,7 +79,7 @@ class HostCase:
         self.S = sc["k"]
         self.idx_q_scale, self.q_scale = sc["idx_q"], sc["q"]
         self.caches = {}
-        for name in ("idx_k", "k", "v"):
+        for name in names:
             x = synth.cache_pages(w, lay, seed, name, 0, P, qhat, hot).numpy()
             self.caches[name] = oracle_pack(x, w.kv_dtype, sc[name])
         self.idx_q = oracle_query(idx_q.numpy(), w.q_dtype, sc["idx_q"])
@@ -216,7 +217,7 @@ def to_host(res):
 def oracle_scores(caches, idx_q, seq_lens, table, T, mode, q_dtype, sequences=None, idx_q_scale=1.0):
     """Oracle block scores, selection and near-tie flags (no attention)."""
     dummy_q = np.zeros((len(seq_lens), T, 64, 128), np.float32)
-    return OM.batch_layer(idx_q, dummy_q, caches["idx_k"], caches["k"], caches["v"], seq_lens, table, T,
+    return OM.batch_layer(idx_q, dummy_q, caches["idx_k"], caches.get("k"), caches.get("v"), seq_lens, table, T,
                           SOFTMAX_SCALE, mode=mode, idx_q_dtype=q_dtype, idx_q_scale=idx_q_scale, q_dtype=q_dtype,
                           sequences=sequences, with_attention=False)
 

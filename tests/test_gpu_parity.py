@@ -684,6 +684,33 @@ def test_indexer_prefix_full_size(M, wname, groups, samples):
         H.compare_scores(got[b:b + 1], ora["block_scores"])
 
 
+@pytest.mark.parametrize("mode", ["exact", "fp8"])
+def test_wide_batch_scan_and_prefix(M, mode):
+    """1,030 one-token sequences, more than the evenly spread scan takes: the
+    per-sequence scan and selection against the oracle, then the shared-prefix call
+    (there the per-sequence scan with skip counts from the workspace) on a sharing
+    table, against the plain call and the oracle."""
+    _say("wide batch", mode)
+    case = H.HostCase("wide_batch", names=("idx_k",)).upload()
+    w, lay = case.w, case.lay
+    res = H.to_host(H.run_path(case, mode, attention=False))
+    ora = H.oracle_scores(case.caches, case.idx_q, lay.seq_lens.numpy(), lay.block_table.numpy(), w.T, mode,
+                          w.q_dtype)
+    H.compare_scores(res["block_scores"], ora["block_scores"])
+    H.compare_selection(res["sel"], ora["sel"], ora["block_scores"], ora["near_tie"], lay.seq_lens.numpy(), w.T)
+    # consecutive groups of up to 64 sequences over the whole batch, sharing 0 .. 3 blocks
+    lens = lay.seq_lens.numpy()
+    groups = [(s0, min(s0 + 64, w.B), min(k % 4, (int(lens[s0:s0 + 64].max()) + 127) // 128))
+              for k, s0 in enumerate(range(0, w.B, 64))]
+    _share_prefixes(case, groups)
+    ref = H.to_host(H.run_path(case, mode, attention=False))
+    got = _prefix_run(M, case, groups, mode)
+    _check_prefix(got, ref["block_scores"], groups, w.B)
+    ora = H.oracle_scores(case.caches, case.idx_q, lay.seq_lens.numpy(), lay.block_table.numpy(), w.T, mode,
+                          w.q_dtype)
+    H.compare_scores(got, ora["block_scores"])
+
+
 # ------------------------------------------------------------------ shared-prefix decode attention
 
 def _force_prefix_blocks(sel, seq_lens, T, groups, per_row=8, seed=0):
