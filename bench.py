@@ -275,7 +275,7 @@ def indexer_kernel_name(w, dequant, path="calls", max_blocks=None, cus=256, skip
         return big // 4
     b = lambda x: str(x).lower()
     if w.T == 1 and not fused and w.B <= 1024:
-        return f"msa::indexer_decode1_flat_kernel<{kt}, {b(fp8mode)}{', true' if skip else ''}>"
+        return f"msa::indexer_decode1_flat_kernel<{kt}, {b(fp8mode)}, {b(skip)}>"
     if w.T == 1:
         return f"msa::indexer_decode1_kernel<{kt}, false, {b(fused)}, {ppw(16, 1)}, {b(fp8mode)}>"
     if w.T <= 8:
