@@ -98,7 +98,12 @@ WORKLOADS = {
     # a row of exactly 2,048 blocks: the largest whose block-table row the selecting
     # attention copies into LDS during its selection
     "rows_2048": Workload("rows_2048", 1, 1, 262144, "nvfp4", "fp8", 4, [], 0.05),
-    # more sequences (1,100) than the evenly spread one-token scan takes, short ragged contexts
+    # speculative decode with the first token's position L - T at and around the scan's
+    # 64-key unit edges (62, 63, 64, 127, 128, 129, 255, 1023): the units that need
+    # the visibility masks start exactly there
+    "spec_edges": Workload("spec_edges", 8, 4, [66, 67, 68, 131, 132, 133, 259, 1027], "nvfp4", "fp8", 0, [], 0.05),
+    "spec_edges8": Workload("spec_edges8", 8, 8, [70, 71, 72, 135, 136, 137, 263, 1031], "fp8", "fp8", 0, [], 0.05),
+    # more sequences (1,030) than the evenly spread one-token scan takes, short ragged contexts
     "wide_batch": Workload("wide_batch", 1030, 1, (1, 300), "nvfp4", "fp8", 2, [], 0.05),
     # enough query rows (2 x 1,100 x 4) for the many-row attention form
     "tiny_prefill_many": Workload("tiny_prefill_many", 2, 1100, (2300, 3600), "nvfp4", "fp8", 8, [], 0.0, True, True),

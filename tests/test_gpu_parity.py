@@ -149,7 +149,9 @@ SMALL = [("c1", "exact"), ("tiny_f32", "exact"), ("tiny_fp8", "exact"), ("tiny_n
          ("tiny_prefill_many", "exact"), ("tiny_t2", "exact"), ("tiny_t2", "fp8"), ("tiny_t3", "exact"),
          ("tiny_edge", "exact"), ("tiny_prefill_nocache", "exact"), ("long_rows", "exact"),
          # 7 speculative tokens (T = 8) and T = 6: the two-row-tile speculative scan and the decode attention
-         ("tiny_spec8", "exact"), ("tiny_spec8", "fp8"), ("tiny_t6", "exact")]
+         ("tiny_spec8", "exact"), ("tiny_spec8", "fp8"), ("tiny_t6", "exact"),
+         # first token's position at the speculative scan's unit edges (T = 4 NVFP4, T = 8 FP8)
+         ("spec_edges", "exact"), ("spec_edges", "fp8"), ("spec_edges8", "exact")]
 SMALL = [(w, m, False) for w, m in SMALL]
 # per-tensor scales other than 1 (index query, query, index keys, K and V all different)
 SMALL += [(w, m, True) for w, m in [
