@@ -28,11 +28,12 @@ namespace msa {
 // current unit is contracted, so memory and math overlap inside the wave;
 // those loads are unconditional (past the last unit a wave re-reads its last
 // unit, which hits in cache) so that every wait covers exactly one unit.
-// The MFMA rows are 4 tokens x 4 groups per row tile; NT = 2 tiles (T = 5..8)
-// contract each decoded key tile twice, so the dequantisation is shared by all
-// T tokens and the scan stays bound by the page reads.  sigma > 0 is applied to the pooled
-// maximum only: fl(sigma*x) is monotone in x, so this equals the maximum of
-// the scaled scores.
+// A key tile is the MFMAs' first operand and a row tile of 16 query rows
+// (4 tokens x 4 groups) their second; NT = 2 row tiles (T = 5..8) contract
+// each decoded key tile twice, so the dequantisation is shared by all T
+// tokens and the scan stays bound by the page reads.  sigma > 0 is applied
+// to the pooled maximum only: fl(sigma*x) is monotone in x, so this equals
+// the maximum of the scaled scores.
 constexpr int kDecPagesPerWave = 8;
 constexpr int kDecTpu = 4;          // 16-key units per NVFP4 lane load (half for FP8)
 constexpr bool kDecPipe = true;     // next unit loaded while the current one is contracted
